@@ -1,0 +1,401 @@
+"""Float64 CPU oracle for S4R-style low-rank compressed-KV attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product: only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  It shares no code with the HIP path and imports
+nothing from it.
+
+Source of the method: the machine review of "S^4R: Selective Sampling,
+Subspaces, and Sparse Reconstruction for Compressed Long-Context KV Caching"
+(pith.science/paper/2608.00528, arXiv 2608.00528).  The review prints one
+formula (the latent score Z = C_Q C_K^T / sqrt(r), 'Referee Report', major
+comment 2, and 'Assumptions & free parameters') and describes the other steps
+in prose ('What carries the argument', 'Core claim', 'Referee Report' summary,
+'Assumptions & free parameters').  Each function below names the passage it
+follows.  Where the review is silent the plainest reading is taken and named
+in the docstring (readings R1..R14 are listed in the design notes).
+
+Everything is float64.  Inputs are read as stored (fp32 or bf16 values,
+widened).  ``rnd(x, storage)`` rounds to the storage type (round to nearest,
+ties to even) and is applied only where the method *stores* a tensor: the
+normalised SVD sample, the bases, the coefficient caches and the fp32 query
+window.  ``storage == "f64"`` disables rounding (used by the exactness pins).
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to something
+other than itself: exact-rank reconstruction, equality with full attention at
+r = D' and k >= |J|, the latent identity at r = D', library SVD, closed-form
+softmax cases, score invariants, pure-Python brute force on tiny inputs,
+sampling counts and the closed-form memory ratio.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+STORAGES = ("f64", "f32", "bf16")
+
+
+# --------------------------------------------------------------------------- #
+# rounding to the storage type
+# --------------------------------------------------------------------------- #
+def rnd(x, storage: str) -> np.ndarray:
+    """Round float64 values to the storage type and widen back to float64.
+
+    bf16 keeps 8 significant bits (1 implicit + 7 stored); the rounding is to
+    nearest with ties to even, done on the float64 value directly so there is
+    no double rounding through fp32.  Values outside the normal bf16 range are
+    not produced by the workloads and are not treated specially.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if storage == "f64":
+        return x.copy()
+    if storage == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if storage == "bf16":
+        m, e = np.frexp(x)  # x = m * 2**e, 0.5 <= |m| < 1
+        q = np.rint(m * 256.0)  # 8 significant bits, ties to even
+        return np.ldexp(q / 256.0, e)
+    raise ValueError(f"unknown storage {storage!r}")
+
+
+# --------------------------------------------------------------------------- #
+# prefill: sinks, sampling, normalisation, bases, projection
+# --------------------------------------------------------------------------- #
+def sample_positions(L: int, n_sink: int, n_sample: int,
+                     recent_num: int = 7, recent_den: int = 10) -> np.ndarray:
+    """Positions of the SVD sample ('Core claim': T' << T non-sink tokens,
+    split 7:3 between recent and uniformly spaced positions; 'Load-bearing
+    premise' and 'Assumptions & free parameters' name the 7:3 split).
+
+    Reading R2: the recent share is floor(7 T'/10) positions ending at the
+    last prompt token; the rest are evenly spaced (no RNG) over the
+    non-sink, non-recent range [s, L - n_r).  Returned in that order
+    (uniform part first, then recent), all distinct.
+    """
+    n_r = (recent_num * n_sample) // recent_den
+    n_u = n_sample - n_r
+    span = L - n_r - n_sink
+    if n_sample < 0 or n_r > L - n_sink or span < n_u:
+        raise ValueError("sample does not fit in the non-sink prompt")
+    uniform = n_sink + (np.arange(n_u, dtype=np.int64) * span) // max(n_u, 1)
+    recent = np.arange(L - n_r, L, dtype=np.int64)
+    return np.concatenate([uniform[:n_u], recent])
+
+
+def normalize_rows(Y: np.ndarray) -> np.ndarray:
+    """Token-wise normalisation of the sampled states ('What carries the
+    argument': the SVD is taken over a sampled, token-wise-normalised
+    subset).  Each row is divided by its Euclidean norm; zero rows stay 0."""
+    Y = np.asarray(Y, dtype=np.float64)
+    n = np.sqrt(np.sum(Y * Y, axis=1, keepdims=True))
+    out = np.zeros_like(Y)
+    nz = n[:, 0] > 0
+    out[nz] = Y[nz] / n[nz]
+    return out
+
+
+def gram(S: np.ndarray) -> np.ndarray:
+    """A = S^T S; its eigenvectors are the right singular vectors of S
+    (Eqs. 1-2 as summarised in 'What carries the argument')."""
+    S = np.asarray(S, dtype=np.float64)
+    return S.T @ S
+
+
+def eig_desc(A: np.ndarray):
+    """Eigenpairs of the symmetric matrix A, eigenvalues descending."""
+    lam, U = np.linalg.eigh(np.asarray(A, dtype=np.float64))
+    order = np.argsort(-lam, kind="stable")
+    return lam[order], U[:, order]
+
+
+def build_basis(X: np.ndarray, n_sink: int, n_sample: int, rank: int,
+                storage: str, recent_num: int = 7, recent_den: int = 10):
+    """Basis B (D' x r) of one state matrix X (L x D') of one layer and one
+    sequence ('What carries the argument': truncated SVD over the sampled,
+    normalised non-sink states; the top-r right singular vectors are B).
+
+    Returns (B, eigenvalues descending, S, positions).  S is the stored
+    (rounded) normalised sample; B is rounded to the storage type.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    L = X.shape[0]
+    pos = sample_positions(L, n_sink, n_sample, recent_num, recent_den)
+    S = rnd(normalize_rows(X[pos]), storage)
+    lam, U = eig_desc(gram(S))
+    B = rnd(U[:, :rank], storage)
+    return B, lam, S, pos
+
+
+def project(X: np.ndarray, B: np.ndarray, storage: str) -> np.ndarray:
+    """Coefficients c = x . B of every row of X (Eq. 3 as summarised in 'What
+    carries the argument': every non-sink token is stored as c = s.B).
+    Reading R1: the stored rows are projected raw (no normalisation)."""
+    return rnd(np.asarray(X, np.float64) @ np.asarray(B, np.float64), storage)
+
+
+# --------------------------------------------------------------------------- #
+# decode
+# --------------------------------------------------------------------------- #
+def query_concat(q: np.ndarray, n_kv_heads: int) -> np.ndarray:
+    """Latent-query inputs (reading R5): with G = H_q / H_kv, vector g is the
+    concatenation over KV heads h of query head h*G + g, so that its dot
+    product with a concatenated key sums the G-th member's per-head logits.
+    q: [H_q][d_h] -> [G][D']."""
+    q = np.asarray(q, np.float64)
+    H_q, d_h = q.shape
+    G = H_q // n_kv_heads
+    return q.reshape(n_kv_heads, G, d_h).transpose(1, 0, 2).reshape(G, n_kv_heads * d_h)
+
+
+def latent_scores(CK_J: np.ndarray, rows: np.ndarray, rank: int) -> np.ndarray:
+    """Latent relevance score of every candidate ('Referee Report' major
+    comment 2: Z = C_Q C_K^T / sqrt(r); 'What carries the argument': softmax
+    attention between the window of query coefficients and the cached key
+    coefficients, Eqs. 8-10).
+
+    rows: the W_eff*G query-coefficient rows; CK_J: the candidates' key
+    coefficients.  Each row's softmax runs over the candidates (reading R4),
+    and the per-candidate score is the sum of the rows' probabilities
+    (reading R6).  Returns score[|J|]."""
+    CK_J = np.asarray(CK_J, np.float64)
+    rows = np.asarray(rows, np.float64)
+    if CK_J.shape[0] == 0 or rows.shape[0] == 0:
+        return np.zeros(CK_J.shape[0])
+    Z = rows @ CK_J.T / math.sqrt(rank)
+    Z = Z - Z.max(axis=1, keepdims=True)
+    P = np.exp(Z)
+    P /= P.sum(axis=1, keepdims=True)
+    return P.sum(axis=0)
+
+
+def max_pool(score: np.ndarray, kappa: int) -> np.ndarray:
+    """Pooling of the scores before selection ('Assumptions & free
+    parameters': pooling kernel 7, taken from SnapKV).  Reading R7: max
+    pooling, stride 1, window clipped at the candidate edges; kappa = 1 is
+    the identity."""
+    score = np.asarray(score, np.float64)
+    if kappa % 2 != 1:
+        raise ValueError("pool width must be odd")
+    h = kappa // 2
+    n = score.shape[0]
+    out = score.copy()
+    for d in range(1, h + 1):
+        if d >= n:
+            break
+        out[:-d] = np.maximum(out[:-d], score[d:])
+        out[d:] = np.maximum(out[d:], score[:-d])
+    return out
+
+
+def select_topk(pooled: np.ndarray, k: int) -> np.ndarray:
+    """Top-k candidate selection ('Core claim': only the local window plus
+    the top-k global positions are reconstructed; Eqs. 13-15).  Reading R8:
+    larger score first, equal scores -> lower index first; the first
+    min(k, n) are returned in ascending index order."""
+    pooled = np.asarray(pooled, np.float64)
+    n = pooled.shape[0]
+    kk = min(max(k, 0), n)
+    order = np.lexsort((np.arange(n), -pooled))  # primary -pooled, then index
+    return np.sort(order[:kk])
+
+
+def softmax_attention(qh: np.ndarray, Kh: np.ndarray, Vh: np.ndarray) -> np.ndarray:
+    """softmax(q K^T / sqrt(d_h)) V for one query head (exact attention,
+    Eqs. 16-18; reading R10 for the 1/sqrt(d_h) scale)."""
+    qh = np.asarray(qh, np.float64)
+    logits = np.asarray(Kh, np.float64) @ qh / math.sqrt(qh.shape[0])
+    logits -= logits.max()
+    p = np.exp(logits)
+    p /= p.sum()
+    return p @ np.asarray(Vh, np.float64)
+
+
+def sparse_attention(q, keys_exact, values_exact, CK_sel, CV_sel, BK, BV,
+                     n_kv_heads: int) -> np.ndarray:
+    """Sparse reconstruction then exact attention ('What carries the
+    argument': only the selected positions are rebuilt, Eq. 16, before exact
+    attention with the uncompressed sink tokens; the exact recent window is
+    reading R3).
+
+    keys_exact/values_exact: [n_exact][D'] uncompressed rows (sinks + recent
+    ring); CK_sel/CV_sel: [k][r] coefficients of the selected positions.
+    Query head a uses KV head a // G (reading R11).  Returns [H_q][d_h]."""
+    q = np.asarray(q, np.float64)
+    H_q, d_h = q.shape
+    G = H_q // n_kv_heads
+    K_hat = np.asarray(CK_sel, np.float64) @ np.asarray(BK, np.float64).T
+    V_hat = np.asarray(CV_sel, np.float64) @ np.asarray(BV, np.float64).T
+    keys = np.concatenate([np.asarray(keys_exact, np.float64), K_hat], axis=0)
+    vals = np.concatenate([np.asarray(values_exact, np.float64), V_hat], axis=0)
+    out = np.zeros((H_q, d_h))
+    for a in range(H_q):
+        h = a // G
+        sl = slice(h * d_h, (h + 1) * d_h)
+        out[a] = softmax_attention(q[a], keys[:, sl], vals[:, sl])
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# the persistent compressed cache of one (layer, sequence)
+# --------------------------------------------------------------------------- #
+@dataclass
+class Cache:
+    """Per-(layer, sequence) state ('What carries the argument': sinks kept
+    exact, every other token as coefficients; 'If this is right': persistent
+    size about r/D' of the full cache).
+
+    Coefficient rows are indexed by absolute position (rows < n_sink unused).
+    The recent ring holds the last n_recent tokens exactly; slot = pos mod
+    n_recent.  qwin holds the last W query-coefficient blocks; slot = step
+    mod W."""
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    rank: int
+    n_sink: int
+    q_window: int
+    top_k: int
+    n_recent: int
+    pool_kernel: int
+    storage: str
+    sink_k: np.ndarray
+    sink_v: np.ndarray
+    ring_k: np.ndarray
+    ring_v: np.ndarray
+    CK: np.ndarray
+    CV: np.ndarray
+    BK: np.ndarray
+    BV: np.ndarray
+    qwin: np.ndarray
+    L: int
+    steps: int = 0
+    last: dict = field(default_factory=dict)
+
+    @property
+    def G(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    def window_rows(self) -> np.ndarray:
+        """The W_eff * G valid query-coefficient rows (reading R9: the window
+        starts empty and includes the current query)."""
+        w_eff = min(self.steps, self.q_window)
+        slots = [(self.steps - 1 - i) % self.q_window for i in range(w_eff)]
+        if not slots:
+            return np.zeros((0, self.rank))
+        return np.concatenate([self.qwin[s] for s in slots], axis=0)
+
+    def candidates(self) -> np.ndarray:
+        """Compressed candidate positions J = [s, L_t - n_recent)."""
+        return np.arange(self.n_sink, max(self.L - self.n_recent, self.n_sink))
+
+
+def prefill(K: np.ndarray, V: np.ndarray, *, n_q_heads: int, n_kv_heads: int,
+            head_dim: int, rank: int, n_sink: int, n_sample: int, q_window: int,
+            top_k: int, n_recent: int, pool_kernel: int, storage: str,
+            L_max: int | None = None, recent_num: int = 7, recent_den: int = 10):
+    """Prefill of one (layer, sequence): sinks and recent ring kept exact,
+    bases from the sample, coefficients of every row in [s, L).
+    K, V: [L][D'] as stored.  Returns (Cache, info)."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    L, Dp = K.shape
+    if Dp != n_kv_heads * head_dim:
+        raise ValueError("D' must equal n_kv_heads * head_dim")
+    if L < n_sink + n_recent:
+        raise ValueError("prompt shorter than sinks + recent window")
+    L_max = L if L_max is None else L_max
+    BK, lamK, SK, pos = build_basis(K, n_sink, n_sample, rank, storage, recent_num, recent_den)
+    BV, lamV, SV, _ = build_basis(V, n_sink, n_sample, rank, storage, recent_num, recent_den)
+    CK = np.zeros((L_max, rank))
+    CV = np.zeros((L_max, rank))
+    CK[n_sink:L] = project(K[n_sink:L], BK, storage)
+    CV[n_sink:L] = project(V[n_sink:L], BV, storage)
+    ring_k = np.zeros((n_recent, Dp))
+    ring_v = np.zeros((n_recent, Dp))
+    for p in range(L - n_recent, L):
+        ring_k[p % n_recent] = K[p]
+        ring_v[p % n_recent] = V[p]
+    G = n_q_heads // n_kv_heads
+    cache = Cache(n_q_heads, n_kv_heads, head_dim, rank, n_sink, q_window, top_k,
+                  n_recent, pool_kernel, storage, K[:n_sink].copy(), V[:n_sink].copy(),
+                  ring_k, ring_v, CK, CV, BK, BV, np.zeros((q_window, G, rank)), L, 0)
+    info = dict(lam_k=lamK, lam_v=lamV, S_k=SK, S_v=SV, positions=pos)
+    return cache, info
+
+
+def decode_append(cache: Cache, q, k_new, v_new):
+    """First stage of a decode step: store the new token and its query.
+
+    The new token's key/value coefficients are appended (Eq. 3 applied to the
+    new token), its exact key/value enter the recent ring (evicting the
+    oldest, which then becomes a compressed candidate), and the queries are
+    projected into the key subspace ('Core claim': queries are projected into
+    the key subspace) and pushed into the query-coefficient window ('What
+    carries the argument': sliding window of query coefficients).
+    Mutates cache; returns the new query-coefficient block [G][r]."""
+    k_cat = np.asarray(k_new, np.float64).reshape(-1)
+    v_cat = np.asarray(v_new, np.float64).reshape(-1)
+    p = cache.L
+    if p >= cache.CK.shape[0]:
+        raise ValueError("coefficient cache is full")
+    cache.CK[p] = rnd(k_cat @ cache.BK, cache.storage)
+    cache.CV[p] = rnd(v_cat @ cache.BV, cache.storage)
+    cache.ring_k[p % cache.n_recent] = k_cat
+    cache.ring_v[p % cache.n_recent] = v_cat
+    cache.L = p + 1
+    cq = rnd(query_concat(q, cache.n_kv_heads) @ cache.BK, "f32")  # fp32 window
+    cache.qwin[cache.steps % cache.q_window] = cq
+    cache.steps += 1
+    return cq
+
+
+def decode_select(cache: Cache):
+    """Latent scoring, pooling and top-k over the current candidates.
+    Returns (positions selected ascending, score, pooled)."""
+    J = cache.candidates()
+    score = latent_scores(cache.CK[J], cache.window_rows(), cache.rank)
+    pooled = max_pool(score, cache.pool_kernel)
+    sel = select_topk(pooled, cache.top_k)
+    return J[sel], score, pooled
+
+
+def decode_attend(cache: Cache, q, positions) -> np.ndarray:
+    """Reconstruction of the selected positions and exact attention over
+    sinks + recent ring + reconstructed rows."""
+    positions = np.asarray(positions, dtype=np.int64)
+    keys_exact = np.concatenate([cache.sink_k, cache.ring_k], axis=0)
+    vals_exact = np.concatenate([cache.sink_v, cache.ring_v], axis=0)
+    return sparse_attention(q, keys_exact, vals_exact, cache.CK[positions],
+                            cache.CV[positions], cache.BK, cache.BV, cache.n_kv_heads)
+
+
+def decode_step(cache: Cache, q, k_new, v_new) -> np.ndarray:
+    """One decode step for one (layer, sequence) (the three stages the
+    'Referee Report' summary lists: window of query coefficients and latent
+    scoring, selection of local window plus top-k, reconstruction and exact
+    attention).  q: [H_q][d_h], k_new/v_new: [H_kv][d_h].  Returns
+    out [H_q][d_h]; cache.last holds positions, score and pooled."""
+    decode_append(cache, q, k_new, v_new)
+    positions, score, pooled = decode_select(cache)
+    out = decode_attend(cache, q, positions)
+    cache.last = dict(positions=positions, score=score, pooled=pooled)
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# accounting
+# --------------------------------------------------------------------------- #
+def persistent_bytes(L: int, D: int, rank: int, n_sink: int, n_recent: int,
+                     elem_bytes: int) -> int:
+    """Persistent cache bytes of one layer and sequence for K and V: exact
+    sinks + exact recent ring + coefficients of the other tokens + bases
+    ('If this is right': the persistent cache per layer tends to r/D' of the
+    full cache for long contexts; memory analysis Eqs. 19-24)."""
+    n_coef = max(L - n_sink, 0)
+    return 2 * elem_bytes * ((n_sink + n_recent) * D + n_coef * rank + D * rank)
+
+
+def full_cache_bytes(L: int, D: int, elem_bytes: int) -> int:
+    return 2 * elem_bytes * L * D
