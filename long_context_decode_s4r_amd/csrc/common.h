@@ -1,0 +1,131 @@
+// Internal helpers shared by the kvlr HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace kvlr {
+
+// ---- vector types used by the bf16 MFMA builtins ---------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 <-> fp32 (storage type for bf16 is uint16_t) ----------------------
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// round to nearest, ties to even; NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// storage element access, T = float (fp32) or uint16_t (bf16)
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p, size_t i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ void st(uint16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+};
+
+// 8 consecutive bf16 (16 bytes, 16-byte aligned) as an MFMA operand
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  u16x8 v = *reinterpret_cast<const u16x8*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (M index) held by accumulator register i of lane l for the 32x32 MFMA
+// result; the column (N index) is l % 32.
+__device__ __forceinline__ int acc_row32(int i, int l) { return 8 * (i >> 2) + 4 * (l >> 5) + (i & 3); }
+
+__device__ __forceinline__ float warp_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace kvlr
+
+// ---- launchers (defined in prefill.hip / decode.hip, called by api.hip) ------
+namespace kvlr {
+
+struct Dims {
+  int Hq, Hkv, dh, D, r, G, s, T, rnum, rden, W, k, nrec, kappa, dtype;
+};
+
+// prefill
+hipError_t launch_sample_normalize(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                                   void* S, hipStream_t st);
+hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm,
+                       hipStream_t st);
+hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_dst,
+                               const double* V_src, double* V_dst, const int* frozen,
+                               hipStream_t st);
+hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
+                               int* final_buf, int cur, int* n_active, double tol,
+                               hipStream_t st);
+hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
+                          const double* V0, const double* V1, const int* frozen,
+                          const int* final_buf, int cur, void* basis_k, void* basis_v,
+                          float* eig_k, float* eig_v, hipStream_t st);
+hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
+                          const void* V, const void* BK, const void* BV, void* CK, void* CV,
+                          hipStream_t st);
+hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                                  void* sink_k, void* sink_v, void* ring_k, void* ring_v,
+                                  float* qwin, float* rowstat, int32_t* lens, hipStream_t st);
+
+// decode
+struct DecodeWs {
+  int32_t* stepinfo;  // [U][4]
+  float* partial;     // [U][Lc_cap]
+  float* spill;       // [U][G][Lc_cap]
+  float* tilestat;    // [U][nsplit][G][2]
+  float* score;       // [U][Lc_cap]
+  uint32_t* keys;     // [U][Lc_cap]
+  int32_t* topk;      // [U][k]
+  float* part;        // [U][Hq][nsa][dh + 2]
+  int Lc_cap, nsplit, chunk, nsa;
+};
+
+struct CachePtrs {
+  void *sink_k, *sink_v, *ring_k, *ring_v, *coef_k, *coef_v, *basis_k, *basis_v;
+  float* qwin;
+  float* rowstat;
+  int32_t* lens;
+  int64_t Lmax;
+};
+
+hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_new,
+                           const void* v_new, const CachePtrs& c, const DecodeWs& w,
+                           hipStream_t st);
+hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                        hipStream_t st);
+hipError_t launch_select(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                         int32_t* topk_user, float* scores_user, hipStream_t st);
+hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
+                         const DecodeWs& w, hipStream_t st);
+hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
+                        hipStream_t st);
+
+// decode tiling decisions shared by the workspace sizing and the launches
+void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, int* Lc_cap, int* nsplit, int* chunk,
+                   int* nsa);
+
+}  // namespace kvlr

@@ -1,0 +1,597 @@
+// Prefill kernels: sample + token-wise normalisation, Gram matrix S^T S,
+// parallel cyclic Jacobi eigensolver, top-r basis extraction, projection of
+// every non-sink token onto the bases, exact sink / recent-window copies.
+//
+// Method: S^4R review (pith.science/paper/2608.00528), 'What carries the
+// argument' (truncated SVD over a sampled, token-wise-normalised subset,
+// Eqs. 1-2; coefficients c = s.B, Eq. 3) and 'Core claim' (s sinks kept in
+// full precision, 7:3 recent-to-uniform sample of T' tokens).
+#include "common.h"
+
+#include <math.h>
+
+namespace kvlr {
+
+// --------------------------------------------------------------------------
+// 1. sample + normalise: S[m][i][:] = rnd(x_p / ||x_p||), m = 2u + (0 K | 1 V)
+//    sample position p(i): the first n_u entries are evenly spaced over
+//    [s, L - n_r), the last n_r are the most recent prompt positions.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ K,
+                                                          const T* __restrict__ V,
+                                                          T* __restrict__ S, int64_t L, int D,
+                                                          int nT, int s, int rnum, int rden) {
+  const int i = blockIdx.x;
+  const int m = blockIdx.y;
+  const int u = m >> 1;
+  const T* X = (m & 1) ? V : K;
+  const int64_t n_r = ((int64_t)rnum * nT) / rden;
+  const int64_t n_u = nT - n_r;
+  int64_t p;
+  if (i < n_u) {
+    const int64_t span = L - n_r - s;
+    p = s + ((int64_t)i * span) / n_u;
+  } else {
+    p = L - n_r + (i - n_u);
+  }
+  const T* row = X + ((int64_t)u * L + p) * D;
+  double ss = 0.0;
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    double x = (double)Elem<T>::ld(row, j);
+    ss += x * x;
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double tot = red[0];
+  const double inv = tot > 0.0 ? 1.0 / sqrt(tot) : 0.0;
+  T* out = S + ((int64_t)m * nT + i) * D;
+  for (int j = threadIdx.x; j < D; j += blockDim.x)
+    Elem<T>::st(out, j, (float)((double)Elem<T>::ld(row, j) * inv));
+}
+
+hipError_t launch_sample_normalize(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                                   void* S, hipStream_t st) {
+  dim3 grid(d.T, 2 * U);
+  if (d.dtype == 0)
+    hipLaunchKernelGGL(k_sample_normalize<float>, grid, dim3(256), 0, st, (const float*)K,
+                       (const float*)V, (float*)S, L, d.D, d.T, d.s, d.rnum, d.rden);
+  else
+    hipLaunchKernelGGL(k_sample_normalize<uint16_t>, grid, dim3(256), 0, st,
+                       (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)S, L, d.D, d.T, d.s,
+                       d.rnum, d.rden);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 2. Gram A = S^T S (fp64 out) and V = I
+// --------------------------------------------------------------------------
+// bf16: MFMA 32x32x16, fp32 accumulation; one 64x64 output tile per block,
+// upper-triangle tile pairs only, mirrored on store.
+__global__ __launch_bounds__(256) void k_gram_bf16(const uint16_t* __restrict__ S,
+                                                   double* __restrict__ A, int nT, int D,
+                                                   int nt) {
+  const int m = blockIdx.y;
+  // tile pair index -> (ti, tj), ti <= tj
+  int idx = blockIdx.x, ti = 0;
+  while (idx >= nt - ti) {
+    idx -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + idx;
+  __shared__ uint16_t Si[32][72];
+  __shared__ uint16_t Sj[32][72];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int wi = w >> 1, wj = w & 1;
+  const uint16_t* Sm = S + (int64_t)m * nT * D;
+  f32x16 acc = {};
+  const int lr = tid >> 3, cg = tid & 7;
+  for (int t0 = 0; t0 < nT; t0 += 32) {
+    {
+      const int t = t0 + lr;
+      const int ci = ti * 64 + 8 * cg, cj = tj * 64 + 8 * cg;
+      u16x8 vi = {}, vj = {};
+      if (t < nT && ci < D) vi = *reinterpret_cast<const u16x8*>(Sm + (int64_t)t * D + ci);
+      if (t < nT && cj < D) vj = *reinterpret_cast<const u16x8*>(Sm + (int64_t)t * D + cj);
+      *reinterpret_cast<u16x8*>(&Si[lr][8 * cg]) = vi;
+      *reinterpret_cast<u16x8*>(&Sj[lr][8 * cg]) = vj;
+    }
+    __syncthreads();
+    const int mm = l & 31, kg = l >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 16) {
+      u16x8 a, b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = Si[kk + 8 * kg + e][32 * wi + mm];
+        b[e] = Sj[kk + 8 * kg + e][32 * wj + mm];
+      }
+      acc = mfma32x32x16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc);
+    }
+    __syncthreads();
+  }
+  double* Am = A + (int64_t)m * D * D;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = ti * 64 + 32 * wi + acc_row32(i, l);
+    const int col = tj * 64 + 32 * wj + (l & 31);
+    if (row < D && col < D) {
+      Am[(int64_t)row * D + col] = (double)acc[i];
+      if (ti != tj) Am[(int64_t)col * D + row] = (double)acc[i];
+    }
+  }
+}
+
+// fp32: plain fp64 accumulation, one output entry per thread
+__global__ __launch_bounds__(256) void k_gram_f32(const float* __restrict__ S,
+                                                  double* __restrict__ A, int nT, int D) {
+  const int m = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)D * D) return;
+  const int i = (int)(e / D), j = (int)(e % D);
+  const float* Sm = S + (int64_t)m * nT * D;
+  double acc = 0.0;
+  for (int t = 0; t < nT; ++t) acc += (double)Sm[(int64_t)t * D + i] * (double)Sm[(int64_t)t * D + j];
+  A[(int64_t)m * D * D + e] = acc;
+}
+
+__global__ void k_eye(double* __restrict__ Vm, int D) {
+  const int m = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)D * D) return;
+  Vm[(int64_t)m * D * D + e] = (e / D == e % D) ? 1.0 : 0.0;
+}
+
+hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm,
+                       hipStream_t st) {
+  const int D = d.D;
+  const int64_t n2 = (int64_t)D * D;
+  if (d.dtype == 0) {
+    hipLaunchKernelGGL(k_gram_f32, dim3((unsigned)((n2 + 255) / 256), nmat), dim3(256), 0, st,
+                       (const float*)S, A, d.T, D);
+  } else {
+    const int nt = (D + 63) / 64;
+    hipLaunchKernelGGL(k_gram_bf16, dim3(nt * (nt + 1) / 2, nmat), dim3(256), 0, st,
+                       (const uint16_t*)S, A, d.T, D, nt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_eye, dim3((unsigned)((n2 + 255) / 256), nmat), dim3(256), 0, st, Vm, D);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 3. parallel cyclic Jacobi (two-sided rotations, fp64).
+//
+// Storage is kept in "pair order": in every round the disjoint rotation pairs
+// are the slot pairs (2a, 2a+1).  After a round every slot's content moves to
+// dest(slot), the round-robin (circle) move that keeps slot 0 fixed and
+// rotates the other n-1 slots by one place, so n-1 consecutive rounds meet
+// every index pair once (one sweep).  A thread owns one 2x2 block, reads it
+// (and the two diagonal blocks that define its rotations) from the source
+// buffer and writes the rotated block to the permuted places of the
+// destination buffer; V accumulates the rotations with the same moves.
+// Rotation: textbook symmetric Schur 2x2 (Golub & Van Loan), zeroing A[p][q].
+// --------------------------------------------------------------------------
+__device__ __forceinline__ int jac_dest(int slot, int n) {
+  if (n <= 2 || slot == 0) return slot;
+  if (slot == 1) return 2;
+  const int k = slot >> 1;
+  if ((slot & 1) == 0) return (k <= (n >> 1) - 2) ? slot + 2 : n - 1;
+  return slot - 2;
+}
+
+__device__ __forceinline__ void jac_rot(const double* A, int n, int a, double* c, double* s,
+                                        double* t) {
+  const double app = A[(int64_t)(2 * a) * n + 2 * a];
+  const double aqq = A[(int64_t)(2 * a + 1) * n + 2 * a + 1];
+  const double apq = A[(int64_t)(2 * a) * n + 2 * a + 1];
+  if (apq == 0.0) {
+    *c = 1.0;
+    *s = 0.0;
+    *t = 0.0;
+    return;
+  }
+  const double tau = (aqq - app) / (2.0 * apq);
+  double tt;
+  if (fabs(tau) > 1e150) {
+    tt = 0.5 / tau;
+  } else {
+    tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+  }
+  const double cc = 1.0 / sqrt(1.0 + tt * tt);
+  *c = cc;
+  *s = tt * cc;
+  *t = tt;
+}
+
+__global__ __launch_bounds__(256) void k_jacobi_round(const double* __restrict__ Asrc,
+                                                      double* __restrict__ Adst,
+                                                      const double* __restrict__ Vsrc,
+                                                      double* __restrict__ Vdst,
+                                                      const int* __restrict__ frozen, int n) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  const int h = n >> 1;
+  const int64_t nA = (int64_t)h * h, nV = (int64_t)n * h;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nA + nV) return;
+  const int64_t off = (int64_t)m * n * n;
+  const double* A = Asrc + off;
+  if (t < nA) {
+    const int a = (int)(t / h), b = (int)(t % h);
+    double ca, sa, ta, cb, sb, tb;
+    jac_rot(A, n, a, &ca, &sa, &ta);
+    double* Ad = Adst + off;
+    const int pa = jac_dest(2 * a, n), qa = jac_dest(2 * a + 1, n);
+    if (a == b) {
+      const double app = A[(int64_t)(2 * a) * n + 2 * a];
+      const double aqq = A[(int64_t)(2 * a + 1) * n + 2 * a + 1];
+      const double apq = A[(int64_t)(2 * a) * n + 2 * a + 1];
+      Ad[(int64_t)pa * n + pa] = app - ta * apq;
+      Ad[(int64_t)qa * n + qa] = aqq + ta * apq;
+      Ad[(int64_t)pa * n + qa] = 0.0;
+      Ad[(int64_t)qa * n + pa] = 0.0;
+      return;
+    }
+    jac_rot(A, n, b, &cb, &sb, &tb);
+    const double m00 = A[(int64_t)(2 * a) * n + 2 * b], m01 = A[(int64_t)(2 * a) * n + 2 * b + 1];
+    const double m10 = A[(int64_t)(2 * a + 1) * n + 2 * b],
+                 m11 = A[(int64_t)(2 * a + 1) * n + 2 * b + 1];
+    // rows: J_a^T M
+    const double r00 = ca * m00 - sa * m10, r01 = ca * m01 - sa * m11;
+    const double r10 = sa * m00 + ca * m10, r11 = sa * m01 + ca * m11;
+    // columns: (J_a^T M) J_b
+    const double n00 = cb * r00 - sb * r01, n01 = sb * r00 + cb * r01;
+    const double n10 = cb * r10 - sb * r11, n11 = sb * r10 + cb * r11;
+    const int pb = jac_dest(2 * b, n), qb = jac_dest(2 * b + 1, n);
+    Ad[(int64_t)pa * n + pb] = n00;
+    Ad[(int64_t)pa * n + qb] = n01;
+    Ad[(int64_t)qa * n + pb] = n10;
+    Ad[(int64_t)qa * n + qb] = n11;
+  } else {
+    const int64_t tv = t - nA;
+    const int i = (int)(tv / h), b = (int)(tv % h);
+    double cb, sb, tb;
+    jac_rot(A, n, b, &cb, &sb, &tb);
+    const double* Vr = Vsrc + off + (int64_t)i * n;
+    const double v0 = Vr[2 * b], v1 = Vr[2 * b + 1];
+    double* Vd = Vdst + off + (int64_t)i * n;
+    Vd[jac_dest(2 * b, n)] = cb * v0 - sb * v1;
+    Vd[jac_dest(2 * b + 1, n)] = sb * v0 + cb * v1;
+  }
+}
+
+hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_dst,
+                               const double* V_src, double* V_dst, const int* frozen,
+                               hipStream_t st) {
+  const int64_t h = n / 2;
+  const int64_t tot = h * h + (int64_t)n * h;
+  hipLaunchKernelGGL(k_jacobi_round, dim3((unsigned)((tot + 255) / 256), nmat), dim3(256), 0, st,
+                     A_src, A_dst, V_src, V_dst, frozen, n);
+  return hipGetLastError();
+}
+
+// convergence test: off(A)_F <= tol * trace(A); partial sums per row chunk,
+// then one thread per matrix sums them in a fixed order
+constexpr int kJacRowsPerBlock = 16;
+
+__global__ __launch_bounds__(256) void k_offnorm(const double* __restrict__ A,
+                                                 const int* __restrict__ frozen,
+                                                 double* __restrict__ part, int n, int nchunk) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  const double* Am = A + (int64_t)m * n * n;
+  const int r0 = blockIdx.x * kJacRowsPerBlock;
+  double off = 0.0, tr = 0.0;
+  for (int r = r0; r < min(r0 + kJacRowsPerBlock, n); ++r) {
+    for (int c = threadIdx.x; c < n; c += blockDim.x) {
+      const double x = Am[(int64_t)r * n + c];
+      if (c == r)
+        tr += x;
+      else
+        off += x * x;
+    }
+  }
+  __shared__ double so[256], st[256];
+  so[threadIdx.x] = off;
+  st[threadIdx.x] = tr;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      so[threadIdx.x] += so[threadIdx.x + o];
+      st[threadIdx.x] += st[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    part[((int64_t)m * nchunk + blockIdx.x) * 2 + 0] = so[0];
+    part[((int64_t)m * nchunk + blockIdx.x) * 2 + 1] = st[0];
+  }
+}
+
+__global__ void k_jacobi_check(const double* __restrict__ part, int* __restrict__ frozen,
+                               int* __restrict__ final_buf, int* __restrict__ n_active, int nmat,
+                               int nchunk, int cur, double tol) {
+  __shared__ int cnt;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  for (int m = threadIdx.x; m < nmat; m += blockDim.x) {
+    if (frozen[m]) continue;
+    double off = 0.0, tr = 0.0;
+    for (int c = 0; c < nchunk; ++c) {
+      off += part[((int64_t)m * nchunk + c) * 2 + 0];
+      tr += part[((int64_t)m * nchunk + c) * 2 + 1];
+    }
+    if (sqrt(off) <= tol * fabs(tr) || off == 0.0) {
+      frozen[m] = 1;
+      final_buf[m] = cur;
+    } else {
+      atomicAdd(&cnt, 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *n_active = cnt;
+}
+
+hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
+                               int* final_buf, int cur, int* n_active, double tol,
+                               hipStream_t st) {
+  const int nchunk = (n + kJacRowsPerBlock - 1) / kJacRowsPerBlock;
+  hipLaunchKernelGGL(k_offnorm, dim3(nchunk, nmat), dim3(256), 0, st, A, frozen, part, n, nchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_jacobi_check, dim3(1), dim3(256), 0, st, part, frozen, final_buf, n_active,
+                     nmat, nchunk, cur, tol);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 4. eigenvalues descending (bitonic sort of (lambda, slot) in LDS), basis =
+//    the first r eigenvector columns, rounded to storage.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
+                                                  const double* __restrict__ A1,
+                                                  const double* __restrict__ V0,
+                                                  const double* __restrict__ V1,
+                                                  const int* __restrict__ frozen,
+                                                  const int* __restrict__ final_buf, int cur,
+                                                  int n, int r, T* __restrict__ BK,
+                                                  T* __restrict__ BV, float* __restrict__ eigK,
+                                                  float* __restrict__ eigV) {
+  extern __shared__ unsigned char smem_raw[];
+  const int m = blockIdx.x, u = m >> 1, kind = m & 1;
+  const int buf = frozen[m] ? final_buf[m] : cur;
+  const double* A = (buf ? A1 : A0) + (int64_t)m * n * n;
+  const double* Vm = (buf ? V1 : V0) + (int64_t)m * n * n;
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  double* key = reinterpret_cast<double*>(smem_raw);
+  int* idx = reinterpret_cast<int*>(key + np2);
+  for (int i = threadIdx.x; i < np2; i += blockDim.x) {
+    key[i] = i < n ? A[(int64_t)i * n + i] : -INFINITY;
+    idx[i] = i;
+  }
+  __syncthreads();
+  // sort descending by key, ties by ascending slot
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < np2; i += blockDim.x) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const double ki = key[i], kj = key[j];
+          const int ii = idx[i], ij = idx[j];
+          // "i before j" in descending order with ascending tie-break
+          const bool i_first = (ki > kj) || (ki == kj && ii < ij);
+          if (i_first != desc) {
+            key[i] = kj;
+            key[j] = ki;
+            idx[i] = ij;
+            idx[j] = ii;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  float* eig = kind ? eigV : eigK;
+  if (eig)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) eig[(int64_t)u * n + i] = (float)key[i];
+  T* B = (kind ? BV : BK) + (int64_t)u * n * r;
+  for (int64_t e = threadIdx.x; e < (int64_t)n * r; e += blockDim.x) {
+    const int i = (int)(e / r), c = (int)(e % r);
+    Elem<T>::st(B, e, (float)Vm[(int64_t)i * n + idx[c]]);
+  }
+}
+
+hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
+                          const double* V0, const double* V1, const int* frozen,
+                          const int* final_buf, int cur, void* basis_k, void* basis_v,
+                          float* eig_k, float* eig_v, hipStream_t st) {
+  int np2 = 1;
+  while (np2 < d.D) np2 <<= 1;
+  const size_t lds = (size_t)np2 * (sizeof(double) + sizeof(int));
+  if (d.dtype == 0)
+    hipLaunchKernelGGL(k_extract<float>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
+                       final_buf, cur, d.D, d.r, (float*)basis_k, (float*)basis_v, eig_k, eig_v);
+  else
+    hipLaunchKernelGGL(k_extract<uint16_t>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
+                       frozen, final_buf, cur, d.D, d.r, (uint16_t*)basis_k, (uint16_t*)basis_v,
+                       eig_k, eig_v);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 5. projection C[j] = rnd(X[j] . B) for j in [s, L)
+// --------------------------------------------------------------------------
+// bf16: block = 64 rows x all r columns (r % 32 == 0, r <= 256), K-loop over
+// D' in chunks of 32 staged through LDS; MFMA 32x32x16, fp32 accumulation.
+__global__ __launch_bounds__(256) void k_project_bf16(const uint16_t* __restrict__ K,
+                                                      const uint16_t* __restrict__ V,
+                                                      const uint16_t* __restrict__ BK,
+                                                      const uint16_t* __restrict__ BV,
+                                                      uint16_t* __restrict__ CK,
+                                                      uint16_t* __restrict__ CV, int64_t L,
+                                                      int64_t Lmax, int D, int r, int s) {
+  const int u = blockIdx.y >> 1, kind = blockIdx.y & 1;
+  const uint16_t* X = (kind ? V : K) + (int64_t)u * L * D;
+  const uint16_t* B = (kind ? BV : BK) + (int64_t)u * D * r;
+  uint16_t* C = (kind ? CV : CK) + (int64_t)u * Lmax * r;
+  const int64_t row0 = s + (int64_t)blockIdx.x * 64;
+  __shared__ uint16_t Xs[64][40];
+  __shared__ uint16_t Bt[256][40];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int ntile = 2 * (r / 32);  // (row block, col block) pairs
+  f32x16 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x16{};
+  for (int k0 = 0; k0 < D; k0 += 32) {
+    {  // X tile: 64 rows x 32 cols, one 16-byte group per thread
+      const int rr = tid >> 2, cg = tid & 3;
+      const int64_t row = row0 + rr;
+      u16x8 v = {};
+      if (row < L && k0 + 8 * cg < D) v = *reinterpret_cast<const u16x8*>(X + row * D + k0 + 8 * cg);
+      *reinterpret_cast<u16x8*>(&Xs[rr][8 * cg]) = v;
+    }
+    // B tile: 32 rows (k) x r cols, stored transposed
+    for (int g = tid; g < 32 * (r / 8); g += 256) {
+      const int kr = g / (r / 8), cg = g % (r / 8);
+      u16x8 v = {};
+      if (k0 + kr < D) v = *reinterpret_cast<const u16x8*>(B + (int64_t)(k0 + kr) * r + 8 * cg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Bt[8 * cg + e][kr] = v[e];
+    }
+    __syncthreads();
+    const int mm = l & 31, kg = l >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tile = w + 4 * q;
+      if (tile < ntile) {
+        const int rb = tile & 1, cb = tile >> 1;
+#pragma unroll
+        for (int kk = 0; kk < 32; kk += 16) {
+          bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Xs[32 * rb + mm][kk + 8 * kg]));
+          bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Bt[32 * cb + mm][kk + 8 * kg]));
+          acc[q] = mfma32x32x16(a, b, acc[q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int tile = w + 4 * q;
+    if (tile < ntile) {
+      const int rb = tile & 1, cb = tile >> 1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = row0 + 32 * rb + acc_row32(i, l);
+        const int col = 32 * cb + (l & 31);
+        if (row < L) C[row * r + col] = f2bf(acc[q][i]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K,
+                                                     const float* __restrict__ V,
+                                                     const float* __restrict__ BK,
+                                                     const float* __restrict__ BV,
+                                                     float* __restrict__ CK, float* __restrict__ CV,
+                                                     int64_t L, int64_t Lmax, int D, int r, int s) {
+  const int u = blockIdx.y >> 1, kind = blockIdx.y & 1;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nrow = L - s;
+  if (e >= nrow * r) return;
+  const int64_t row = s + e / r;
+  const int c = (int)(e % r);
+  const float* X = (kind ? V : K) + ((int64_t)u * L + row) * D;
+  const float* B = (kind ? BV : BK) + (int64_t)u * D * r;
+  double acc = 0.0;  // fp64 accumulation, rounded once to fp32
+  for (int k = 0; k < D; ++k) acc += (double)X[k] * (double)B[(int64_t)k * r + c];
+  (kind ? CV : CK)[((int64_t)u * Lmax + row) * r + c] = (float)acc;
+}
+
+hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
+                          const void* V, const void* BK, const void* BV, void* CK, void* CV,
+                          hipStream_t st) {
+  const int64_t nrow = L - d.s;
+  if (nrow <= 0) return hipSuccess;
+  if (d.dtype == 0) {
+    const int64_t tot = nrow * d.r;
+    hipLaunchKernelGGL(k_project_f32, dim3((unsigned)((tot + 255) / 256), 2 * U), dim3(256), 0, st,
+                       (const float*)K, (const float*)V, (const float*)BK, (const float*)BV,
+                       (float*)CK, (float*)CV, L, Lmax, d.D, d.r, d.s);
+  } else {
+    hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)((nrow + 63) / 64), 2 * U), dim3(256), 0,
+                       st, (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)BK,
+                       (const uint16_t*)BV, (uint16_t*)CK, (uint16_t*)CV, L, Lmax, d.D, d.r, d.s);
+  }
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 6. exact sinks + recent ring, window / statistics reset, lens = {L, 0}
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
+                                                     const T* __restrict__ V, T* __restrict__ sk,
+                                                     T* __restrict__ sv, T* __restrict__ rk,
+                                                     T* __restrict__ rv, float* __restrict__ qwin,
+                                                     float* __restrict__ rowstat,
+                                                     int32_t* __restrict__ lens, int64_t L, int D,
+                                                     int s, int nrec, int qw_per_unit,
+                                                     int rs_per_unit) {
+  const int u = blockIdx.y;
+  const int row = blockIdx.x;  // [0, s + nrec) exact rows, then one block for the reset
+  if (row < s) {
+    const T* src = K + ((int64_t)u * L + row) * D;
+    const T* srcv = V + ((int64_t)u * L + row) * D;
+    for (int j = threadIdx.x; j < D; j += blockDim.x) {
+      sk[((int64_t)u * s + row) * D + j] = src[j];
+      sv[((int64_t)u * s + row) * D + j] = srcv[j];
+    }
+  } else if (row < s + nrec) {
+    const int64_t p = L - nrec + (row - s);
+    const int slot = (int)(p % nrec);
+    const T* src = K + ((int64_t)u * L + p) * D;
+    const T* srcv = V + ((int64_t)u * L + p) * D;
+    for (int j = threadIdx.x; j < D; j += blockDim.x) {
+      rk[((int64_t)u * nrec + slot) * D + j] = src[j];
+      rv[((int64_t)u * nrec + slot) * D + j] = srcv[j];
+    }
+  } else {
+    for (int j = threadIdx.x; j < qw_per_unit; j += blockDim.x) qwin[(int64_t)u * qw_per_unit + j] = 0.f;
+    for (int j = threadIdx.x; j < rs_per_unit; j += blockDim.x) rowstat[(int64_t)u * rs_per_unit + j] = 0.f;
+    if (threadIdx.x == 0) {
+      lens[2 * u] = (int32_t)L;
+      lens[2 * u + 1] = 0;
+    }
+  }
+}
+
+hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                                  void* sink_k, void* sink_v, void* ring_k, void* ring_v,
+                                  float* qwin, float* rowstat, int32_t* lens, hipStream_t st) {
+  dim3 grid(d.s + d.nrec + 1, U);
+  const int qw = d.W * d.G * d.r, rs = d.W * d.G * 2;
+  if (d.dtype == 0)
+    hipLaunchKernelGGL(k_exact_reset<float>, grid, dim3(256), 0, st, (const float*)K,
+                       (const float*)V, (float*)sink_k, (float*)sink_v, (float*)ring_k,
+                       (float*)ring_v, qwin, rowstat, lens, L, d.D, d.s, d.nrec, qw, rs);
+  else
+    hipLaunchKernelGGL(k_exact_reset<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
+                       (const uint16_t*)V, (uint16_t*)sink_k, (uint16_t*)sink_v,
+                       (uint16_t*)ring_k, (uint16_t*)ring_v, qwin, rowstat, lens, L, d.D, d.s,
+                       d.nrec, qw, rs);
+  return hipGetLastError();
+}
+
+}  // namespace kvlr

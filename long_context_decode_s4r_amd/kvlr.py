@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libkvlr.so (include/kvlr.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors used as device memory; work goes on the
+current torch stream.  ``load()`` raises when the library has not been built
+(there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvlr.so")
+
+F32, BF16 = 0, 1
+OK, EINVAL, EWORKSPACE, EDEVICE, ELAUNCH = 0, 1, 2, 3, 4
+OP_BUILD_BASES, OP_PROJECT, OP_DECODE = 0, 1, 2
+BUFFERS = ("sink_k", "sink_v", "ring_k", "ring_v", "coef_k", "coef_v", "basis_k", "basis_v",
+           "qwin", "rowstat", "lens")
+STAGES = ("prologue", "score", "select", "attend", "merge")
+
+
+class KvlrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvlr status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_q_heads", "n_kv_heads", "head_dim", "rank", "n_sink", "n_sample",
+        "sample_recent_num", "sample_recent_den", "q_window", "top_k", "n_recent",
+        "pool_kernel", "dtype", "reserved")]
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS[:8]] + [
+        ("qwin", ctypes.c_void_p), ("rowstat", ctypes.c_void_p), ("lens", ctypes.c_void_p),
+        ("L_max", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load():
+    """Load libkvlr.so (built by long_context_decode_s4r_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i64, i32, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    cfgp, cachep = ctypes.POINTER(Config), ctypes.POINTER(CacheStruct)
+    sig = {
+        "kvlr_check_config": (i32, [cfgp]),
+        "kvlr_cache_bytes": (i32, [cfgp, i64, i64, ctypes.POINTER(sz)]),
+        "kvlr_workspace_bytes": (i32, [cfgp, i32, i64, i64, ctypes.POINTER(sz)]),
+        "kvlr_build_bases": (i32, [cfgp, i64, i64, P, P, cachep, P, P, P, sz, P]),
+        "kvlr_project": (i32, [cfgp, i64, i64, P, P, cachep, P, sz, P]),
+        "kvlr_decode_step": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P, sz, P]),
+        "kvlr_last_error": (ctypes.c_char_p, []),
+        "kvlr_abi_version": (i32, []),
+        "kvlr_build_info": (ctypes.c_char_p, []),
+        "kvlr_profile_enable": (i32, [i32]),
+        "kvlr_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise KvlrError(status, load().kvlr_last_error().decode())
+
+
+def make_config(n_q_heads, n_kv_heads, head_dim, rank, n_sink, n_sample, q_window, top_k,
+                n_recent, pool_kernel, storage, sample_recent_num=7, sample_recent_den=10) -> Config:
+    return Config(n_q_heads, n_kv_heads, head_dim, rank, n_sink, n_sample, sample_recent_num,
+                  sample_recent_den, q_window, top_k, n_recent, pool_kernel,
+                  {"f32": F32, "bf16": BF16}[storage], 0)
+
+
+def config_of(w) -> Config:
+    """Config of a configs.Workload."""
+    return make_config(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rank, w.n_sink, w.n_sample,
+                       w.q_window, w.top_k, w.n_recent, w.pool_kernel, w.storage,
+                       w.sample_recent_num, w.sample_recent_den)
+
+
+def storage_of(cfg: Config) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == BF16 else torch.float32
+
+
+def check_config(cfg: Config) -> None:
+    _check(load().kvlr_check_config(ctypes.byref(cfg)))
+
+
+def cache_bytes(cfg: Config, n_units: int, L_max: int):
+    arr = (ctypes.c_size_t * len(BUFFERS))()
+    _check(load().kvlr_cache_bytes(ctypes.byref(cfg), n_units, L_max, arr))
+    return dict(zip(BUFFERS, list(arr)))
+
+
+def workspace_bytes(cfg: Config, op: int, n_units: int, L: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().kvlr_workspace_bytes(ctypes.byref(cfg), op, n_units, L, ctypes.byref(out)))
+    return out.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class KVCache:
+    """Caller-owned persistent state of n_units (layer, sequence) units."""
+    cfg: Config
+    n_units: int
+    L_max: int
+    sink_k: torch.Tensor
+    sink_v: torch.Tensor
+    ring_k: torch.Tensor
+    ring_v: torch.Tensor
+    coef_k: torch.Tensor
+    coef_v: torch.Tensor
+    basis_k: torch.Tensor
+    basis_v: torch.Tensor
+    qwin: torch.Tensor
+    rowstat: torch.Tensor
+    lens: torch.Tensor
+
+    @staticmethod
+    def allocate(cfg: Config, n_units: int, L_max: int, device="cuda") -> "KVCache":
+        check_config(cfg)
+        dt = storage_of(cfg)
+        D = cfg.n_kv_heads * cfg.head_dim
+        G = cfg.n_q_heads // cfg.n_kv_heads
+        U, r = n_units, cfg.rank
+        z = lambda *shape, dtype=dt: torch.zeros(*shape, dtype=dtype, device=device)
+        c = KVCache(cfg, U, L_max,
+                    z(U, cfg.n_sink, D), z(U, cfg.n_sink, D),
+                    z(U, cfg.n_recent, D), z(U, cfg.n_recent, D),
+                    z(U, L_max, r), z(U, L_max, r), z(U, D, r), z(U, D, r),
+                    z(U, cfg.q_window, G, r, dtype=torch.float32),
+                    z(U, cfg.q_window, G, 2, dtype=torch.float32),
+                    z(U, 2, dtype=torch.int32))
+        want = cache_bytes(cfg, U, L_max)
+        for name in BUFFERS:
+            t = getattr(c, name)
+            assert t.numel() * t.element_size() == want[name], name
+        return c
+
+    def units(self, start: int, count: int) -> "KVCache":
+        """View of units [start, start + count) sharing storage."""
+        sl = slice(start, start + count)
+        return KVCache(self.cfg, count, self.L_max,
+                       *[getattr(self, n)[sl] for n in BUFFERS])
+
+    def clone(self) -> "KVCache":
+        return KVCache(self.cfg, self.n_units, self.L_max,
+                       *[getattr(self, n).clone() for n in BUFFERS])
+
+    def struct(self) -> CacheStruct:
+        s = CacheStruct()
+        for n in BUFFERS:
+            t = getattr(self, n)
+            assert t.is_contiguous(), n
+            setattr(s, n, t.data_ptr() if t.numel() else None)
+        s.L_max = self.L_max
+        return s
+
+
+def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def build_bases(cache: KVCache, K: torch.Tensor, V: torch.Tensor, eig_k=None, eig_v=None,
+                ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    cfg = cache.cfg
+    U, L = K.shape[0], K.shape[1]
+    D = cfg.n_kv_heads * cfg.head_dim
+    _check_tensor(K, "K", storage_of(cfg), (cache.n_units, L, D))
+    _check_tensor(V, "V", storage_of(cfg), (cache.n_units, L, D))
+    for name, e in (("eig_k", eig_k), ("eig_v", eig_v)):
+        if e is not None:
+            _check_tensor(e, name, torch.float32, (U, D))
+    need = workspace_bytes(cfg, OP_BUILD_BASES, U, L)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=K.device)
+    st = cache.struct()
+    _check(load().kvlr_build_bases(ctypes.byref(cfg), U, L, _ptr(K), _ptr(V), ctypes.byref(st),
+                                   _ptr(eig_k), _ptr(eig_v), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def project(cache: KVCache, K: torch.Tensor, V: torch.Tensor, stream=None) -> None:
+    cfg = cache.cfg
+    U, L = K.shape[0], K.shape[1]
+    D = cfg.n_kv_heads * cfg.head_dim
+    _check_tensor(K, "K", storage_of(cfg), (cache.n_units, L, D))
+    _check_tensor(V, "V", storage_of(cfg), (cache.n_units, L, D))
+    st = cache.struct()
+    _check(load().kvlr_project(ctypes.byref(cfg), U, L, _ptr(K), _ptr(V), ctypes.byref(st), None, 0,
+                               _stream(stream)))
+
+
+def decode_workspace(cache: KVCache) -> torch.Tensor:
+    need = workspace_bytes(cache.cfg, OP_DECODE, cache.n_units, cache.L_max)
+    return torch.empty(need, dtype=torch.uint8, device=cache.coef_k.device)
+
+
+def decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                out: torch.Tensor, topk: Optional[torch.Tensor] = None,
+                scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                stream=None, check: bool = True) -> None:
+    cfg = cache.cfg
+    U = cache.n_units
+    if check:
+        dt = storage_of(cfg)
+        _check_tensor(q, "q", dt, (U, cfg.n_q_heads, cfg.head_dim))
+        _check_tensor(k_new, "k_new", dt, (U, cfg.n_kv_heads, cfg.head_dim))
+        _check_tensor(v_new, "v_new", dt, (U, cfg.n_kv_heads, cfg.head_dim))
+        _check_tensor(out, "out", torch.float32, (U, cfg.n_q_heads, cfg.head_dim))
+        if topk is not None:
+            _check_tensor(topk, "topk", torch.int32, (U, cfg.top_k))
+        if scores is not None:
+            _check_tensor(scores, "scores", torch.float32, (U, cache.L_max))
+    if ws is None:
+        ws = decode_workspace(cache)
+    st = cache.struct()
+    _check(load().kvlr_decode_step(ctypes.byref(cfg), U, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   ctypes.byref(st), _ptr(out), _ptr(topk), _ptr(scores), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+
+
+def profile_enable(on: bool) -> None:
+    _check(load().kvlr_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    ms = (ctypes.c_float * len(STAGES))()
+    steps = ctypes.c_int(0)
+    _check(load().kvlr_profile_read(ms, len(STAGES), ctypes.byref(steps)))
+    return dict(zip(STAGES, list(ms))), steps.value

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Prefill: eigenvalues and captured energy of the bases, projection rows within
+one storage ulp, exact sinks and ring.  Decode: every step of every checked
+unit compared stage by stage on the GPU's own stored bits (see
+tests/gpu_helpers.py for the protocol and tolerances).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_s4r_amd import configs, synth
+from oracle import s4r
+
+from gpu_helpers import (check_bases, check_rows, np64, run_checked_steps, run_prefill,
+                         snapshot)
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_checks(w, prompt, kc, ek, ev, units):
+    L = prompt.K.shape[1]
+    for u in units:
+        Ku, Vu = np64(prompt.K[u]), np64(prompt.V[u])
+        check_bases(w, Ku, np64(kc.basis_k[u]), np64(ek[u]), f"unit {u} K basis")
+        check_bases(w, Vu, np64(kc.basis_v[u]), np64(ev[u]), f"unit {u} V basis")
+        # projection on the GPU's bases
+        BK, BV = np64(kc.basis_k[u]), np64(kc.basis_v[u])
+        CK = s4r.project(Ku[w.n_sink:L], BK, w.storage)
+        CV = s4r.project(Vu[w.n_sink:L], BV, w.storage)
+        check_rows(np64(kc.coef_k[u, w.n_sink:L]), CK, w.storage, f"unit {u} C^K",
+                   np.abs(Ku[w.n_sink:L]) @ np.abs(BK))
+        check_rows(np64(kc.coef_v[u, w.n_sink:L]), CV, w.storage, f"unit {u} C^V",
+                   np.abs(Vu[w.n_sink:L]) @ np.abs(BV))
+        snap = snapshot(kc, u, w)
+        assert np.array_equal(snap.sink_k, Ku[:w.n_sink]) and np.array_equal(snap.sink_v, Vu[:w.n_sink])
+        for p in range(L - w.n_recent, L):
+            assert np.array_equal(snap.ring_k[p % w.n_recent], Ku[p])
+            assert np.array_equal(snap.ring_v[p % w.n_recent], Vu[p])
+        assert snap.L == L and snap.steps == 0
+
+
+def _run(w, L, batch, steps, L_extra=8, units=None, check_every=1, n_layers=1):
+    print(f"case {w.name} L={L} batch={batch} steps={steps}", flush=True)
+    prompt = synth.make_prompt(w, L=L, batch=batch, n_layers=n_layers)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=batch, n_layers=n_layers)
+    kc, K, V, ek, ev = run_prefill(_kvlr(), w, prompt, L + steps + L_extra)
+    U = batch * n_layers
+    _prefill_checks(w, prompt, kc, ek, ev, range(U) if units is None else units)
+    stats = run_checked_steps(_kvlr(), w, kc, dec, steps, units=units, check_every=check_every)
+    print(f"  checked={stats.n_checked} topk_near_tie_diffs={stats.topk_diffs} "
+          f"worst_gap={stats.worst_gap:.3g} max_out_err={stats.max_out_err:.3g} "
+          f"max_score_err={stats.max_score_err:.3g}", flush=True)
+    return stats
+
+
+def _kvlr():
+    from long_context_decode_s4r_amd import kvlr
+    kvlr.load()
+    return kvlr
+
+
+def test_tiny_f32_all_steps(gpu_lib):
+    """fp32 single head, L = 1024, all 64 decode steps checked."""
+    st = _run(configs.TINY_F32, 1024, 1, 64)
+    assert st.n_checked == 64
+    assert st.max_out_err <= 1e-5
+
+
+def test_llama_layer_bf16_small(gpu_lib):
+    """Llama-3-8B layer shape (D' = 1024, r = 256, G = 4, W = 16), ragged L."""
+    w = configs.LLAMA8B_32K.with_(n_sample=512, top_k=128)
+    st = _run(w, 2500, 2, 20)
+    assert st.n_checked == 40
+
+
+def test_qwen_layer_bf16_small(gpu_lib):
+    """Qwen-2.5-7B layer shape (D' = 512, r = 128, G = 7 -> 112 window rows)."""
+    w = configs.QWEN7B_64K.with_(n_sample=512, top_k=96, exponents=(0.9,))
+    st = _run(w, 3001, 2, 18)
+    assert st.n_checked == 36
+
+
+def test_r192_planted_bf16_small(gpu_lib):
+    """r = 192 with 2% planted 4x-norm rows (the 128K workload's stress)."""
+    w = configs.LLAMA8B_128K.with_(n_sample=512, top_k=200)
+    st = _run(w, 4096, 1, 17)
+    assert st.n_checked == 17
+
+
+def test_multi_layer_units(gpu_lib):
+    """Several layers x sequences as independent units, per-layer spectra."""
+    w = configs.QWEN7B_64K.with_(n_sample=256, top_k=64, n_layers=3,
+                                 exponents=(0.5, 0.85, 1.2))
+    st = _run(w, 1500, 2, 6, n_layers=3)
+    assert st.n_checked == 36
+
+
+@pytest.mark.parametrize("variant", ["k_all", "k_zero", "kappa1", "no_sink", "short_prompt"])
+def test_edge_cases_f32(gpu_lib, variant):
+    base = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=32, rank=16,
+                                  q_window=4, top_k=24, n_recent=8, n_sample=64)
+    L = 300
+    if variant == "k_all":
+        w = base.with_(top_k=10_000)
+    elif variant == "k_zero":
+        w = base.with_(top_k=0)
+    elif variant == "kappa1":
+        w = base.with_(pool_kernel=1)
+    elif variant == "no_sink":
+        w = base.with_(n_sink=0)
+    else:
+        w = base.with_(n_sample=4)
+        L = w.n_sink + w.n_recent
+    st = _run(w, L, 2, 9)
+    assert st.n_checked == 18
+
+
+def test_full_rank_all_selected_equals_full_attention(gpu_lib):
+    """r = D' and k >= |J|: the GPU output equals plain full attention over
+    every token (fp32 storage)."""
+    kvlr = _kvlr()
+    w = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=32, rank=64, q_window=4,
+                               top_k=100_000, n_recent=8, n_sample=96, model="power",
+                               exponents=(0.5,))
+    L, steps = 200, 5
+    prompt = synth.make_prompt(w, L=L, batch=1)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=1)
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps)
+    out = torch.empty(1, 4, 32, device="cuda")
+    Kall, Vall = np64(prompt.K[0]), np64(prompt.V[0])
+    for t in range(steps):
+        kvlr.decode_step(kc, dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), out)
+        Kall = np.vstack([Kall, np64(dec.k[t][0]).reshape(1, -1)])
+        Vall = np.vstack([Vall, np64(dec.v[t][0]).reshape(1, -1)])
+        q = np64(dec.q[t][0])
+        ref = np.stack([s4r.softmax_attention(q[a], Kall[:, (a // 2) * 32:(a // 2 + 1) * 32],
+                                              Vall[:, (a // 2) * 32:(a // 2 + 1) * 32])
+                        for a in range(4)])
+        err = np.max(np.abs(np64(out[0]) - ref)) / np.max(np.abs(ref))
+        assert err < 1e-5, err
+
+
+def test_exact_rank_reconstruction_gpu(gpu_lib):
+    """Exactly rank-16 states (no noise): C . B^T reproduces every non-sink row."""
+    kvlr = _kvlr()
+    w = configs.TINY_F32.with_(noise=0.0)
+    prompt = synth.make_prompt(w)
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, w.L + 4)
+    X = np64(prompt.K[0])[w.n_sink:]
+    C = np64(kc.coef_k[0])[w.n_sink:w.L]
+    B = np64(kc.basis_k[0])
+    rel = np.linalg.norm(C @ B.T - X) / np.linalg.norm(X)
+    assert rel < 1e-5, rel
+
+
+def test_capacity_full_unit(gpu_lib):
+    """A unit whose cache is full is left unchanged and outputs zeros."""
+    kvlr = _kvlr()
+    w = configs.TINY_F32.with_(n_q_heads=2, n_kv_heads=1, head_dim=32, rank=8, q_window=4,
+                               top_k=8, n_recent=4, n_sample=32)
+    L = 100
+    prompt = synth.make_prompt(w, L=L, batch=1)
+    dec = synth.make_decode_inputs(w, prompt, 5, batch=1)
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + 2)
+    out = torch.empty(1, 2, 32, device="cuda")
+    topk = torch.empty(1, 8, dtype=torch.int32, device="cuda")
+    for t in range(5):
+        before = kc.coef_k.clone()
+        kvlr.decode_step(kc, dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), out, topk)
+        torch.cuda.synchronize()
+        lens = kc.lens[0].tolist()
+        if t < 2:
+            assert lens == [L + t + 1, t + 1]
+            assert torch.any(out != 0)
+        else:
+            assert lens == [L + 2, 2]
+            assert torch.all(out == 0) and torch.all(topk == -1)
+            assert torch.equal(before, kc.coef_k)
+
+
+def test_repeatable(gpu_lib):
+    """Two identical runs give bit-identical outputs (no atomics in the sums)."""
+    kvlr = _kvlr()
+    w = configs.LLAMA8B_32K.with_(n_sample=256, top_k=64)
+    prompt = synth.make_prompt(w, L=1200, batch=2)
+    dec = synth.make_decode_inputs(w, prompt, 4, batch=2)
+    outs = []
+    for rep in range(2):
+        kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, 1300)
+        out = torch.empty(2, 32, 128, device="cuda")
+        res = []
+        for t in range(4):
+            kvlr.decode_step(kc, dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), out)
+            res.append(out.clone())
+        outs.append(torch.stack(res))
+    assert torch.equal(outs[0], outs[1])
