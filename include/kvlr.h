@@ -97,13 +97,17 @@ typedef struct kvlr_cache {
                                                     softmax (base-2 domain)  */
   int32_t* lens;    /* [U][2]              int32    {tokens cached, decode
                                                     steps taken}             */
+  void* qsplit;     /* [U][W][G][2][r]     bf16     qwin * log2(e)/sqrt(r)
+                                                    as hi + lo bf16 parts
+                                                    (MFMA operands of the
+                                                    latent scoring)          */
   int64_t L_max;    /* capacity in tokens (prompt + decode steps)           */
 } kvlr_cache;
 
 enum {
   KVLR_BUF_SINK_K = 0, KVLR_BUF_SINK_V, KVLR_BUF_RING_K, KVLR_BUF_RING_V,
   KVLR_BUF_COEF_K, KVLR_BUF_COEF_V, KVLR_BUF_BASIS_K, KVLR_BUF_BASIS_V,
-  KVLR_BUF_QWIN, KVLR_BUF_ROWSTAT, KVLR_BUF_LENS, KVLR_BUF_COUNT
+  KVLR_BUF_QWIN, KVLR_BUF_ROWSTAT, KVLR_BUF_LENS, KVLR_BUF_QSPLIT, KVLR_BUF_COUNT
 };
 
 enum { KVLR_OP_BUILD_BASES = 0, KVLR_OP_PROJECT = 1, KVLR_OP_DECODE = 2 };
@@ -146,7 +150,7 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L,
  * stored as c = x.B; sinks kept exact, 'Core claim').
  *   K, V      device, [U][L][D'] storage (same prompt as kvlr_build_bases).
  *   cache     reads basis_k/v; writes coef_k/v rows [s, L), sink_k/v, ring
- *             (positions [L - n_recent, L)), zeroes qwin and rowstat and sets
+ *             (positions [L - n_recent, L)), zeroes qwin, qsplit and rowstat, sets
  *             lens = {L, 0}.  Requires L <= cache->L_max.
  *   ws        unused by this op (may be NULL when ws_bytes == 0). */
 int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
@@ -185,10 +189,11 @@ const char* kvlr_build_info(void);
 
 /* Stage timing for measurement.  kvlr_profile_enable(1) makes every following
  * kvlr_decode_step record HIP events between its stages on its stream
- * (stages: 0 prologue, 1 latent scoring, 2 selection, 3 reconstruction +
- * attention, 4 merge); kvlr_profile_enable(0) stops.  kvlr_profile_read
+ * (stages: 0 prologue, 1 latent scoring, 2 score finalisation + pooling,
+ * 3 top-k selection, 4 reconstruction + attention, 5 split merge);
+ * kvlr_profile_enable(0) stops.  kvlr_profile_read
  * waits for the recorded events, writes the summed milliseconds per stage to
- * ms (host, n entries, n <= 5) and the number of profiled steps to *steps,
+ * ms (host, n entries, n <= 6) and the number of profiled steps to *steps,
  * then clears the record.  Records at most 8192 steps. */
 int kvlr_profile_enable(int on);
 int kvlr_profile_read(float* ms, int n, int* steps);

@@ -44,7 +44,9 @@ bool rank_supported_bf16(int r) { return r == 32 || r == 64 || r == 128 || r == 
 
 size_t attend_lds(const kvlr_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
-  return ((size_t)2 * 64 * (c->head_dim + 1) + (size_t)G * c->head_dim + G * 64 + 2 * G) * 4;
+  size_t b = ((size_t)2 * 32 * (c->head_dim + 4) + (size_t)G * c->head_dim + G * 32 + 24) * 4;
+  if (c->dtype == KVLR_BF16) b += (size_t)2 * 32 * (c->rank + 8) * 2;
+  return b;
 }
 
 int check_cfg(const kvlr_config* c) {
@@ -60,8 +62,11 @@ int check_cfg(const kvlr_config* c) {
   if (c->head_dim > 256) return fail(KVLR_EINVAL, "head_dim %d > 256 is not supported", c->head_dim);
   const int64_t D = (int64_t)c->n_kv_heads * c->head_dim;
   if (D % 2 != 0 || D > 4096) return fail(KVLR_EINVAL, "D' = %lld must be even and <= 4096", (long long)D);
-  if ((1 + G) * D > 16384) return fail(KVLR_EINVAL, "(1 + G) * D' = %lld exceeds 16384", (long long)((1 + G) * D));
+  if ((1 + G) * D > 12288) return fail(KVLR_EINVAL, "(1 + G) * D' = %lld exceeds 12288", (long long)((1 + G) * D));
+  if ((int64_t)G * c->head_dim > 1024) return fail(KVLR_EINVAL, "G * head_dim must be <= 1024");
   if (c->rank < 1 || c->rank > D) return fail(KVLR_EINVAL, "rank %d must be in [1, D' = %lld]", c->rank, (long long)D);
+  if (c->rank % 8 != 0) return fail(KVLR_EINVAL, "rank %d must be a multiple of 8", c->rank);
+  if (c->head_dim % 8 != 0) return fail(KVLR_EINVAL, "head_dim %d must be a multiple of 8", c->head_dim);
   if (c->n_sink < 0) return fail(KVLR_EINVAL, "n_sink must be >= 0");
   if (c->n_sample < 1) return fail(KVLR_EINVAL, "n_sample must be >= 1");
   if (c->sample_recent_den < 1 || c->sample_recent_num < 0 || c->sample_recent_num > c->sample_recent_den)
@@ -73,7 +78,8 @@ int check_cfg(const kvlr_config* c) {
     return fail(KVLR_EINVAL, "pool_kernel must be odd and in [1, 255]");
   if (c->dtype == KVLR_BF16) {
     if (!rank_supported_bf16(c->rank)) return fail(KVLR_EINVAL, "bf16 storage needs rank in {32, 64, 128, 192, 256}");
-    if (c->head_dim % 32 != 0) return fail(KVLR_EINVAL, "bf16 storage needs head_dim %% 32 == 0");
+    if (c->head_dim % 32 != 0 || c->head_dim > 128)
+      return fail(KVLR_EINVAL, "bf16 storage needs head_dim %% 32 == 0 and head_dim <= 128");
     if (c->q_window * G > 128) return fail(KVLR_EINVAL, "bf16 storage needs q_window * G <= 128");
   } else {
     if ((int64_t)c->q_window * G * c->rank > 8192)
@@ -150,31 +156,27 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
 }
 
 struct DecodeLayout {
-  size_t stepinfo, partial, spill, tilestat, score, keys, topk, part, total;
-  int Lc_cap, nsplit, chunk, nsa;
+  size_t stepinfo, partial, spill, tilestat, keys, topk, part, total;
+  int Lc_cap, nsplit, chunk, nsa, rows_per_split;
 };
 
 DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   DecodeLayout L;
   Dims d = dims_of(c);
-  decode_tiling(d, U, Lmax, &L.Lc_cap, &L.nsplit, &L.chunk, &L.nsa);
+  decode_tiling(d, U, Lmax, &L.Lc_cap, &L.nsplit, &L.chunk, &L.nsa, &L.rows_per_split);
   size_t off = 0;
-  L.stepinfo = off;
-  off = align_up(off + (size_t)U * 4 * sizeof(int32_t));
-  L.partial = off;
-  off = align_up(off + (size_t)U * L.Lc_cap * sizeof(float));
-  L.spill = off;
-  off = align_up(off + (size_t)U * d.G * L.Lc_cap * sizeof(float));
-  L.tilestat = off;
-  off = align_up(off + (size_t)U * L.nsplit * d.G * 2 * sizeof(float));
-  L.score = off;
-  off = align_up(off + (size_t)U * L.Lc_cap * sizeof(float));
-  L.keys = off;
-  off = align_up(off + (size_t)U * L.Lc_cap * sizeof(uint32_t));
-  L.topk = off;
-  off = align_up(off + (size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
-  L.part = off;
-  off = align_up(off + (size_t)U * d.Hq * L.nsa * (d.dh + 2) * sizeof(float));
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.stepinfo = take((size_t)U * 4 * sizeof(int32_t));
+  L.partial = take((size_t)U * L.Lc_cap * sizeof(float));
+  L.spill = take((size_t)U * d.G * L.Lc_cap * sizeof(float));
+  L.tilestat = take((size_t)U * L.nsplit * d.G * 2 * sizeof(float));
+  L.keys = take((size_t)U * L.Lc_cap * sizeof(uint32_t));
+  L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
+  L.part = take((size_t)U * d.Hq * L.nsa * (d.dh + 2) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -186,7 +188,7 @@ int check_cache(const kvlr_cache* cache, bool need_state, int n_sink) {
     if (n_sink > 0 && (!cache->sink_k || !cache->sink_v))
       return fail(KVLR_EINVAL, "sink buffers are NULL");
     if (!cache->ring_k || !cache->ring_v || !cache->coef_k ||
-        !cache->coef_v || !cache->qwin || !cache->rowstat || !cache->lens)
+        !cache->coef_v || !cache->qwin || !cache->rowstat || !cache->lens || !cache->qsplit)
       return fail(KVLR_EINVAL, "a cache buffer is NULL");
     if (cache->L_max < 1) return fail(KVLR_EINVAL, "cache L_max must be >= 1");
   }
@@ -204,6 +206,7 @@ CachePtrs cache_ptrs(const kvlr_cache* c) {
   p.basis_k = c->basis_k;
   p.basis_v = c->basis_v;
   p.qwin = c->qwin;
+  p.qsplit = (uint16_t*)c->qsplit;
   p.rowstat = c->rowstat;
   p.lens = c->lens;
   p.Lmax = c->L_max;
@@ -211,7 +214,7 @@ CachePtrs cache_ptrs(const kvlr_cache* c) {
 }
 
 // ---- stage timing -------------------------------------------------------------
-constexpr int kStages = 5;
+constexpr int kStages = 6;
 constexpr int kMaxProfiled = 8192;
 std::mutex g_prof_mu;
 bool g_prof_on = false;
@@ -242,6 +245,7 @@ int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max, siz
   bytes[KVLR_BUF_QWIN] = (size_t)n_units * cfg->q_window * G * cfg->rank * sizeof(float);
   bytes[KVLR_BUF_ROWSTAT] = (size_t)n_units * cfg->q_window * G * 2 * sizeof(float);
   bytes[KVLR_BUF_LENS] = (size_t)n_units * 2 * sizeof(int32_t);
+  bytes[KVLR_BUF_QSPLIT] = (size_t)n_units * cfg->q_window * G * 2 * cfg->rank * sizeof(uint16_t);
   return ok();
 }
 
@@ -337,7 +341,8 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
                            cache->coef_k, cache->coef_v, st)) != hipSuccess)
     return hip_fail(he, "project");
   if ((he = launch_exact_and_reset(d, (int)n_units, L, K, V, cache->sink_k, cache->sink_v, cache->ring_k,
-                                   cache->ring_v, cache->qwin, cache->rowstat, cache->lens, st)) != hipSuccess)
+                                   cache->ring_v, cache->qwin, cache->rowstat, cache->lens,
+                                   (uint16_t*)cache->qsplit, st)) != hipSuccess)
     return hip_fail(he, "exact/reset");
   return ok();
 }
@@ -362,7 +367,6 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   dw.partial = (float*)(w + dl.partial);
   dw.spill = (float*)(w + dl.spill);
   dw.tilestat = (float*)(w + dl.tilestat);
-  dw.score = (float*)(w + dl.score);
   dw.keys = (uint32_t*)(w + dl.keys);
   dw.topk = (int32_t*)(w + dl.topk);
   dw.part = (float*)(w + dl.part);
@@ -370,6 +374,7 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   dw.nsplit = dl.nsplit;
   dw.chunk = dl.chunk;
   dw.nsa = dl.nsa;
+  dw.rows_per_split = dl.rows_per_split;
   const CachePtrs cp = cache_ptrs(cache);
   const int U = (int)n_units;
 
@@ -387,12 +392,14 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   if (ev) (void)hipEventRecord(ev[1], st);
   if ((he = launch_score(d, U, cp, dw, st)) != hipSuccess) return hip_fail(he, "score");
   if (ev) (void)hipEventRecord(ev[2], st);
-  if ((he = launch_select(d, U, cp, dw, topk_idx, scores, st)) != hipSuccess) return hip_fail(he, "select");
+  if ((he = launch_pool(d, U, cp, dw, scores, st)) != hipSuccess) return hip_fail(he, "pool");
   if (ev) (void)hipEventRecord(ev[3], st);
-  if ((he = launch_attend(d, U, q, cp, dw, st)) != hipSuccess) return hip_fail(he, "attend");
+  if ((he = launch_topk(d, U, cp, dw, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
   if (ev) (void)hipEventRecord(ev[4], st);
-  if ((he = launch_merge(d, U, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
+  if ((he = launch_attend(d, U, q, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "attend");
   if (ev) (void)hipEventRecord(ev[5], st);
+  if ((he = launch_merge(d, U, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
+  if (ev) (void)hipEventRecord(ev[6], st);
   return ok();
 }
 

@@ -41,6 +41,40 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS byte offset of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Eight 16-byte LDS reads issued back to back; the asm waits for all of
+// them before it ends, so no read is left in flight past the statement.
+// Kept opaque so the compiler's tracking of direct global->LDS loads does
+// not add waits for other LDS buffers in front of it.
+__device__ __forceinline__ void lds_read8(const uint32_t a[8], bf16x8 out[8]) {
+  u16x8 o0, o1, o2, o3, o4, o5, o6, o7;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3), "=&v"(o4), "=&v"(o5), "=&v"(o6), "=&v"(o7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+  out[0] = __builtin_bit_cast(bf16x8, o0);
+  out[1] = __builtin_bit_cast(bf16x8, o1);
+  out[2] = __builtin_bit_cast(bf16x8, o2);
+  out[3] = __builtin_bit_cast(bf16x8, o3);
+  out[4] = __builtin_bit_cast(bf16x8, o4);
+  out[5] = __builtin_bit_cast(bf16x8, o5);
+  out[6] = __builtin_bit_cast(bf16x8, o6);
+  out[7] = __builtin_bit_cast(bf16x8, o7);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -89,19 +123,22 @@ hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const v
                           hipStream_t st);
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   void* sink_k, void* sink_v, void* ring_k, void* ring_v,
-                                  float* qwin, float* rowstat, int32_t* lens, hipStream_t st);
+                                  float* qwin, float* rowstat, int32_t* lens, uint16_t* qsplit,
+                                  hipStream_t st);
 
 // decode
+constexpr int kHistBins = 4096;  // selection histogram over the top 12 key bits
+constexpr int kPoolChunk = 2048; // candidates per block of the pooling kernel
+
 struct DecodeWs {
-  int32_t* stepinfo;  // [U][4]
-  float* partial;     // [U][Lc_cap]
-  float* spill;       // [U][G][Lc_cap]
-  float* tilestat;    // [U][nsplit][G][2]
-  float* score;       // [U][Lc_cap]
-  uint32_t* keys;     // [U][Lc_cap]
-  int32_t* topk;      // [U][k]
-  float* part;        // [U][Hq][nsa][dh + 2]
-  int Lc_cap, nsplit, chunk, nsa;
+  int32_t* stepinfo;  // [U][4]     {tokens cached, steps taken, unit full, -}
+  float* partial;     // [U][Lc_cap] score contribution of the older window rows
+  float* spill;       // [U][G][Lc_cap] base-2 logits of the current rows
+  float* tilestat;    // [U][nsplit][G][2] per-split (max, sum) of the current rows
+  uint32_t* keys;     // [U][Lc_cap] pooled scores as ordered bit patterns
+  int32_t* topk;      // [U][k] selected positions, ascending
+  float* part;        // [U][Hq][nsa][dh + 2] attention split partials
+  int Lc_cap, nsplit, chunk, nsa, rows_per_split;
 };
 
 struct CachePtrs {
@@ -109,6 +146,7 @@ struct CachePtrs {
   float* qwin;
   float* rowstat;
   int32_t* lens;
+  uint16_t* qsplit;  // [U][W][G][2][r] bf16 hi / lo of qwin * qscale
   int64_t Lmax;
 };
 
@@ -117,15 +155,16 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
                            hipStream_t st);
 hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                         hipStream_t st);
-hipError_t launch_select(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
-                         int32_t* topk_user, float* scores_user, hipStream_t st);
+hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                       float* scores_user, hipStream_t st);
+hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                       int32_t* topk_user, float* out, hipStream_t st);
 hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
-                         const DecodeWs& w, hipStream_t st);
-hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
-                        hipStream_t st);
+                         const DecodeWs& w, float* out, hipStream_t st);
+hipError_t launch_merge(const Dims& d, int U, const DecodeWs& w, float* out, hipStream_t st);
 
 // decode tiling decisions shared by the workspace sizing and the launches
 void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, int* Lc_cap, int* nsplit, int* chunk,
-                   int* nsa);
+                   int* nsa, int* rows_per_split);
 
 }  // namespace kvlr

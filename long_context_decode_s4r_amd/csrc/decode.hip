@@ -1,6 +1,6 @@
 // Decode-step kernels: prologue (append + query coefficients + window),
-// latent scoring, pooled top-k selection, sparse reconstruction + exact
-// attention (split over rows), merge of the splits.
+// latent scoring, pooled top-k selection (two kernels), sparse reconstruction
+// + exact attention (split over rows, splits merged by the last block).
 //
 // Method: S^4R review (pith.science/paper/2608.00528): 'What carries the
 // argument' (latent-space relevance scoring between a sliding window of query
@@ -16,8 +16,12 @@
 // updated with that one logit in the prologue and stays exact.  Only the G
 // rows of the current step need a full pass: the scoring kernel writes their
 // logits to a spill buffer together with per-split (m, S) partials, and the
-// selection kernel merges them before adding their probabilities.  The key
+// pooling kernel merges them before adding their probabilities.  The key
 // coefficients are therefore read once per step.
+//
+// Per-step flow of the unit state: the prologue reads lens and snapshots it
+// in stepinfo; every later kernel reads stepinfo; the top-k kernel (one
+// block per unit) advances lens.
 #include "common.h"
 
 #include <float.h>
@@ -28,261 +32,519 @@ namespace kvlr {
 static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, int* Lc_cap, int* nsplit, int* chunk,
-                   int* nsa) {
+                   int* nsa, int* rows_per_split) {
   int64_t lc = Lmax - d.s - d.nrec;
   if (lc < 1) lc = 1;
   lc = round_up(lc, 64);
   *Lc_cap = (int)lc;
-  int64_t target = (1024 + U - 1) / U;
+  int64_t target = (512 + U - 1) / U;
   if (target < 1) target = 1;
   int64_t maxsplit = lc / 256;
   if (maxsplit < 1) maxsplit = 1;
   int64_t ns = target < maxsplit ? target : maxsplit;
-  int64_t ch = round_up((lc + ns - 1) / ns, 32);
+  int64_t ch = round_up((lc + ns - 1) / ns, 64);
   ns = (lc + ch - 1) / ch;
   *nsplit = (int)ns;
   *chunk = (int)ch;
-  *nsa = (d.s + d.nrec + d.k + 63) / 64;
+  // attention: about 512 blocks over (unit, KV head, row split), 32-row tiles
+  const int64_t R = (int64_t)d.s + d.nrec + d.k;
+  int64_t sa = (512 + U * d.Hkv - 1) / (U * d.Hkv);
+  if (sa < 1) sa = 1;
+  int64_t rows = round_up((R + sa - 1) / sa, 32);
+  if (rows < 32) rows = 32;
+  *rows_per_split = (int)rows;
+  *nsa = (int)((R + rows - 1) / rows);
 }
 
 __device__ __forceinline__ int wrap_slot(int x, int W) { return ((x % W) + W) % W; }
 
+// 16 bytes of storage elements -> fp32
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void ld(const float* p, float* o) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+  }
+};
+template <> struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void ld(const uint16_t* p, float* o) {
+    const u16x8 v = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = bf2f(v[e]);
+  }
+};
+
 // --------------------------------------------------------------------------
-// prologue: grid (ceil(r/64), U, 2 {K, V}), 256 threads
-//   K part: c^K(new) = k_cat . B^K, c_q[g] = q_cat[g] . B^K (window push),
-//           old window rows' (m, S) updated with the entering candidate.
-//   V part: c^V(new) = v_cat . B^V.
-//   chunk 0 of each part pushes the exact k / v into the recent ring.
+// prologue: grid (2 * ncb + 1, U), 256 threads.
+//   blocks [0, ncb):      c^K(new) = k_cat . B^K and c_q[g] = q_cat[g] . B^K
+//                         (window push) for 4*VEC basis columns each;
+//   blocks [ncb, 2 ncb):  c^V(new) = v_cat . B^V;
+//   block 2 ncb:          exact ring push of k and v; the older window rows'
+//                         (m, S) updated with the candidate entering this
+//                         step.
+// GEMV layout: thread (row group rg = tid / 4, column group cg = tid % 4)
+// reads 16 bytes of a basis row per iteration (rows rg, rg + 64, ...);
+// partial sums are reduced over row groups with lane shuffles and LDS.
 // --------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* __restrict__ q,
                                                   const T* __restrict__ kn,
-                                                  const T* __restrict__ vn,
-                                                  int32_t* __restrict__ stepinfo, float qscale) {
-  const int chunk = blockIdx.x, u = blockIdx.y, kind = blockIdx.z;
-  const int tid = threadIdx.x;
+                                                  const T* __restrict__ vn, DecodeWs w,
+                                                  float qscale, int ncb) {
+  constexpr int VEC = Vec16<T>::N;
+  constexpr int NVMAX = 9;  // 1 + G, G <= 8
+  const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int D = d.D, r = d.r, G = d.G, W = d.W;
   const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
   const bool full = (int64_t)Lcur >= c.Lmax;
-  if (chunk == 0 && kind == 0 && tid == 0) {
-    stepinfo[4 * u + 0] = Lcur;
-    stepinfo[4 * u + 1] = steps;
-    stepinfo[4 * u + 2] = full ? 1 : 0;
-    stepinfo[4 * u + 3] = 0;
+  if (b == 0 && tid == 0) {
+    w.stepinfo[4 * u + 0] = Lcur;
+    w.stepinfo[4 * u + 1] = steps;
+    w.stepinfo[4 * u + 2] = full ? 1 : 0;
+    w.stepinfo[4 * u + 3] = 0;
   }
   if (full) return;
   const int64_t p = Lcur;
-  const int slot = steps % W;
-  const int nvec = kind == 0 ? 1 + G : 1;
   extern __shared__ float sm[];
-  float* xs = sm;                    // [nvec][D]
-  float* red = xs + nvec * D;        // [4][nvec][64]
-  float* ce = red + 4 * nvec * 64;   // [r]
-  const T* x0 = (kind == 0 ? kn : vn) + (int64_t)u * D;
-  for (int i = tid; i < D; i += 256) xs[i] = Elem<T>::ld(x0, i);
-  if (kind == 0) {
-    const T* qu = q + (int64_t)u * d.Hq * d.dh;
-    for (int i = tid; i < G * D; i += 256) {
-      const int g = i / D, idx = i % D, h = idx / d.dh, j = idx % d.dh;
-      xs[(1 + g) * D + idx] = Elem<T>::ld(qu, (int64_t)(h * G + g) * d.dh + j);
+  if (b < 2 * ncb) {
+    const int kind = b >= ncb ? 1 : 0;
+    const int cb = kind ? b - ncb : b;
+    const int nvec = kind == 0 ? 1 + G : 1;
+    float* xs = sm;                         // [nvec][D]
+    float* red = xs + nvec * D;             // [4 waves][nvec][4 * VEC]
+    // stage x_0 (k or v) and the G concatenated query vectors as fp32; every
+    // thread owns 16-byte pieces, all loads are issued before the stores
+    {
+      const T* x0 = (kind == 0 ? kn : vn) + (int64_t)u * D;
+      const T* qu = q + (int64_t)u * d.Hq * d.dh;
+      const int nx = D / VEC, nq = kind == 0 ? d.Hq * d.dh / VEC : 0;
+      constexpr int NP = (12288 / VEC + 255) / 256;  // (1 + G) * D <= 12288
+      float buf[NP][VEC];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int pc = tid + 256 * i;
+        const T* src = pc < nx ? x0 + pc * VEC : qu + min(pc - nx, max(nq - 1, 0)) * VEC;
+        Vec16<T>::ld(src, buf[i]);  // pieces past the end re-read a valid one
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int pc = tid + 256 * i;
+        if (pc < nx) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xs[pc * VEC + e] = buf[i][e];
+        } else if (pc < nx + nq) {
+          // query element (head a = h * G + g, j) -> vector g, channel h * dh + j
+          const int qe = (pc - nx) * VEC, a = qe / d.dh, j = qe % d.dh;
+          const int h = a / G, g = a % G;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xs[(1 + g) * D + h * d.dh + j + e] = buf[i][e];
+        }
+      }
     }
-  }
-  __syncthreads();
-  const T* B = (const T*)(kind == 0 ? c.basis_k : c.basis_v) + (int64_t)u * D * r;
-  const int col = chunk * 64 + (tid & 63), rg = tid >> 6;
-  float acc[9];
+    __syncthreads();
+    const T* B = (const T*)(kind == 0 ? c.basis_k : c.basis_v) + (int64_t)u * D * r;
+    const int cg = tid & 3, rg = tid >> 2;
+    const int col = cb * 4 * VEC + cg * VEC;
+    float acc[NVMAX][VEC];
 #pragma unroll
-  for (int v = 0; v < 9; ++v) acc[v] = 0.f;
-  if (col < r) {
-    for (int kk = rg; kk < D; kk += 4) {
-      const float b = Elem<T>::ld(B, (int64_t)kk * r + col);
+    for (int v = 0; v < NVMAX; ++v)
 #pragma unroll
-      for (int v = 0; v < 9; ++v)
-        if (v < nvec) acc[v] += xs[v * D + kk] * b;
+      for (int e = 0; e < VEC; ++e) acc[v][e] = 0.f;
+    if (col < r) {
+      for (int kk0 = rg; kk0 < D; kk0 += 64 * 8) {
+        float bvals[8][VEC];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kk = min(kk0 + 64 * i, D - 1);  // rows past D are read, then skipped
+          Vec16<T>::ld(B + (int64_t)kk * r + col, bvals[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kk = kk0 + 64 * i;
+          if (kk < D) {
+#pragma unroll
+            for (int v = 0; v < NVMAX; ++v) {
+              if (v < nvec) {
+                const float x = xs[v * D + kk];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[v][e] += x * bvals[i][e];
+              }
+            }
+          }
+        }
+      }
     }
-  }
+    // reduce over the 16 row groups of a wave (lane bits 2..5), then waves
+    const int lane = tid & 63, wv = tid >> 6;
 #pragma unroll
-  for (int v = 0; v < 9; ++v)
-    if (v < nvec) red[(rg * nvec + v) * 64 + (tid & 63)] = acc[v];
-  __syncthreads();
-  if (rg == 0 && col < r) {
-    for (int v = 0; v < nvec; ++v) {
-      const float sum = red[(0 * nvec + v) * 64 + tid] + red[(1 * nvec + v) * 64 + tid] +
-                        red[(2 * nvec + v) * 64 + tid] + red[(3 * nvec + v) * 64 + tid];
+    for (int v = 0; v < NVMAX; ++v) {
+      if (v < nvec) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float x = acc[v][e];
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          x += __shfl_xor(x, 16);
+          x += __shfl_xor(x, 32);
+          if (lane < 4) red[(wv * nvec + v) * 4 * VEC + lane * VEC + e] = x;
+        }
+      }
+    }
+    __syncthreads();
+    for (int t = tid; t < nvec * 4 * VEC; t += 256) {
+      const int v = t / (4 * VEC), cc = t % (4 * VEC);
+      const int cl = cb * 4 * VEC + cc;
+      if (cl >= r) continue;
+      const float sum = red[(0 * nvec + v) * 4 * VEC + cc] + red[(1 * nvec + v) * 4 * VEC + cc] +
+                        red[(2 * nvec + v) * 4 * VEC + cc] + red[(3 * nvec + v) * 4 * VEC + cc];
       if (v == 0) {
         T* C = (T*)(kind == 0 ? c.coef_k : c.coef_v);
-        Elem<T>::st(C, ((int64_t)u * c.Lmax + p) * r + col, sum);
+        Elem<T>::st(C, ((int64_t)u * c.Lmax + p) * r + cl, sum);
       } else {
-        c.qwin[(((int64_t)u * W + slot) * G + (v - 1)) * r + col] = sum;
+        const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
+        c.qwin[row * r + cl] = sum;
+        const float x = sum * qscale;  // MFMA operands of the latent scoring
+        const uint16_t hb = f2bf(x);
+        c.qsplit[(row * 2 + 0) * r + cl] = hb;
+        c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
+      }
+    }
+    return;
+  }
+  // ---- state block ----
+  {  // exact ring push, 16-byte pieces, loads before stores
+    const int rs = (int)(p % d.nrec);
+    constexpr int NP = (4096 / VEC + 255) / 256;  // D <= 4096
+    u16x8 bk[NP], bv[NP];
+    const int np = D / VEC;
+    const u16x8* sk = reinterpret_cast<const u16x8*>(kn + (int64_t)u * D);
+    const u16x8* sv = reinterpret_cast<const u16x8*>(vn + (int64_t)u * D);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = min(tid + 256 * i, np - 1);
+      bk[i] = sk[pc];
+      bv[i] = sv[pc];
+    }
+    u16x8* dk = reinterpret_cast<u16x8*>((T*)c.ring_k + ((int64_t)u * d.nrec + rs) * D);
+    u16x8* dv = reinterpret_cast<u16x8*>((T*)c.ring_v + ((int64_t)u * d.nrec + rs) * D);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + 256 * i;
+      if (pc < np) {
+        dk[pc] = bk[i];
+        dv[pc] = bv[i];
       }
     }
   }
-  if (chunk != 0) return;
-  {  // exact ring push
-    T* ring = (T*)(kind == 0 ? c.ring_k : c.ring_v);
-    const int rs = (int)(p % d.nrec);
-    for (int i = tid; i < D; i += 256) ring[((int64_t)u * d.nrec + rs) * D + i] = x0[i];
-  }
-  if (kind != 0) return;
-  // old rows: add the candidate entering the compressed set this step
   const int weff = min(steps + 1, W);
   const int nold = (weff - 1) * G;
   if (nold <= 0) return;
-  const int64_t pe = (int64_t)Lcur - d.nrec;
+  float* ce = sm;  // [r]
+  const int64_t pe = (int64_t)Lcur - d.nrec;  // candidate entering the compressed set
   const T* cep = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pe) * r;
   for (int i = tid; i < r; i += 256) ce[i] = Elem<T>::ld(cep, i);
   __syncthreads();
-  for (int o = tid; o < nold; o += 256) {
-    const int i = 1 + o / G, g = o % G;
-    const int sl = wrap_slot(steps - i, W);
-    const float* qr = c.qwin + (((int64_t)u * W + sl) * G + g) * r;
+  for (int o0 = 0; o0 < nold; o0 += 64) {
+    const int o = o0 + (tid >> 2), part = tid & 3;
     float z = 0.f;
-    for (int kk = 0; kk < r; ++kk) z += qr[kk] * ce[kk];
-    z *= qscale;
-    float* rs = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
-    const float m = rs[0], S = rs[1];
-    const float mn = fmaxf(m, z);
-    rs[0] = mn;
-    rs[1] = S * exp2f(m - mn) + exp2f(z - mn);
+    int sl = 0, g = 0;
+    if (o < nold) {
+      const int i = 1 + o / G;
+      g = o % G;
+      sl = wrap_slot(steps - i, W);
+      const float* qr = c.qwin + (((int64_t)u * W + sl) * G + g) * r;
+#pragma unroll 16
+      for (int kk = part; kk < r; kk += 4) z += qr[kk] * ce[kk];
+    }
+    z += __shfl_xor(z, 1);
+    z += __shfl_xor(z, 2);
+    if (o < nold && part == 0) {
+      z *= qscale;
+      float* rsp = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
+      const float m = rsp[0], S = rsp[1];
+      const float mn = fmaxf(m, z);
+      rsp[0] = mn;
+      rsp[1] = S * exp2f(m - mn) + exp2f(z - mn);
+    }
   }
 }
 
 hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_new,
                            const void* v_new, const CachePtrs& c, const DecodeWs& w,
                            hipStream_t st) {
+  const int vec = d.dtype == 0 ? 4 : 8;
+  const int ncb = (d.r + 4 * vec - 1) / (4 * vec);
   const int nvec = 1 + d.G;
-  const size_t lds = ((size_t)nvec * d.D + 4 * nvec * 64 + d.r) * sizeof(float);
-  dim3 grid((d.r + 63) / 64, U, 2);
+  size_t lds = ((size_t)nvec * d.D + 4 * nvec * 4 * vec) * sizeof(float);
+  if (lds < (size_t)d.r * sizeof(float)) lds = (size_t)d.r * sizeof(float);
+  dim3 grid(2 * ncb + 1, U);
   const float qscale = kLog2e / sqrtf((float)d.r);
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
-                       (const float*)k_new, (const float*)v_new, w.stepinfo, qscale);
+                       (const float*)k_new, (const float*)v_new, w, qscale, ncb);
   else
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, w.stepinfo, qscale);
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ncb);
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
-// latent scoring, bf16 storage: grid (nsplit, U), 64 * ceil(W*G/32) threads.
-// Wave w owns window rows [32w, 32w + 32) in "age order" (row rho = i*G + g is
-// query head-group g of the step i steps ago; rows 0..G-1 are the current
-// step).  The fp32 query coefficients (scaled by log2(e)/sqrt(r)) are split
-// into bf16 hi + lo parts held in registers for the whole block; key
-// coefficients stream through registers, 32 positions per MFMA tile.
-// K-index permutation: lane (n, kg) of the B operand holds, for k-step ks, the
-// 8 coefficients kg*r/2 + 8*ks + [0, 8) of position n (a contiguous run per
-// lane); the A operand uses the same permutation.
+// latent scoring, bf16 storage: grid (nsplit, U), 256 threads (4 waves).
+//
+// Key coefficients stream through a 3-stage LDS ring, 64 positions per tile,
+// filled by direct global->LDS loads (global_load_lds_dwordx4): two tiles are
+// in flight while the third is computed, without spending registers on them.
+// The block waits for a tile with an explicit vmcnt and a plain s_barrier;
+// the stages are distinct LDS objects, so the compiler's own LDS-DMA
+// tracking does not add a full wait.  Within a position row the 16-byte
+// chunks are XOR-swizzled by the position index, so the MFMA operand reads
+// (lane n reads chunk c of position n) hit distinct banks.
+//
+// Work units: (row block rb of 32 window rows, column block cb of 32 tile
+// positions); wave w owns units w, w + 4, ...  Window rows are in "age
+// order" (row rho = i*G + g is query head-group g of the step i steps ago;
+// rows 0..G-1 are the current step).  The fp32 query coefficients, scaled by
+// log2(e)/sqrt(r), are split into bf16 hi + lo parts held in registers as
+// MFMA A operands (32x32x16); the K-index permutation gives lane (n, kg) of
+// the B operand the chunks kg*r/16 + ks of position n, and the A operand the
+// same k's.
 // --------------------------------------------------------------------------
+constexpr int kScoreTP = 64;     // positions per tile
+constexpr int kScoreSeg = 512;   // positions per output segment (buffered in LDS)
+constexpr int kScoreNST = 4;     // LDS ring stages (3 tiles in flight)
+
 template <int KS>
-__global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeWs w,
-                                                    float qscale) {
+struct ScoreStage {
+  __attribute__((aligned(16))) uint8_t b[kScoreTP * KS * 32];  // 64 rows x r bf16
+};
+
+template <int KS, int NU>
+__global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeWs w) {
   constexpr int r = KS * 16, half = KS * 8;
+  constexpr int ROWB = r * 2;                 // bytes per coefficient row
+  constexpr int TILEB = kScoreTP * ROWB;
+  constexpr int NCH = r / 8;                  // 16-byte chunks per row
+  constexpr int SWZ = (NCH % 16 == 0) ? 15 : (NCH % 8 == 0) ? 7 : (NCH % 4 == 0) ? 3 : 0;
+  constexpr int PW = TILEB / 4096;            // DMA instructions per wave per tile
+  constexpr int SEGT = kScoreSeg / kScoreTP;  // tiles per segment
+  static_assert(TILEB % 4096 == 0, "tile must split into 1 KB pieces per wave");
+  static_assert(SEGT % kScoreNST == 0, "segment must hold whole rounds of the ring");
+  __shared__ ScoreStage<KS> st0, st1, st2, st3;
+  __shared__ float wstat[4][8][2];
+  __shared__ float segred[4][kScoreSeg];      // per row block partial scores
+  __shared__ float segspill[8][kScoreSeg];    // current rows' logits
+
   const int split = blockIdx.x, u = blockIdx.y;
-  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;
   const int Lcur = si[0], steps = si[1];
   const int G = d.G, W = d.W, s = d.s;
   const int weff = min(steps + 1, W);
   const int nrows = weff * G;
+  const int nrb = (W * G + 31) / 32;
   const int64_t cend = (int64_t)Lcur + 1 - d.nrec;
   const int64_t j0 = s + (int64_t)split * w.chunk;
   const int64_t j1 = min(j0 + (int64_t)w.chunk, cend);
-  float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
-  extern __shared__ float red[];  // [nw][chunk]
+  const int npos = (int)max(j1 - j0, (int64_t)0);
 
-  const int mm = l & 31, kg = l >> 5;
-  bf16x8 ahi[KS], alo[KS];
-  {
-    const int rho = 32 * wv + mm;
-    const float* qr = nullptr;
-    if (rho < nrows) {
-      const int i = rho / G, g = rho % G;
+  // ---- per-unit operands ---------------------------------------------------
+  int urb[NU], ucb[NU];
+  bool uact[NU];
+  bf16x8 ahi[NU][KS], alo[NU][KS];
+  float mrow[NU][16], irow[NU][16];
+  float nm[NU][4], ns[NU][4];
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    const int ui = wv + 4 * j;
+    uact[j] = ui < 2 * nrb;
+    urb[j] = uact[j] ? ui >> 1 : 0;
+    ucb[j] = ui & 1;
+    {  // A fragments from the window's hi / lo split (rows past the window -> 0)
+      const int rho = 32 * urb[j] + mm;
+      const bool valid = rho < nrows;
+      const int rv = valid ? rho : 0;
+      const int i = rv / G, g = rv % G;
       const int sl = wrap_slot(steps - i, W);
-      qr = c.qwin + (((int64_t)u * W + sl) * G + g) * r + kg * half;
-    }
+      const uint16_t* qh = c.qsplit + ((((int64_t)u * W + sl) * G + g) * 2) * r + kg * half;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u16x8 hv, lv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = qr ? qr[8 * ks + e] * qscale : 0.f;
-        const uint16_t hb = f2bf(x);
-        hv[e] = hb;
-        lv[e] = f2bf(x - bf2f(hb));
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 h = ld_bf16x8(qh + 8 * ks);
+        const bf16x8 lo = ld_bf16x8(qh + r + 8 * ks);
+        ahi[j][ks] = valid ? h : __builtin_bit_cast(bf16x8, u16x8{});
+        alo[j][ks] = valid ? lo : __builtin_bit_cast(bf16x8, u16x8{});
       }
-      ahi[ks] = __builtin_bit_cast(bf16x8, hv);
-      alo[ks] = __builtin_bit_cast(bf16x8, lv);
+    }
+    {  // older rows' running (max, sum); current and invalid rows excluded
+      float2 stv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 32 * urb[j] + acc_row32(i, l);
+        const int rv = rr < nrows ? rr : 0;
+        const int ii = rv / G, g = rv % G;
+        const int sl = wrap_slot(steps - ii, W);
+        stv[i] = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 32 * urb[j] + acc_row32(i, l);
+        const bool old_row = uact[j] && rr >= G && rr < nrows;
+        mrow[j][i] = old_row ? stv[i].x : FLT_MAX;
+        irow[j][i] = old_row ? 1.f / stv[i].y : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nm[j][i] = -INFINITY;
+      ns[j][i] = 0.f;
     }
   }
-  float mrow[16], irow[16];
+
+  // ---- DMA of one tile into a stage ----------------------------------------
+  // Piece q of this lane: LDS row pl, slot sl holds global chunk sl ^ (pl & SWZ);
+  // the lane offsets are the same for every tile, only the tile base moves.
+  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(
+      (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  uint32_t qoff[PW];
+  int qrow[PW];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rr = 32 * wv + acc_row32(i, l);
-    if (rr < G || rr >= nrows) {
-      mrow[i] = FLT_MAX;
-      irow[i] = 0.f;
-    } else {
-      const int ii = rr / G, g = rr % G;
-      const int sl = wrap_slot(steps - ii, W);
-      const float* rs = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
-      mrow[i] = rs[0];
-      irow[i] = 1.f / rs[1];
-    }
+  for (int q = 0; q < PW; ++q) {
+    const int Q = (wvu * PW + q) * 64 + l;
+    const int pl = Q / NCH, slot = Q % NCH;
+    qrow[q] = pl;
+    qoff[q] = (uint32_t)(pl * ROWB + ((slot ^ (pl & SWZ)) << 4));
   }
-  float nm[4], ns[4];
+  auto issue = [&](int64_t p0, uint8_t* stage) {
+    const uint8_t* tb = cbase + p0 * ROWB;
+    const bool tail = p0 + kScoreTP > c.Lmax;  // last tile of the buffer: clamp rows
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    nm[i] = -INFINITY;
-    ns[i] = 0.f;
-  }
-  const uint16_t* base = (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r + kg * half;
-  float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
-  for (int64_t p0 = j0; p0 < j1; p0 += 32) {
-    const int64_t jn = p0 + mm;
-    const bool pv = jn < j1;
-    const uint16_t* src = base + (pv ? jn : j0) * r;
-    bf16x8 b[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[ks] = ld_bf16x8(src + 8 * ks);
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc = mfma32x32x16(ahi[ks], b[ks], acc);
-      acc = mfma32x32x16(alo[ks], b[ks], acc);
+    for (int q = 0; q < PW; ++q) {
+      const uint8_t* src = tb + qoff[q];
+      if (tail) {
+        const int64_t pos = min(p0 + qrow[q], c.Lmax - 1);
+        src = cbase + pos * ROWB + (qoff[q] - qrow[q] * ROWB);
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
     }
-    float ps = 0.f;
+  };
+  constexpr int kWaitN = (kScoreNST - 1) * PW;  // groups allowed in flight
+  constexpr int kWaitImm = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int kLgkm0 = 0xF | (3 << 14) | (7 << 4);  // lgkmcnt(0)
+  constexpr int kVm0 = (7 << 4) | (15 << 8);          // vmcnt(0)
+
+  // tile t of the segment starting at seg0 (positions seg0 + t*TP + pl)
+  auto compute = [&](int seg0, int t, const uint8_t* stage) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ps += exp2f(acc[i] - mrow[i]) * irow[i];
-    ps += __shfl_xor(ps, 32);
-    if (l < 32) red[wv * w.chunk + (int)(p0 - j0) + mm] = ps;
-    if (wv == 0 && pv) {
+    for (int j = 0; j < NU; ++j) {
+      if (!uact[j]) continue;
+      const int pl = ucb[j] * 32 + mm;
+      const uint8_t* rowp = stage + pl * ROWB;
+      const int sw = pl & SWZ;
+      f32x16 acc = {};
+      if constexpr (KS % 8 == 0) {
+        const uint32_t rbase = lds_offset(rowp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * kg + i;
-        if (row < G) {
-          const float z = acc[i];
-          spill[(int64_t)row * w.Lc_cap + (jn - s)] = z;
-          const float mx = fmaxf(nm[i], z);
-          ns[i] = ns[i] * exp2f(nm[i] - mx) + exp2f(z - mx);
-          nm[i] = mx;
+        for (int k0 = 0; k0 < KS; k0 += 8) {
+          uint32_t ad[8];
+          bf16x8 bb[8];
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) ad[kk] = rbase + (((kg * KS + k0 + kk) ^ sw) << 4);
+          lds_read8(ad, bb);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            acc = mfma32x32x16(ahi[j][k0 + kk], bb[kk], acc);
+            acc = mfma32x32x16(alo[j][k0 + kk], bb[kk], acc);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(rowp + ((kg * KS + ks) ^ sw) * 16);
+          acc = mfma32x32x16(ahi[j][ks], bb, acc);
+          acc = mfma32x32x16(alo[j][ks], bb, acc);
+        }
+      }
+      // arguments are <= 0 (or -huge for excluded rows): the hardware exp2
+      // is exact enough and its flush of tiny results is harmless here
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(acc[i] - mrow[j][i]) * irow[j][i];
+      ps += __shfl_xor(ps, 32);
+      const int sp = t * kScoreTP + pl;         // position within the segment
+      if (l < 32) segred[urb[j]][sp] = ps;
+      if (urb[j] == 0) {
+        const bool pv = seg0 + sp < npos;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * kg + i;
+          if (row < G) {
+            const float z = acc[i];
+            segspill[row][sp] = z;
+            if (pv) {
+              const float mx = fmaxf(nm[j][i], z);
+              ns[j][i] = ns[j][i] * __builtin_amdgcn_exp2f(nm[j][i] - mx) +
+                         __builtin_amdgcn_exp2f(z - mx);
+              nm[j][i] = mx;
+            }
+          }
         }
       }
     }
-  }
-  __syncthreads();
+  };
+
   float* partial = w.partial + (int64_t)u * w.Lc_cap + (j0 - s);
-  for (int t = threadIdx.x; t < (int)(j1 - j0); t += blockDim.x) {
-    float sum = 0.f;
-    for (int q2 = 0; q2 < nw; ++q2) sum += red[q2 * w.chunk + t];
-    partial[t] = sum;
+  float* spill = w.spill + (int64_t)u * G * w.Lc_cap + (j0 - s);
+  for (int seg0 = 0; seg0 < npos; seg0 += kScoreSeg) {
+    const int segn = min(kScoreSeg, npos - seg0);
+    const int ntl = (segn + kScoreTP - 1) / kScoreTP;
+    const int64_t p0 = j0 + seg0;
+    auto tp = [&](int t) { return p0 + (int64_t)min(t, ntl - 1) * kScoreTP; };
+    issue(tp(0), st0.b);
+    issue(tp(1), st1.b);
+    issue(tp(2), st2.b);
+    // tile t lives in stage t % 4; one DMA group is issued per tile so the
+    // wave's outstanding count stays exactly three groups behind
+    for (int t = 0; t < ntl; t += kScoreNST) {
+#define KVLR_SCORE_STEP(k, SREAD, SNEXT)                 \
+      if (t + k >= ntl) break;                             \
+      issue(tp(t + k + 3), SNEXT);                         \
+      __builtin_amdgcn_s_waitcnt(kWaitImm);                \
+      __builtin_amdgcn_s_barrier();                        \
+      compute(seg0, t + k, SREAD);                         \
+      __builtin_amdgcn_s_waitcnt(kLgkm0);                  \
+      __builtin_amdgcn_s_barrier();
+      KVLR_SCORE_STEP(0, st0.b, st3.b)
+      KVLR_SCORE_STEP(1, st1.b, st0.b)
+      KVLR_SCORE_STEP(2, st2.b, st1.b)
+      KVLR_SCORE_STEP(3, st3.b, st2.b)
+#undef KVLR_SCORE_STEP
+    }
+    __builtin_amdgcn_s_waitcnt(kVm0);  // drain the ring before the flush
+    __syncthreads();
+    for (int e = tid; e < segn; e += 256) {
+      float sum = 0.f;
+      for (int q2 = 0; q2 < nrb; ++q2) sum += segred[q2][e];
+      partial[seg0 + e] = sum;
+    }
+    for (int e = tid; e < G * segn; e += 256) {
+      const int row = e / segn, sp = e % segn;
+      spill[(int64_t)row * w.Lc_cap + seg0 + sp] = segspill[row][sp];
+    }
+    __syncthreads();
   }
-  if (wv == 0) {
+
+  // current rows' (max, sum) over this split: lanes of one kg half, then waves
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float m = nm[i], sm = ns[i];
+      float m = nm[j][i], sm = ns[j][i];
+#pragma unroll
       for (int o = 1; o < 32; o <<= 1) {
         const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
         const float mx = fmaxf(m, m2);
@@ -291,12 +553,39 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
         sm = a + b2;
         m = mx;
       }
-      const int row = 4 * kg + i;
-      if (mm == 0 && row < G) {
-        tst[row * 2 + 0] = m;
-        tst[row * 2 + 1] = sm;
-      }
+      nm[j][i] = m;
+      ns[j][i] = sm;
     }
+  }
+  if (mm == 0) {
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kg + i;
+      float m = -INFINITY, sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        if (uact[j] && urb[j] == 0 && ns[j][i] > 0.f) {
+          const float mx = fmaxf(m, nm[j][i]);
+          sm = (m == -INFINITY ? 0.f : sm * exp2f(m - mx)) + ns[j][i] * exp2f(nm[j][i] - mx);
+          m = mx;
+        }
+      }
+      wstat[wv][row][0] = m;
+      wstat[wv][row][1] = sm;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = -INFINITY, sm = 0.f;
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const float m2 = wstat[q2][tid][0], s2 = wstat[q2][tid][1];
+      if (!(s2 > 0.f)) continue;
+      const float mx = fmaxf(m, m2);
+      sm = (m == -INFINITY ? 0.f : sm * exp2f(m - mx)) + s2 * exp2f(m2 - mx);
+      m = mx;
+    }
+    float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
+    tst[tid * 2 + 0] = m;
+    tst[tid * 2 + 1] = sm;
   }
 }
 
@@ -376,410 +665,682 @@ __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs
   }
 }
 
+template <int KS>
+static hipError_t launch_score_bf16(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                                    hipStream_t st) {
+  const int nrb = (d.W * d.G + 31) / 32;
+  dim3 grid(w.nsplit, U);
+  if (2 * nrb <= 4)
+    hipLaunchKernelGGL((k_score_bf16<KS, 1>), grid, dim3(256), 0, st, d, c, w);
+  else
+    hipLaunchKernelGGL((k_score_bf16<KS, 2>), grid, dim3(256), 0, st, d, c, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                         hipStream_t st) {
   const float qscale = kLog2e / sqrtf((float)d.r);
-  dim3 grid(w.nsplit, U);
   if (d.dtype == 0) {
+    dim3 grid(w.nsplit, U);
     const size_t lds = ((size_t)d.W * d.G * d.r + 2 * d.W * d.G + 512) * sizeof(float);
     hipLaunchKernelGGL(k_score_f32, grid, dim3(256), lds, st, d, c, w, qscale);
     return hipGetLastError();
   }
-  const int nw = (d.W * d.G + 31) / 32;
-  const size_t lds = (size_t)nw * w.chunk * sizeof(float);
   switch (d.r) {
-    case 128: hipLaunchKernelGGL(k_score_bf16<8>, grid, dim3(64 * nw), lds, st, d, c, w, qscale); break;
-    case 192: hipLaunchKernelGGL(k_score_bf16<12>, grid, dim3(64 * nw), lds, st, d, c, w, qscale); break;
-    case 256: hipLaunchKernelGGL(k_score_bf16<16>, grid, dim3(64 * nw), lds, st, d, c, w, qscale); break;
-    case 64: hipLaunchKernelGGL(k_score_bf16<4>, grid, dim3(64 * nw), lds, st, d, c, w, qscale); break;
-    case 32: hipLaunchKernelGGL(k_score_bf16<2>, grid, dim3(64 * nw), lds, st, d, c, w, qscale); break;
+    case 128: return launch_score_bf16<8>(d, U, c, w, st);
+    case 192: return launch_score_bf16<12>(d, U, c, w, st);
+    case 256: return launch_score_bf16<16>(d, U, c, w, st);
+    case 64: return launch_score_bf16<4>(d, U, c, w, st);
+    case 32: return launch_score_bf16<2>(d, U, c, w, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+
+// --------------------------------------------------------------------------
+// pooling: grid (ceil(Lc_cap / kPoolChunk), U), 256 threads.
+//   1. merge the current rows' per-split (m, S) (every block; block 0 stores
+//      them in rowstat at this step's window slot);
+//   2. score[j] = partial[j] + sum_g exp2(z_g[j] - m_g) / S_g for the block's
+//      candidates plus a halo of kappa/2 on each side;
+//   3. pooled key = max over |d| <= kappa/2 inside the candidates, stored as
+//      the float's bit pattern (scores are >= 0, so bits order like values).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
+  if (!(s2 > 0.f)) return;
+  if (!(s > 0.f)) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mx = fmaxf(m, m2);
+  s = s * exp2f(m - mx) + s2 * exp2f(m2 - mx);
+  m = mx;
+}
+
+__global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
+                                              float* __restrict__ scores_user) {
+  const int blk = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int32_t* si = w.stepinfo + 4 * u;
+  if (si[2]) return;
+  const int Lcur = si[0], steps = si[1];
+  const int G = d.G, s = d.s;
+  const int nc = Lcur + 1 - d.nrec - s;
+  const int c0 = blk * kPoolChunk;
+  if (c0 >= nc && blk != 0) return;
+  const int c1 = min(c0 + kPoolChunk, nc);
+  const int h = d.kappa >> 1;
+  __shared__ float Mg[8], Ig[8];
+  __shared__ float wm[4][8], wsum[4][8];
+  __shared__ float sc[kPoolChunk + 256];
+  {  // 1. current rows' statistics (all G rows at once)
+    const int lane = tid & 63, wv = tid >> 6;
+    const float* tp = w.tilestat + (int64_t)u * w.nsplit * G * 2;
+    float m[8], sm[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      m[g] = 0.f;
+      sm[g] = 0.f;
+    }
+    for (int sp = tid; sp < w.nsplit; sp += 256) {
+      float2 v[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        v[g] = *reinterpret_cast<const float2*>(tp + (sp * G + min(g, G - 1)) * 2);
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g < G) ms_combine(m[g], sm[g], v[g].x, v[g].y);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < G) {
+          const float m2 = __shfl_xor(m[g], o), s2 = __shfl_xor(sm[g], o);
+          ms_combine(m[g], sm[g], m2, s2);
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        wm[wv][g] = m[g];
+        wsum[wv][g] = sm[g];
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mm = wm[0][tid], ss = wsum[0][tid];
+      for (int q2 = 1; q2 < 4; ++q2) ms_combine(mm, ss, wm[q2][tid], wsum[q2][tid]);
+      Mg[tid] = mm;
+      Ig[tid] = 1.f / ss;
+      if (blk == 0) {
+        float* rs = c.rowstat + (((int64_t)u * d.W + steps % d.W) * G + tid) * 2;
+        rs[0] = mm;
+        rs[1] = ss;
+      }
+    }
+    __syncthreads();
+  }
+  if (c0 >= nc) return;
+  const float* part = w.partial + (int64_t)u * w.Lc_cap;
+  const float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
+  const int lo = max(c0 - h, 0), hi = min(c1 + h, nc);
+  constexpr int NIT = (kPoolChunk + 256) / 256;
+  float vals[NIT];
+  float pv[NIT], sv[NIT][8];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {  // clamped, unconditional loads
+    const int j = min(lo + tid + 256 * it, hi - 1);
+    pv[it] = part[j];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) sv[it][g] = spill[(int64_t)min(g, G - 1) * w.Lc_cap + j];
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    float v = pv[it];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < G) v += exp2f(sv[it][g] - Mg[g]) * Ig[g];
+    vals[it] = v;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int j = lo + tid + 256 * it;
+    if (j < hi) {
+      sc[j - lo] = vals[it];
+      if (scores_user && j >= c0 && j < c1) scores_user[(int64_t)u * c.Lmax + s + j] = vals[it];
+    }
+  }
+  __syncthreads();
+  uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
+  // thread t: candidates c0 + 8t .. c0 + 8t + 7 (kPoolChunk = 8 * 256)
+  const int jb = c0 + 8 * tid;
+  if (jb < c1) {
+    if (h <= 4) {
+      float win[16];  // sc at jb - 4 .. jb + 11, -inf outside the candidates
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = jb - 4 + e;
+        win[e] = (j >= 0 && j < nc) ? sc[min(max(j - lo, 0), kPoolChunk + 255)] : -INFINITY;
+      }
+      uint32_t kv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float mx = win[e + 4];
+#pragma unroll
+        for (int dd = 1; dd <= 4; ++dd)
+          if (dd <= h) mx = fmaxf(mx, fmaxf(win[e + 4 - dd], win[e + 4 + dd]));
+        kv[e] = __float_as_uint(mx);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (jb + e < c1) keys[jb + e] = kv[e];
+    } else {
+      for (int j = jb; j < min(jb + 8, c1); ++j) {
+        float mx = sc[j - lo];
+        for (int dd = 1; dd <= h; ++dd) {
+          if (j - dd >= 0) mx = fmaxf(mx, sc[j - dd - lo]);
+          if (j + dd < nc) mx = fmaxf(mx, sc[j + dd - lo]);
+        }
+        keys[j] = __float_as_uint(mx);
+      }
+    }
+  }
+}
+
+hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                       float* scores_user, hipStream_t st) {
+  dim3 grid((w.Lc_cap + kPoolChunk - 1) / kPoolChunk, U);
+  hipLaunchKernelGGL(k_pool, grid, dim3(256), 0, st, d, c, w, scores_user);
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
-// selection: one 1024-thread block per unit.
-//   1. merge the current rows' split statistics -> rowstat of this slot
-//   2. score[j] = partial[j] + sum_g exp2(z_g[j] - m_g) / S_g
-//   3. pooled key = max over |d| <= kappa/2 inside the candidates (bits of a
-//      non-negative float order like the float)
-//   4. radix select (4 x 8 bits, most significant first) of the k-th key T
-//   5. ordered compaction: keys > T, then keys == T in index order until k
+// top-k: one 1024-thread block per unit.
+//   Thread t owns a contiguous run of keys (kept in registers while the run
+//   fits, else re-read per pass).  Threshold key T = the k-th largest key:
+//   a 12-bit histogram of the keys' top bits, then two 10-bit refinement
+//   passes over the keys with that prefix.  Ordered compaction: every key
+//   > T, and the first (k - #{key > T}) keys == T in position order (ties ->
+//   lower position), written in ascending position order.  Also advances
+//   lens and writes the outputs of units whose cache is full (topk = -1,
+//   out = 0).
 // --------------------------------------------------------------------------
-__device__ __forceinline__ int block_excl_scan_flag(bool f, int* wsum, int* total) {
-  // 1024 threads = 16 waves; wsum: 16 ints of LDS
+constexpr int kTopkRegKeys = 32;  // keys per thread held in registers
+
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* wtot, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(f);
-  const int within = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wid] = __popcll(bal);
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wid] = x;
   __syncthreads();
   int before = 0, tot = 0;
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int v = wsum[i];
-    if (i < wid) before += v;
-    tot += v;
+    const int t = wtot[i];
+    if (i < wid) before += t;
+    tot += t;
   }
   __syncthreads();
   *total = tot;
-  return before + within;
+  return before + x - v;
 }
 
-__global__ __launch_bounds__(1024) void k_select(Dims d, CachePtrs c, DecodeWs w,
-                                                 int32_t* __restrict__ topk_user,
-                                                 float* __restrict__ scores_user) {
+// apply f(key, position) to the thread's run [j0, j1) in position order
+template <typename F>
+__device__ __forceinline__ void for_keys(const uint32_t* keys, int j0, int j1, bool in_regs,
+                                         const uint32_t* kr, F&& f) {
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; ++i)
+      if (j0 + i < j1) f(kr[i], j0 + i);
+  } else {
+    for (int jb = j0; jb < j1; jb += kTopkRegKeys) {
+      uint32_t buf[kTopkRegKeys];
+#pragma unroll
+      for (int i = 0; i < kTopkRegKeys; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + jb + i);
+        buf[i] = v.x;
+        buf[i + 1] = v.y;
+        buf[i + 2] = v.z;
+        buf[i + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < kTopkRegKeys; ++i)
+        if (jb + i < j1) f(buf[i], jb + i);
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_topk(Dims d, CachePtrs c, DecodeWs w,
+                                               int32_t* __restrict__ topk_user,
+                                               float* __restrict__ out) {
   const int u = blockIdx.x, tid = threadIdx.x;
   const int32_t* si = w.stepinfo + 4 * u;
-  const int G = d.G, W = d.W, s = d.s, k = d.k;
+  const int k = d.k;
   if (si[2]) {
     if (topk_user)
-      for (int i = tid; i < k; i += blockDim.x) topk_user[(int64_t)u * k + i] = -1;
+      for (int i = tid; i < k; i += 1024) topk_user[(int64_t)u * k + i] = -1;
+    for (int i = tid; i < d.Hq * d.dh; i += 1024) out[(int64_t)u * d.Hq * d.dh + i] = 0.f;
     return;
   }
   const int Lcur = si[0], steps = si[1];
-  const int slot = steps % W;
+  const int s = d.s;
   const int nc = Lcur + 1 - d.nrec - s;
-  __shared__ float Mg[8], Ig[8];
-  __shared__ unsigned int hist[256];
-  __shared__ int wsum[16];
-  __shared__ unsigned int sh_prefix;
-  __shared__ int sh_remaining;
-  if (tid < G) {
-    float M = -INFINITY, S = 0.f;
-    const float* tp = w.tilestat + (int64_t)u * w.nsplit * G * 2;
-    for (int sp = 0; sp < w.nsplit; ++sp) {
-      const float m2 = tp[(sp * G + tid) * 2], s2 = tp[(sp * G + tid) * 2 + 1];
-      if (!(s2 > 0.f)) continue;
-      const float mx = fmaxf(M, m2);
-      S = (M == -INFINITY ? 0.f : S * exp2f(M - mx)) + s2 * exp2f(m2 - mx);
-      M = mx;
-    }
-    Mg[tid] = M;
-    Ig[tid] = 1.f / S;
-    float* rs = c.rowstat + (((int64_t)u * W + slot) * G + tid) * 2;
-    rs[0] = M;
-    rs[1] = S;
-  }
-  __syncthreads();
-  const float* part = w.partial + (int64_t)u * w.Lc_cap;
-  const float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
-  float* score = w.score + (int64_t)u * w.Lc_cap;
-  for (int j = tid; j < nc; j += blockDim.x) {
-    float sc = part[j];
-    for (int g = 0; g < G; ++g) sc += exp2f(spill[(int64_t)g * w.Lc_cap + j] - Mg[g]) * Ig[g];
-    score[j] = sc;
-    if (scores_user) scores_user[(int64_t)u * c.Lmax + s + j] = sc;
-  }
-  __threadfence_block();
-  __syncthreads();
-  uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
-  const int hk = d.kappa >> 1;
-  for (int j = tid; j < nc; j += blockDim.x) {
-    float mx = score[j];
-    for (int dd = 1; dd <= hk; ++dd) {
-      if (j - dd >= 0) mx = fmaxf(mx, score[j - dd]);
-      if (j + dd < nc) mx = fmaxf(mx, score[j + dd]);
-    }
-    keys[j] = __float_as_uint(mx);
-  }
-  __threadfence_block();
-  __syncthreads();
   const int kk = min(k, nc);
-  int32_t* out = w.topk + (int64_t)u * k;
-  if (kk > 0) {
-    unsigned int prefix = 0, mask = 0;
-    int remaining = kk;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int j = tid; j < nc; j += blockDim.x) {
-        const unsigned int key = keys[j];
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int cum = 0, sel = 0;
-        for (int b = 255; b >= 0; --b) {
-          const int h = (int)hist[b];
-          if (cum + h >= remaining) {
-            sel = b;
-            break;
-          }
-          cum += h;
-        }
-        sh_prefix = prefix | ((unsigned int)sel << shift);
-        sh_remaining = remaining - cum;
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      remaining = sh_remaining;
-      mask |= 255u << shift;
-    }
-    const unsigned int T = prefix;
-    const int need_eq = remaining;
-    int base = 0, eq_base = 0;
-    for (int c0 = 0; c0 < nc; c0 += blockDim.x) {
-      const int j = c0 + tid;
-      const unsigned int key = j < nc ? keys[j] : 0u;
-      const bool gt = j < nc && key > T;
-      const bool eq = j < nc && key == T;
-      int eq_tot, sel_tot;
-      const int eq_rank = eq_base + block_excl_scan_flag(eq, wsum, &eq_tot);
-      const bool take = gt || (eq && eq_rank < need_eq);
-      const int pos = base + block_excl_scan_flag(take, wsum, &sel_tot);
-      if (take) {
-        out[pos] = s + j;
-        if (topk_user) topk_user[(int64_t)u * k + pos] = s + j;
-      }
-      base += sel_tot;
-      eq_base += eq_tot;
-    }
+  if (tid == 0) {
+    c.lens[2 * u] = Lcur + 1;
+    c.lens[2 * u + 1] = steps + 1;
   }
   if (topk_user)
-    for (int i = kk + tid; i < k; i += blockDim.x) topk_user[(int64_t)u * k + i] = -1;
+    for (int i = kk + tid; i < k; i += 1024) topk_user[(int64_t)u * k + i] = -1;
+  if (kk <= 0) return;
+  __shared__ unsigned int hs[kHistBins];
+  __shared__ int wtot[16];
+  __shared__ unsigned int sh_prefix;
+  __shared__ int sh_rem;
+  const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
+  // runs of `per` keys (multiple of 32, so vector reads stay aligned and
+  // inside the padded key buffer)
+  const int per = ((nc + 1023) / 1024 + kTopkRegKeys - 1) / kTopkRegKeys * kTopkRegKeys;
+  const int j0 = tid * per, j1 = min(j0 + per, nc);
+  const bool in_regs = per == kTopkRegKeys;
+  uint32_t kr[kTopkRegKeys];
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; i += 4) {
+      // runs start inside the padded buffer; entries past j1 are ignored
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0, w.Lc_cap - kTopkRegKeys) + i);
+      kr[i] = v.x;
+      kr[i + 1] = v.y;
+      kr[i + 2] = v.z;
+      kr[i + 3] = v.w;
+    }
+  }
+  for (int i = tid; i < kHistBins; i += 1024) hs[i] = 0u;
+  __syncthreads();
+  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) { atomicAdd(&hs[key >> 20], 1u); });
+  __syncthreads();
+  int tot;
+  {  // level 1: thread t owns bins [4t, 4t + 4)
+    const int b0 = 4 * tid;
+    const int local = (int)(hs[b0] + hs[b0 + 1] + hs[b0 + 2] + hs[b0 + 3]);
+    const int excl = block_excl_scan_1024(local, wtot, &tot);
+    int above = tot - excl - local;  // keys in higher bins
+    if (above < kk && above + local >= kk) {
+      for (int bb = b0 + 3; bb >= b0; --bb) {
+        if (above + (int)hs[bb] >= kk) {
+          sh_prefix = (unsigned int)bb << 20;
+          sh_rem = kk - above;
+          break;
+        }
+        above += (int)hs[bb];
+      }
+    }
+    __syncthreads();
+  }
+  unsigned int prefix = sh_prefix, mask = 0xFFF00000u;
+  int rem = sh_rem;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = 10 - 10 * pass;
+    hs[tid] = 0u;
+    __syncthreads();
+    for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
+      if ((key & mask) == prefix) atomicAdd(&hs[(key >> shift) & 1023u], 1u);
+    });
+    __syncthreads();
+    const int local = (int)hs[tid];
+    const int excl = block_excl_scan_1024(local, wtot, &tot);
+    const int above = tot - excl - local;
+    if (above < rem && above + local >= rem) {
+      sh_prefix = prefix | ((unsigned int)tid << shift);
+      sh_rem = rem - above;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    rem = sh_rem;
+    mask |= 1023u << shift;
+  }
+  const unsigned int T = prefix;
+  const int need_eq = rem;
+  int c_gt = 0, c_eq = 0;
+  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
+    c_gt += key > T;
+    c_eq += key == T;
+  });
+  const int eq_base = block_excl_scan_1024(c_eq, wtot, &tot);
+  const int take_eq = max(0, min(need_eq - eq_base, c_eq));
+  int off = block_excl_scan_1024(c_gt + take_eq, wtot, &tot);
+  int32_t* sel = w.topk + (int64_t)u * k;
+  int seen = 0;
+  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
+    bool take = key > T;
+    if (key == T) {
+      take = seen < take_eq;
+      ++seen;
+    }
+    if (take) {
+      sel[off] = s + j;
+      if (topk_user) topk_user[(int64_t)u * k + off] = s + j;
+      ++off;
+    }
+  });
 }
 
-hipError_t launch_select(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
-                         int32_t* topk_user, float* scores_user, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(U), dim3(1024), 0, st, d, c, w, topk_user, scores_user);
+hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                       int32_t* topk_user, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_topk, dim3(U), dim3(1024), 0, st, d, c, w, topk_user, out);
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
 // sparse reconstruction + exact attention: grid (nsa, H_kv, U), 256 threads.
-// Split `split` owns rows [64 split, 64 split + 64) of the row list
+// Block (split, h, u) owns rows [split * rps, (split + 1) * rps) of the row list
 //   [0, s)            sinks (exact)
 //   [s, s + nrec)     recent ring (exact)
 //   [s + nrec, R)     selected positions, reconstructed as c . B^T
-// For bf16 the reconstruction is an MFMA 32x32x16 product [rows x r] x
-// [r x d_h] per KV head (the basis rows of head h are contiguous in r);
-// fp32 storage uses plain dot products.  Then for the G query heads of this
-// KV head: logits, split-local softmax (max, sum) and sum p.V into part.
+// processed in tiles of 32 rows with an online softmax for the G query heads
+// of KV head h.  bf16: wave w owns channels [32w, 32w + 32) of the head and
+// keeps its basis rows (K and V) in registers as MFMA B operands; the tile's
+// gathered coefficient rows are staged in LDS (coalesced 16-byte loads) and
+// read as A operands; MFMA 32x32x16 gives K_hat and V_hat in fp32.  fp32
+// storage reconstructs with plain dot products.  The last block of a
+// (unit, head) to finish merges the splits (online-softmax combination) into
+// the output.
 // --------------------------------------------------------------------------
-template <typename T, int KS>
+__host__ __device__ __forceinline__ int attend_ldk(int dh) { return dh % 4 == 0 ? dh + 4 : dh + 1; }
+
+template <typename T, int KS, int DH>
 __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
-                                                const T* __restrict__ q, float sm_scale) {
+                                                const T* __restrict__ q, float* __restrict__ out,
+                                                float sm_scale) {
   const int split = blockIdx.x, h = blockIdx.y, u = blockIdx.z;
   const int tid = threadIdx.x;
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;
   const int Lcur = si[0];
-  const int s = d.s, nrec = d.nrec, dh = d.dh, G = d.G, D = d.D, r = d.r;
+  const int s = d.s, nrec = d.nrec, G = d.G, D = d.D, r = d.r;
+  const int dh = DH > 0 ? DH : d.dh;
   const int nc = Lcur + 1 - nrec - s;
   const int kk = min(d.k, nc);
   const int R = s + nrec + kk;
-  const int row0 = split * 64;
-  const int ldk = dh + 1;
-  float* part = w.part + (int64_t)u * d.Hq * w.nsa * (dh + 2);
-  if (row0 >= R) {
-    for (int e = tid; e < G * (dh + 2); e += blockDim.x) {
-      const int g = e / (dh + 2), j = e % (dh + 2);
-      part[((int64_t)(h * G + g) * w.nsa + split) * (dh + 2) + j] = (j == 0) ? -INFINITY : 0.f;
-    }
-    return;
-  }
-  extern __shared__ float sm[];
-  float* Kh = sm;                 // [64][dh + 1]
-  float* Vh = Kh + 64 * ldk;      // [64][dh + 1]
-  float* qs = Vh + 64 * ldk;      // [G][dh]
-  float* pl = qs + G * dh;        // [G][64]
-  float* hs = pl + G * 64;        // [G][2]
-  for (int e = tid; e < G * dh; e += blockDim.x) {
+  const int row0 = split * w.rows_per_split;
+  const int row1 = min(row0 + w.rows_per_split, R);
+  const int ldk = attend_ldk(dh);
+  constexpr int ROWP = KS * 16 + 8;  // padded LDS row of staged coefficients (bf16)
+  extern __shared__ float smf[];
+  float* Kt = smf;                   // [32][dh + 1]
+  float* Vt = Kt + 32 * ldk;         // [32][dh + 1]
+  float* qs = Vt + 32 * ldk;         // [G][dh]
+  float* pl = qs + G * dh;           // [G][32]
+  float* alpha = pl + G * 32;        // [G]
+  float* run = alpha + 8;            // [G][2] running (max, sum)
+  uint16_t* Ak = reinterpret_cast<uint16_t*>(run + 16);  // [32][ROWP] (bf16 only)
+  uint16_t* Av = Ak + 32 * ROWP;
+  for (int e = tid; e < G * dh; e += 256) {
     const int g = e / dh, j = e % dh;
     qs[e] = Elem<T>::ld(q, ((int64_t)u * d.Hq + h * G + g) * dh + j);
   }
+  if (tid < G) {
+    run[2 * tid] = -INFINITY;
+    run[2 * tid + 1] = 0.f;
+  }
   const int32_t* sel = w.topk + (int64_t)u * d.k;
+  const int wv = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
+  const int ncb = dh / 32;
+  bf16x8 bk[KS > 0 ? KS : 1], bv[KS > 0 ? KS : 1];
   if constexpr (KS > 0) {
     constexpr int half = KS * 8;
-    const int wv = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
-    const int ncb = dh / 32;
-    for (int kind = 0; kind < 2; ++kind) {
-      const uint16_t* Cb = (const uint16_t*)(kind ? c.coef_v : c.coef_k);
-      const uint16_t* Bb = (const uint16_t*)(kind ? c.basis_v : c.basis_k);
-      float* dst = kind ? Vh : Kh;
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = row0 + 32 * mb + mm;
-        const bool rec = row >= s + nrec && row < R;
-        const int64_t pos = rec ? sel[row - s - nrec] : 0;
-        const uint16_t* asrc = Cb + ((int64_t)u * c.Lmax + pos) * (KS * 16) + kg * half;
-        bf16x8 a[KS];
+    if (wv < ncb) {
+      const int ch = h * dh + 32 * wv + mm;
+      const uint16_t* pk = (const uint16_t*)c.basis_k + ((int64_t)u * D + ch) * (KS * 16) + kg * half;
+      const uint16_t* pv = (const uint16_t*)c.basis_v + ((int64_t)u * D + ch) * (KS * 16) + kg * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bk[ks] = ld_bf16x8(pk + 8 * ks);
+        bv[ks] = ld_bf16x8(pv + 8 * ks);
+      }
+    }
+  }
+  float oacc[4] = {0.f, 0.f, 0.f, 0.f};
+  // gathered coefficient rows of a tile: thread-owned 16-byte pieces
+  // e = tid + 256 i (row e / (r / 8), piece e % (r / 8)); the next tile is
+  // fetched into registers while the current one is computed
+  constexpr int NPIECE = KS > 0 ? (32 * KS * 2 + 255) / 256 : 1;
+  u16x8 fk[NPIECE], fv[NPIECE];
+  auto fetch = [&](int t0) {
+    if constexpr (KS > 0) {
+      constexpr int r16 = KS * 16;
+#pragma unroll
+      for (int i = 0; i < NPIECE; ++i) {
+        const int e = tid + 256 * i;
+        const int rr = e / (r16 / 8), cc = e % (r16 / 8);
+        const int row = t0 + rr;
+        // exact or out-of-range rows read selected entry 0 and are zeroed
+        const bool rec = e < 32 * (r16 / 8) && row >= s + nrec && row < R;
+        const int si2 = rec ? row - s - nrec : 0;  // entry 0 always exists
+        const int64_t pos = min(max((int64_t)sel[si2], (int64_t)0), c.Lmax - 1);
+        const int ccl = cc < r16 / 8 ? cc : 0;
+        const u16x8 a = *reinterpret_cast<const u16x8*>((const uint16_t*)c.coef_k + ((int64_t)u * c.Lmax + pos) * r16 + 8 * ccl);
+        const u16x8 b = *reinterpret_cast<const u16x8*>((const uint16_t*)c.coef_v + ((int64_t)u * c.Lmax + pos) * r16 + 8 * ccl);
+        fk[i] = rec ? a : u16x8{};
+        fv[i] = rec ? b : u16x8{};
+      }
+    }
+  };
+  if (row0 < row1) fetch(row0);
+  for (int t0 = row0; t0 < row1; t0 += 32) {
+    if constexpr (KS > 0) {
+      constexpr int r16 = KS * 16, half = KS * 8;
+#pragma unroll
+      for (int i = 0; i < NPIECE; ++i) {
+        const int e = tid + 256 * i;
+        if (e < 32 * (r16 / 8)) {
+          const int rr = e / (r16 / 8), cc = e % (r16 / 8);
+          *reinterpret_cast<u16x8*>(Ak + rr * ROWP + 8 * cc) = fk[i];
+          *reinterpret_cast<u16x8*>(Av + rr * ROWP + 8 * cc) = fv[i];
+        }
+      }
+      __syncthreads();
+      if (t0 + 32 < row1) fetch(t0 + 32);
+      if (wv < ncb) {
+        f32x16 ak = {}, av = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if (rec)
-            a[ks] = ld_bf16x8(asrc + 8 * ks);
-          else
-            a[ks] = __builtin_bit_cast(bf16x8, u16x8{});
+          const bf16x8 a1 = ld_bf16x8(Ak + mm * ROWP + kg * half + 8 * ks);
+          const bf16x8 a2 = ld_bf16x8(Av + mm * ROWP + kg * half + 8 * ks);
+          ak = mfma32x32x16(a1, bk[ks], ak);
+          av = mfma32x32x16(a2, bv[ks], av);
         }
-        for (int cb = wv; cb < ncb; cb += 4) {
-          const int ch = h * dh + 32 * cb + mm;
-          const uint16_t* bsrc = Bb + ((int64_t)u * D + ch) * (KS * 16) + kg * half;
-          f32x16 acc = {};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[ks], ld_bf16x8(bsrc + 8 * ks), acc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) dst[(32 * mb + acc_row32(i, l)) * ldk + 32 * cb + mm] = acc[i];
+        for (int i = 0; i < 16; ++i) {
+          Kt[acc_row32(i, l) * ldk + 32 * wv + mm] = ak[i];
+          Vt[acc_row32(i, l) * ldk + 32 * wv + mm] = av[i];
         }
       }
-    }
-  } else {
-    for (int e = tid; e < 64 * dh; e += blockDim.x) {
-      const int rr = e / dh, j = e % dh;
-      const int row = row0 + rr;
-      float kv = 0.f, vv = 0.f;
-      if (row >= s + nrec && row < R) {
-        const int64_t pos = sel[row - s - nrec];
-        const T* ck = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pos) * r;
-        const T* cv = (const T*)c.coef_v + ((int64_t)u * c.Lmax + pos) * r;
-        const T* bk = (const T*)c.basis_k + ((int64_t)u * D + h * dh + j) * r;
-        const T* bv = (const T*)c.basis_v + ((int64_t)u * D + h * dh + j) * r;
-        for (int i = 0; i < r; ++i) {
-          kv += Elem<T>::ld(ck, i) * Elem<T>::ld(bk, i);
-          vv += Elem<T>::ld(cv, i) * Elem<T>::ld(bv, i);
-        }
-      }
-      Kh[rr * ldk + j] = kv;
-      Vh[rr * ldk + j] = vv;
-    }
-  }
-  __syncthreads();
-  // exact rows
-  for (int e = tid; e < 64 * dh; e += blockDim.x) {
-    const int rr = e / dh, j = e % dh;
-    const int row = row0 + rr;
-    if (row < s) {
-      Kh[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_k, ((int64_t)u * s + row) * D + h * dh + j);
-      Vh[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_v, ((int64_t)u * s + row) * D + h * dh + j);
-    } else if (row < s + nrec) {
-      const int slot = row - s;
-      Kh[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_k, ((int64_t)u * nrec + slot) * D + h * dh + j);
-      Vh[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_v, ((int64_t)u * nrec + slot) * D + h * dh + j);
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * 64; e += blockDim.x) {
-    const int g = e >> 6, rr = e & 63;
-    float z = -INFINITY;
-    if (row0 + rr < R) {
-      float dot = 0.f;
-      for (int j = 0; j < dh; ++j) dot += qs[g * dh + j] * Kh[rr * ldk + j];
-      z = dot * sm_scale;
-    }
-    pl[e] = z;
-  }
-  __syncthreads();
-  {
-    const int wv = tid >> 6, l = tid & 63;
-    for (int g = wv; g < G; g += 4) {
-      const float z = pl[g * 64 + l];
-      const float m = warp_max(z);
-      const float e = (z == -INFINITY) ? 0.f : exp2f(z - m);
-      const float ls = warp_sum(e);
-      pl[g * 64 + l] = e;
-      if (l == 0) {
-        hs[2 * g] = m;
-        hs[2 * g + 1] = ls;
-      }
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * (dh + 2); e += blockDim.x) {
-    const int g = e / (dh + 2), j = e % (dh + 2);
-    float v;
-    if (j < 2) {
-      v = hs[2 * g + j];
     } else {
-      v = 0.f;
-      for (int rr = 0; rr < 64; ++rr) v += pl[g * 64 + rr] * Vh[rr * ldk + (j - 2)];
+      for (int e = tid; e < 32 * dh; e += 256) {
+        const int rr = e / dh, j = e % dh;
+        const int row = t0 + rr;
+        float kv = 0.f, vv = 0.f;
+        if (row >= s + nrec && row < R) {
+          const int64_t pos = sel[row - s - nrec];
+          const T* ck = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pos) * r;
+          const T* cv = (const T*)c.coef_v + ((int64_t)u * c.Lmax + pos) * r;
+          const T* bkp = (const T*)c.basis_k + ((int64_t)u * D + h * dh + j) * r;
+          const T* bvp = (const T*)c.basis_v + ((int64_t)u * D + h * dh + j) * r;
+          for (int i = 0; i < r; ++i) {
+            kv += Elem<T>::ld(ck, i) * Elem<T>::ld(bkp, i);
+            vv += Elem<T>::ld(cv, i) * Elem<T>::ld(bvp, i);
+          }
+        }
+        Kt[rr * ldk + j] = kv;
+        Vt[rr * ldk + j] = vv;
+      }
     }
-    part[((int64_t)(h * G + g) * w.nsa + split) * (dh + 2) + j] = v;
+    __syncthreads();
+    // exact rows of this tile
+    if (t0 < s + nrec) {
+      for (int e = tid; e < 32 * dh; e += 256) {
+        const int rr = e / dh, j = e % dh;
+        const int row = t0 + rr;
+        if (row < s) {
+          Kt[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_k, ((int64_t)u * s + row) * D + h * dh + j);
+          Vt[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_v, ((int64_t)u * s + row) * D + h * dh + j);
+        } else if (row < s + nrec) {
+          const int slot = row - s;
+          Kt[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_k, ((int64_t)u * nrec + slot) * D + h * dh + j);
+          Vt[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_v, ((int64_t)u * nrec + slot) * D + h * dh + j);
+        }
+      }
+      __syncthreads();
+    }
+    // logits and online softmax; thread (g, rr) = (tid / 32, tid % 32)
+    {
+      const int g = tid >> 5, rr = tid & 31;
+      float z = -INFINITY;
+      if (g < G && t0 + rr < row1) {
+        float dot = 0.f;
+        if constexpr (DH > 0) {
+          const f32x4* kr = reinterpret_cast<const f32x4*>(Kt + rr * ldk);
+          const f32x4* qv = reinterpret_cast<const f32x4*>(qs + g * DH);
+          f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j4 = 0; j4 < DH / 4; ++j4) a4 += qv[j4] * kr[j4];
+          dot = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        } else {
+          for (int j = 0; j < dh; ++j) dot += qs[g * dh + j] * Kt[rr * ldk + j];
+        }
+        z = dot * sm_scale;
+      }
+      float tmax = z;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+      const float m_old = g < G ? run[2 * g] : 0.f;
+      const float m_new = fmaxf(m_old, tmax);
+      const float pz = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
+      float ps = pz;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o);
+      __syncthreads();
+      if (g < G) {
+        pl[g * 32 + rr] = pz;
+        if (rr == 0) {
+          const float a = (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
+          alpha[g] = a;
+          run[2 * g] = m_new;
+          run[2 * g + 1] = run[2 * g + 1] * a + ps;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      if (e < G * dh) {
+        const int g = e / dh, j = e % dh;
+        float acc = oacc[i] * alpha[g];
+        for (int rr = 0; rr < 32; ++rr) acc += pl[g * 32 + rr] * Vt[rr * ldk + j];
+        oacc[i] = acc;
+      }
+    }
+    __syncthreads();
   }
+  // split partial
+  float* part = w.part + (int64_t)u * d.Hq * w.nsa * (dh + 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    if (e < G * dh) {
+      const int g = e / dh, j = e % dh;
+      part[((int64_t)(h * G + g) * w.nsa + split) * (dh + 2) + 2 + j] = oacc[i];
+    }
+  }
+  if (tid < G) {
+    part[((int64_t)(h * G + tid) * w.nsa + split) * (dh + 2) + 0] = run[2 * tid];
+    part[((int64_t)(h * G + tid) * w.nsa + split) * (dh + 2) + 1] = run[2 * tid + 1];
+  }
+}
+
+// merge of the row splits of one (unit, query head): online-softmax
+// combination of the split partials (max, sum, unnormalised output)
+__global__ __launch_bounds__(128) void k_merge(Dims d, DecodeWs w, float* __restrict__ out) {
+  const int a = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  if (w.stepinfo[4 * u + 2]) return;  // full unit: the top-k kernel wrote zeros
+  const int dh = d.dh;
+  const float* pp = w.part + ((int64_t)u * d.Hq + a) * w.nsa * (dh + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < w.nsa; ++sp) M = fmaxf(M, pp[sp * (dh + 2)]);
+  for (int j = tid; j < dh; j += blockDim.x) {
+    float Ls = 0.f, O = 0.f;
+    for (int sp = 0; sp < w.nsa; ++sp) {
+      const float m = pp[sp * (dh + 2)];
+      if (m == -INFINITY) continue;
+      const float f = exp2f(m - M);
+      Ls += pp[sp * (dh + 2) + 1] * f;
+      O += pp[sp * (dh + 2) + 2 + j] * f;
+    }
+    out[((int64_t)u * d.Hq + a) * dh + j] = O / Ls;
+  }
+}
+
+hipError_t launch_merge(const Dims& d, int U, const DecodeWs& w, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_merge, dim3(d.Hq, U), dim3(128), 0, st, d, w, out);
+  return hipGetLastError();
 }
 
 // The attention tile can exceed the default 64 KB dynamic LDS limit; raise it
 // once per kernel instantiation (gfx950 has 160 KB of LDS per CU).
-template <typename T, int KS>
+template <typename T, int KS, int DH>
 static hipError_t allow_lds(size_t lds) {
   static size_t done = 0;
   if (lds <= 65536 || lds <= done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attend<T, KS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attend<T, KS, DH>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e == hipSuccess) done = lds;
   return e;
 }
 
-hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
-                         const DecodeWs& w, hipStream_t st) {
-  dim3 grid(w.nsa, d.Hkv, U);
-  const size_t lds = ((size_t)2 * 64 * (d.dh + 1) + d.G * d.dh + d.G * 64 + 2 * d.G) * sizeof(float);
+template <typename T, int KS, int DH>
+static hipError_t launch_attend_t(const Dims& d, int U, const void* q, const CachePtrs& c,
+                                  const DecodeWs& w, float* out, hipStream_t st) {
+  const int rowp = KS * 16 + 8;
+  size_t lds = ((size_t)2 * 32 * attend_ldk(d.dh) + d.G * d.dh + d.G * 32 + 8 + 16) * sizeof(float);
+  if (KS > 0) lds += (size_t)2 * 32 * rowp * sizeof(uint16_t);
+  hipError_t e = allow_lds<T, KS, DH>(lds);
+  if (e != hipSuccess) return e;
   const float sm_scale = kLog2e / sqrtf((float)d.dh);
-  hipError_t e = hipSuccess;
-  if (d.dtype == 0) {
-    if ((e = allow_lds<float, 0>(lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attend<float, 0>), grid, dim3(256), lds, st, d, c, w, (const float*)q, sm_scale);
-    return hipGetLastError();
+  hipLaunchKernelGGL((k_attend<T, KS, DH>), dim3(w.nsa, d.Hkv, U), dim3(256), lds, st, d, c, w,
+                     (const T*)q, out, sm_scale);
+  return hipGetLastError();
+}
+
+template <int KS>
+static hipError_t launch_attend_bf16(const Dims& d, int U, const void* q, const CachePtrs& c,
+                                     const DecodeWs& w, float* out, hipStream_t st) {
+  switch (d.dh) {
+    case 128: return launch_attend_t<uint16_t, KS, 128>(d, U, q, c, w, out, st);
+    case 64: return launch_attend_t<uint16_t, KS, 64>(d, U, q, c, w, out, st);
+    default: return launch_attend_t<uint16_t, KS, 0>(d, U, q, c, w, out, st);
   }
-  const uint16_t* qb = (const uint16_t*)q;
+}
+
+hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
+                         const DecodeWs& w, float* out, hipStream_t st) {
+  if (d.dtype == 0) return launch_attend_t<float, 0, 0>(d, U, q, c, w, out, st);
   switch (d.r) {
-    case 128:
-      if ((e = allow_lds<uint16_t, 8>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((k_attend<uint16_t, 8>), grid, dim3(256), lds, st, d, c, w, qb, sm_scale); break;
-    case 192:
-      if ((e = allow_lds<uint16_t, 12>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((k_attend<uint16_t, 12>), grid, dim3(256), lds, st, d, c, w, qb, sm_scale); break;
-    case 256:
-      if ((e = allow_lds<uint16_t, 16>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((k_attend<uint16_t, 16>), grid, dim3(256), lds, st, d, c, w, qb, sm_scale); break;
-    case 64:
-      if ((e = allow_lds<uint16_t, 4>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((k_attend<uint16_t, 4>), grid, dim3(256), lds, st, d, c, w, qb, sm_scale); break;
-    case 32:
-      if ((e = allow_lds<uint16_t, 2>(lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL((k_attend<uint16_t, 2>), grid, dim3(256), lds, st, d, c, w, qb, sm_scale); break;
+    case 128: return launch_attend_bf16<8>(d, U, q, c, w, out, st);
+    case 192: return launch_attend_bf16<12>(d, U, q, c, w, out, st);
+    case 256: return launch_attend_bf16<16>(d, U, q, c, w, out, st);
+    case 64: return launch_attend_bf16<4>(d, U, q, c, w, out, st);
+    case 32: return launch_attend_bf16<2>(d, U, q, c, w, out, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-// --------------------------------------------------------------------------
-// merge of the row splits (online-softmax combination) + advance lens
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
-                                               float* __restrict__ out) {
-  const int a = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int dh = d.dh;
-  const int32_t* si = w.stepinfo + 4 * u;
-  float* o = out + ((int64_t)u * d.Hq + a) * dh;
-  if (si[2]) {
-    for (int j = tid; j < dh; j += blockDim.x) o[j] = 0.f;
-    return;
-  }
-  const float* pp = w.part + ((int64_t)u * d.Hq + a) * w.nsa * (dh + 2);
-  float M = -INFINITY;
-  for (int sp = 0; sp < w.nsa; ++sp) M = fmaxf(M, pp[sp * (dh + 2)]);
-  float Lsum = 0.f;
-  for (int sp = 0; sp < w.nsa; ++sp) {
-    const float m = pp[sp * (dh + 2)];
-    if (m != -INFINITY) Lsum += pp[sp * (dh + 2) + 1] * exp2f(m - M);
-  }
-  for (int j = tid; j < dh; j += blockDim.x) {
-    float acc = 0.f;
-    for (int sp = 0; sp < w.nsa; ++sp) {
-      const float m = pp[sp * (dh + 2)];
-      if (m != -INFINITY) acc += pp[sp * (dh + 2) + 2 + j] * exp2f(m - M);
-    }
-    o[j] = acc / Lsum;
-  }
-  if (a == 0 && tid == 0) {
-    c.lens[2 * u] = si[0] + 1;
-    c.lens[2 * u + 1] = si[1] + 1;
-  }
-}
-
-hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(d.Hq, U), dim3(256), 0, st, d, c, w, out);
-  return hipGetLastError();
 }
 
 }  // namespace kvlr

@@ -545,6 +545,7 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
                                                      const T* __restrict__ V, T* __restrict__ sk,
                                                      T* __restrict__ sv, T* __restrict__ rk,
                                                      T* __restrict__ rv, float* __restrict__ qwin,
+                                                     uint16_t* __restrict__ qsplit,
                                                      float* __restrict__ rowstat,
                                                      int32_t* __restrict__ lens, int64_t L, int D,
                                                      int s, int nrec, int qw_per_unit,
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
     }
   } else {
     for (int j = threadIdx.x; j < qw_per_unit; j += blockDim.x) qwin[(int64_t)u * qw_per_unit + j] = 0.f;
+    for (int j = threadIdx.x; j < 2 * qw_per_unit; j += blockDim.x) qsplit[(int64_t)u * 2 * qw_per_unit + j] = 0;
     for (int j = threadIdx.x; j < rs_per_unit; j += blockDim.x) rowstat[(int64_t)u * rs_per_unit + j] = 0.f;
     if (threadIdx.x == 0) {
       lens[2 * u] = (int32_t)L;
@@ -579,17 +581,18 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
 
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   void* sink_k, void* sink_v, void* ring_k, void* ring_v,
-                                  float* qwin, float* rowstat, int32_t* lens, hipStream_t st) {
+                                  float* qwin, float* rowstat, int32_t* lens, uint16_t* qsplit,
+                                  hipStream_t st) {
   dim3 grid(d.s + d.nrec + 1, U);
   const int qw = d.W * d.G * d.r, rs = d.W * d.G * 2;
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_exact_reset<float>, grid, dim3(256), 0, st, (const float*)K,
                        (const float*)V, (float*)sink_k, (float*)sink_v, (float*)ring_k,
-                       (float*)ring_v, qwin, rowstat, lens, L, d.D, d.s, d.nrec, qw, rs);
+                       (float*)ring_v, qwin, qsplit, rowstat, lens, L, d.D, d.s, d.nrec, qw, rs);
   else
     hipLaunchKernelGGL(k_exact_reset<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
                        (const uint16_t*)V, (uint16_t*)sink_k, (uint16_t*)sink_v,
-                       (uint16_t*)ring_k, (uint16_t*)ring_v, qwin, rowstat, lens, L, d.D, d.s,
+                       (uint16_t*)ring_k, (uint16_t*)ring_v, qwin, qsplit, rowstat, lens, L, d.D, d.s,
                        d.nrec, qw, rs);
   return hipGetLastError();
 }

@@ -21,8 +21,8 @@ F32, BF16 = 0, 1
 OK, EINVAL, EWORKSPACE, EDEVICE, ELAUNCH = 0, 1, 2, 3, 4
 OP_BUILD_BASES, OP_PROJECT, OP_DECODE = 0, 1, 2
 BUFFERS = ("sink_k", "sink_v", "ring_k", "ring_v", "coef_k", "coef_v", "basis_k", "basis_v",
-           "qwin", "rowstat", "lens")
-STAGES = ("prologue", "score", "select", "attend", "merge")
+           "qwin", "rowstat", "lens", "qsplit")
+STAGES = ("prologue", "score", "pool", "topk", "attend", "merge")
 
 
 class KvlrError(RuntimeError):
@@ -41,7 +41,7 @@ class Config(ctypes.Structure):
 class CacheStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS[:8]] + [
         ("qwin", ctypes.c_void_p), ("rowstat", ctypes.c_void_p), ("lens", ctypes.c_void_p),
-        ("L_max", ctypes.c_int64)]
+        ("qsplit", ctypes.c_void_p), ("L_max", ctypes.c_int64)]
 
 
 _lib = None
@@ -144,6 +144,7 @@ class KVCache:
     qwin: torch.Tensor
     rowstat: torch.Tensor
     lens: torch.Tensor
+    qsplit: torch.Tensor
 
     @staticmethod
     def allocate(cfg: Config, n_units: int, L_max: int, device="cuda") -> "KVCache":
@@ -159,7 +160,8 @@ class KVCache:
                     z(U, L_max, r), z(U, L_max, r), z(U, D, r), z(U, D, r),
                     z(U, cfg.q_window, G, r, dtype=torch.float32),
                     z(U, cfg.q_window, G, 2, dtype=torch.float32),
-                    z(U, 2, dtype=torch.int32))
+                    z(U, 2, dtype=torch.int32),
+                    z(U, cfg.q_window, G, 2, r, dtype=torch.bfloat16))
         want = cache_bytes(cfg, U, L_max)
         for name in BUFFERS:
             t = getattr(c, name)
@@ -266,3 +268,26 @@ def profile_read():
     steps = ctypes.c_int(0)
     _check(load().kvlr_profile_read(ms, len(STAGES), ctypes.byref(steps)))
     return dict(zip(STAGES, list(ms))), steps.value
+
+
+class Decoder:
+    """Repeated decode steps on one cache with the ctypes arguments prepared
+    once (no per-call validation beyond the library's own)."""
+
+    def __init__(self, cache: KVCache, out: torch.Tensor, topk: Optional[torch.Tensor] = None,
+                 scores: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+        self.cache = cache
+        self.lib = load()
+        self.cfg = cache.cfg
+        self.U = cache.n_units
+        self.ws = decode_workspace(cache) if ws is None else ws
+        self.out, self.topk, self.scores = out, topk, scores
+        self._st = cache.struct()
+        self._args_tail = (_ptr(out), _ptr(topk), _ptr(scores), _ptr(self.ws), self.ws.numel())
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        st = self.lib.kvlr_decode_step(ctypes.byref(self.cfg), self.U, q.data_ptr(),
+                                       k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(self._st),
+                                       *self._args_tail, _stream(stream))
+        if st != OK:
+            _check(st)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(kvlr.Config) == 14 * 4
-    assert ctypes.sizeof(kvlr.CacheStruct) == 11 * 8 + 8
+    assert ctypes.sizeof(kvlr.CacheStruct) == 12 * 8 + 8
 
 
 @pytest.mark.parametrize("w", configs.ALL, ids=lambda w: w.name)
