@@ -42,11 +42,24 @@ size_t elem_bytes(const kvlr_config* c) { return c->dtype == KVLR_BF16 ? 2 : 4; 
 
 bool rank_supported_bf16(int r) { return r == 32 || r == 64 || r == 128 || r == 192 || r == 256; }
 
-size_t attend_lds(const kvlr_config* c) {
-  const int G = c->n_q_heads / c->n_kv_heads;
-  size_t b = ((size_t)2 * 32 * (c->head_dim + 4) + (size_t)G * c->head_dim + G * 32 + 24) * 4;
-  if (c->dtype == KVLR_BF16) b += (size_t)2 * 32 * (c->rank + 8) * 2;
-  return b;
+Dims dims_of(const kvlr_config* c) {
+  Dims d;
+  d.Hq = c->n_q_heads;
+  d.Hkv = c->n_kv_heads;
+  d.dh = c->head_dim;
+  d.D = c->n_kv_heads * c->head_dim;
+  d.r = c->rank;
+  d.G = c->n_q_heads / c->n_kv_heads;
+  d.s = c->n_sink;
+  d.T = c->n_sample;
+  d.rnum = c->sample_recent_num;
+  d.rden = c->sample_recent_den;
+  d.W = c->q_window;
+  d.k = c->top_k;
+  d.nrec = c->n_recent;
+  d.kappa = c->pool_kernel;
+  d.dtype = c->dtype;
+  return d;
 }
 
 int check_cfg(const kvlr_config* c) {
@@ -78,36 +91,16 @@ int check_cfg(const kvlr_config* c) {
     return fail(KVLR_EINVAL, "pool_kernel must be odd and in [1, 255]");
   if (c->dtype == KVLR_BF16) {
     if (!rank_supported_bf16(c->rank)) return fail(KVLR_EINVAL, "bf16 storage needs rank in {32, 64, 128, 192, 256}");
-    if (c->head_dim % 32 != 0 || c->head_dim > 128)
-      return fail(KVLR_EINVAL, "bf16 storage needs head_dim %% 32 == 0 and head_dim <= 128");
     if (c->q_window * G > 128) return fail(KVLR_EINVAL, "bf16 storage needs q_window * G <= 128");
   } else {
     if ((int64_t)c->q_window * G * c->rank > 8192)
       return fail(KVLR_EINVAL, "fp32 storage needs q_window * G * rank <= 8192");
   }
-  if (attend_lds(c) > 160 * 1024) return fail(KVLR_EINVAL, "head_dim too large for the attention tile");
+  if (attend_lds_bytes(dims_of(c)) == 0)
+    return fail(KVLR_EINVAL, "rank / head shape too large for the attention tile (160 KB LDS)");
   return KVLR_OK;
 }
 
-Dims dims_of(const kvlr_config* c) {
-  Dims d;
-  d.Hq = c->n_q_heads;
-  d.Hkv = c->n_kv_heads;
-  d.dh = c->head_dim;
-  d.D = c->n_kv_heads * c->head_dim;
-  d.r = c->rank;
-  d.G = c->n_q_heads / c->n_kv_heads;
-  d.s = c->n_sink;
-  d.T = c->n_sample;
-  d.rnum = c->sample_recent_num;
-  d.rden = c->sample_recent_den;
-  d.W = c->q_window;
-  d.k = c->top_k;
-  d.nrec = c->n_recent;
-  d.kappa = c->pool_kernel;
-  d.dtype = c->dtype;
-  return d;
-}
 
 int check_sample_fits(const kvlr_config* c, int64_t L) {
   if (L < (int64_t)c->n_sink + c->n_recent)
@@ -156,14 +149,14 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
 }
 
 struct DecodeLayout {
-  size_t stepinfo, partial, spill, tilestat, keys, topk, part, total;
-  int Lc_cap, nsplit, chunk, nsa, rows_per_split;
+  size_t stepinfo, partial, spill, tilestat, keys, topk, qlat, ylat, yex, astat, total;
+  DecodeWs t;  // tiling fields
 };
 
 DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   DecodeLayout L;
   Dims d = dims_of(c);
-  decode_tiling(d, U, Lmax, &L.Lc_cap, &L.nsplit, &L.chunk, &L.nsa, &L.rows_per_split);
+  decode_tiling(d, U, Lmax, &L.t);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -171,12 +164,15 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
     return at;
   };
   L.stepinfo = take((size_t)U * 4 * sizeof(int32_t));
-  L.partial = take((size_t)U * L.Lc_cap * sizeof(float));
-  L.spill = take((size_t)U * d.G * L.Lc_cap * sizeof(float));
-  L.tilestat = take((size_t)U * L.nsplit * d.G * 2 * sizeof(float));
-  L.keys = take((size_t)U * L.Lc_cap * sizeof(uint32_t));
+  L.partial = take((size_t)U * L.t.Lc_cap * sizeof(float));
+  L.spill = take((size_t)U * d.G * L.t.Lc_cap * sizeof(float));
+  L.tilestat = take((size_t)U * L.t.nsplit * d.G * 2 * sizeof(float));
+  L.keys = take((size_t)U * L.t.Lc_cap * sizeof(uint32_t));
   L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
-  L.part = take((size_t)U * d.Hq * L.nsa * (d.dh + 2) * sizeof(float));
+  L.qlat = take((size_t)U * d.Hq * d.r * sizeof(float));
+  L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.r * sizeof(float));
+  L.yex = take((size_t)U * L.t.nse * d.Hq * d.dh * sizeof(float));
+  L.astat = take((size_t)U * (L.t.nsl + L.t.nse) * d.Hq * 2 * sizeof(float));
   L.total = off;
   return L;
 }
@@ -362,19 +358,17 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   hipStream_t st = (hipStream_t)stream;
   const Dims d = dims_of(cfg);
   char* w = (char*)ws;
-  DecodeWs dw;
+  DecodeWs dw = dl.t;
   dw.stepinfo = (int32_t*)(w + dl.stepinfo);
   dw.partial = (float*)(w + dl.partial);
   dw.spill = (float*)(w + dl.spill);
   dw.tilestat = (float*)(w + dl.tilestat);
   dw.keys = (uint32_t*)(w + dl.keys);
   dw.topk = (int32_t*)(w + dl.topk);
-  dw.part = (float*)(w + dl.part);
-  dw.Lc_cap = dl.Lc_cap;
-  dw.nsplit = dl.nsplit;
-  dw.chunk = dl.chunk;
-  dw.nsa = dl.nsa;
-  dw.rows_per_split = dl.rows_per_split;
+  dw.qlat = (float*)(w + dl.qlat);
+  dw.ylat = (float*)(w + dl.ylat);
+  dw.yex = (float*)(w + dl.yex);
+  dw.astat = (float*)(w + dl.astat);
   const CachePtrs cp = cache_ptrs(cache);
   const int U = (int)n_units;
 
@@ -396,9 +390,9 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   if (ev) (void)hipEventRecord(ev[3], st);
   if ((he = launch_topk(d, U, cp, dw, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
   if (ev) (void)hipEventRecord(ev[4], st);
-  if ((he = launch_attend(d, U, q, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "attend");
+  if ((he = launch_attend(d, U, q, cp, dw, st)) != hipSuccess) return hip_fail(he, "attend");
   if (ev) (void)hipEventRecord(ev[5], st);
-  if ((he = launch_merge(d, U, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
+  if ((he = launch_merge(d, U, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
   if (ev) (void)hipEventRecord(ev[6], st);
   return ok();
 }

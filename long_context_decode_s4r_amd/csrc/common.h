@@ -137,8 +137,18 @@ struct DecodeWs {
   float* tilestat;    // [U][nsplit][G][2] per-split (max, sum) of the current rows
   uint32_t* keys;     // [U][Lc_cap] pooled scores as ordered bit patterns
   int32_t* topk;      // [U][k] selected positions, ascending
-  float* part;        // [U][Hq][nsa][dh + 2] attention split partials
-  int Lc_cap, nsplit, chunk, nsa, rows_per_split;
+  float* qlat;        // [U][Hq][r] query heads projected onto their KV head's
+                      //            slice of B^K, times log2(e)/sqrt(d_h)
+  float* ylat;        // [U][nsl][Hq][r] per split: sum_j p_j c^V_j (latent)
+  float* yex;         // [U][nse][Hq][dh] per split: sum_j p_j v_j (exact rows)
+  float* astat;       // [U][nsl + nse][Hq][2] per split: (max, sum) of the
+                      //            base-2 attention logits
+  // tiling (decode_tiling)
+  int Lc_cap, nsplit, chunk;  // scoring: candidate capacity, splits, split length
+  int nsl, nhg, hb, rsl;      // attention over selected rows: row splits, head
+                              // groups, heads per group, rows per split
+  int nse, rse;               // attention over exact rows: splits, rows per split
+  int attend_lds;             // dynamic LDS of the attention kernel (bytes)
 };
 
 struct CachePtrs {
@@ -160,11 +170,14 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                        int32_t* topk_user, float* out, hipStream_t st);
 hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
-                         const DecodeWs& w, float* out, hipStream_t st);
-hipError_t launch_merge(const Dims& d, int U, const DecodeWs& w, float* out, hipStream_t st);
+                         const DecodeWs& w, hipStream_t st);
+hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
+                        hipStream_t st);
 
-// decode tiling decisions shared by the workspace sizing and the launches
-void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, int* Lc_cap, int* nsplit, int* chunk,
-                   int* nsa, int* rows_per_split);
+// decode tiling decisions shared by the workspace sizing and the launches:
+// fills the int fields of *w (pointers untouched)
+void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w);
+// dynamic LDS bytes of the attention kernel for this shape (0 if it cannot fit)
+size_t attend_lds_bytes(const Dims& d);
 
 }  // namespace kvlr

@@ -31,29 +31,65 @@ namespace kvlr {
 
 static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, int* Lc_cap, int* nsplit, int* chunk,
-                   int* nsa, int* rows_per_split) {
+// Attention tile over the selected rows: hb query heads (multiple of 8) and
+// rsl rows (multiple of 4, <= 64) per block.  LDS: projected queries
+// [hb][r + 4] fp32, probabilities [hb][rsl + 1] fp32, coefficient rows of K
+// and V [rsl][r] storage type with 16 bytes of padding per row.
+static size_t latent_lds(const Dims& d, int hb, int rsl) {
+  const size_t el = d.dtype == 0 ? 4 : 2;
+  return (size_t)hb * (d.r + 4) * 4 + (size_t)hb * (rsl + 1) * 4 + 16 +
+         (size_t)2 * rsl * (d.r * el + 16);
+}
+// exact rows, per wave: queries [G][dh] fp32, probabilities [G][32] fp32,
+// value rows [32][dh + 16 bytes] storage type
+__host__ __device__ inline int exact_wave_floats(int G, int dh, int el) {
+  return G * dh + G * 32 + 8 * (dh * el + 16);
+}
+static size_t exact_lds(const Dims& d) {
+  return (size_t)4 * exact_wave_floats(d.G, d.dh, d.dtype == 0 ? 4 : 2) * 4;
+}
+static void attend_tile(const Dims& d, int* hb, int* rsl) {
+  int h = (int)round_up(d.Hq, 8);
+  if (h > 32) h = 32;
+  int rs = 32;
+  while (latent_lds(d, h, rs) > 96 * 1024 && rs > 8) rs /= 2;
+  while (latent_lds(d, h, rs) > 96 * 1024 && h > 8) h /= 2;
+  *hb = h;
+  *rsl = rs;
+}
+
+size_t attend_lds_bytes(const Dims& d) {
+  int hb, rsl;
+  attend_tile(d, &hb, &rsl);
+  size_t a = latent_lds(d, hb, rsl), b = exact_lds(d);
+  a = a > b ? a : b;
+  return a <= 160 * 1024 ? a : 0;
+}
+
+void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
   int64_t lc = Lmax - d.s - d.nrec;
   if (lc < 1) lc = 1;
   lc = round_up(lc, 64);
-  *Lc_cap = (int)lc;
-  int64_t target = (512 + U - 1) / U;
+  w->Lc_cap = (int)lc;
+  // scoring: one round of blocks (the kernel holds one block per CU)
+  int64_t target = (256 + U - 1) / U;
   if (target < 1) target = 1;
   int64_t maxsplit = lc / 256;
   if (maxsplit < 1) maxsplit = 1;
   int64_t ns = target < maxsplit ? target : maxsplit;
   int64_t ch = round_up((lc + ns - 1) / ns, 64);
   ns = (lc + ch - 1) / ch;
-  *nsplit = (int)ns;
-  *chunk = (int)ch;
-  // attention: about 512 blocks over (unit, KV head, row split), 32-row tiles
-  const int64_t R = (int64_t)d.s + d.nrec + d.k;
-  int64_t sa = (512 + U * d.Hkv - 1) / (U * d.Hkv);
-  if (sa < 1) sa = 1;
-  int64_t rows = round_up((R + sa - 1) / sa, 32);
-  if (rows < 32) rows = 32;
-  *rows_per_split = (int)rows;
-  *nsa = (int)((R + rows - 1) / rows);
+  w->nsplit = (int)ns;
+  w->chunk = (int)ch;
+  // attention: selected rows in splits of rsl rows x hb heads, exact rows in
+  // splits of at most 32 rows
+  attend_tile(d, &w->hb, &w->rsl);
+  w->nhg = (d.Hq + w->hb - 1) / w->hb;
+  w->nsl = (d.k + w->rsl - 1) / w->rsl;
+  const int nex = d.s + d.nrec;
+  w->nse = (nex + 31) / 32;
+  w->rse = (nex + w->nse - 1) / w->nse;
+  w->attend_lds = (int)attend_lds_bytes(d);
 }
 
 __device__ __forceinline__ int wrap_slot(int x, int W) { return ((x % W) + W) % W; }
@@ -77,13 +113,16 @@ template <> struct Vec16<uint16_t> {
 };
 
 // --------------------------------------------------------------------------
-// prologue: grid (2 * ncb + 1, U), 256 threads.
+// prologue: grid (2 * ncb + 1 + H_kv, U), 256 threads.
 //   blocks [0, ncb):      c^K(new) = k_cat . B^K and c_q[g] = q_cat[g] . B^K
 //                         (window push) for 4*VEC basis columns each;
 //   blocks [ncb, 2 ncb):  c^V(new) = v_cat . B^V;
 //   block 2 ncb:          exact ring push of k and v; the older window rows'
 //                         (m, S) updated with the candidate entering this
-//                         step.
+//                         step;
+//   block 2 ncb + 1 + h:  the G query heads of KV head h projected onto the
+//                         rows of B^K that belong to head h, for attention in
+//                         the coefficient space.
 // GEMV layout: thread (row group rg = tid / 4, column group cg = tid % 4)
 // reads 16 bytes of a basis row per iteration (rows rg, rg + 64, ...);
 // partial sums are reduced over row groups with lane shuffles and LDS.
@@ -92,7 +131,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* __restrict__ q,
                                                   const T* __restrict__ kn,
                                                   const T* __restrict__ vn, DecodeWs w,
-                                                  float qscale, int ncb) {
+                                                  float qscale, float ascale, int ncb) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int NVMAX = 9;  // 1 + G, G <= 8
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
@@ -213,6 +252,59 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
     }
     return;
   }
+  if (b > 2 * ncb) {
+    // qlat[h G + g] = ascale * q[h G + g] . B^K[h dh : (h + 1) dh, :]
+    const int h = b - 2 * ncb - 1, dh = d.dh;
+    float* qs = sm;                 // [G][dh]
+    float* red = qs + G * dh;       // [4 waves][G][32 * VEC]
+    const T* qh = q + ((int64_t)u * d.Hq + h * G) * dh;
+    for (int e = tid; e < G * dh; e += 256) qs[e] = Elem<T>::ld(qh, e) * ascale;
+    __syncthreads();
+    const T* B = (const T*)c.basis_k + ((int64_t)u * D + (int64_t)h * dh) * r;
+    const int cg = tid & 31, rg = tid >> 5, lane = tid & 63, wv = tid >> 6;
+    for (int c0 = 0; c0 < r; c0 += 32 * VEC) {
+      const int colc = min(c0 + cg * VEC, r - VEC);  // columns past r: computed, not stored
+      float acc[8][VEC];
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
+#pragma unroll 4
+      for (int j = rg; j < dh; j += 8) {
+        float bv[VEC];
+        Vec16<T>::ld(B + (int64_t)j * r + colc, bv);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (g < G) {
+            const float x = qs[g * dh + j];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[g][e] += x * bv[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < G) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float x = acc[g][e] + __shfl_xor(acc[g][e], 32);
+            if (lane < 32) red[(wv * G + g) * 32 * VEC + cg * VEC + e] = x;
+          }
+        }
+      }
+      __syncthreads();
+      for (int t = tid; t < G * 32 * VEC; t += 256) {
+        const int g = t / (32 * VEC), cc = t % (32 * VEC);
+        if (c0 + cc < r) {
+          const int o = g * 32 * VEC + cc, st = G * 32 * VEC;
+          w.qlat[((int64_t)u * d.Hq + h * G + g) * r + c0 + cc] =
+              (red[o] + red[o + st]) + (red[o + 2 * st] + red[o + 3 * st]);
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
   // ---- state block ----
   {  // exact ring push, 16-byte pieces, loads before stores
     const int rs = (int)(p % d.nrec);
@@ -279,14 +371,17 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
   const int nvec = 1 + d.G;
   size_t lds = ((size_t)nvec * d.D + 4 * nvec * 4 * vec) * sizeof(float);
   if (lds < (size_t)d.r * sizeof(float)) lds = (size_t)d.r * sizeof(float);
-  dim3 grid(2 * ncb + 1, U);
+  const size_t lq = ((size_t)d.G * d.dh + (size_t)4 * d.G * 32 * vec) * sizeof(float);
+  if (lds < lq) lds = lq;
+  dim3 grid(2 * ncb + 1 + d.Hkv, U);
   const float qscale = kLog2e / sqrtf((float)d.r);
+  const float ascale = kLog2e / sqrtf((float)d.dh);
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
-                       (const float*)k_new, (const float*)v_new, w, qscale, ncb);
+                       (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb);
   else
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ncb);
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
   return hipGetLastError();
 }
 
@@ -350,6 +445,46 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
   const int64_t j1 = min(j0 + (int64_t)w.chunk, cend);
   const int npos = (int)max(j1 - j0, (int64_t)0);
 
+  // ---- DMA of one tile into a stage ----------------------------------------
+  // Piece q of this lane: LDS row pl, slot sl holds global chunk sl ^ (pl & SWZ);
+  // the lane offsets are the same for every tile, only the tile base moves.
+  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(
+      (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  uint32_t qoff[PW];
+  int qrow[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    const int Q = (wvu * PW + q) * 64 + l;
+    const int pl = Q / NCH, slot = Q % NCH;
+    qrow[q] = pl;
+    qoff[q] = (uint32_t)(pl * ROWB + ((slot ^ (pl & SWZ)) << 4));
+  }
+  auto issue = [&](int64_t p0, uint8_t* stage) {
+    const uint8_t* tb = cbase + p0 * ROWB;
+    const bool tail = p0 + kScoreTP > c.Lmax;  // last tile of the buffer: clamp rows
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+      const uint8_t* src = tb + qoff[q];
+      if (tail) {
+        const int64_t pos = min(p0 + qrow[q], c.Lmax - 1);
+        src = cbase + pos * ROWB + (qoff[q] - qrow[q] * ROWB);
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+    }
+  };
+  // the block's tiles: t covers positions j0 + t * TP + [0, TP); requests past
+  // the last tile re-read it (harmless, keeps the ring's count uniform)
+  const int ntl = (npos + kScoreTP - 1) / kScoreTP;
+  auto tp = [&](int t) { return j0 + (int64_t)min(t, max(ntl - 1, 0)) * kScoreTP; };
+  if (ntl > 0) {  // prime the ring before the operand loads below
+    issue(tp(0), st0.b);
+    issue(tp(1), st1.b);
+    issue(tp(2), st2.b);
+  }
+
   // ---- per-unit operands ---------------------------------------------------
   int urb[NU], ucb[NU];
   bool uact[NU];
@@ -402,43 +537,13 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
     }
   }
 
-  // ---- DMA of one tile into a stage ----------------------------------------
-  // Piece q of this lane: LDS row pl, slot sl holds global chunk sl ^ (pl & SWZ);
-  // the lane offsets are the same for every tile, only the tile base moves.
-  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(
-      (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r);
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);
-  uint32_t qoff[PW];
-  int qrow[PW];
-#pragma unroll
-  for (int q = 0; q < PW; ++q) {
-    const int Q = (wvu * PW + q) * 64 + l;
-    const int pl = Q / NCH, slot = Q % NCH;
-    qrow[q] = pl;
-    qoff[q] = (uint32_t)(pl * ROWB + ((slot ^ (pl & SWZ)) << 4));
-  }
-  auto issue = [&](int64_t p0, uint8_t* stage) {
-    const uint8_t* tb = cbase + p0 * ROWB;
-    const bool tail = p0 + kScoreTP > c.Lmax;  // last tile of the buffer: clamp rows
-#pragma unroll
-    for (int q = 0; q < PW; ++q) {
-      const uint8_t* src = tb + qoff[q];
-      if (tail) {
-        const int64_t pos = min(p0 + qrow[q], c.Lmax - 1);
-        src = cbase + pos * ROWB + (qoff[q] - qrow[q] * ROWB);
-      }
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
-    }
-  };
   constexpr int kWaitN = (kScoreNST - 1) * PW;  // groups allowed in flight
   constexpr int kWaitImm = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8);
   constexpr int kLgkm0 = 0xF | (3 << 14) | (7 << 4);  // lgkmcnt(0)
   constexpr int kVm0 = (7 << 4) | (15 << 8);          // vmcnt(0)
 
-  // tile t of the segment starting at seg0 (positions seg0 + t*TP + pl)
-  auto compute = [&](int seg0, int t, const uint8_t* stage) {
+  // tile t of the block (positions j0 + t*TP + pl; segment slot (t % SEGT)*TP + pl)
+  auto compute = [&](int t, const uint8_t* stage) {
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
       if (!uact[j]) continue;
@@ -475,10 +580,10 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
 #pragma unroll
       for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(acc[i] - mrow[j][i]) * irow[j][i];
       ps += __shfl_xor(ps, 32);
-      const int sp = t * kScoreTP + pl;         // position within the segment
+      const int sp = (t % SEGT) * kScoreTP + pl;  // position within the segment
       if (l < 32) segred[urb[j]][sp] = ps;
       if (urb[j] == 0) {
-        const bool pv = seg0 + sp < npos;
+        const bool pv = t * kScoreTP + pl < npos;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * kg + i;
@@ -499,33 +604,10 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
 
   float* partial = w.partial + (int64_t)u * w.Lc_cap + (j0 - s);
   float* spill = w.spill + (int64_t)u * G * w.Lc_cap + (j0 - s);
-  for (int seg0 = 0; seg0 < npos; seg0 += kScoreSeg) {
+  // flush of segment sg (tiles [sg * SEGT, ...)) after its last tile
+  auto flush = [&](int sg) {
+    const int seg0 = sg * kScoreSeg;
     const int segn = min(kScoreSeg, npos - seg0);
-    const int ntl = (segn + kScoreTP - 1) / kScoreTP;
-    const int64_t p0 = j0 + seg0;
-    auto tp = [&](int t) { return p0 + (int64_t)min(t, ntl - 1) * kScoreTP; };
-    issue(tp(0), st0.b);
-    issue(tp(1), st1.b);
-    issue(tp(2), st2.b);
-    // tile t lives in stage t % 4; one DMA group is issued per tile so the
-    // wave's outstanding count stays exactly three groups behind
-    for (int t = 0; t < ntl; t += kScoreNST) {
-#define KVLR_SCORE_STEP(k, SREAD, SNEXT)                 \
-      if (t + k >= ntl) break;                             \
-      issue(tp(t + k + 3), SNEXT);                         \
-      __builtin_amdgcn_s_waitcnt(kWaitImm);                \
-      __builtin_amdgcn_s_barrier();                        \
-      compute(seg0, t + k, SREAD);                         \
-      __builtin_amdgcn_s_waitcnt(kLgkm0);                  \
-      __builtin_amdgcn_s_barrier();
-      KVLR_SCORE_STEP(0, st0.b, st3.b)
-      KVLR_SCORE_STEP(1, st1.b, st0.b)
-      KVLR_SCORE_STEP(2, st2.b, st1.b)
-      KVLR_SCORE_STEP(3, st3.b, st2.b)
-#undef KVLR_SCORE_STEP
-    }
-    __builtin_amdgcn_s_waitcnt(kVm0);  // drain the ring before the flush
-    __syncthreads();
     for (int e = tid; e < segn; e += 256) {
       float sum = 0.f;
       for (int q2 = 0; q2 < nrb; ++q2) sum += segred[q2][e];
@@ -535,8 +617,32 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
       const int row = e / segn, sp = e % segn;
       spill[(int64_t)row * w.Lc_cap + seg0 + sp] = segspill[row][sp];
     }
-    __syncthreads();
+  };
+  // tile t lives in stage t % 4; one DMA group is issued per tile, so the
+  // tile being waited for always has exactly three groups behind it (plus any
+  // flush stores, which only make the wait stricter)
+  for (int t = 0; t < ntl; t += kScoreNST) {
+#define KVLR_SCORE_STEP(k, SREAD, SNEXT)                   \
+    if (t + k >= ntl) break;                               \
+    issue(tp(t + k + 3), SNEXT);                           \
+    __builtin_amdgcn_s_waitcnt(kWaitImm);                  \
+    __builtin_amdgcn_s_barrier();                          \
+    compute(t + k, SREAD);                                 \
+    __builtin_amdgcn_s_waitcnt(kLgkm0);                    \
+    __builtin_amdgcn_s_barrier();                          \
+    if ((t + k) % SEGT == SEGT - 1 || t + k == ntl - 1) {  \
+      flush((t + k) / SEGT);                               \
+      __builtin_amdgcn_s_waitcnt(kLgkm0);                  \
+      __builtin_amdgcn_s_barrier();                        \
+    }
+    KVLR_SCORE_STEP(0, st0.b, st3.b)
+    KVLR_SCORE_STEP(1, st1.b, st0.b)
+    KVLR_SCORE_STEP(2, st2.b, st1.b)
+    KVLR_SCORE_STEP(3, st3.b, st2.b)
+#undef KVLR_SCORE_STEP
   }
+  __builtin_amdgcn_s_waitcnt(kVm0);  // no request left in flight at exit
+  __syncthreads();
 
   // current rows' (max, sum) over this split: lanes of one kg half, then waves
 #pragma unroll
@@ -1039,308 +1145,454 @@ hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 }
 
 // --------------------------------------------------------------------------
-// sparse reconstruction + exact attention: grid (nsa, H_kv, U), 256 threads.
-// Block (split, h, u) owns rows [split * rps, (split + 1) * rps) of the row list
-//   [0, s)            sinks (exact)
-//   [s, s + nrec)     recent ring (exact)
-//   [s + nrec, R)     selected positions, reconstructed as c . B^T
-// processed in tiles of 32 rows with an online softmax for the G query heads
-// of KV head h.  bf16: wave w owns channels [32w, 32w + 32) of the head and
-// keeps its basis rows (K and V) in registers as MFMA B operands; the tile's
-// gathered coefficient rows are staged in LDS (coalesced 16-byte loads) and
-// read as A operands; MFMA 32x32x16 gives K_hat and V_hat in fp32.  fp32
-// storage reconstructs with plain dot products.  The last block of a
-// (unit, head) to finish merges the splits (online-softmax combination) into
-// the output.
+// Sparse reconstruction + exact attention, evaluated in coefficient space.
+//
+// For a selected position j of KV head h, the reconstructed key is
+// k_hat = B^K_h c^K_j (B^K_h: the d_h rows of B^K that belong to head h), so
+// q . k_hat = (B^K_h^T q) . c^K_j, and sum_j p_j v_hat_j = B^V_h (sum_j p_j
+// c^V_j).  The prologue writes qlat = B^K_h^T q (times log2(e)/sqrt(d_h));
+// here every block scores rows against all query heads at once, which reads
+// each selected coefficient row once per step instead of once per KV head,
+// and the merge applies B^V_h once per head.  The algebra is exact; only the
+// fp32 summation order differs from rebuilding the keys and values first.
+//
+// grid (nsl * nhg + nse * ceil(H_kv / 4), U), 256 threads (4 waves):
+//   block (split, hg) < nsl * nhg: selected rows [split * rsl, +rsl) of the
+//     top-k list, heads [hg * hb, +hb): logits c^K_j . qlat[a], a split-local
+//     softmax, ylat[a] = sum_j p_j c^V_j;
+//   then block (e, hq): exact rows [e * rse, +rse) of (sinks, recent ring),
+//     wave w takes KV head 4 hq + w; lane = row for the logits, lane =
+//     channel for the values; yex[a] = sum_j p_j v_j.
+// Every split stores its (max, sum) per head; k_merge combines them.
 // --------------------------------------------------------------------------
-__host__ __device__ __forceinline__ int attend_ldk(int dh) { return dh % 4 == 0 ? dh + 4 : dh + 1; }
+template <typename T> struct Quad;  // 4 storage elements
+template <> struct Quad<float> {
+  typedef f32x4 V;
+  static __device__ __forceinline__ f32x4 f(V v) { return v; }
+};
+template <> struct Quad<uint16_t> {
+  typedef unsigned short V __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 f(V v) {
+    return f32x4{bf2f(v[0]), bf2f(v[1]), bf2f(v[2]), bf2f(v[3])};
+  }
+};
 
-template <typename T, int KS, int DH>
+template <typename T>
 __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
-                                                const T* __restrict__ q, float* __restrict__ out,
-                                                float sm_scale) {
-  const int split = blockIdx.x, h = blockIdx.y, u = blockIdx.z;
-  const int tid = threadIdx.x;
+                                                const T* __restrict__ q, float ascale) {
+  typedef typename Quad<T>::V QV;
+  const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int32_t* si = w.stepinfo + 4 * u;
+  if (si[2]) return;  // full unit: the top-k kernel wrote zeros
+  const int Lcur = si[0];
+  const int r = d.r, Hq = d.Hq;
+  const int nc = Lcur + 1 - d.nrec - d.s;
+  const int kk = max(0, min(d.k, nc));
+  extern __shared__ __attribute__((aligned(16))) float smf[];
+  const int wv = tid >> 6, l = tid & 63;
+
+  if (b < w.nsl * w.nhg) {
+    // ---------------- selected rows, coefficient space ----------------
+    const int split = b / w.nhg, hg = b % w.nhg;
+    const int row0 = split * w.rsl;
+    const int nrow = min(w.rsl, kk - row0);
+    if (nrow <= 0) return;
+    const int hb = w.hb, a0 = hg * hb, na = min(hb, Hq - a0);
+    constexpr int E = 16 / sizeof(T);                 // elements per 16-byte piece
+    const int ldq = r + 4, ldz = w.rsl + 1, ldc = r + E, r4 = r / 4, rE = r / E;
+    float* qt = smf;                                  // [hb][ldq]
+    float* zs = qt + hb * ldq;                        // [hb][ldz]
+    T* ck = reinterpret_cast<T*>(zs + ((hb * ldz + 3) & ~3));  // [rsl][ldc]
+    T* cv = ck + w.rsl * ldc;
+    const int32_t* sel = w.topk + (int64_t)u * d.k + row0;
+    {
+      // every thread issues its loads (8 pieces of K and of V per round)
+      // before it stores any of them
+      const T* cks = (const T*)c.coef_k + (int64_t)u * c.Lmax * r;
+      const T* cvs = (const T*)c.coef_v + (int64_t)u * c.Lmax * r;
+      const int npc = nrow * rE;
+      for (int e0 = 0; e0 < npc; e0 += 256 * 8) {
+        u16x8 xk[8], xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = min(e0 + tid + 256 * i, npc - 1);
+          const int j = e / rE, iE = e % rE;
+          const int64_t pos = min(max((int64_t)sel[j], (int64_t)0), c.Lmax - 1);
+          xk[i] = *reinterpret_cast<const u16x8*>(cks + pos * r + iE * E);
+          xv[i] = *reinterpret_cast<const u16x8*>(cvs + pos * r + iE * E);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = e0 + tid + 256 * i;
+          if (e < npc) {
+            const int j = e / rE, iE = e % rE;
+            *reinterpret_cast<u16x8*>(ck + j * ldc + iE * E) = xk[i];
+            *reinterpret_cast<u16x8*>(cv + j * ldc + iE * E) = xv[i];
+          }
+        }
+      }
+      const float* qsrc = w.qlat + ((int64_t)u * Hq + a0) * r;
+      const int nq = na * r4;
+      for (int e0 = 0; e0 < nq; e0 += 256 * 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = min(e0 + tid + 256 * i, nq - 1);
+          x[i] = *reinterpret_cast<const f32x4*>(qsrc + (int64_t)(e / r4) * r + 4 * (e % r4));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = e0 + tid + 256 * i;
+          if (e < nq) *reinterpret_cast<f32x4*>(qt + (e / r4) * ldq + 4 * (e % r4)) = x[i];
+        }
+      }
+    }
+    __syncthreads();
+    // logits: item (a, row group of 4); rows past nrow are computed from
+    // stale LDS and discarded
+    const int ngj = (nrow + 3) >> 2;
+    for (int e = tid; e < na * ngj; e += 256) {
+      const int a = e / ngj, jg = e % ngj;
+      const float* qa = qt + a * ldq;
+      const T* c0 = ck + 4 * jg * ldc;
+      f32x4 acc[4] = {};
+      for (int i = 0; i < r; i += 4) {
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(qa + i);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[jj] += q4 * Quad<T>::f(*reinterpret_cast<const QV*>(c0 + jj * ldc + i));
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (4 * jg + jj < nrow)
+          zs[a * ldz + 4 * jg + jj] = (acc[jj][0] + acc[jj][1]) + (acc[jj][2] + acc[jj][3]);
+    }
+    __syncthreads();
+    // split-local softmax per head: a wave per head, a lane per row
+    for (int a = wv; a < na; a += 4) {
+      const float z = l < nrow ? zs[a * ldz + l] : -INFINITY;
+      const float m = warp_max(z);
+      const float pz = l < nrow ? __builtin_amdgcn_exp2f(z - m) : 0.f;
+      const float S = warp_sum(pz);
+      if (l < nrow) zs[a * ldz + l] = pz;
+      if (l == 0) {
+        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + split) * Hq + a0 + a) * 2;
+        stp[0] = m;
+        stp[1] = S;
+      }
+    }
+    __syncthreads();
+    // ylat[a] = sum_j p[a][j] c^V_j: item (8 heads, 4 coefficients)
+    const int nag = (na + 7) >> 3;
+    for (int e = tid; e < nag * r4; e += 256) {
+      const int ag = e / r4, i4 = e % r4;
+      f32x4 acc[8] = {};
+      for (int j = 0; j < nrow; ++j) {
+        const f32x4 v4 = Quad<T>::f(*reinterpret_cast<const QV*>(cv + j * ldc + 4 * i4));
+#pragma unroll
+        for (int aa = 0; aa < 8; ++aa) acc[aa] += zs[(8 * ag + aa) * ldz + j] * v4;
+      }
+#pragma unroll
+      for (int aa = 0; aa < 8; ++aa) {
+        const int a = 8 * ag + aa;
+        if (a < na)
+          *reinterpret_cast<f32x4*>(w.ylat + (((int64_t)u * w.nsl + split) * Hq + a0 + a) * r +
+                                    4 * i4) = acc[aa];
+      }
+    }
+    return;
+  }
+
+  // ---------------- exact rows: sinks then the recent ring ----------------
+  // block (e, hq): rows [e * rse, +rse) (rse <= 32), KV head h = 4 hq + wave.
+  // Lane l < nrow loads row l's K and V slices of head h in one phase (V goes
+  // to LDS), scores it against the G query heads, and after the softmax the
+  // lanes switch to channels (c = l + 64 i) to sum the values from LDS.
+  const int be = b - w.nsl * w.nhg;
+  const int nhq = (d.Hkv + 3) >> 2;
+  const int e = be / nhq, h = (be % nhq) * 4 + wv;
+  const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
+  const int row0 = e * w.rse;
+  const int nrow = min(w.rse, s + nrec - row0);
+  if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
+  constexpr int VEC = Vec16<T>::N;
+  const int ldv = dh + VEC;                        // padded LDS row (storage elements)
+  float* qs = smf + wv * exact_wave_floats(G, dh, (int)sizeof(T));  // [G][dh] queries, times ascale
+  float* pw = qs + G * dh;                          // [G][32] probabilities
+  T* vs = reinterpret_cast<T*>(pw + G * 32);        // [32][ldv] value rows
+  const bool live = l < nrow;
+  const int row = row0 + min(l, nrow - 1);  // lanes past nrow repeat the last row
+  const int64_t roff = row < s ? ((int64_t)u * s + row) * D : ((int64_t)u * nrec + (row - s)) * D;
+  const T* krow = (row < s ? (const T*)c.sink_k : (const T*)c.ring_k) + roff + (int64_t)h * dh;
+  const T* vrow = (row < s ? (const T*)c.sink_v : (const T*)c.ring_v) + roff + (int64_t)h * dh;
+  const T* qh = q + ((int64_t)u * Hq + h * G) * dh;
+  const int npc = dh / VEC;  // 16-byte pieces per row slice
+  float z[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) z[g] = 0.f;
+  for (int p0 = 0; p0 < npc; p0 += 16) {
+    u16x8 kr[16], vr[16], qr[4];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int pc = min(p0 + t, npc - 1);
+      kr[t] = *reinterpret_cast<const u16x8*>(krow + pc * VEC);
+      vr[t] = *reinterpret_cast<const u16x8*>(vrow + pc * VEC);
+    }
+    if (p0 == 0) {  // the G query rows: G * dh / VEC pieces over 64 lanes
+#pragma unroll
+      for (int t = 0; t < 4; ++t)  // G * dh <= 1024: at most 256 pieces
+        qr[t] = *reinterpret_cast<const u16x8*>(qh + min(l + 64 * t, G * npc - 1) * VEC);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pc = l + 64 * t;
+        if (pc < G * npc) {
+          const T* qv = reinterpret_cast<const T*>(&qr[t]);
+#pragma unroll
+          for (int x = 0; x < VEC; ++x) qs[pc * VEC + x] = Elem<T>::ld(qv, x) * ascale;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (live && p0 + t < npc) *reinterpret_cast<u16x8*>(vs + l * ldv + (p0 + t) * VEC) = vr[t];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (p0 + t < npc) {
+        const T* kv = reinterpret_cast<const T*>(&kr[t]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (g < G) {
+            const float* qg = qs + g * dh + (p0 + t) * VEC;
+#pragma unroll
+            for (int x = 0; x < VEC; ++x) z[g] += qg[x] * Elem<T>::ld(kv, x);
+          }
+        }
+      }
+    }
+  }
+  float m[8], S[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const float zz = live ? z[g] : -INFINITY;
+      m[g] = warp_max(zz);
+      const float p = live ? __builtin_amdgcn_exp2f(zz - m[g]) : 0.f;
+      S[g] = warp_sum(p);
+      if (l < 32) pw[g * 32 + l] = p;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  float o[8][4];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[g][i] = 0.f;
+  for (int j = 0; j < nrow; ++j) {
+    float vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = Elem<T>::ld(vs + j * ldv, min(l + 64 * i, dh - 1));
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g < G) {
+        const float p = pw[g * 32 + j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[g][i] += p * vv[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const int a = h * G + g;
+      float* yo = w.yex + (((int64_t)u * w.nse + e) * Hq + a) * dh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (l + 64 * i < dh) yo[l + 64 * i] = o[g][i];
+      if (l == 0) {
+        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + w.nsl + e) * Hq + a) * 2;
+        stp[0] = m[g];
+        stp[1] = S[g];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// merge: grid (H_kv, U), 256 threads.  For the G query heads a of KV head h:
+// M = max over splits, weights f = 2^(m_split - M), L = sum f S_split;
+//   out[a] = (sum_exact f yex + B^V_h (sum_selected f ylat)) / L.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
+                                               float* __restrict__ out) {
+  const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;
   const int Lcur = si[0];
-  const int s = d.s, nrec = d.nrec, G = d.G, D = d.D, r = d.r;
-  const int dh = DH > 0 ? DH : d.dh;
-  const int nc = Lcur + 1 - nrec - s;
-  const int kk = min(d.k, nc);
-  const int R = s + nrec + kk;
-  const int row0 = split * w.rows_per_split;
-  const int row1 = min(row0 + w.rows_per_split, R);
-  const int ldk = attend_ldk(dh);
-  constexpr int ROWP = KS * 16 + 8;  // padded LDS row of staged coefficients (bf16)
-  extern __shared__ float smf[];
-  float* Kt = smf;                   // [32][dh + 1]
-  float* Vt = Kt + 32 * ldk;         // [32][dh + 1]
-  float* qs = Vt + 32 * ldk;         // [G][dh]
-  float* pl = qs + G * dh;           // [G][32]
-  float* alpha = pl + G * 32;        // [G]
-  float* run = alpha + 8;            // [G][2] running (max, sum)
-  uint16_t* Ak = reinterpret_cast<uint16_t*>(run + 16);  // [32][ROWP] (bf16 only)
-  uint16_t* Av = Ak + 32 * ROWP;
-  for (int e = tid; e < G * dh; e += 256) {
-    const int g = e / dh, j = e % dh;
-    qs[e] = Elem<T>::ld(q, ((int64_t)u * d.Hq + h * G + g) * dh + j);
-  }
-  if (tid < G) {
-    run[2 * tid] = -INFINITY;
-    run[2 * tid + 1] = 0.f;
-  }
-  const int32_t* sel = w.topk + (int64_t)u * d.k;
-  const int wv = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
-  const int ncb = dh / 32;
-  bf16x8 bk[KS > 0 ? KS : 1], bv[KS > 0 ? KS : 1];
-  if constexpr (KS > 0) {
-    constexpr int half = KS * 8;
-    if (wv < ncb) {
-      const int ch = h * dh + 32 * wv + mm;
-      const uint16_t* pk = (const uint16_t*)c.basis_k + ((int64_t)u * D + ch) * (KS * 16) + kg * half;
-      const uint16_t* pv = (const uint16_t*)c.basis_v + ((int64_t)u * D + ch) * (KS * 16) + kg * half;
+  const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
+  const int nc = Lcur + 1 - d.nrec - d.s;
+  const int kk = max(0, min(d.k, nc));
+  const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
+  const int nst = w.nsl + w.nse;
+  extern __shared__ __attribute__((aligned(16))) float smf[];
+  float* ys = smf;                 // [G][r]
+  float* fs = ys + G * r;          // [G][nst]
+  float* Lg = fs + G * nst;        // [8]
+  float* stl = Lg + 8;             // [G][nst][2]
+  // thread (channel ch = tid / 2 + 128 m, half hf = tid % 2) later dots the
+  // half [i0, i1) of B^V row h dh + ch with ys[g]; the first 16 pieces of
+  // that half are requested now, before the split statistics
+  constexpr int VEC = Vec16<T>::N;
+  const int hf = tid & 1;
+  const int rh = (r / VEC + 1) / 2 * VEC;
+  const int i0 = hf ? rh : 0, i1 = hf ? r : rh;
+  const T* bbase = (const T*)c.basis_v + ((int64_t)u * d.D + (int64_t)h * dh) * r;
+  u16x8 br[16];
+  auto load_b = [&](int cb, int ib) {
+    const T* brow = bbase + (int64_t)min(cb + (tid >> 1), dh - 1) * r;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bk[ks] = ld_bf16x8(pk + 8 * ks);
-        bv[ks] = ld_bf16x8(pv + 8 * ks);
-      }
-    }
-  }
-  float oacc[4] = {0.f, 0.f, 0.f, 0.f};
-  // gathered coefficient rows of a tile: thread-owned 16-byte pieces
-  // e = tid + 256 i (row e / (r / 8), piece e % (r / 8)); the next tile is
-  // fetched into registers while the current one is computed
-  constexpr int NPIECE = KS > 0 ? (32 * KS * 2 + 255) / 256 : 1;
-  u16x8 fk[NPIECE], fv[NPIECE];
-  auto fetch = [&](int t0) {
-    if constexpr (KS > 0) {
-      constexpr int r16 = KS * 16;
-#pragma unroll
-      for (int i = 0; i < NPIECE; ++i) {
-        const int e = tid + 256 * i;
-        const int rr = e / (r16 / 8), cc = e % (r16 / 8);
-        const int row = t0 + rr;
-        // exact or out-of-range rows read selected entry 0 and are zeroed
-        const bool rec = e < 32 * (r16 / 8) && row >= s + nrec && row < R;
-        const int si2 = rec ? row - s - nrec : 0;  // entry 0 always exists
-        const int64_t pos = min(max((int64_t)sel[si2], (int64_t)0), c.Lmax - 1);
-        const int ccl = cc < r16 / 8 ? cc : 0;
-        const u16x8 a = *reinterpret_cast<const u16x8*>((const uint16_t*)c.coef_k + ((int64_t)u * c.Lmax + pos) * r16 + 8 * ccl);
-        const u16x8 b = *reinterpret_cast<const u16x8*>((const uint16_t*)c.coef_v + ((int64_t)u * c.Lmax + pos) * r16 + 8 * ccl);
-        fk[i] = rec ? a : u16x8{};
-        fv[i] = rec ? b : u16x8{};
-      }
-    }
+    for (int t = 0; t < 16; ++t)
+      br[t] = *reinterpret_cast<const u16x8*>(brow + max(min(ib + t * VEC, i1 - VEC), 0));
   };
-  if (row0 < row1) fetch(row0);
-  for (int t0 = row0; t0 < row1; t0 += 32) {
-    if constexpr (KS > 0) {
-      constexpr int r16 = KS * 16, half = KS * 8;
+  load_b(0, i0);
+  for (int x = tid; x < G * nst; x += 256) {
+    const int g = x / nst, sp = x % nst;
+    const bool ran = sp < nl || sp >= w.nsl;
+    const float* st = w.astat + (((int64_t)u * nst + sp) * Hq + h * G + g) * 2;
+    const float m = st[0], S = st[1];
+    stl[2 * x] = ran ? m : -INFINITY;
+    stl[2 * x + 1] = ran ? S : 0.f;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < nst; ++sp) M = fmaxf(M, stl[2 * (tid * nst + sp)]);
+    float L = 0.f;
+    for (int sp = 0; sp < nst; ++sp) {
+      const float m = stl[2 * (tid * nst + sp)];
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      fs[tid * nst + sp] = f;
+      L += f * stl[2 * (tid * nst + sp) + 1];
+    }
+    Lg[tid] = L;
+  }
+  __syncthreads();
+  // ys[g][i] = sum over the selected-row splits of f * ylat; thread = column
+  // i, its loads for 8 splits x 8 heads (clamped to G) issued together
+  for (int i = tid; i < r; i += 256) {
+    const float* yp = w.ylat + ((int64_t)u * w.nsl * Hq + h * G) * r + i;
+    float acc[8];
 #pragma unroll
-      for (int i = 0; i < NPIECE; ++i) {
-        const int e = tid + 256 * i;
-        if (e < 32 * (r16 / 8)) {
-          const int rr = e / (r16 / 8), cc = e % (r16 / 8);
-          *reinterpret_cast<u16x8*>(Ak + rr * ROWP + 8 * cc) = fk[i];
-          *reinterpret_cast<u16x8*>(Av + rr * ROWP + 8 * cc) = fv[i];
-        }
-      }
-      __syncthreads();
-      if (t0 + 32 < row1) fetch(t0 + 32);
-      if (wv < ncb) {
-        f32x16 ak = {}, av = {};
+    for (int g = 0; g < 8; ++g) acc[g] = 0.f;
+    for (int sp0 = 0; sp0 < nl; sp0 += 8) {
+      float v[8][8];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a1 = ld_bf16x8(Ak + mm * ROWP + kg * half + 8 * ks);
-          const bf16x8 a2 = ld_bf16x8(Av + mm * ROWP + kg * half + 8 * ks);
-          ak = mfma32x32x16(a1, bk[ks], ak);
-          av = mfma32x32x16(a2, bv[ks], av);
-        }
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          Kt[acc_row32(i, l) * ldk + 32 * wv + mm] = ak[i];
-          Vt[acc_row32(i, l) * ldk + 32 * wv + mm] = av[i];
-        }
-      }
-    } else {
-      for (int e = tid; e < 32 * dh; e += 256) {
-        const int rr = e / dh, j = e % dh;
-        const int row = t0 + rr;
-        float kv = 0.f, vv = 0.f;
-        if (row >= s + nrec && row < R) {
-          const int64_t pos = sel[row - s - nrec];
-          const T* ck = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pos) * r;
-          const T* cv = (const T*)c.coef_v + ((int64_t)u * c.Lmax + pos) * r;
-          const T* bkp = (const T*)c.basis_k + ((int64_t)u * D + h * dh + j) * r;
-          const T* bvp = (const T*)c.basis_v + ((int64_t)u * D + h * dh + j) * r;
-          for (int i = 0; i < r; ++i) {
-            kv += Elem<T>::ld(ck, i) * Elem<T>::ld(bkp, i);
-            vv += Elem<T>::ld(cv, i) * Elem<T>::ld(bvp, i);
+        for (int g = 0; g < 8; ++g)
+          v[t][g] = yp[((int64_t)min(sp0 + t, nl - 1) * Hq + min(g, G - 1)) * r];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (sp0 + t < nl)
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < G) acc[g] += fs[g * nst + sp0 + t] * v[t][g];
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < G) ys[g * r + i] = acc[g];
+  }
+  __syncthreads();
+  for (int cb = 0; cb < dh; cb += 128) {
+    const int ch = cb + (tid >> 1);
+    float acc[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc[g] = 0.f;
+    for (int ib = i0; ib < i1; ib += 16 * VEC) {
+      if (cb > 0 || ib > i0) load_b(cb, ib);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (ib + t * VEC < i1) {
+          const T* bv = reinterpret_cast<const T*>(&br[t]);
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            if (g < G) {
+              const float* yg = ys + g * r + ib + t * VEC;
+#pragma unroll
+              for (int x = 0; x < VEC; ++x) acc[g] += Elem<T>::ld(bv, x) * yg[x];
+            }
           }
         }
-        Kt[rr * ldk + j] = kv;
-        Vt[rr * ldk + j] = vv;
       }
     }
-    __syncthreads();
-    // exact rows of this tile
-    if (t0 < s + nrec) {
-      for (int e = tid; e < 32 * dh; e += 256) {
-        const int rr = e / dh, j = e % dh;
-        const int row = t0 + rr;
-        if (row < s) {
-          Kt[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_k, ((int64_t)u * s + row) * D + h * dh + j);
-          Vt[rr * ldk + j] = Elem<T>::ld((const T*)c.sink_v, ((int64_t)u * s + row) * D + h * dh + j);
-        } else if (row < s + nrec) {
-          const int slot = row - s;
-          Kt[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_k, ((int64_t)u * nrec + slot) * D + h * dh + j);
-          Vt[rr * ldk + j] = Elem<T>::ld((const T*)c.ring_v, ((int64_t)u * nrec + slot) * D + h * dh + j);
-        }
-      }
-      __syncthreads();
-    }
-    // logits and online softmax; thread (g, rr) = (tid / 32, tid % 32)
-    {
-      const int g = tid >> 5, rr = tid & 31;
-      float z = -INFINITY;
-      if (g < G && t0 + rr < row1) {
-        float dot = 0.f;
-        if constexpr (DH > 0) {
-          const f32x4* kr = reinterpret_cast<const f32x4*>(Kt + rr * ldk);
-          const f32x4* qv = reinterpret_cast<const f32x4*>(qs + g * DH);
-          f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j4 = 0; j4 < DH / 4; ++j4) a4 += qv[j4] * kr[j4];
-          dot = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-        } else {
-          for (int j = 0; j < dh; ++j) dot += qs[g * dh + j] * Kt[rr * ldk + j];
-        }
-        z = dot * sm_scale;
-      }
-      float tmax = z;
+    for (int g = 0; g < 8; ++g) acc[g] += __shfl_xor(acc[g], 1);
+    if (ch < dh) {
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
-      const float m_old = g < G ? run[2 * g] : 0.f;
-      const float m_new = fmaxf(m_old, tmax);
-      const float pz = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
-      float ps = pz;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o);
-      __syncthreads();
-      if (g < G) {
-        pl[g * 32 + rr] = pz;
-        if (rr == 0) {
-          const float a = (m_old == -INFINITY) ? 0.f : exp2f(m_old - m_new);
-          alpha[g] = a;
-          run[2 * g] = m_new;
-          run[2 * g + 1] = run[2 * g + 1] * a + ps;
+      for (int g = 0; g < 8; ++g) {
+        if (g < G && (g & 1) == hf) {  // the two lanes of a channel share the stores
+          const int a = h * G + g;
+          float o = acc[g];
+          for (int e = 0; e < w.nse; ++e)
+            o += fs[g * nst + w.nsl + e] * w.yex[(((int64_t)u * w.nse + e) * Hq + a) * dh + ch];
+          out[((int64_t)u * Hq + a) * dh + ch] = o / Lg[g];
         }
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i;
-      if (e < G * dh) {
-        const int g = e / dh, j = e % dh;
-        float acc = oacc[i] * alpha[g];
-        for (int rr = 0; rr < 32; ++rr) acc += pl[g * 32 + rr] * Vt[rr * ldk + j];
-        oacc[i] = acc;
-      }
-    }
-    __syncthreads();
-  }
-  // split partial
-  float* part = w.part + (int64_t)u * d.Hq * w.nsa * (dh + 2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i;
-    if (e < G * dh) {
-      const int g = e / dh, j = e % dh;
-      part[((int64_t)(h * G + g) * w.nsa + split) * (dh + 2) + 2 + j] = oacc[i];
-    }
-  }
-  if (tid < G) {
-    part[((int64_t)(h * G + tid) * w.nsa + split) * (dh + 2) + 0] = run[2 * tid];
-    part[((int64_t)(h * G + tid) * w.nsa + split) * (dh + 2) + 1] = run[2 * tid + 1];
   }
 }
 
-// merge of the row splits of one (unit, query head): online-softmax
-// combination of the split partials (max, sum, unnormalised output)
-__global__ __launch_bounds__(128) void k_merge(Dims d, DecodeWs w, float* __restrict__ out) {
-  const int a = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  if (w.stepinfo[4 * u + 2]) return;  // full unit: the top-k kernel wrote zeros
-  const int dh = d.dh;
-  const float* pp = w.part + ((int64_t)u * d.Hq + a) * w.nsa * (dh + 2);
-  float M = -INFINITY;
-  for (int sp = 0; sp < w.nsa; ++sp) M = fmaxf(M, pp[sp * (dh + 2)]);
-  for (int j = tid; j < dh; j += blockDim.x) {
-    float Ls = 0.f, O = 0.f;
-    for (int sp = 0; sp < w.nsa; ++sp) {
-      const float m = pp[sp * (dh + 2)];
-      if (m == -INFINITY) continue;
-      const float f = exp2f(m - M);
-      Ls += pp[sp * (dh + 2) + 1] * f;
-      O += pp[sp * (dh + 2) + 2 + j] * f;
-    }
-    out[((int64_t)u * d.Hq + a) * dh + j] = O / Ls;
-  }
+static size_t merge_lds(const Dims& d, const DecodeWs& w) {
+  return ((size_t)d.G * d.r + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
 
-hipError_t launch_merge(const Dims& d, int U, const DecodeWs& w, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(d.Hq, U), dim3(128), 0, st, d, w, out);
-  return hipGetLastError();
-}
-
-// The attention tile can exceed the default 64 KB dynamic LDS limit; raise it
-// once per kernel instantiation (gfx950 has 160 KB of LDS per CU).
-template <typename T, int KS, int DH>
-static hipError_t allow_lds(size_t lds) {
-  static size_t done = 0;
-  if (lds <= 65536 || lds <= done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attend<T, KS, DH>),
+// Kernels that may need more than the default 64 KB of dynamic LDS get the
+// limit raised once (gfx950 has 160 KB of LDS per CU).
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t lds, size_t* done) {
+  if (lds <= 65536 || lds <= *done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e == hipSuccess) done = lds;
+  if (e == hipSuccess) *done = lds;
   return e;
 }
 
-template <typename T, int KS, int DH>
+template <typename T>
 static hipError_t launch_attend_t(const Dims& d, int U, const void* q, const CachePtrs& c,
-                                  const DecodeWs& w, float* out, hipStream_t st) {
-  const int rowp = KS * 16 + 8;
-  size_t lds = ((size_t)2 * 32 * attend_ldk(d.dh) + d.G * d.dh + d.G * 32 + 8 + 16) * sizeof(float);
-  if (KS > 0) lds += (size_t)2 * 32 * rowp * sizeof(uint16_t);
-  hipError_t e = allow_lds<T, KS, DH>(lds);
+                                  const DecodeWs& w, hipStream_t st) {
+  static size_t done = 0;
+  if (w.attend_lds <= 0) return hipErrorInvalidValue;
+  hipError_t e = allow_lds(&k_attend<T>, (size_t)w.attend_lds, &done);
   if (e != hipSuccess) return e;
-  const float sm_scale = kLog2e / sqrtf((float)d.dh);
-  hipLaunchKernelGGL((k_attend<T, KS, DH>), dim3(w.nsa, d.Hkv, U), dim3(256), lds, st, d, c, w,
-                     (const T*)q, out, sm_scale);
+  const float ascale = kLog2e / sqrtf((float)d.dh);
+  hipLaunchKernelGGL(k_attend<T>, dim3(w.nsl * w.nhg + w.nse * ((d.Hkv + 3) / 4), U), dim3(256),
+                     w.attend_lds, st, d,
+                     c, w, (const T*)q, ascale);
   return hipGetLastError();
 }
 
-template <int KS>
-static hipError_t launch_attend_bf16(const Dims& d, int U, const void* q, const CachePtrs& c,
-                                     const DecodeWs& w, float* out, hipStream_t st) {
-  switch (d.dh) {
-    case 128: return launch_attend_t<uint16_t, KS, 128>(d, U, q, c, w, out, st);
-    case 64: return launch_attend_t<uint16_t, KS, 64>(d, U, q, c, w, out, st);
-    default: return launch_attend_t<uint16_t, KS, 0>(d, U, q, c, w, out, st);
-  }
+hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
+                         const DecodeWs& w, hipStream_t st) {
+  if (d.dtype == 0) return launch_attend_t<float>(d, U, q, c, w, st);
+  return launch_attend_t<uint16_t>(d, U, q, c, w, st);
 }
 
-hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
-                         const DecodeWs& w, float* out, hipStream_t st) {
-  if (d.dtype == 0) return launch_attend_t<float, 0, 0>(d, U, q, c, w, out, st);
-  switch (d.r) {
-    case 128: return launch_attend_bf16<8>(d, U, q, c, w, out, st);
-    case 192: return launch_attend_bf16<12>(d, U, q, c, w, out, st);
-    case 256: return launch_attend_bf16<16>(d, U, q, c, w, out, st);
-    case 64: return launch_attend_bf16<4>(d, U, q, c, w, out, st);
-    case 32: return launch_attend_bf16<2>(d, U, q, c, w, out, st);
-    default: return hipErrorInvalidValue;
-  }
+template <typename T>
+static hipError_t launch_merge_t(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+                                 float* out, hipStream_t st) {
+  static size_t done = 0;
+  const size_t lds = merge_lds(d, w);
+  hipError_t e = allow_lds(&k_merge<T>, lds, &done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_merge<T>, dim3(d.Hkv, U), dim3(256), lds, st, d, c, w, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
+                        hipStream_t st) {
+  if (d.dtype == 0) return launch_merge_t<float>(d, U, c, w, out, st);
+  return launch_merge_t<uint16_t>(d, U, c, w, out, st);
 }
 
 }  // namespace kvlr

@@ -58,7 +58,7 @@ def _cfg(**kw):
     (dict(pool_kernel=4), "odd"),
     (dict(n_recent=0), "n_recent"),
     (dict(top_k=-1), "top_k"),
-    (dict(head_dim=48), "head_dim"),
+    (dict(head_dim=44), "head_dim"),
     (dict(q_window=64), "q_window"),
     (dict(n_sample=0), "n_sample"),
     (dict(storage="f32", rank=256, q_window=16), "8192"),
