@@ -92,6 +92,48 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Reductions over the 64 lanes of a wave without LDS round trips: four DPP
+// steps inside each row of 16 lanes (quad xor 1, quad xor 2, half-row mirror,
+// row mirror) leave every lane of a row holding the row's value (bit-identical
+// across the row), then the four rows are combined from v_readlane results,
+// so every lane returns the same wave value.  N independent values are
+// reduced together to overlap their latencies.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<0xB1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<0x4E>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<0x141>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<0x140>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = (lane_f(v[i], 0) + lane_f(v[i], 16)) + (lane_f(v[i], 32) + lane_f(v[i], 48));
+}
+template <int N>
+__device__ __forceinline__ void wave_max_n(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<0xB1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<0x4E>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<0x141>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp_f<0x140>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = fmaxf(fmaxf(lane_f(v[i], 0), lane_f(v[i], 16)), fmaxf(lane_f(v[i], 32), lane_f(v[i], 48)));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace kvlr

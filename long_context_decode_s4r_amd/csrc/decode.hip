@@ -33,22 +33,29 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 
 // Attention tile over the selected rows: hb query heads (multiple of 8) and
 // rsl rows (multiple of 4, <= 64) per block.  LDS: projected queries
-// [hb][r + 4] fp32, probabilities [hb][rsl + 1] fp32, coefficient rows of K
+// [hb][r + 4] fp32, logits [hb][rsl + 1] fp32, probabilities [rsl][hb] fp32,
+// coefficient rows of K
 // and V [rsl][r] storage type with 16 bytes of padding per row.
 static size_t latent_lds(const Dims& d, int hb, int rsl) {
   const size_t el = d.dtype == 0 ? 4 : 2;
-  return (size_t)hb * (d.r + 4) * 4 + (size_t)hb * (rsl + 1) * 4 + 16 +
+  return (size_t)hb * (d.r + 4) * 4 + (size_t)hb * (rsl + 1) * 4 + 16 + (size_t)rsl * hb * 4 +
          (size_t)2 * rsl * (d.r * el + 16);
 }
-// exact rows, per wave: queries [G][dh] fp32, probabilities [G][32] fp32,
+// exact rows, per wave: queries [G][dh] fp32, probabilities [32][8] fp32,
 // value rows [32][dh + 16 bytes] storage type
 __host__ __device__ inline int exact_wave_floats(int G, int dh, int el) {
-  return G * dh + G * 32 + 8 * (dh * el + 16);
+  return G * dh + 32 * 8 + 8 * (dh * el + 16);
 }
 static size_t exact_lds(const Dims& d) {
   return (size_t)4 * exact_wave_floats(d.G, d.dh, d.dtype == 0 ? 4 : 2) * 4;
 }
+static int attn_tile_bytes(int r);
 static void attend_tile(const Dims& d, int* hb, int* rsl) {
+  if (d.dtype != 0) {  // bf16: MFMA tiles of 64 rows x 32 heads
+    *hb = 32;
+    *rsl = 64;
+    return;
+  }
   int h = (int)round_up(d.Hq, 8);
   if (h > 32) h = 32;
   int rs = 32;
@@ -61,7 +68,8 @@ static void attend_tile(const Dims& d, int* hb, int* rsl) {
 size_t attend_lds_bytes(const Dims& d) {
   int hb, rsl;
   attend_tile(d, &hb, &rsl);
-  size_t a = latent_lds(d, hb, rsl), b = exact_lds(d);
+  size_t a = d.dtype != 0 ? (size_t)attn_tile_bytes(d.r) : latent_lds(d, hb, rsl);
+  size_t b = exact_lds(d);
   a = a > b ? a : b;
   return a <= 160 * 1024 ? a : 0;
 }
@@ -93,6 +101,8 @@ void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
 }
 
 __device__ __forceinline__ int wrap_slot(int x, int W) { return ((x % W) + W) % W; }
+__device__ __forceinline__ int wv_of(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+__device__ __forceinline__ int l_of(int tid) { return tid & 63; }
 
 // 16 bytes of storage elements -> fp32
 template <typename T> struct Vec16;
@@ -254,6 +264,7 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
   }
   if (b > 2 * ncb) {
     // qlat[h G + g] = ascale * q[h G + g] . B^K[h dh : (h + 1) dh, :]
+    // (fp32 storage: fp32 rows; bf16 storage: bf16 hi and lo rows)
     const int h = b - 2 * ncb - 1, dh = d.dh;
     float* qs = sm;                 // [G][dh]
     float* red = qs + G * dh;       // [4 waves][G][32 * VEC]
@@ -297,8 +308,16 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
         const int g = t / (32 * VEC), cc = t % (32 * VEC);
         if (c0 + cc < r) {
           const int o = g * 32 * VEC + cc, st = G * 32 * VEC;
-          w.qlat[((int64_t)u * d.Hq + h * G + g) * r + c0 + cc] =
-              (red[o] + red[o + st]) + (red[o + 2 * st] + red[o + 3 * st]);
+          const float x = (red[o] + red[o + st]) + (red[o + 2 * st] + red[o + 3 * st]);
+          const int64_t a = (int64_t)u * d.Hq + h * G + g;
+          if constexpr (sizeof(T) == 4) {
+            w.qlat[a * r + c0 + cc] = x;
+          } else {  // MFMA operands: bf16 hi and lo rows
+            uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + a * 2 * r + c0 + cc;
+            const uint16_t hb = f2bf(x);
+            ql[0] = hb;
+            ql[r] = f2bf(x - bf2f(hb));
+          }
         }
       }
       __syncthreads();
@@ -1177,22 +1196,164 @@ template <> struct Quad<uint16_t> {
   }
 };
 
+// Exact rows (sinks, then the recent ring) of one block: block index be
+// among the exact blocks; needs no unit state (a full unit's results are
+// never read).
+template <typename T>
+__device__ __forceinline__ void attend_exact(const Dims& d, const CachePtrs& c, const DecodeWs& w,
+                                             const T* __restrict__ q, float ascale, int be, int u,
+                                             int tid, float* smf) {
+  const int wv = tid >> 6, l = tid & 63, Hq = d.Hq;
+  // block (e, hq): rows [e * rse, +rse) (rse <= 32), KV head h = 4 hq + wave.
+  // Lane l < nrow loads row l's K and V slices of head h in one phase (V goes
+  // to LDS), scores it against the G query heads, and after the softmax the
+  // lanes switch to channels (c = l + 64 i) to sum the values from LDS.
+  const int nhq = (d.Hkv + 3) >> 2;
+  const int e = be / nhq, h = (be % nhq) * 4 + wv;
+  const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
+  const int row0 = e * w.rse;
+  const int nrow = min(w.rse, s + nrec - row0);
+  if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
+  constexpr int VEC = Vec16<T>::N;
+  const int ldv = dh + VEC;                        // padded LDS row (storage elements)
+  float* qs = smf + wv * exact_wave_floats(G, dh, (int)sizeof(T));  // [G][dh] queries, times ascale
+  float* pw = qs + G * dh;                          // [32][8] probabilities
+  T* vs = reinterpret_cast<T*>(pw + 32 * 8);        // [32][ldv] value rows
+  const bool live = l < nrow;
+  const int row = row0 + min(l, nrow - 1);  // lanes past nrow repeat the last row
+  const int64_t roff = row < s ? ((int64_t)u * s + row) * D : ((int64_t)u * nrec + (row - s)) * D;
+  const T* krow = (row < s ? (const T*)c.sink_k : (const T*)c.ring_k) + roff + (int64_t)h * dh;
+  const T* vrow = (row < s ? (const T*)c.sink_v : (const T*)c.ring_v) + roff + (int64_t)h * dh;
+  const T* qh = q + ((int64_t)u * Hq + h * G) * dh;
+  const int npc = dh / VEC;  // 16-byte pieces per row slice
+  float z[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) z[g] = 0.f;
+  for (int p0 = 0; p0 < npc; p0 += 16) {
+    u16x8 kr[16], vr[16], qr[4];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int pc = min(p0 + t, npc - 1);
+      kr[t] = *reinterpret_cast<const u16x8*>(krow + pc * VEC);
+      vr[t] = *reinterpret_cast<const u16x8*>(vrow + pc * VEC);
+    }
+    if (p0 == 0) {  // the G query rows: G * dh / VEC pieces over 64 lanes
+#pragma unroll
+      for (int t = 0; t < 4; ++t)  // G * dh <= 1024: at most 256 pieces
+        qr[t] = *reinterpret_cast<const u16x8*>(qh + min(l + 64 * t, G * npc - 1) * VEC);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pc = l + 64 * t;
+        if (pc < G * npc) {
+          const T* qv = reinterpret_cast<const T*>(&qr[t]);
+#pragma unroll
+          for (int x = 0; x < VEC; x += 4)
+            *reinterpret_cast<f32x4*>(qs + pc * VEC + x) =
+                f32x4{Elem<T>::ld(qv, x), Elem<T>::ld(qv, x + 1), Elem<T>::ld(qv, x + 2),
+                      Elem<T>::ld(qv, x + 3)} * ascale;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (live && p0 + t < npc) *reinterpret_cast<u16x8*>(vs + l * ldv + (p0 + t) * VEC) = vr[t];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (p0 + t < npc) {
+        const T* kv = reinterpret_cast<const T*>(&kr[t]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (g < G) {
+            const float* qg = qs + g * dh + (p0 + t) * VEC;
+#pragma unroll
+            for (int x = 0; x < VEC; x += 4) {
+              const f32x4 q4 = *reinterpret_cast<const f32x4*>(qg + x);
+              z[g] += q4[0] * Elem<T>::ld(kv, x) + q4[1] * Elem<T>::ld(kv, x + 1) +
+                      q4[2] * Elem<T>::ld(kv, x + 2) + q4[3] * Elem<T>::ld(kv, x + 3);
+            }
+          }
+        }
+      }
+    }
+  }
+  float m[8], S[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) m[g] = live ? z[g] : -INFINITY;
+  wave_max_n<8>(m);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) S[g] = live ? __builtin_amdgcn_exp2f(z[g] - m[g]) : 0.f;
+  if (l < 32) {  // pw[row][g], g padded to 8
+    *reinterpret_cast<f32x4*>(pw + l * 8) = f32x4{S[0], S[1], S[2], S[3]};
+    *reinterpret_cast<f32x4*>(pw + l * 8 + 4) = f32x4{S[4], S[5], S[6], S[7]};
+  }
+  wave_sum_n<8>(S);
+  __builtin_amdgcn_wave_barrier();
+  // values: lane l holds channel pairs c = 2 l + 128 i, i < 2 (d_h <= 256)
+  float o[8][4];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[g][i] = 0.f;
+  const int c0 = min(2 * l, dh - 2), c1 = min(2 * l + 128, dh - 2);
+#pragma unroll 4
+  for (int j = 0; j < nrow; ++j) {
+    const T* vj = vs + j * ldv;
+    const float v0 = Elem<T>::ld(vj, c0), v1 = Elem<T>::ld(vj, c0 + 1);
+    const float v2 = Elem<T>::ld(vj, c1), v3 = Elem<T>::ld(vj, c1 + 1);
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(pw + j * 8);
+    const f32x4 pb = G > 4 ? *reinterpret_cast<const f32x4*>(pw + j * 8 + 4) : f32x4{};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float p = g < 4 ? pa[g] : pb[g - 4];
+      o[g][0] += p * v0;
+      o[g][1] += p * v1;
+      o[g][2] += p * v2;
+      o[g][3] += p * v3;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const int a = h * G + g;
+      float* yo = w.yex + (((int64_t)u * w.nse + e) * Hq + a) * dh;
+      if (2 * l < dh) {
+        yo[2 * l] = o[g][0];
+        yo[2 * l + 1] = o[g][1];
+      }
+      if (2 * l + 128 < dh) {
+        yo[2 * l + 128] = o[g][2];
+        yo[2 * l + 129] = o[g][3];
+      }
+      if (l == 0) {
+        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + w.nsl + e) * Hq + a) * 2;
+        stp[0] = m[g];
+        stp[1] = S[g];
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
                                                 const T* __restrict__ q, float ascale) {
   typedef typename Quad<T>::V QV;
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  extern __shared__ __attribute__((aligned(16))) float smf[];
+  if (b >= w.nsl * w.nhg) {
+    attend_exact<T>(d, c, w, q, ascale, b - w.nsl * w.nhg, u, tid, smf);
+    return;
+  }
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;  // full unit: the top-k kernel wrote zeros
   const int Lcur = si[0];
   const int r = d.r, Hq = d.Hq;
   const int nc = Lcur + 1 - d.nrec - d.s;
   const int kk = max(0, min(d.k, nc));
-  extern __shared__ __attribute__((aligned(16))) float smf[];
   const int wv = tid >> 6, l = tid & 63;
 
-  if (b < w.nsl * w.nhg) {
-    // ---------------- selected rows, coefficient space ----------------
+  {
+    // ---------------- selected rows, coefficient space (fp32 VALU) ----------------
     const int split = b / w.nhg, hg = b % w.nhg;
     const int row0 = split * w.rsl;
     const int nrow = min(w.rsl, kk - row0);
@@ -1202,7 +1363,7 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
     const int ldq = r + 4, ldz = w.rsl + 1, ldc = r + E, r4 = r / 4, rE = r / E;
     float* qt = smf;                                  // [hb][ldq]
     float* zs = qt + hb * ldq;                        // [hb][ldz]
-    T* ck = reinterpret_cast<T*>(zs + ((hb * ldz + 3) & ~3));  // [rsl][ldc]
+    T* ck = reinterpret_cast<T*>(zs + ((hb * ldz + 3) & ~3) + w.rsl * hb);  // [rsl][ldc]
     T* cv = ck + w.rsl * ldc;
     const int32_t* sel = w.topk + (int64_t)u * d.k + row0;
     {
@@ -1256,6 +1417,7 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
       const float* qa = qt + a * ldq;
       const T* c0 = ck + 4 * jg * ldc;
       f32x4 acc[4] = {};
+#pragma unroll 4
       for (int i = 0; i < r; i += 4) {
         const f32x4 q4 = *reinterpret_cast<const f32x4*>(qa + i);
 #pragma unroll
@@ -1268,17 +1430,38 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
           zs[a * ldz + 4 * jg + jj] = (acc[jj][0] + acc[jj][1]) + (acc[jj][2] + acc[jj][3]);
     }
     __syncthreads();
-    // split-local softmax per head: a wave per head, a lane per row
-    for (int a = wv; a < na; a += 4) {
-      const float z = l < nrow ? zs[a * ldz + l] : -INFINITY;
-      const float m = warp_max(z);
-      const float pz = l < nrow ? __builtin_amdgcn_exp2f(z - m) : 0.f;
-      const float S = warp_sum(pz);
-      if (l < nrow) zs[a * ldz + l] = pz;
-      if (l == 0) {
-        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + split) * Hq + a0 + a) * 2;
-        stp[0] = m;
-        stp[1] = S;
+    // split-local softmax: a wave takes 8 heads at a time, a lane per row;
+    // probabilities go to pT[row][head]
+    float* pT = zs + hb * ldz;  // [rsl][hb]
+    for (int ab = wv * 8; ab < na; ab += 32) {
+      float z[8], m[8], p[8], S[8];
+#pragma unroll
+      for (int aa = 0; aa < 8; ++aa) {
+        const bool ok = l < nrow && ab + aa < na;
+        z[aa] = ok ? zs[(ab + aa) * ldz + l] : -INFINITY;
+        m[aa] = z[aa];
+      }
+      wave_max_n<8>(m);
+#pragma unroll
+      for (int aa = 0; aa < 8; ++aa) {
+        p[aa] = z[aa] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[aa] - m[aa]);
+        S[aa] = p[aa];
+      }
+      wave_sum_n<8>(S);
+      if (l < nrow) {
+        *reinterpret_cast<f32x4*>(pT + l * hb + ab) = f32x4{p[0], p[1], p[2], p[3]};
+        *reinterpret_cast<f32x4*>(pT + l * hb + ab + 4) = f32x4{p[4], p[5], p[6], p[7]};
+      }
+      if (l < 8 && ab + l < na) {
+        float mm = m[0], ss = S[0];
+#pragma unroll
+        for (int aa = 1; aa < 8; ++aa) {
+          mm = l == aa ? m[aa] : mm;
+          ss = l == aa ? S[aa] : ss;
+        }
+        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + split) * Hq + a0 + ab + l) * 2;
+        stp[0] = mm;
+        stp[1] = ss;
       }
     }
     __syncthreads();
@@ -1287,10 +1470,19 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
     for (int e = tid; e < nag * r4; e += 256) {
       const int ag = e / r4, i4 = e % r4;
       f32x4 acc[8] = {};
+#pragma unroll 4
       for (int j = 0; j < nrow; ++j) {
         const f32x4 v4 = Quad<T>::f(*reinterpret_cast<const QV*>(cv + j * ldc + 4 * i4));
-#pragma unroll
-        for (int aa = 0; aa < 8; ++aa) acc[aa] += zs[(8 * ag + aa) * ldz + j] * v4;
+        const f32x4 pa = *reinterpret_cast<const f32x4*>(pT + j * hb + 8 * ag);
+        const f32x4 pb = *reinterpret_cast<const f32x4*>(pT + j * hb + 8 * ag + 4);
+        acc[0] += pa[0] * v4;
+        acc[1] += pa[1] * v4;
+        acc[2] += pa[2] * v4;
+        acc[3] += pa[3] * v4;
+        acc[4] += pb[0] * v4;
+        acc[5] += pb[1] * v4;
+        acc[6] += pb[2] * v4;
+        acc[7] += pb[3] * v4;
       }
 #pragma unroll
       for (int aa = 0; aa < 8; ++aa) {
@@ -1302,118 +1494,203 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
     }
     return;
   }
+}
 
-  // ---------------- exact rows: sinks then the recent ring ----------------
-  // block (e, hq): rows [e * rse, +rse) (rse <= 32), KV head h = 4 hq + wave.
-  // Lane l < nrow loads row l's K and V slices of head h in one phase (V goes
-  // to LDS), scores it against the G query heads, and after the softmax the
-  // lanes switch to channels (c = l + 64 i) to sum the values from LDS.
-  const int be = b - w.nsl * w.nhg;
-  const int nhq = (d.Hkv + 3) >> 2;
-  const int e = be / nhq, h = (be % nhq) * 4 + wv;
-  const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
-  const int row0 = e * w.rse;
-  const int nrow = min(w.rse, s + nrec - row0);
-  if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
-  constexpr int VEC = Vec16<T>::N;
-  const int ldv = dh + VEC;                        // padded LDS row (storage elements)
-  float* qs = smf + wv * exact_wave_floats(G, dh, (int)sizeof(T));  // [G][dh] queries, times ascale
-  float* pw = qs + G * dh;                          // [G][32] probabilities
-  T* vs = reinterpret_cast<T*>(pw + G * 32);        // [32][ldv] value rows
-  const bool live = l < nrow;
-  const int row = row0 + min(l, nrow - 1);  // lanes past nrow repeat the last row
-  const int64_t roff = row < s ? ((int64_t)u * s + row) * D : ((int64_t)u * nrec + (row - s)) * D;
-  const T* krow = (row < s ? (const T*)c.sink_k : (const T*)c.ring_k) + roff + (int64_t)h * dh;
-  const T* vrow = (row < s ? (const T*)c.sink_v : (const T*)c.ring_v) + roff + (int64_t)h * dh;
-  const T* qh = q + ((int64_t)u * Hq + h * G) * dh;
-  const int npc = dh / VEC;  // 16-byte pieces per row slice
-  float z[8];
+// --------------------------------------------------------------------------
+// Selected rows for bf16 storage with MFMA (16x16x32, bf16 in, fp32 out):
+// block (split, hg): 64 rows x 32 heads.  The projected queries and the
+// probabilities enter as bf16 hi + lo pairs (two MFMAs each), so products
+// carry about 16 mantissa bits; the coefficients are exact bf16.
+//   logits: wave w -> head tile w / 2, row tiles 2 (w % 2) + {0, 1}, K = r;
+//   softmax as in the fp32 kernel (a lane per row), probabilities to LDS;
+//   values: wave w -> head tile w % 2, half of the r / 16 coefficient tiles,
+//     K = the 64 rows; the V rows are staged transposed ([coefficient][row])
+//     so every MFMA operand is one 16-byte LDS read.
+// Loads that do not depend on the unit state (top-k entries, query
+// fragments) are issued together with it.
+// --------------------------------------------------------------------------
+constexpr int kAttnRows = 64;
+template <int R>
+struct AttnTile {
+  static constexpr int KC = R / 8;                 // 16-byte chunks per coefficient row
+  static constexpr int CKB = R * 2 + 16;           // bytes per staged K row
+  static constexpr int CVB = kAttnRows * 2 + 16;   // bytes per transposed V row
+  static constexpr int ZLD = kAttnRows + 1, PLD = kAttnRows + 4;  // fp32 strides
+  static constexpr int ck = 0;
+  static constexpr int cv = ck + kAttnRows * CKB;
+  static constexpr int zs = cv + R * CVB;
+  static constexpr int pz = zs + ((32 * ZLD * 4 + 15) & ~15);
+  static constexpr int bytes = pz + 32 * PLD * 4;
+};
+static int attn_tile_bytes(int r) {
+  return kAttnRows * (r * 2 + 16) + r * (kAttnRows * 2 + 16) + ((32 * (kAttnRows + 1) * 4 + 15) & ~15) +
+         32 * (kAttnRows + 4) * 4;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16 hi / lo pair of 8 fp32 values as MFMA operands
+__device__ __forceinline__ void split8(f32x4 p0, f32x4 p1, bf16x8* hi, bf16x8* lo) {
+  u16x8 ph, pl;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) z[g] = 0.f;
-  for (int p0 = 0; p0 < npc; p0 += 16) {
-    u16x8 kr[16], vr[16], qr[4];
+  for (int x = 0; x < 8; ++x) {
+    const float pv = x < 4 ? p0[x] : p1[x - 4];
+    const uint16_t hb = f2bf(pv);
+    ph[x] = hb;
+    pl[x] = f2bf(pv - bf2f(hb));
+  }
+  *hi = __builtin_bit_cast(bf16x8, ph);
+  *lo = __builtin_bit_cast(bf16x8, pl);
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, DecodeWs w,
+                                                     const uint16_t* __restrict__ q, float ascale) {
+  typedef AttnTile<R> Lay;
+  constexpr int NR = kAttnRows;
+  constexpr int KC = Lay::KC, KS = KC / 4, NT = R / 16;
+  constexpr int NPC = NR * KC;                 // pieces per staged matrix
+  constexpr int NP = (NPC + 255) / 256;        // pieces per thread
+  static_assert(KC % 4 == 0 && NT % 2 == 0, "rank must be a multiple of 32");
+  const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  extern __shared__ __attribute__((aligned(16))) float smf[];
+  if (b >= w.nsl * w.nhg) {
+    attend_exact<uint16_t>(d, c, w, q, ascale, b - w.nsl * w.nhg, u, tid, smf);
+    return;
+  }
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smf);
+  const int wv = tid >> 6, l = tid & 63, n16 = l & 15, kg = l >> 4;
+  const int Hq = d.Hq;
+  const int split = b / w.nhg, hg = b % w.nhg;
+  const int row0 = split * NR, a0 = hg * 32;
+  // ---- unit state, this split's top-k entries and the query fragments
+  const int32_t* si = w.stepinfo + 4 * u;
+  const int full = si[2], Lcur = si[0];
+  int selv[NP];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int pc = min(p0 + t, npc - 1);
-      kr[t] = *reinterpret_cast<const u16x8*>(krow + pc * VEC);
-      vr[t] = *reinterpret_cast<const u16x8*>(vrow + pc * VEC);
+  for (int i = 0; i < NP; ++i) {
+    const int j = min(tid + 256 * i, NPC - 1) / KC;
+    selv[i] = w.topk[(int64_t)u * d.k + min(row0 + j, d.k - 1)];
+  }
+  const int ht = wv >> 1, rt0 = 2 * (wv & 1);
+  const int ah = min(a0 + 16 * ht + n16, Hq - 1);  // heads past H_q repeat the last one
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(w.qlat) + ((int64_t)u * Hq + ah) * 2 * R;
+  bf16x8 ahi[KS], alo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    ahi[ks] = ld_bf16x8(qp + (4 * ks + kg) * 8);
+    alo[ks] = ld_bf16x8(qp + R + (4 * ks + kg) * 8);
+  }
+  if (full) return;  // the top-k kernel wrote zeros
+  const int nc = Lcur + 1 - d.nrec - d.s;
+  const int kk = max(0, min(d.k, nc));
+  const int nrow = min(NR, kk - row0);
+  if (nrow <= 0) return;
+  // ---- gather the rows: K row-major, V transposed (rows past nrow: V zeroed)
+  {
+    const uint16_t* cks = (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * R;
+    const uint16_t* cvs = (const uint16_t*)c.coef_v + (int64_t)u * c.Lmax * R;
+    u16x8 xk[NP], xv[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int e = min(tid + 256 * i, NPC - 1);
+      const int cc = e % KC;
+      const int64_t pos = min(max((int64_t)selv[i], (int64_t)0), c.Lmax - 1);
+      xk[i] = *reinterpret_cast<const u16x8*>(cks + pos * R + cc * 8);
+      xv[i] = *reinterpret_cast<const u16x8*>(cvs + pos * R + cc * 8);
     }
-    if (p0 == 0) {  // the G query rows: G * dh / VEC pieces over 64 lanes
 #pragma unroll
-      for (int t = 0; t < 4; ++t)  // G * dh <= 1024: at most 256 pieces
-        qr[t] = *reinterpret_cast<const u16x8*>(qh + min(l + 64 * t, G * npc - 1) * VEC);
+    for (int i = 0; i < NP; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NPC) {
+        const int j = e / KC, cc = e % KC;
+        *reinterpret_cast<u16x8*>(lds + Lay::ck + j * Lay::CKB + cc * 16) = xk[i];
+        const u16x8 v = j < nrow ? xv[i] : u16x8{};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int pc = l + 64 * t;
-        if (pc < G * npc) {
-          const T* qv = reinterpret_cast<const T*>(&qr[t]);
-#pragma unroll
-          for (int x = 0; x < VEC; ++x) qs[pc * VEC + x] = Elem<T>::ld(qv, x) * ascale;
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-      if (live && p0 + t < npc) *reinterpret_cast<u16x8*>(vs + l * ldv + (p0 + t) * VEC) = vr[t];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      if (p0 + t < npc) {
-        const T* kv = reinterpret_cast<const T*>(&kr[t]);
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          if (g < G) {
-            const float* qg = qs + g * dh + (p0 + t) * VEC;
-#pragma unroll
-            for (int x = 0; x < VEC; ++x) z[g] += qg[x] * Elem<T>::ld(kv, x);
-          }
-        }
+        for (int x = 0; x < 8; ++x)
+          *reinterpret_cast<uint16_t*>(lds + Lay::cv + (cc * 8 + x) * Lay::CVB + j * 2) = v[x];
       }
     }
   }
-  float m[8], S[8];
+  __syncthreads();
+  // ---- logits: 16 heads x 32 rows per wave (two 16 x 16 tiles)
+  float* zs = reinterpret_cast<float*>(lds + Lay::zs);
+  {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* k0 = lds + Lay::ck + (16 * rt0 + n16) * Lay::CKB;
+    const uint8_t* k1 = k0 + 16 * Lay::CKB;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      const float zz = live ? z[g] : -INFINITY;
-      m[g] = warp_max(zz);
-      const float p = live ? __builtin_amdgcn_exp2f(zz - m[g]) : 0.f;
-      S[g] = warp_sum(p);
-      if (l < 32) pw[g * 32 + l] = p;
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(k0 + (4 * ks + kg) * 16);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(k1 + (4 * ks + kg) * 16);
+      acc0 = mfma16x16x32(ahi[ks], b0, acc0);
+      acc1 = mfma16x16x32(ahi[ks], b1, acc1);
+      acc0 = mfma16x16x32(alo[ks], b0, acc0);
+      acc1 = mfma16x16x32(alo[ks], b1, acc1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      zs[(16 * ht + 4 * kg + i) * Lay::ZLD + 16 * rt0 + n16] = acc0[i];
+      zs[(16 * ht + 4 * kg + i) * Lay::ZLD + 16 * rt0 + 16 + n16] = acc1[i];
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  float o[8][4];
+  __syncthreads();
+  // ---- split-local softmax: wave w takes heads [8w, 8w + 8), lane = row
+  float* pz = reinterpret_cast<float*>(lds + Lay::pz);
+  {
+    const int ab = 8 * wv;
+    float z[8], m[8], S[8];
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
+    for (int aa = 0; aa < 8; ++aa) {
+      z[aa] = l < nrow ? zs[(ab + aa) * Lay::ZLD + l] : -INFINITY;
+      m[aa] = z[aa];
+    }
+    wave_max_n<8>(m);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[g][i] = 0.f;
-  for (int j = 0; j < nrow; ++j) {
-    float vv[4];
+    for (int aa = 0; aa < 8; ++aa) {
+      S[aa] = l < nrow ? __builtin_amdgcn_exp2f(z[aa] - m[aa]) : 0.f;
+      pz[(ab + aa) * Lay::PLD + l] = S[aa];
+    }
+    wave_sum_n<8>(S);
+    if (l < 8 && a0 + ab + l < Hq) {
+      float mm = m[0], ss = S[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = Elem<T>::ld(vs + j * ldv, min(l + 64 * i, dh - 1));
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      if (g < G) {
-        const float p = pw[g * 32 + j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[g][i] += p * vv[i];
+      for (int aa = 1; aa < 8; ++aa) {
+        mm = l == aa ? m[aa] : mm;
+        ss = l == aa ? S[aa] : ss;
       }
+      float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + split) * Hq + a0 + ab + l) * 2;
+      stp[0] = mm;
+      stp[1] = ss;
     }
   }
+  __syncthreads();
+  // ---- values: ylat[head][i] = sum_rows p[head][row] c^V[row][i], K = 64 rows
+  {
+    const int ht2 = wv & 1;
+    const float* prow = pz + (16 * ht2 + n16) * Lay::PLD + 8 * kg;
+    bf16x8 ph0, pl0, ph1, pl1;
+    split8(*reinterpret_cast<const f32x4*>(prow), *reinterpret_cast<const f32x4*>(prow + 4), &ph0, &pl0);
+    split8(*reinterpret_cast<const f32x4*>(prow + 32), *reinterpret_cast<const f32x4*>(prow + 36), &ph1,
+           &pl1);
+    const int hd = a0 + 16 * ht2 + 4 * kg;
+    float* yb = w.ylat + ((int64_t)u * w.nsl + split) * Hq * R;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if (g < G) {
-      const int a = h * G + g;
-      float* yo = w.yex + (((int64_t)u * w.nse + e) * Hq + a) * dh;
+    for (int t = 0; t < NT / 2; ++t) {
+      const int it = (wv >> 1) * (NT / 2) + t;
+      const uint8_t* vr = lds + Lay::cv + (16 * it + n16) * Lay::CVB + kg * 16;
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(vr);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(vr + 64);
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      y = mfma16x16x32(ph0, b0, y);
+      y = mfma16x16x32(ph1, b1, y);
+      y = mfma16x16x32(pl0, b0, y);
+      y = mfma16x16x32(pl1, b1, y);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (l + 64 * i < dh) yo[l + 64 * i] = o[g][i];
-      if (l == 0) {
-        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + w.nsl + e) * Hq + a) * 2;
-        stp[0] = m[g];
-        stp[1] = S[g];
-      }
+        if (hd + i < Hq) yb[(int64_t)(hd + i) * R + 16 * it + n16] = y[i];
     }
   }
 }
@@ -1427,22 +1704,20 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
                                                float* __restrict__ out) {
   const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int32_t* si = w.stepinfo + 4 * u;
-  if (si[2]) return;
-  const int Lcur = si[0];
+  const int l = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
-  const int nc = Lcur + 1 - d.nrec - d.s;
-  const int kk = max(0, min(d.k, nc));
-  const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
   const int nst = w.nsl + w.nse;
   extern __shared__ __attribute__((aligned(16))) float smf[];
   float* ys = smf;                 // [G][r]
-  float* fs = ys + G * r;          // [G][nst]
+  float* oe = ys + G * r;          // [G][dh] exact-row part of the output
+  float* fs = oe + G * dh;         // [G][nst]
   float* Lg = fs + G * nst;        // [8]
   float* stl = Lg + 8;             // [G][nst][2]
-  // thread (channel ch = tid / 2 + 128 m, half hf = tid % 2) later dots the
-  // half [i0, i1) of B^V row h dh + ch with ys[g]; the first 16 pieces of
-  // that half are requested now, before the split statistics
+  // ---- every load that does not need the unit state goes out first: the
+  // state itself, this thread's B^V row pieces, split statistics, the first
+  // 8 selected-row partials of column tid and 4 exact partials per item
+  const int32_t* si = w.stepinfo + 4 * u;
+  const int full = si[2], Lcur = si[0];
   constexpr int VEC = Vec16<T>::N;
   const int hf = tid & 1;
   const int rh = (r / VEC + 1) / 2 * VEC;
@@ -1456,36 +1731,79 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
       br[t] = *reinterpret_cast<const u16x8*>(brow + max(min(ib + t * VEC, i1 - VEC), 0));
   };
   load_b(0, i0);
-  for (int x = tid; x < G * nst; x += 256) {
-    const int g = x / nst, sp = x % nst;
-    const bool ran = sp < nl || sp >= w.nsl;
-    const float* st = w.astat + (((int64_t)u * nst + sp) * Hq + h * G + g) * 2;
-    const float m = st[0], S = st[1];
-    stl[2 * x] = ran ? m : -INFINITY;
-    stl[2 * x + 1] = ran ? S : 0.f;
+  const float* stb = w.astat + ((int64_t)u * nst * Hq + h * G) * 2;
+  float2 stv[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int x = min(tid + 256 * t, G * nst - 1);
+    stv[t] = *reinterpret_cast<const float2*>(stb + ((int64_t)(x % nst) * Hq + x / nst) * 2);
   }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < nst; ++sp) M = fmaxf(M, stl[2 * (tid * nst + sp)]);
-    float L = 0.f;
-    for (int sp = 0; sp < nst; ++sp) {
-      const float m = stl[2 * (tid * nst + sp)];
-      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      fs[tid * nst + sp] = f;
-      L += f * stl[2 * (tid * nst + sp) + 1];
+  const int icol = min(tid, r - 1);
+  const float* ylb = w.ylat + ((int64_t)u * w.nsl * Hq + h * G) * r + icol;
+  const int nsl1 = max(w.nsl, 1);
+  float yv[8][8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) yv[t][g] = ylb[((int64_t)min(t, nsl1 - 1) * Hq + min(g, G - 1)) * r];
+  const float* yeb = w.yex + ((int64_t)u * w.nse * Hq + h * G) * dh;
+  float ev[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int x = min(tid + 256 * m, G * dh - 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ev[m][e] = yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh];
+  }
+  if (full) return;  // the top-k kernel wrote zeros
+  const int nc = Lcur + 1 - d.nrec - d.s;
+  const int kk = max(0, min(d.k, nc));
+  const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
+  for (int t = 0; t * 256 < G * nst; ++t) {
+    const int x = tid + 256 * t;
+    if (x < G * nst) {
+      const int sp = x % nst;
+      const bool ran = sp < nl || sp >= w.nsl;
+      float2 v = t < 2 ? stv[t] : *reinterpret_cast<const float2*>(stb + ((int64_t)sp * Hq + x / nst) * 2);
+      stl[2 * ((x / nst) * nst + sp)] = ran ? v.x : -INFINITY;
+      stl[2 * ((x / nst) * nst + sp) + 1] = ran ? v.y : 0.f;
     }
-    Lg[tid] = L;
   }
   __syncthreads();
-  // ys[g][i] = sum over the selected-row splits of f * ylat; thread = column
-  // i, its loads for 8 splits x 8 heads (clamped to G) issued together
+  // per head (a wave each): M = max over splits, f = 2^(m - M), L = sum f S
+  for (int g = wv; g < G; g += 4) {
+    float mx[1] = {-INFINITY};
+    for (int sp = l; sp < nst; sp += 64) mx[0] = fmaxf(mx[0], stl[2 * (g * nst + sp)]);
+    wave_max_n<1>(mx);
+    float L[1] = {0.f};
+    for (int sp = l; sp < nst; sp += 64) {
+      const float m = stl[2 * (g * nst + sp)];
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx[0]);
+      fs[g * nst + sp] = f;
+      L[0] += f * stl[2 * (g * nst + sp) + 1];
+    }
+    wave_sum_n<1>(L);
+    if (l == 0) Lg[g] = L[0];
+  }
+  __syncthreads();
+  // selected-row part: ys[g][i] = sum over splits of f * ylat; column tid's
+  // first 8 splits come from the registers loaded above
   for (int i = tid; i < r; i += 256) {
-    const float* yp = w.ylat + ((int64_t)u * w.nsl * Hq + h * G) * r + i;
     float acc[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) acc[g] = 0.f;
-    for (int sp0 = 0; sp0 < nl; sp0 += 8) {
+    int sp0 = 0;
+    if (i == tid) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (t < nl)
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < G) acc[g] += fs[g * nst + t] * yv[t][g];
+      sp0 = 8;
+    }
+    const float* yp = w.ylat + ((int64_t)u * w.nsl * Hq + h * G) * r + i;
+    for (; sp0 < nl; sp0 += 8) {
       float v[8][8];
 #pragma unroll
       for (int t = 0; t < 8; ++t)
@@ -1503,7 +1821,32 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
     for (int g = 0; g < 8; ++g)
       if (g < G) ys[g * r + i] = acc[g];
   }
+  // exact-row part: oe[g][ch] = sum over exact splits of f * yex; the first
+  // 4 splits of this thread's first 4 items come from registers
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int x = tid + 256 * m;
+    if (x < G * dh) {
+      const int g = x / dh;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < w.nse) acc += fs[g * nst + w.nsl + e] * ev[m][e];
+      for (int e = 4; e < w.nse; ++e)
+        acc += fs[g * nst + w.nsl + e] * yeb[((int64_t)e * Hq + g) * dh + x % dh];
+      oe[x] = acc;
+    }
+  }
+  for (int x = tid + 1024; x < G * dh; x += 256) {
+    const int g = x / dh;
+    float acc = 0.f;
+    for (int e = 0; e < w.nse; ++e)
+      acc += fs[g * nst + w.nsl + e] * yeb[((int64_t)e * Hq + g) * dh + x % dh];
+    oe[x] = acc;
+  }
   __syncthreads();
+  // out: thread (channel ch = tid / 2 + 128 m, half hf) dots half [i0, i1)
+  // of B^V row h dh + ch with ys[g]; halves combined by a lane shuffle
   for (int cb = 0; cb < dh; cb += 128) {
     const int ch = cb + (tid >> 1);
     float acc[8];
@@ -1520,7 +1863,11 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
             if (g < G) {
               const float* yg = ys + g * r + ib + t * VEC;
 #pragma unroll
-              for (int x = 0; x < VEC; ++x) acc[g] += Elem<T>::ld(bv, x) * yg[x];
+              for (int x = 0; x < VEC; x += 4) {
+                const f32x4 y4 = *reinterpret_cast<const f32x4*>(yg + x);
+                acc[g] += Elem<T>::ld(bv, x) * y4[0] + Elem<T>::ld(bv, x + 1) * y4[1] +
+                          Elem<T>::ld(bv, x + 2) * y4[2] + Elem<T>::ld(bv, x + 3) * y4[3];
+              }
             }
           }
         }
@@ -1533,10 +1880,7 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
       for (int g = 0; g < 8; ++g) {
         if (g < G && (g & 1) == hf) {  // the two lanes of a channel share the stores
           const int a = h * G + g;
-          float o = acc[g];
-          for (int e = 0; e < w.nse; ++e)
-            o += fs[g * nst + w.nsl + e] * w.yex[(((int64_t)u * w.nse + e) * Hq + a) * dh + ch];
-          out[((int64_t)u * Hq + a) * dh + ch] = o / Lg[g];
+          out[((int64_t)u * Hq + a) * dh + ch] = (acc[g] + oe[g * dh + ch]) / Lg[g];
         }
       }
     }
@@ -1544,7 +1888,7 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
 }
 
 static size_t merge_lds(const Dims& d, const DecodeWs& w) {
-  return ((size_t)d.G * d.r + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
+  return ((size_t)d.G * (d.r + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
 
 // Kernels that may need more than the default 64 KB of dynamic LDS get the
@@ -1572,10 +1916,30 @@ static hipError_t launch_attend_t(const Dims& d, int U, const void* q, const Cac
   return hipGetLastError();
 }
 
+template <int R>
+static hipError_t launch_attend_mfma(const Dims& d, int U, const void* q, const CachePtrs& c,
+                                     const DecodeWs& w, hipStream_t st) {
+  static size_t done = 0;
+  if (w.attend_lds <= 0) return hipErrorInvalidValue;
+  hipError_t e = allow_lds(&k_attend_mfma<R>, (size_t)w.attend_lds, &done);
+  if (e != hipSuccess) return e;
+  const float ascale = kLog2e / sqrtf((float)d.dh);
+  hipLaunchKernelGGL(k_attend_mfma<R>, dim3(w.nsl * w.nhg + w.nse * ((d.Hkv + 3) / 4), U),
+                     dim3(256), w.attend_lds, st, d, c, w, (const uint16_t*)q, ascale);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
                          const DecodeWs& w, hipStream_t st) {
   if (d.dtype == 0) return launch_attend_t<float>(d, U, q, c, w, st);
-  return launch_attend_t<uint16_t>(d, U, q, c, w, st);
+  switch (d.r) {
+    case 32: return launch_attend_mfma<32>(d, U, q, c, w, st);
+    case 64: return launch_attend_mfma<64>(d, U, q, c, w, st);
+    case 128: return launch_attend_mfma<128>(d, U, q, c, w, st);
+    case 192: return launch_attend_mfma<192>(d, U, q, c, w, st);
+    case 256: return launch_attend_mfma<256>(d, U, q, c, w, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T>
