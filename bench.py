@@ -15,7 +15,6 @@ Prints one JSON line.  ``--gpus`` above 1 is refused: the path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -27,7 +26,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from long_context_decode_s4r_amd import configs, kvlr, synth  # noqa: E402
+from long_context_decode_s4r_amd import configs, kvlr, profiling, synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
@@ -52,14 +51,6 @@ def algorithmic_bytes(w, U: int, n_cand: float):
     return scan, scan + gathered + bases + exact + io
 
 
-def source_sha() -> str:
-    h = hashlib.sha256()
-    for f in ("decode.hip", "common.h"):
-        with open(os.path.join(ROOT, "long_context_decode_s4r_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(kernel: str, workload: str):
     """HBM traffic per launch measured with rocprofv3 counters, if it was taken
     on the current kernel sources (profiles/traffic.json)."""
@@ -69,7 +60,7 @@ def stored_traffic(kernel: str, workload: str):
     try:
         d = json.load(open(p))
         e = d[kernel][workload]
-        if e.get("source_sha") != source_sha():
+        if e.get("source_sha") != profiling.source_sha():
             return None
         return float(e["bytes_per_launch"])
     except Exception:
@@ -97,15 +88,17 @@ def cpu_baseline(kc, dec, w, U, budget_s: float):
     except Exception:
         threads = 1
     o = oracle_cache_of(kc, 0, w)
+    room = kc.L_max - o.L  # steps the copied cache can still take
+    qs = [dec.q[t][0].float().cpu().double().numpy() for t in range(dec.q.shape[0])]
+    ks = [dec.k[t][0].float().cpu().double().numpy() for t in range(dec.q.shape[0])]
+    vs = [dec.v[t][0].float().cpu().double().numpy() for t in range(dec.q.shape[0])]
     n, t0 = 0, time.perf_counter()
     while True:
-        t = n % dec.q.shape[0]
-        s4r.decode_step(o, dec.q[t][0].float().cpu().double().numpy(),
-                        dec.k[t][0].float().cpu().double().numpy(),
-                        dec.v[t][0].float().cpu().double().numpy())
+        t = n % len(qs)
+        s4r.decode_step(o, qs[t], ks[t], vs[t])
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s or n >= room:
             break
     per_unit_step = el / n
     return {"value": 1.0 / (per_unit_step * U), "unit": "steps/s", "cores": threads,
@@ -146,6 +139,20 @@ def run_prefill_leg(args):
             "project_mfma_frac": flops / (t_p / 1e3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """Five copies of a 1 GiB device buffer (reads and writes 1 GiB each): the
+    reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.ones(COPY_PROBE_BYTES // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,12 +163,17 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the compressed-KV path has no multi-GPU part "
               "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe()
+        return
     w = configs.by_name(args.workload)
     if w is None:
         sys.exit(f"unknown workload {args.workload}")
