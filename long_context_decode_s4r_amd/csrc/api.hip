@@ -167,7 +167,7 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   L.partial = take((size_t)U * L.t.Lc_cap * sizeof(float));
   L.spill = take((size_t)U * d.G * L.t.Lc_cap * sizeof(float));
   L.tilestat = take((size_t)U * L.t.nsplit * d.G * 2 * sizeof(float));
-  L.keys = take((size_t)U * L.t.Lc_cap * sizeof(uint32_t));
+  L.keys = take(((size_t)U * L.t.Lc_cap + kKeyPad) * sizeof(uint32_t));
   L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
   L.qlat = take((size_t)U * d.Hq * d.r * sizeof(float));
   L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.r * sizeof(float));

@@ -171,13 +171,14 @@ hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K
 // decode
 constexpr int kHistBins = 4096;  // selection histogram over the top 12 key bits
 constexpr int kPoolChunk = 2048; // candidates per block of the pooling kernel
+constexpr int kKeyPad = 128;     // entries of slack after the last unit's keys
 
 struct DecodeWs {
   int32_t* stepinfo;  // [U][4]     {tokens cached, steps taken, unit full, -}
   float* partial;     // [U][Lc_cap] score contribution of the older window rows
   float* spill;       // [U][G][Lc_cap] base-2 logits of the current rows
   float* tilestat;    // [U][nsplit][G][2] per-split (max, sum) of the current rows
-  uint32_t* keys;     // [U][Lc_cap] pooled scores as ordered bit patterns
+  uint32_t* keys;     // [U][Lc_cap] (+ kKeyPad slack) pooled scores as ordered bit patterns
   int32_t* topk;      // [U][k] selected positions, ascending
   float* qlat;        // [U][Hq][r] query heads projected onto their KV head's
                       //            slice of B^K, times log2(e)/sqrt(d_h)

@@ -147,6 +147,25 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int D = d.D, r = d.r, G = d.G, W = d.W;
   const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
+  // basis pieces of this thread are requested together with the unit state:
+  // GEMV blocks rows rg + 64 i of their column slice, projected-query blocks
+  // rows rg + 8 i of head h's slice (first column pass)
+  constexpr int PF = 16;
+  u16x8 bpre[PF];
+  if (b < 2 * ncb) {
+    const T* B = (const T*)(b >= ncb ? c.basis_v : c.basis_k) + (int64_t)u * D * r;
+    const int col = min((b >= ncb ? b - ncb : b) * 4 * VEC + (tid & 3) * VEC, r - VEC);
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      bpre[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)min((tid >> 2) + 64 * i, D - 1) * r + col);
+  } else if (b > 2 * ncb) {
+    const int h = b - 2 * ncb - 1;
+    const T* B = (const T*)c.basis_k + ((int64_t)u * D + (int64_t)h * d.dh) * r;
+    const int col = min((tid & 31) * VEC, r - VEC);
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      bpre[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)min((tid >> 5) + 8 * i, d.dh - 1) * r + col);
+  }
   const bool full = (int64_t)Lcur >= c.Lmax;
   if (b == 0 && tid == 0) {
     w.stepinfo[4 * u + 0] = Lcur;
@@ -162,7 +181,7 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
     const int cb = kind ? b - ncb : b;
     const int nvec = kind == 0 ? 1 + G : 1;
     float* xs = sm;                         // [nvec][D]
-    float* red = xs + nvec * D;             // [4 waves][nvec][4 * VEC]
+    float* red = xs + nvec * D;             // [16 lane rows][nvec][4 * VEC]
     // stage x_0 (k or v) and the G concatenated query vectors as fp32; every
     // thread owns 16-byte pieces, all loads are issued before the stores
     {
@@ -202,42 +221,48 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[v][e] = 0.f;
     if (col < r) {
-      for (int kk0 = rg; kk0 < D; kk0 += 64 * 8) {
-        float bvals[8][VEC];
+      for (int kk0 = rg; kk0 < D; kk0 += 64 * PF) {
+        u16x8 braw[PF];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = min(kk0 + 64 * i, D - 1);  // rows past D are read, then skipped
-          Vec16<T>::ld(B + (int64_t)kk * r + col, bvals[i]);
+        for (int i = 0; i < PF; ++i) {
+          if (kk0 == rg) {
+            braw[i] = bpre[i];
+          } else {
+            const int kk = min(kk0 + 64 * i, D - 1);  // rows past D are read, then skipped
+            braw[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)kk * r + col);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < PF; ++i) {
           const int kk = kk0 + 64 * i;
           if (kk < D) {
+            const T* bv = reinterpret_cast<const T*>(&braw[i]);
 #pragma unroll
             for (int v = 0; v < NVMAX; ++v) {
               if (v < nvec) {
                 const float x = xs[v * D + kk];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[v][e] += x * bvals[i][e];
+                for (int e = 0; e < VEC; ++e) acc[v][e] += x * Elem<T>::ld(bv, e);
               }
             }
           }
         }
       }
     }
-    // reduce over the 16 row groups of a wave (lane bits 2..5), then waves
+    // reduce over the row groups: DPP rotations by 4 and 8 inside each row of
+    // 16 lanes leave lanes 0..3 of the row holding the sum of its 4 row
+    // groups (per column group); the 16 rows of the block meet in LDS
     const int lane = tid & 63, wv = tid >> 6;
+    const int prow = wv * 4 + (lane >> 4);
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) {
       if (v < nvec) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           float x = acc[v][e];
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 8);
-          x += __shfl_xor(x, 16);
-          x += __shfl_xor(x, 32);
-          if (lane < 4) red[(wv * nvec + v) * 4 * VEC + lane * VEC + e] = x;
+          x += dpp_f<0x124>(x);  // row_ror:4
+          x += dpp_f<0x128>(x);  // row_ror:8
+          if ((lane & 15) < 4) red[(prow * nvec + v) * 4 * VEC + (lane & 3) * VEC + e] = x;
         }
       }
     }
@@ -246,8 +271,9 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
       const int v = t / (4 * VEC), cc = t % (4 * VEC);
       const int cl = cb * 4 * VEC + cc;
       if (cl >= r) continue;
-      const float sum = red[(0 * nvec + v) * 4 * VEC + cc] + red[(1 * nvec + v) * 4 * VEC + cc] +
-                        red[(2 * nvec + v) * 4 * VEC + cc] + red[(3 * nvec + v) * 4 * VEC + cc];
+      float sum = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 16; ++q2) sum += red[(q2 * nvec + v) * 4 * VEC + cc];
       if (v == 0) {
         T* C = (T*)(kind == 0 ? c.coef_k : c.coef_v);
         Elem<T>::st(C, ((int64_t)u * c.Lmax + p) * r + cl, sum);
@@ -280,16 +306,28 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
       for (int g = 0; g < 8; ++g)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[g][e] = 0.f;
-#pragma unroll 4
-      for (int j = rg; j < dh; j += 8) {
-        float bv[VEC];
-        Vec16<T>::ld(B + (int64_t)j * r + colc, bv);
+      for (int j0 = rg; j0 < dh; j0 += 8 * PF) {
+        u16x8 braw[PF];
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          if (g < G) {
-            const float x = qs[g * dh + j];
+        for (int i = 0; i < PF; ++i) {
+          if (c0 == 0 && j0 == rg)
+            braw[i] = bpre[i];
+          else
+            braw[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)min(j0 + 8 * i, dh - 1) * r + colc);
+        }
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[g][e] += x * bv[e];
+        for (int i = 0; i < PF; ++i) {
+          const int j = j0 + 8 * i;
+          if (j < dh) {
+            const T* bv = reinterpret_cast<const T*>(&braw[i]);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+              if (g < G) {
+                const float x = qs[g * dh + j];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[g][e] += x * Elem<T>::ld(bv, e);
+              }
+            }
           }
         }
       }
@@ -388,7 +426,7 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
   const int vec = d.dtype == 0 ? 4 : 8;
   const int ncb = (d.r + 4 * vec - 1) / (4 * vec);
   const int nvec = 1 + d.G;
-  size_t lds = ((size_t)nvec * d.D + 4 * nvec * 4 * vec) * sizeof(float);
+  size_t lds = ((size_t)nvec * d.D + 16 * nvec * 4 * vec) * sizeof(float);
   if (lds < (size_t)d.r * sizeof(float)) lds = (size_t)d.r * sizeof(float);
   const size_t lq = ((size_t)d.G * d.dh + (size_t)4 * d.G * 32 * vec) * sizeof(float);
   if (lds < lq) lds = lq;
@@ -858,45 +896,55 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
   __shared__ float Mg[8], Ig[8];
   __shared__ float wm[4][8], wsum[4][8];
   __shared__ float sc[kPoolChunk + 256];
-  {  // 1. current rows' statistics (all G rows at once)
-    const int lane = tid & 63, wv = tid >> 6;
-    const float* tp = w.tilestat + (int64_t)u * w.nsplit * G * 2;
+  const int lane = tid & 63, wv = tid >> 6;
+  // the split statistics of the current rows and this block's score inputs
+  // are requested together (both need only the unit state)
+  const float* tp = w.tilestat + (int64_t)u * w.nsplit * G * 2;
+  float2 tv[8];
+  {
+    const int sp = min(tid, w.nsplit - 1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      tv[g] = *reinterpret_cast<const float2*>(tp + (sp * G + min(g, G - 1)) * 2);
+  }
+  const bool have = c0 < nc;
+  const float* part = w.partial + (int64_t)u * w.Lc_cap;
+  const float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
+  const int lo = max(c0 - h, 0), hi = max(min(c1 + h, nc), lo + 1);
+  constexpr int NIT = (kPoolChunk + 256) / 256;
+  float pv[NIT], sv[NIT][8];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {  // clamped, unconditional loads
+    const int j = min(lo + tid + 256 * it, hi - 1);
+    pv[it] = part[j];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) sv[it][g] = spill[(int64_t)min(g, G - 1) * w.Lc_cap + j];
+  }
+  {  // 1. current rows' softmax statistics over all splits: max, then the
+     //    rescaled sums (splits past nsplit contribute nothing)
+    const bool ok = tid < w.nsplit;
     float m[8], sm[8];
 #pragma unroll
+    for (int g = 0; g < 8; ++g) m[g] = ok && tv[g].y > 0.f ? tv[g].x : -INFINITY;
+    wave_max_n<8>(m);
+    if (lane == 0)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) wm[wv][g] = m[g];
+    __syncthreads();
+    float M[8];
+#pragma unroll
     for (int g = 0; g < 8; ++g) {
-      m[g] = 0.f;
-      sm[g] = 0.f;
+      M[g] = fmaxf(fmaxf(wm[0][g], wm[1][g]), fmaxf(wm[2][g], wm[3][g]));
+      sm[g] = ok && tv[g].y > 0.f ? tv[g].y * __builtin_amdgcn_exp2f(tv[g].x - M[g]) : 0.f;
     }
-    for (int sp = tid; sp < w.nsplit; sp += 256) {
-      float2 v[8];
+    wave_sum_n<8>(sm);
+    if (lane == 0)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        v[g] = *reinterpret_cast<const float2*>(tp + (sp * G + min(g, G - 1)) * 2);
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g < G) ms_combine(m[g], sm[g], v[g].x, v[g].y);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        if (g < G) {
-          const float m2 = __shfl_xor(m[g], o), s2 = __shfl_xor(sm[g], o);
-          ms_combine(m[g], sm[g], m2, s2);
-        }
-      }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        wm[wv][g] = m[g];
-        wsum[wv][g] = sm[g];
-      }
-    }
+      for (int g = 0; g < 8; ++g) wsum[wv][g] = sm[g];
     __syncthreads();
     if (tid < G) {
-      float mm = wm[0][tid], ss = wsum[0][tid];
-      for (int q2 = 1; q2 < 4; ++q2) ms_combine(mm, ss, wm[q2][tid], wsum[q2][tid]);
+      const float mm = M[tid];
+      const float ss = (wsum[0][tid] + wsum[1][tid]) + (wsum[2][tid] + wsum[3][tid]);
       Mg[tid] = mm;
       Ig[tid] = 1.f / ss;
       if (blk == 0) {
@@ -907,26 +955,14 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
     }
     __syncthreads();
   }
-  if (c0 >= nc) return;
-  const float* part = w.partial + (int64_t)u * w.Lc_cap;
-  const float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
-  const int lo = max(c0 - h, 0), hi = min(c1 + h, nc);
-  constexpr int NIT = (kPoolChunk + 256) / 256;
+  if (!have) return;
   float vals[NIT];
-  float pv[NIT], sv[NIT][8];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {  // clamped, unconditional loads
-    const int j = min(lo + tid + 256 * it, hi - 1);
-    pv[it] = part[j];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) sv[it][g] = spill[(int64_t)min(g, G - 1) * w.Lc_cap + j];
-  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     float v = pv[it];
 #pragma unroll
     for (int g = 0; g < 8; ++g)
-      if (g < G) v += exp2f(sv[it][g] - Mg[g]) * Ig[g];
+      if (g < G) v += __builtin_amdgcn_exp2f(sv[it][g] - Mg[g]) * Ig[g];
     vals[it] = v;
   }
 #pragma unroll
@@ -983,18 +1019,26 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 
 // --------------------------------------------------------------------------
 // top-k: one 1024-thread block per unit.
-//   Thread t owns a contiguous run of keys (kept in registers while the run
-//   fits, else re-read per pass).  Threshold key T = the k-th largest key:
-//   a 12-bit histogram of the keys' top bits, then two 10-bit refinement
-//   passes over the keys with that prefix.  Ordered compaction: every key
-//   > T, and the first (k - #{key > T}) keys == T in position order (ties ->
-//   lower position), written in ascending position order.  Also advances
-//   lens and writes the outputs of units whose cache is full (topk = -1,
-//   out = 0).
+//   Thread t owns a contiguous run of keys (pooled scores as ordered bit
+//   patterns), kept in registers while the run fits, else re-read per pass.
+//   Threshold key T = the k-th largest key, by a radix select over the key
+//   range actually present: with lo / hi the smallest / largest key, the
+//   first histogram bins (key - lo) >> shift into 4096 bins, then 10-bit
+//   refinements of the selected bin until it is resolved to one key value or
+//   taken whole.  Consecutive keys of a run that fall in the same bin are
+//   counted with one LDS atomic (max-pooling repeats values).  Ordered
+//   compaction: every key above the threshold bin, and the first
+//   (k - #above) keys of that bin in position order (ties -> lower
+//   position), written in ascending position order.  Also advances lens and
+//   writes the outputs of units whose cache is full (topk = -1, out = 0).
 // --------------------------------------------------------------------------
-constexpr int kTopkRegKeys = 32;  // keys per thread held in registers
+constexpr int kTopkThreads = 1024; // 16 waves; <= 128 VGPRs per thread
+constexpr int kTopkRegKeys = 32;   // keys per thread held in registers (32 768 candidates)
+constexpr int kTopkRefineBits = 10; // refinement digits: one bin per thread
+static_assert(kKeyPad >= kTopkRegKeys, "key buffer padding must cover one register run");
 
-__device__ __forceinline__ int block_excl_scan_1024(int v, int* wtot, int* total) {
+__device__ __forceinline__ int block_excl_scan(int v, int* wtot, int* total) {
+  constexpr int NW = kTopkThreads / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -1006,7 +1050,7 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* wtot, int* total
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int t = wtot[i];
     if (i < wid) before += t;
     tot += t;
@@ -1016,42 +1060,40 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* wtot, int* total
   return before + x - v;
 }
 
-// apply f(key, position) to the thread's run [j0, j1) in position order
+// apply f(key, position) to the thread's run [j0, j1) in position order, in
+// batches of kTopkRegKeys held in kr; a run of one batch stays in kr across
+// passes (in_regs), longer runs reload every batch on every pass
 template <typename F>
 __device__ __forceinline__ void for_keys(const uint32_t* keys, int j0, int j1, bool in_regs,
-                                         const uint32_t* kr, F&& f) {
-  if (in_regs) {
-#pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i)
-      if (j0 + i < j1) f(kr[i], j0 + i);
-  } else {
-    for (int jb = j0; jb < j1; jb += kTopkRegKeys) {
-      uint32_t buf[kTopkRegKeys];
+                                         uint32_t* kr, F&& f) {
+  for (int jb = j0; jb < j1; jb += kTopkRegKeys) {
+    if (!in_regs) {
 #pragma unroll
       for (int i = 0; i < kTopkRegKeys; i += 4) {
         const uint4 v = *reinterpret_cast<const uint4*>(keys + jb + i);
-        buf[i] = v.x;
-        buf[i + 1] = v.y;
-        buf[i + 2] = v.z;
-        buf[i + 3] = v.w;
+        kr[i] = v.x;
+        kr[i + 1] = v.y;
+        kr[i + 2] = v.z;
+        kr[i + 3] = v.w;
       }
-#pragma unroll
-      for (int i = 0; i < kTopkRegKeys; ++i)
-        if (jb + i < j1) f(buf[i], jb + i);
     }
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; ++i)
+      if (jb + i < j1) f(kr[i], jb + i);
   }
 }
 
-__global__ __launch_bounds__(1024) void k_topk(Dims d, CachePtrs c, DecodeWs w,
+__global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, DecodeWs w,
                                                int32_t* __restrict__ topk_user,
                                                float* __restrict__ out) {
   const int u = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
   const int32_t* si = w.stepinfo + 4 * u;
   const int k = d.k;
   if (si[2]) {
     if (topk_user)
-      for (int i = tid; i < k; i += 1024) topk_user[(int64_t)u * k + i] = -1;
-    for (int i = tid; i < d.Hq * d.dh; i += 1024) out[(int64_t)u * d.Hq * d.dh + i] = 0.f;
+      for (int i = tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
+    for (int i = tid; i < d.Hq * d.dh; i += kTopkThreads) out[(int64_t)u * d.Hq * d.dh + i] = 0.f;
     return;
   }
   const int Lcur = si[0], steps = si[1];
@@ -1063,45 +1105,80 @@ __global__ __launch_bounds__(1024) void k_topk(Dims d, CachePtrs c, DecodeWs w,
     c.lens[2 * u + 1] = steps + 1;
   }
   if (topk_user)
-    for (int i = kk + tid; i < k; i += 1024) topk_user[(int64_t)u * k + i] = -1;
+    for (int i = kk + tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
   if (kk <= 0) return;
   __shared__ unsigned int hs[kHistBins];
-  __shared__ int wtot[16];
-  __shared__ unsigned int sh_prefix;
-  __shared__ int sh_rem;
+  __shared__ int wtot[kTopkThreads / 64];
+  __shared__ unsigned int wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
+  __shared__ unsigned int sh_bin;
+  __shared__ int sh_rem, sh_cnt;
   const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
-  // runs of `per` keys (multiple of 32, so vector reads stay aligned and
-  // inside the padded key buffer)
-  const int per = ((nc + 1023) / 1024 + kTopkRegKeys - 1) / kTopkRegKeys * kTopkRegKeys;
+  // runs of `per` keys, whole batches of kTopkRegKeys (vector reads stay
+  // aligned); reads past the unit's candidates land in the next unit's keys
+  // or in the kKeyPad entries of slack at the end of the buffer and are ignored
+  const int per = ((nc + kTopkThreads - 1) / kTopkThreads + kTopkRegKeys - 1) / kTopkRegKeys *
+                  kTopkRegKeys;
   const int j0 = tid * per, j1 = min(j0 + per, nc);
   const bool in_regs = per == kTopkRegKeys;
   uint32_t kr[kTopkRegKeys];
   if (in_regs) {
 #pragma unroll
     for (int i = 0; i < kTopkRegKeys; i += 4) {
-      // runs start inside the padded buffer; entries past j1 are ignored
-      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0, w.Lc_cap - kTopkRegKeys) + i);
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0, nc) + i);
       kr[i] = v.x;
       kr[i + 1] = v.y;
       kr[i + 2] = v.z;
       kr[i + 3] = v.w;
     }
   }
-  for (int i = tid; i < kHistBins; i += 1024) hs[i] = 0u;
+  for (int i = tid; i < kHistBins; i += kTopkThreads) hs[i] = 0u;
+  // key range present
+  unsigned int kmin = 0xFFFFFFFFu, kmax = 0u;
+  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  });
+  {
+    unsigned int a = kmin, b2 = kmax;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      a = min(a, (unsigned int)__shfl_xor((int)a, o));
+      b2 = max(b2, (unsigned int)__shfl_xor((int)b2, o));
+    }
+    if (lane == 0) {
+      wmin[wid] = a;
+      wmax[wid] = b2;
+    }
+  }
   __syncthreads();
-  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) { atomicAdd(&hs[key >> 20], 1u); });
+  unsigned int lo = wmin[0], hi = wmax[0];
+#pragma unroll
+  for (int i = 1; i < kTopkThreads / 64; ++i) {
+    lo = min(lo, wmin[i]);
+    hi = max(hi, wmax[i]);
+  }
+  const unsigned int range = hi - lo;
+  const int bits = range == 0u ? 0 : 32 - __clz((int)range);
+  int shift = max(bits - 12, 0);
+  // level 1 over the range
+  for_keys(keys, j0, j1, in_regs, kr,
+           [&](uint32_t key, int) { atomicAdd(&hs[(key - lo) >> shift], 1u); });
   __syncthreads();
   int tot;
-  {  // level 1: thread t owns bins [4t, 4t + 4)
-    const int b0 = 4 * tid;
-    const int local = (int)(hs[b0] + hs[b0 + 1] + hs[b0 + 2] + hs[b0 + 3]);
-    const int excl = block_excl_scan_1024(local, wtot, &tot);
+  {  // thread t owns bins [BPT t, BPT t + BPT)
+    constexpr int BPT = kHistBins / kTopkThreads;
+    const int b0 = BPT * tid;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) local += (int)hs[b0 + i];
+    const int excl = block_excl_scan(local, wtot, &tot);
     int above = tot - excl - local;  // keys in higher bins
     if (above < kk && above + local >= kk) {
-      for (int bb = b0 + 3; bb >= b0; --bb) {
+      for (int bb = b0 + BPT - 1; bb >= b0; --bb) {
         if (above + (int)hs[bb] >= kk) {
-          sh_prefix = (unsigned int)bb << 20;
+          sh_bin = (unsigned int)bb;
           sh_rem = kk - above;
+          sh_cnt = (int)hs[bb];
           break;
         }
         above += (int)hs[bb];
@@ -1109,43 +1186,51 @@ __global__ __launch_bounds__(1024) void k_topk(Dims d, CachePtrs c, DecodeWs w,
     }
     __syncthreads();
   }
-  unsigned int prefix = sh_prefix, mask = 0xFFF00000u;
-  int rem = sh_rem;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = 10 - 10 * pass;
-    hs[tid] = 0u;
+  // the selected bin, as a prefix of (key - lo) at resolution `shift`
+  unsigned int bin = sh_bin;
+  int rem = sh_rem, cnt_bin = sh_cnt;
+  while (shift > 0 && rem < cnt_bin) {
+    const int nsh = max(shift - kTopkRefineBits, 0);
+    const unsigned int nb = 1u << (shift - nsh);
+    if (tid < (int)nb) hs[tid] = 0u;
     __syncthreads();
     for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
-      if ((key & mask) == prefix) atomicAdd(&hs[(key >> shift) & 1023u], 1u);
+      const unsigned int rk = key - lo;
+      if ((rk >> shift) == bin) atomicAdd(&hs[(rk >> nsh) & (nb - 1u)], 1u);
     });
     __syncthreads();
-    const int local = (int)hs[tid];
-    const int excl = block_excl_scan_1024(local, wtot, &tot);
+    const int local = tid < (int)nb ? (int)hs[tid] : 0;
+    const int excl = block_excl_scan(local, wtot, &tot);
     const int above = tot - excl - local;
-    if (above < rem && above + local >= rem) {
-      sh_prefix = prefix | ((unsigned int)tid << shift);
+    if (tid < (int)nb && above < rem && above + local >= rem) {
+      sh_bin = (bin << (shift - nsh)) | (unsigned int)tid;
       sh_rem = rem - above;
+      sh_cnt = local;
     }
     __syncthreads();
-    prefix = sh_prefix;
+    bin = sh_bin;
     rem = sh_rem;
-    mask |= 1023u << shift;
+    cnt_bin = sh_cnt;
+    shift = nsh;
   }
-  const unsigned int T = prefix;
+  // compaction: keys with (key - lo) >> shift above `bin`, then the first
+  // `rem` keys of the bin in position order
   const int need_eq = rem;
   int c_gt = 0, c_eq = 0;
   for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
-    c_gt += key > T;
-    c_eq += key == T;
+    const unsigned int bn = (key - lo) >> shift;
+    c_gt += bn > bin;
+    c_eq += bn == bin;
   });
-  const int eq_base = block_excl_scan_1024(c_eq, wtot, &tot);
+  const int eq_base = block_excl_scan(c_eq, wtot, &tot);
   const int take_eq = max(0, min(need_eq - eq_base, c_eq));
-  int off = block_excl_scan_1024(c_gt + take_eq, wtot, &tot);
+  int off = block_excl_scan(c_gt + take_eq, wtot, &tot);
   int32_t* sel = w.topk + (int64_t)u * k;
   int seen = 0;
   for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
-    bool take = key > T;
-    if (key == T) {
+    const unsigned int bn = (key - lo) >> shift;
+    bool take = bn > bin;
+    if (bn == bin) {
       take = seen < take_eq;
       ++seen;
     }
@@ -1159,7 +1244,7 @@ __global__ __launch_bounds__(1024) void k_topk(Dims d, CachePtrs c, DecodeWs w,
 
 hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                        int32_t* topk_user, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3(U), dim3(1024), 0, st, d, c, w, topk_user, out);
+  hipLaunchKernelGGL(k_topk, dim3(U), dim3(kTopkThreads), 0, st, d, c, w, topk_user, out);
   return hipGetLastError();
 }
 
