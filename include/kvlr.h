@@ -123,8 +123,9 @@ int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max,
 /* Device workspace needed by one call of `op` (KVLR_OP_*) on n_units units;
  * L = prompt length for the prefill ops, the cache capacity L_max for
  * KVLR_OP_DECODE.  *bytes (host) is written on success.  The workspace holds
- * only scratch (sample, Gram/eigensolver matrices, partial scores, spilled
- * logits, attention partials); its contents between calls are unspecified. */
+ * only scratch (sample, Gram/eigensolver matrices, transposed bases, partial
+ * scores, spilled logits, attention partials); its contents between calls
+ * are unspecified. */
 int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units,
                          int64_t L, size_t* bytes);
 
@@ -152,7 +153,9 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L,
  *   cache     reads basis_k/v; writes coef_k/v rows [s, L), sink_k/v, ring
  *             (positions [L - n_recent, L)), zeroes qwin, qsplit and rowstat, sets
  *             lens = {L, 0}.  Requires L <= cache->L_max.
- *   ws        unused by this op (may be NULL when ws_bytes == 0). */
+ *   ws        device workspace, ws_bytes >= kvlr_workspace_bytes(PROJECT): the
+ *             bases transposed ([U][2][r][D'] storage) for the MFMA kernel; the
+ *             size is 0 (ws may be NULL) for fp32 storage or r % 64 != 0. */
 int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
                  const void* K, const void* V, kvlr_cache* cache,
                  void* ws, size_t ws_bytes, void* stream);

@@ -252,7 +252,7 @@ int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units, int64_
   if (n_units < 1 || L < 1) return fail(KVLR_EINVAL, "n_units and L must be >= 1");
   switch (op) {
     case KVLR_OP_BUILD_BASES: *bytes = build_layout(cfg, n_units).total; break;
-    case KVLR_OP_PROJECT: *bytes = 0; break;
+    case KVLR_OP_PROJECT: *bytes = project_ws_bytes(dims_of(cfg), n_units); break;
     case KVLR_OP_DECODE: *bytes = decode_layout(cfg, n_units, L).total; break;
     default: return fail(KVLR_EINVAL, "unknown op %d", op);
   }
@@ -319,8 +319,6 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
 
 int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void* K, const void* V,
                  kvlr_cache* cache, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int e = check_cfg(cfg);
   if (e) return e;
   if (n_units < 1 || n_units > (1 << 20)) return fail(KVLR_EINVAL, "n_units out of range");
@@ -332,9 +330,12 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
   if (L > INT32_MAX - 1) return fail(KVLR_EINVAL, "prompt too long");
   hipStream_t st = (hipStream_t)stream;
   const Dims d = dims_of(cfg);
+  const size_t need = project_ws_bytes(d, n_units);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(KVLR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   hipError_t he;
   if ((he = launch_project(d, (int)n_units, L, cache->L_max, K, V, cache->basis_k, cache->basis_v,
-                           cache->coef_k, cache->coef_v, st)) != hipSuccess)
+                           cache->coef_k, cache->coef_v, ws, st)) != hipSuccess)
     return hip_fail(he, "project");
   if ((he = launch_exact_and_reset(d, (int)n_units, L, K, V, cache->sink_k, cache->sink_v, cache->ring_k,
                                    cache->ring_v, cache->qwin, cache->rowstat, cache->lens,

@@ -162,7 +162,9 @@ hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const doubl
                           float* eig_k, float* eig_v, hipStream_t st);
 hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
                           const void* V, const void* BK, const void* BV, void* CK, void* CV,
-                          hipStream_t st);
+                          void* ws, hipStream_t st);
+// workspace bytes of launch_project (transposed bases; 0 when not used)
+size_t project_ws_bytes(const Dims& d, int64_t U);
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   void* sink_k, void* sink_v, void* ring_k, void* ring_v,
                                   float* qwin, float* rowstat, int32_t* lens, uint16_t* qsplit,

@@ -500,6 +500,137 @@ __global__ __launch_bounds__(256) void k_project_bf16(const uint16_t* __restrict
   }
 }
 
+// bf16, r a multiple of 64: the bases are first transposed (B^T[n][k]) into
+// the call's workspace so that every MFMA operand is one K-contiguous
+// 16-byte read.  Block: 256 rows x all r columns of one (unit, K | V); 8
+// waves (two per SIMD), wave w owns rows [32 w, 32 w + 32) and every column
+// block (accumulators in AGPRs).  The K loop advances 64 channels per step:
+//   - the wave's X fragments (lane (m, kg): row m, channels 8 kg + 16 kk)
+//     stream from global memory straight into registers three steps ahead;
+//   - the B^T tile of a step (r rows x 128 bytes) is loaded into registers
+//     two steps ahead and stored to the free half of a 2-stage LDS buffer
+//     one step ahead, before the step's barrier; within a row the 16-byte
+//     chunk c sits in slot c ^ ((n >> 1) & 7), so the operand reads of 16
+//     consecutive rows hit distinct banks.
+constexpr int kProjRows = 256;   // rows per block
+constexpr int kProjWaves = 8;    // waves per block
+constexpr int kProjK = 64;       // channels per K step
+constexpr int kProjRing = 4;     // X fragment ring depth (steps)
+
+__global__ __launch_bounds__(256) void k_basis_t(const uint16_t* __restrict__ BK,
+                                                 const uint16_t* __restrict__ BV,
+                                                 uint16_t* __restrict__ BT, int D, int r) {
+  // tile of 32 channels x 32 columns; BT[u][kind][n][k] = B[u][kind][k][n]
+  __shared__ uint16_t t[32][33];
+  const int um = blockIdx.z, u = um >> 1, kind = um & 1;
+  const uint16_t* B = (kind ? BV : BK) + (int64_t)u * D * r;
+  uint16_t* T = BT + (int64_t)um * r * D;
+  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int kk = e >> 5, nn = e & 31;
+    if (k0 + kk < D && n0 + nn < r) t[kk][nn] = B[(int64_t)(k0 + kk) * r + n0 + nn];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int nn = e >> 5, kk = e & 31;
+    if (k0 + kk < D && n0 + nn < r) T[(int64_t)(n0 + nn) * D + k0 + kk] = t[kk][nn];
+  }
+}
+
+// NS = D' / 64 steps when known at compile time (the loop then unrolls), 0 =
+// runtime
+template <int R, int NS>
+__global__ __launch_bounds__(kProjWaves * 64) void k_project_mfma(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ BT, uint16_t* __restrict__ CK, uint16_t* __restrict__ CV,
+    int64_t L, int64_t Lmax, int D, int s) {
+  constexpr int NT = kProjWaves * 64;
+  constexpr int NCB = R / 32;
+  constexpr int SB = R * kProjK * 2;         // stage bytes
+  constexpr int NPB = SB / 16 / NT;          // 16-byte B^T pieces per thread per step
+  constexpr int AR = kProjRing;
+  static_assert(SB % (16 * NT) == 0, "rank must be a multiple of 64");
+  __shared__ __attribute__((aligned(16))) uint8_t stg[2 * SB];
+  const int um = blockIdx.y, u = um >> 1, kind = um & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
+  const uint16_t* X = (kind ? V : K) + (int64_t)u * L * D;
+  const uint16_t* Bt = BT + (int64_t)um * R * D;
+  uint16_t* C = (kind ? CV : CK) + (int64_t)u * Lmax * R;
+  const int64_t row0 = s + (int64_t)blockIdx.x * kProjRows;
+  const int nsteps = NS > 0 ? NS : D / kProjK;
+  // this lane's X row (rows past L re-read the last one; their results are not stored)
+  const uint16_t* xr = X + min(row0 + 32 * w + mm, L - 1) * D + 8 * kg;
+  // B^T pieces of this thread: piece p = tid + NT i -> row n = p / 8, chunk p % 8
+  uint32_t bsrc[NPB], bdst[NPB];
+#pragma unroll
+  for (int i = 0; i < NPB; ++i) {
+    const int p = tid + NT * i, n = p >> 3, c = p & 7;
+    bsrc[i] = (uint32_t)(n * D + 8 * c);
+    bdst[i] = (uint32_t)(n * (kProjK * 2) + ((c ^ ((n >> 1) & 7)) << 4));
+  }
+  auto load_b = [&](int step, u16x8* br) {
+    const uint16_t* src = Bt + (int64_t)min(step, nsteps - 1) * kProjK;
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) br[i] = *reinterpret_cast<const u16x8*>(src + bsrc[i]);
+  };
+  auto store_b = [&](int step, const u16x8* br) {
+    uint8_t* stage = stg + (step & 1) * SB;
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) *reinterpret_cast<u16x8*>(stage + bdst[i]) = br[i];
+  };
+  auto load_a = [&](int step, bf16x8* a) {
+    const uint16_t* p = xr + (int64_t)min(step, nsteps - 1) * kProjK;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = ld_bf16x8(p + 16 * kk);
+  };
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+  // lane (n = mm, kg) reads chunk 2 kk + kg of B^T row 32 cb + n
+  const int sw = (mm >> 1) & 7;  // (n >> 1) & 7, the same for every column block
+  auto compute = [&](int step, const bf16x8* a) {
+    const uint8_t* stage = stg + (step & 1) * SB + mm * (kProjK * 2);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int co = ((2 * kk + kg) ^ sw) << 4;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(stage + 32 * cb * (kProjK * 2) + co);
+        acc[cb] = mfma32x32x16(a[kk], bb, acc[cb]);
+      }
+    }
+  };
+  // A ring of AR steps (AR - 1 ahead) and B^T 2 steps ahead in registers;
+  // D' is a multiple of AR steps, so the loop has a single exit
+  bf16x8 ar[AR][4];
+  u16x8 bA[NPB], bB[NPB];
+  load_b(0, bA);
+  load_b(1, bB);
+#pragma unroll
+  for (int i = 0; i < AR - 1; ++i) load_a(i, ar[i]);
+  store_b(0, bA);
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < nsteps; t += AR) {
+#pragma unroll
+    for (int k = 0; k < AR; ++k) {
+      load_b(t + k + 2, (k & 1) ? bB : bA);
+      load_a(t + k + AR - 1, ar[(k + AR - 1) % AR]);
+      compute(t + k, ar[k]);
+      store_b(t + k + 1, (k & 1) ? bA : bB);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t row = row0 + 32 * w + acc_row32(i, l);
+      if (row < L) C[row * R + 32 * cb + mm] = f2bf(acc[cb][i]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K,
                                                      const float* __restrict__ V,
                                                      const float* __restrict__ BK,
@@ -519,11 +650,48 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K
   (kind ? CV : CK)[((int64_t)u * Lmax + row) * r + c] = (float)acc;
 }
 
+template <int R>
+static hipError_t launch_project_mfma(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
+                                      const void* V, const void* BK, const void* BV, void* CK,
+                                      void* CV, uint16_t* BT, hipStream_t st) {
+  hipLaunchKernelGGL(k_basis_t, dim3((d.D + 31) / 32, R / 32, 2 * U), dim3(256), 0, st,
+                     (const uint16_t*)BK, (const uint16_t*)BV, BT, d.D, R);
+  const int64_t nrow = L - d.s;
+  const dim3 grid((unsigned)((nrow + kProjRows - 1) / kProjRows), 2 * U);
+#define KVLR_PROJ_LAUNCH(NS)                                                                     \
+  hipLaunchKernelGGL((k_project_mfma<R, NS>), grid, dim3(kProjWaves * 64), 0, st,               \
+                     (const uint16_t*)K,                                                        \
+                     (const uint16_t*)V, (const uint16_t*)BT, (uint16_t*)CK, (uint16_t*)CV, L,  \
+                     Lmax, d.D, d.s)
+  switch (d.D / kProjK) {
+    case 8: KVLR_PROJ_LAUNCH(8); break;
+    case 16: KVLR_PROJ_LAUNCH(16); break;
+    default: KVLR_PROJ_LAUNCH(0); break;
+  }
+#undef KVLR_PROJ_LAUNCH
+  return hipGetLastError();
+}
+
+size_t project_ws_bytes(const Dims& d, int64_t U) {
+  if (d.dtype == 0 || d.r % 64 != 0 || d.D % (kProjRing * kProjK) != 0) return 0;
+  return (size_t)U * 2 * d.r * d.D * sizeof(uint16_t);
+}
+
 hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
                           const void* V, const void* BK, const void* BV, void* CK, void* CV,
-                          hipStream_t st) {
+                          void* ws, hipStream_t st) {
   const int64_t nrow = L - d.s;
   if (nrow <= 0) return hipSuccess;
+  if (project_ws_bytes(d, U) > 0) {
+    uint16_t* BT = (uint16_t*)ws;
+    switch (d.r) {
+      case 64: return launch_project_mfma<64>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
+      case 128: return launch_project_mfma<128>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
+      case 192: return launch_project_mfma<192>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
+      case 256: return launch_project_mfma<256>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
+      default: break;
+    }
+  }
   if (d.dtype == 0) {
     const int64_t tot = nrow * d.r;
     hipLaunchKernelGGL(k_project_f32, dim3((unsigned)((tot + 255) / 256), 2 * U), dim3(256), 0, st,

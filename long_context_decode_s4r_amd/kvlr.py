@@ -219,15 +219,19 @@ def build_bases(cache: KVCache, K: torch.Tensor, V: torch.Tensor, eig_k=None, ei
                                    _ptr(eig_k), _ptr(eig_v), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def project(cache: KVCache, K: torch.Tensor, V: torch.Tensor, stream=None) -> None:
+def project(cache: KVCache, K: torch.Tensor, V: torch.Tensor, ws: Optional[torch.Tensor] = None,
+            stream=None) -> None:
     cfg = cache.cfg
     U, L = K.shape[0], K.shape[1]
     D = cfg.n_kv_heads * cfg.head_dim
     _check_tensor(K, "K", storage_of(cfg), (cache.n_units, L, D))
     _check_tensor(V, "V", storage_of(cfg), (cache.n_units, L, D))
+    if ws is None:
+        need = workspace_bytes(cfg, OP_PROJECT, U, L)
+        ws = torch.empty(need, dtype=torch.uint8, device=K.device) if need > 0 else None
     st = cache.struct()
-    _check(load().kvlr_project(ctypes.byref(cfg), U, L, _ptr(K), _ptr(V), ctypes.byref(st), None, 0,
-                               _stream(stream)))
+    _check(load().kvlr_project(ctypes.byref(cfg), U, L, _ptr(K), _ptr(V), ctypes.byref(st), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def decode_workspace(cache: KVCache) -> torch.Tensor:

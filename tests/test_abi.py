@@ -93,7 +93,8 @@ def test_cache_and_workspace_sizes(lib):
     assert ws > 16 * 34000 * (4 + 4 * 4)
     wb = kvlr.workspace_bytes(cfg, kvlr.OP_BUILD_BASES, 16, 32768)
     assert wb > 4 * 32 * 1024 * 1024 * 8
-    assert kvlr.workspace_bytes(cfg, kvlr.OP_PROJECT, 16, 32768) == 0
+    # projection: the two bases of every unit, transposed, in bf16
+    assert kvlr.workspace_bytes(cfg, kvlr.OP_PROJECT, 16, 32768) == 16 * 2 * 256 * 1024 * 2
     with pytest.raises(kvlr.KvlrError):
         kvlr.workspace_bytes(cfg, 9, 16, 100)
 
