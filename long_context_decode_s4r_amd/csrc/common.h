@@ -75,6 +75,24 @@ __device__ __forceinline__ void lds_read8(const uint32_t a[8], bf16x8 out[8]) {
   out[7] = __builtin_bit_cast(bf16x8, o7);
 }
 
+// Four 16-byte LDS reads, same contract as lds_read8.
+__device__ __forceinline__ void lds_read4(const uint32_t a[4], bf16x8 out[4]) {
+  u16x8 o0, o1, o2, o3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o0), "=&v"(o1), "=&v"(o2), "=&v"(o3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  out[0] = __builtin_bit_cast(bf16x8, o0);
+  out[1] = __builtin_bit_cast(bf16x8, o1);
+  out[2] = __builtin_bit_cast(bf16x8, o2);
+  out[3] = __builtin_bit_cast(bf16x8, o3);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -443,63 +443,92 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
 }
 
 // --------------------------------------------------------------------------
-// latent scoring, bf16 storage: grid (nsplit, U), 256 threads (4 waves).
+// latent scoring, bf16 storage: grid (nsplit, U), 512 threads (8 waves, two
+// per SIMD).
 //
-// Key coefficients stream through a 3-stage LDS ring, 64 positions per tile,
-// filled by direct global->LDS loads (global_load_lds_dwordx4): two tiles are
-// in flight while the third is computed, without spending registers on them.
-// The block waits for a tile with an explicit vmcnt and a plain s_barrier;
-// the stages are distinct LDS objects, so the compiler's own LDS-DMA
-// tracking does not add a full wait.  Within a position row the 16-byte
-// chunks are XOR-swizzled by the position index, so the MFMA operand reads
-// (lane n reads chunk c of position n) hit distinct banks.
+// Key coefficients stream through a 4-stage LDS ring, 64 positions per tile,
+// filled by direct global->LDS loads (global_load_lds_dwordx4), three tiles
+// ahead, without spending registers on them.  One block barrier per tile: a
+// wave waits (vmcnt) for its own pieces of tile t, and after the barrier
+// every piece of t has landed and every wave is done with tile t-1, whose
+// stage then takes the request for tile t+3.  The stages are distinct LDS
+// objects and the waits are asm statements with a memory clobber, so the
+// compiler's own LDS-DMA tracking adds no full wait; the MFMA operand reads
+// are inline asm (lds_read8) for the same reason.  Within a position row the
+// 16-byte chunks are XOR-swizzled by the position index, so the operand
+// reads of 16 consecutive positions hit distinct banks.
 //
-// Work units: (row block rb of 32 window rows, column block cb of 32 tile
-// positions); wave w owns units w, w + 4, ...  Window rows are in "age
-// order" (row rho = i*G + g is query head-group g of the step i steps ago;
-// rows 0..G-1 are the current step).  The fp32 query coefficients, scaled by
-// log2(e)/sqrt(r), are split into bf16 hi + lo parts held in registers as
-// MFMA A operands (32x32x16); the K-index permutation gives lane (n, kg) of
-// the B operand the chunks kg*r/16 + ks of position n, and the A operand the
-// same k's.
+// Work units: MFMA 16x16x32 tiles of (16 window rows, 16 tile positions).
+// Window rows are in "age order" (row rho = i*G + g is query head-group g of
+// the step i steps ago; rows 0..G-1 are the current step), in NRB blocks of
+// 16.  The row blocks form NG groups of RBW; wave w owns group w % NG (its A
+// operands stay in registers: the fp32 query coefficients, scaled by
+// log2(e)/sqrt(r), as bf16 hi + lo parts, two MFMAs per step, ~16 mantissa
+// bits) and the column blocks w / NG + (8 / NG) j of every tile.  The
+// K-index permutation gives lane (n, kq) of both operands the chunks
+// 4 ks + kq.  Per position, a group's probability sum over its rows lands in
+// an LDS segment buffer; every 256 positions the block sums the groups and
+// stores the segment, together with the current rows' logits.
 // --------------------------------------------------------------------------
 constexpr int kScoreTP = 64;     // positions per tile
 constexpr int kScoreSeg = 512;   // positions per output segment (buffered in LDS)
 constexpr int kScoreNST = 4;     // LDS ring stages (3 tiles in flight)
+constexpr int kScoreWaves = 8;
 
 template <int KS>
 struct ScoreStage {
   __attribute__((aligned(16))) uint8_t b[kScoreTP * KS * 32];  // 64 rows x r bf16
 };
 
-template <int KS, int NU>
-__global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeWs w) {
-  constexpr int r = KS * 16, half = KS * 8;
-  constexpr int ROWB = r * 2;                 // bytes per coefficient row
+// sum over the four 16-lane rows of a wave, result in every lane
+__device__ __forceinline__ float sum_lane_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int KS, int NG, int RBW>
+__global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeWs w) {
+  constexpr int r = KS * 16;
+  constexpr int ROWB = r * 2;                  // bytes per coefficient row
   constexpr int TILEB = kScoreTP * ROWB;
-  constexpr int NCH = r / 8;                  // 16-byte chunks per row
+  constexpr int NCH = r / 8;                   // 16-byte chunks per row
   constexpr int SWZ = (NCH % 16 == 0) ? 15 : (NCH % 8 == 0) ? 7 : (NCH % 4 == 0) ? 3 : 0;
-  constexpr int PW = TILEB / 4096;            // DMA instructions per wave per tile
-  constexpr int SEGT = kScoreSeg / kScoreTP;  // tiles per segment
-  static_assert(TILEB % 4096 == 0, "tile must split into 1 KB pieces per wave");
-  static_assert(SEGT % kScoreNST == 0, "segment must hold whole rounds of the ring");
+  constexpr int DW = TILEB / 1024 < kScoreWaves ? TILEB / 1024 : kScoreWaves;  // DMA waves
+  constexpr int PW = TILEB / (DW * 1024);      // DMA instructions per DMA wave per tile
+  constexpr int SEGT = kScoreSeg / kScoreTP;   // tiles per segment
+  constexpr int NKS = r / 32;                  // MFMA K steps
+  constexpr int WPG = kScoreWaves / NG;        // waves per row-block group
+  constexpr int NUW = WPG >= 4 ? 1 : 4 / WPG;  // column blocks per wave and tile
+  constexpr int KB = (RBW == 2 && NKS > 6) ? 4 : 8;  // operand reads per batch (register budget)
+  static_assert(TILEB % (DW * 1024) == 0, "tile must split into 1 KB pieces per wave");
+  static_assert(NCH % 4 == 0, "rank must be a multiple of 32");
+  static_assert(kScoreSeg % 256 == 0, "flush: 4 positions per lane");
   __shared__ ScoreStage<KS> st0, st1, st2, st3;
-  __shared__ float wstat[4][8][2];
-  __shared__ float segred[4][kScoreSeg];      // per row block partial scores
-  __shared__ float segspill[8][kScoreSeg];    // current rows' logits
+  __shared__ __attribute__((aligned(16))) float segred[NG][kScoreSeg];   // per group partial scores
+  __shared__ __attribute__((aligned(16))) float segspill[8][kScoreSeg];  // current rows' logits
 
   const int split = blockIdx.x, u = blockIdx.y;
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, n16 = l & 15, kq = l >> 4;
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;
   const int Lcur = si[0], steps = si[1];
   const int G = d.G, W = d.W, s = d.s;
   const int weff = min(steps + 1, W);
   const int nrows = weff * G;
-  const int nrb = (W * G + 31) / 32;
+  const int nrb = (W * G + 15) / 16;
+  const int ngr = (nrb + RBW - 1) / RBW;       // groups holding row blocks
   const int64_t cend = (int64_t)Lcur + 1 - d.nrec;
-  const int64_t j0 = s + (int64_t)split * w.chunk;
-  const int64_t j1 = min(j0 + (int64_t)w.chunk, cend);
+  // the unit's candidates split evenly over the grid, in whole tiles
+  const int64_t per = (max(cend - s, (int64_t)0) + w.nsplit - 1) / w.nsplit;
+  const int64_t chunk = (per + kScoreTP - 1) / kScoreTP * kScoreTP;
+  const int64_t j0 = s + (int64_t)split * chunk;
+  const int64_t j1 = min(j0 + chunk, cend);
   const int npos = (int)max(j1 - j0, (int64_t)0);
 
   // ---- DMA of one tile into a stage ----------------------------------------
@@ -509,27 +538,30 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
       (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r);
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   uint32_t qoff[PW];
-  int qrow[PW];
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
     const int Q = (wvu * PW + q) * 64 + l;
     const int pl = Q / NCH, slot = Q % NCH;
-    qrow[q] = pl;
     qoff[q] = (uint32_t)(pl * ROWB + ((slot ^ (pl & SWZ)) << 4));
   }
   auto issue = [&](int64_t p0, uint8_t* stage) {
+    if (DW < kScoreWaves && wvu >= DW) return;
     const uint8_t* tb = cbase + p0 * ROWB;
-    const bool tail = p0 + kScoreTP > c.Lmax;  // last tile of the buffer: clamp rows
+    if (p0 + kScoreTP <= c.Lmax) {
 #pragma unroll
-    for (int q = 0; q < PW; ++q) {
-      const uint8_t* src = tb + qoff[q];
-      if (tail) {
-        const int64_t pos = min(p0 + qrow[q], c.Lmax - 1);
-        src = cbase + pos * ROWB + (qoff[q] - qrow[q] * ROWB);
+      for (int q = 0; q < PW; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(tb + qoff[q]),
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+    } else {  // last tile of the buffer: clamp rows
+#pragma unroll
+      for (int q = 0; q < PW; ++q) {
+        const int pl = ((wvu * PW + q) * 64 + l) / NCH;
+        const int64_t pos = min(p0 + pl, c.Lmax - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(cbase + pos * ROWB + (qoff[q] - pl * ROWB)),
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
     }
   };
   // the block's tiles: t covers positions j0 + t * TP + [0, TP); requests past
@@ -542,213 +574,181 @@ __global__ __launch_bounds__(256) void k_score_bf16(Dims d, CachePtrs c, DecodeW
     issue(tp(2), st2.b);
   }
 
-  // ---- per-unit operands ---------------------------------------------------
-  int urb[NU], ucb[NU];
-  bool uact[NU];
-  bf16x8 ahi[NU][KS], alo[NU][KS];
-  float mrow[NU][16], irow[NU][16];
-  float nm[NU][4], ns[NU][4];
+  // ---- this wave's row blocks and column blocks ----------------------------
+  const int rg = wv % NG, cw = wv / NG;
+  const bool wact = rg < ngr && cw < 4;
+  // A fragments: row rho = 16 (RBW rg + b) + n16 of the window (rows past it -> 0)
+  bf16x8 ahi[RBW][NKS], alo[RBW][NKS];
+  // older rows' log-normaliser m + log2(S) for this lane's accumulator rows
+  // 16 rb + 4 kq + i; current and invalid rows get +huge (probability 0)
+  float mrow[RBW][4];
 #pragma unroll
-  for (int j = 0; j < NU; ++j) {
-    const int ui = wv + 4 * j;
-    uact[j] = ui < 2 * nrb;
-    urb[j] = uact[j] ? ui >> 1 : 0;
-    ucb[j] = ui & 1;
-    {  // A fragments from the window's hi / lo split (rows past the window -> 0)
-      const int rho = 32 * urb[j] + mm;
-      const bool valid = rho < nrows;
-      const int rv = valid ? rho : 0;
-      const int i = rv / G, g = rv % G;
-      const int sl = wrap_slot(steps - i, W);
-      const uint16_t* qh = c.qsplit + ((((int64_t)u * W + sl) * G + g) * 2) * r + kg * half;
+  for (int b = 0; b < RBW; ++b) {
+    const int rb = RBW * rg + b;
+    const int rho = 16 * rb + n16;
+    const bool valid = wact && rho < nrows;
+    const int rv = valid ? rho : 0;
+    const int i = rv / G, g = rv % G;
+    const int sl = wrap_slot(steps - i, W);
+    const uint16_t* qh = c.qsplit + ((((int64_t)u * W + sl) * G + g) * 2) * r;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 h = ld_bf16x8(qh + 8 * ks);
-        const bf16x8 lo = ld_bf16x8(qh + r + 8 * ks);
-        ahi[j][ks] = valid ? h : __builtin_bit_cast(bf16x8, u16x8{});
-        alo[j][ks] = valid ? lo : __builtin_bit_cast(bf16x8, u16x8{});
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 h = ld_bf16x8(qh + (4 * ks + kq) * 8);
+      const bf16x8 lo = ld_bf16x8(qh + r + (4 * ks + kq) * 8);
+      ahi[b][ks] = valid ? h : __builtin_bit_cast(bf16x8, u16x8{});
+      alo[b][ks] = valid ? lo : __builtin_bit_cast(bf16x8, u16x8{});
     }
-    {  // older rows' running (max, sum); current and invalid rows excluded
-      float2 stv[16];
+    float2 stv[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = 32 * urb[j] + acc_row32(i, l);
-        const int rv = rr < nrows ? rr : 0;
-        const int ii = rv / G, g = rv % G;
-        const int sl = wrap_slot(steps - ii, W);
-        stv[i] = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = 32 * urb[j] + acc_row32(i, l);
-        const bool old_row = uact[j] && rr >= G && rr < nrows;
-        mrow[j][i] = old_row ? stv[i].x : FLT_MAX;
-        irow[j][i] = old_row ? 1.f / stv[i].y : 0.f;
-      }
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int rr = 16 * rb + 4 * kq + i2;
+      const int rv2 = rr < nrows ? rr : 0;
+      const int ii = rv2 / G, g2 = rv2 % G;
+      const int sl2 = wrap_slot(steps - ii, W);
+      stv[i2] = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl2) * G + g2) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      nm[j][i] = -INFINITY;
-      ns[j][i] = 0.f;
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int rr = 16 * rb + 4 * kq + i2;
+      const bool old_row = wact && rr >= G && rr < nrows;
+      mrow[b][i2] = old_row ? stv[i2].x + log2f(stv[i2].y) : FLT_MAX;
     }
   }
-
-  constexpr int kWaitN = (kScoreNST - 1) * PW;  // groups allowed in flight
-  constexpr int kWaitImm = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8);
-  constexpr int kLgkm0 = 0xF | (3 << 14) | (7 << 4);  // lgkmcnt(0)
-  constexpr int kVm0 = (7 << 4) | (15 << 8);          // vmcnt(0)
+  // current row g = wave index (g < G): running (max, sum) over the
+  // positions this lane flushes
+  float nm = -INFINITY, ns = 0.f;
 
   // tile t of the block (positions j0 + t*TP + pl; segment slot (t % SEGT)*TP + pl)
   auto compute = [&](int t, const uint8_t* stage) {
-#pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      if (!uact[j]) continue;
-      const int pl = ucb[j] * 32 + mm;
-      const uint8_t* rowp = stage + pl * ROWB;
+    if (!wact) return;
+    const uint32_t sbase = lds_offset(stage);
+#pragma unroll 1
+    for (int j = 0; j < NUW; ++j) {
+      const int cb = cw + WPG * j;  // < 4: cw < min(WPG, 4) and WPG * NUW = 4 or NUW = 1
+      const int pl = 16 * cb + n16;  // position row of this lane's B operand
+      const uint32_t rbase = sbase + pl * ROWB;
       const int sw = pl & SWZ;
-      f32x16 acc = {};
-      if constexpr (KS % 8 == 0) {
-        const uint32_t rbase = lds_offset(rowp);
+      f32x4 acc[RBW];
 #pragma unroll
-        for (int k0 = 0; k0 < KS; k0 += 8) {
-          uint32_t ad[8];
-          bf16x8 bb[8];
+      for (int b = 0; b < RBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) ad[kk] = rbase + (((kg * KS + k0 + kk) ^ sw) << 4);
+      for (int k0 = 0; k0 < NKS; k0 += KB) {
+        uint32_t ad[KB];
+        bf16x8 bb[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+          ad[kk] = rbase + (((4 * min(k0 + kk, NKS - 1) + kq) ^ sw) << 4);
+        if constexpr (KB == 8)
           lds_read8(ad, bb);
+        else
+          lds_read4(ad, bb);
 #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            acc = mfma32x32x16(ahi[j][k0 + kk], bb[kk], acc);
-            acc = mfma32x32x16(alo[j][k0 + kk], bb[kk], acc);
+        for (int kk = 0; kk < KB; ++kk) {
+          if (k0 + kk < NKS) {
+#pragma unroll
+            for (int b = 0; b < RBW; ++b) acc[b] = mfma16(ahi[b][k0 + kk], bb[kk], acc[b]);
+#pragma unroll
+            for (int b = 0; b < RBW; ++b) acc[b] = mfma16(alo[b][k0 + kk], bb[kk], acc[b]);
           }
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(rowp + ((kg * KS + ks) ^ sw) * 16);
-          acc = mfma32x32x16(ahi[j][ks], bb, acc);
-          acc = mfma32x32x16(alo[j][ks], bb, acc);
         }
       }
       // arguments are <= 0 (or -huge for excluded rows): the hardware exp2
       // is exact enough and its flush of tiny results is harmless here
       float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(acc[i] - mrow[j][i]) * irow[j][i];
-      ps += __shfl_xor(ps, 32);
-      const int sp = (t % SEGT) * kScoreTP + pl;  // position within the segment
-      if (l < 32) segred[urb[j]][sp] = ps;
-      if (urb[j] == 0) {
-        const bool pv = t * kScoreTP + pl < npos;
+      for (int b = 0; b < RBW; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 4 * kg + i;
-          if (row < G) {
-            const float z = acc[i];
-            segspill[row][sp] = z;
-            if (pv) {
-              const float mx = fmaxf(nm[j][i], z);
-              ns[j][i] = ns[j][i] * __builtin_amdgcn_exp2f(nm[j][i] - mx) +
-                         __builtin_amdgcn_exp2f(z - mx);
-              nm[j][i] = mx;
-            }
-          }
-        }
+        for (int i = 0; i < 4; ++i) ps += __builtin_amdgcn_exp2f(acc[b][i] - mrow[b][i]);
+      ps = sum_lane_rows(ps);
+      const int sp = (t % SEGT) * kScoreTP + pl;  // position within the segment
+      if (l < 16) segred[rg][sp] = ps;
+      if (rg == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * kq + i < G) segspill[4 * kq + i][sp] = acc[0][i];
       }
     }
   };
 
   float* partial = w.partial + (int64_t)u * w.Lc_cap + (j0 - s);
   float* spill = w.spill + (int64_t)u * G * w.Lc_cap + (j0 - s);
-  // flush of segment sg (tiles [sg * SEGT, ...)) after its last tile
+  // flush of segment sg, four positions per lane and one 16-byte store per
+  // wave: the last wave stores the group sums, wave g < G the current row g's
+  // logits (and folds them into its running max and sum)
   auto flush = [&](int sg) {
     const int seg0 = sg * kScoreSeg;
     const int segn = min(kScoreSeg, npos - seg0);
-    for (int e = tid; e < segn; e += 256) {
-      float sum = 0.f;
-      for (int q2 = 0; q2 < nrb; ++q2) sum += segred[q2][e];
-      partial[seg0 + e] = sum;
+#pragma unroll
+    for (int e0 = 4 * l; e0 < kScoreSeg; e0 += 256) {
+    if (wv == kScoreWaves - 1 && e0 < segn) {
+      f32x4 sum = *reinterpret_cast<const f32x4*>(&segred[0][e0]);
+      for (int q2 = 1; q2 < ngr; ++q2) sum += *reinterpret_cast<const f32x4*>(&segred[q2][e0]);
+      if (e0 + 4 <= segn) {
+        *reinterpret_cast<f32x4*>(partial + seg0 + e0) = sum;
+      } else {
+        for (int e = 0; e < segn - e0; ++e) partial[seg0 + e0 + e] = sum[e];
+      }
     }
-    for (int e = tid; e < G * segn; e += 256) {
-      const int row = e / segn, sp = e % segn;
-      spill[(int64_t)row * w.Lc_cap + seg0 + sp] = segspill[row][sp];
+    if (wv < G && e0 < segn) {
+      const f32x4 z = *reinterpret_cast<const f32x4*>(&segspill[wv][e0]);
+      float* dst = spill + (int64_t)wv * w.Lc_cap + seg0 + e0;
+      const int ne = min(4, segn - e0);
+      if (ne == 4) {
+        *reinterpret_cast<f32x4*>(dst) = z;
+      } else {
+        for (int e = 0; e < ne; ++e) dst[e] = z[e];
+      }
+      float mx = nm;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = e < ne ? fmaxf(mx, z[e]) : mx;
+      float acc = ns * __builtin_amdgcn_exp2f(nm - mx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += e < ne ? __builtin_amdgcn_exp2f(z[e] - mx) : 0.f;
+      nm = mx;
+      ns = acc;
+    }
     }
   };
-  // tile t lives in stage t % 4; one DMA group is issued per tile, so the
-  // tile being waited for always has exactly three groups behind it (plus any
-  // flush stores, which only make the wait stricter)
+  // tile t lives in stage t % 4.  At the wait of step t the wave's requests
+  // issued after tile t are exactly tiles t+1 and t+2 (flush stores go out
+  // before the next request), so vmcnt(2 PW) means tile t has landed.
+  constexpr int kWaitN = (kScoreNST - 2) * PW;
   for (int t = 0; t < ntl; t += kScoreNST) {
-#define KVLR_SCORE_STEP(k, SREAD, SNEXT)                   \
-    if (t + k >= ntl) break;                               \
-    issue(tp(t + k + 3), SNEXT);                           \
-    __builtin_amdgcn_s_waitcnt(kWaitImm);                  \
-    __builtin_amdgcn_s_barrier();                          \
-    compute(t + k, SREAD);                                 \
-    __builtin_amdgcn_s_waitcnt(kLgkm0);                    \
-    __builtin_amdgcn_s_barrier();                          \
-    if ((t + k) % SEGT == SEGT - 1 || t + k == ntl - 1) {  \
-      flush((t + k) / SEGT);                               \
-      __builtin_amdgcn_s_waitcnt(kLgkm0);                  \
-      __builtin_amdgcn_s_barrier();                        \
-    }
+#define KVLR_SCORE_STEP(k, SREAD, SNEXT)                                                    \
+    if (t + k >= ntl) break;                                                                \
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWaitN) : "memory");  \
+    if ((t + k) % SEGT == 0 && t + k > 0) {                                                 \
+      flush((t + k) / SEGT - 1);                                                            \
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                       \
+    }                                                                                       \
+    issue(tp(t + k + 3), SNEXT);                                                            \
+    compute(t + k, SREAD);
     KVLR_SCORE_STEP(0, st0.b, st3.b)
     KVLR_SCORE_STEP(1, st1.b, st0.b)
     KVLR_SCORE_STEP(2, st2.b, st1.b)
     KVLR_SCORE_STEP(3, st3.b, st2.b)
 #undef KVLR_SCORE_STEP
   }
-  __builtin_amdgcn_s_waitcnt(kVm0);  // no request left in flight at exit
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (ntl > 0) flush((ntl - 1) / SEGT);
 
-  // current rows' (max, sum) over this split: lanes of one kg half, then waves
+  // current row g's (max, sum) over this split, from the lanes of wave g
+  if (wv < G) {
+    float m = nm, sm = ns;
 #pragma unroll
-  for (int j = 0; j < NU; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = nm[j][i], sm = ns[j][i];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
-        const float mx = fmaxf(m, m2);
-        const float a = (m == -INFINITY) ? 0.f : sm * exp2f(m - mx);
-        const float b2 = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mx);
-        sm = a + b2;
-        m = mx;
-      }
-      nm[j][i] = m;
-      ns[j][i] = sm;
-    }
-  }
-  if (mm == 0) {
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kg + i;
-      float m = -INFINITY, sm = 0.f;
-#pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        if (uact[j] && urb[j] == 0 && ns[j][i] > 0.f) {
-          const float mx = fmaxf(m, nm[j][i]);
-          sm = (m == -INFINITY ? 0.f : sm * exp2f(m - mx)) + ns[j][i] * exp2f(nm[j][i] - mx);
-          m = mx;
-        }
-      }
-      wstat[wv][row][0] = m;
-      wstat[wv][row][1] = sm;
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    float m = -INFINITY, sm = 0.f;
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const float m2 = wstat[q2][tid][0], s2 = wstat[q2][tid][1];
-      if (!(s2 > 0.f)) continue;
+    for (int o = 1; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
       const float mx = fmaxf(m, m2);
-      sm = (m == -INFINITY ? 0.f : sm * exp2f(m - mx)) + s2 * exp2f(m2 - mx);
+      const float a = (m == -INFINITY) ? 0.f : sm * exp2f(m - mx);
+      const float b2 = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mx);
+      sm = a + b2;
       m = mx;
     }
-    float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
-    tst[tid * 2 + 0] = m;
-    tst[tid * 2 + 1] = sm;
+    if (l == 0) {
+      float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
+      tst[wv * 2 + 0] = m;
+      tst[wv * 2 + 1] = sm;
+    }
   }
 }
 
@@ -831,12 +831,16 @@ __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs
 template <int KS>
 static hipError_t launch_score_bf16(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                                     hipStream_t st) {
-  const int nrb = (d.W * d.G + 31) / 32;
+  const int nrb = (d.W * d.G + 15) / 16;
   dim3 grid(w.nsplit, U);
-  if (2 * nrb <= 4)
-    hipLaunchKernelGGL((k_score_bf16<KS, 1>), grid, dim3(256), 0, st, d, c, w);
+  if (nrb <= 1)
+    hipLaunchKernelGGL((k_score_bf16<KS, 1, 1>), grid, dim3(512), 0, st, d, c, w);
+  else if (nrb <= 2)
+    hipLaunchKernelGGL((k_score_bf16<KS, 2, 1>), grid, dim3(512), 0, st, d, c, w);
+  else if (nrb <= 4)
+    hipLaunchKernelGGL((k_score_bf16<KS, 2, 2>), grid, dim3(512), 0, st, d, c, w);
   else
-    hipLaunchKernelGGL((k_score_bf16<KS, 2>), grid, dim3(256), 0, st, d, c, w);
+    hipLaunchKernelGGL((k_score_bf16<KS, 4, 2>), grid, dim3(512), 0, st, d, c, w);
   return hipGetLastError();
 }
 
