@@ -1024,44 +1024,88 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 // --------------------------------------------------------------------------
 // top-k: one 1024-thread block per unit.
 //   Thread t owns a contiguous run of keys (pooled scores as ordered bit
-//   patterns), kept in registers while the run fits, else re-read per pass.
-//   Threshold key T = the k-th largest key, by a radix select over the key
-//   range actually present: with lo / hi the smallest / largest key, the
-//   first histogram bins (key - lo) >> shift into 4096 bins, then 10-bit
-//   refinements of the selected bin until it is resolved to one key value or
-//   taken whole.  Consecutive keys of a run that fall in the same bin are
-//   counted with one LDS atomic (max-pooling repeats values).  Ordered
-//   compaction: every key above the threshold bin, and the first
-//   (k - #above) keys of that bin in position order (ties -> lower
-//   position), written in ascending position order.  Also advances lens and
-//   writes the outputs of units whose cache is full (topk = -1, out = 0).
+//   patterns), kept in registers while the run fits, else re-read per pass;
+//   the register run is requested before the unit state arrives.
+//   1. Floor: with kk <= 1024 picks, the kk-th largest per-thread maximum is
+//      at most the kk-th largest key (kk threads each hold a key at least
+//      that large), and so is the lower edge of its histogram bin.
+//   2. The keys >= floor (candidates) are compacted, in position order, into
+//      an LDS list; every later pass runs over that short list with full,
+//      mostly conflict-free LDS atomics.  (More than kTopkCap candidates, or
+//      kk > 1024: the passes run over the thread runs instead.)
+//   3. Threshold T = the kk-th largest key, by a radix select over
+//      [floor, max]: 2^14-bin histograms of (key - floor) >> shift, refined
+//      until the selected bin is one key value (also when the bin turns out
+//      to hold a single value) or is taken whole.
+//   4. Ordered compaction: every key above the threshold bin, and the first
+//      (kk - #above) keys of that bin in position order (ties -> lower
+//      position), in ascending position order; one block scan of (#above,
+//      #in-bin) per thread gives both offsets.  The picks leave through LDS
+//      in one coalesced pass.
+//   Also advances lens and writes the outputs of units whose cache is full
+//   (topk = -1, out = 0).
 // --------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024; // 16 waves; <= 128 VGPRs per thread
 constexpr int kTopkRegKeys = 32;   // keys per thread held in registers (32 768 candidates)
-constexpr int kTopkRefineBits = 10; // refinement digits: one bin per thread
+constexpr int kTopkBinBits = 14;   // histogram digits per pass
+constexpr int kTopkBins = 1 << kTopkBinBits;
+constexpr int kTopkCap = 8192;     // candidate list capacity
 static_assert(kKeyPad >= kTopkRegKeys, "key buffer padding must cover one register run");
 
-__device__ __forceinline__ int block_excl_scan(int v, int* wtot, int* total) {
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+// inclusive prefix sum over the wave: row_shr 1, 2, 4, 8 within rows of 16,
+// then row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3)
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF>(x);
+  x += dpp_i<0x112, 0xF>(x);
+  x += dpp_i<0x114, 0xF>(x);
+  x += dpp_i<0x118, 0xF>(x);
+  x += dpp_i<0x142, 0xA>(x);
+  x += dpp_i<0x143, 0xC>(x);
+  return x;
+}
+
+// min and max over the wave (xor-pattern DPP, then the four rows), in every lane
+__device__ __forceinline__ void wave_minmax_u(unsigned int& mn, unsigned int& mx) {
+#define KVLR_MM(CTRL)                                                                          \
+  mn = min(mn, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mn, CTRL, 0xF, 0xF, false)); \
+  mx = max(mx, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mx, CTRL, 0xF, 0xF, false));
+  KVLR_MM(0xB1)
+  KVLR_MM(0x4E)
+  KVLR_MM(0x141)
+  KVLR_MM(0x140)
+#undef KVLR_MM
+  mn = min(min((unsigned int)__builtin_amdgcn_readlane((int)mn, 0), (unsigned int)__builtin_amdgcn_readlane((int)mn, 16)),
+           min((unsigned int)__builtin_amdgcn_readlane((int)mn, 32), (unsigned int)__builtin_amdgcn_readlane((int)mn, 48)));
+  mx = max(max((unsigned int)__builtin_amdgcn_readlane((int)mx, 0), (unsigned int)__builtin_amdgcn_readlane((int)mx, 16)),
+           max((unsigned int)__builtin_amdgcn_readlane((int)mx, 32), (unsigned int)__builtin_amdgcn_readlane((int)mx, 48)));
+}
+
+// exclusive block prefix sums of two counters (a, b); totals in *ta, *tb
+__device__ __forceinline__ int2 block_excl_scan2(int a, int b, int2* wtot, int* ta, int* tb) {
   constexpr int NW = kTopkThreads / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wtot[wid] = x;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) wtot[wid] = make_int2(ia, ib);
   __syncthreads();
-  int before = 0, tot = 0;
+  int ba = 0, bb = 0, sa = 0, sb = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int t = wtot[i];
-    if (i < wid) before += t;
-    tot += t;
+    const int2 t = wtot[i];
+    if (i < wid) {
+      ba += t.x;
+      bb += t.y;
+    }
+    sa += t.x;
+    sb += t.y;
   }
   __syncthreads();
-  *total = tot;
-  return before + x - v;
+  *ta = sa;
+  *tb = sb;
+  return make_int2(ba + ia - a, bb + ib - b);
 }
 
 // apply f(key, position) to the thread's run [j0, j1) in position order, in
@@ -1070,6 +1114,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wtot, int* total) {
 template <typename F>
 __device__ __forceinline__ void for_keys(const uint32_t* keys, int j0, int j1, bool in_regs,
                                          uint32_t* kr, F&& f) {
+  if (in_regs && j1 - j0 == kTopkRegKeys) {  // a full register run: no bound checks
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; ++i) f(kr[i], j0 + i);
+    return;
+  }
   for (int jb = j0; jb < j1; jb += kTopkRegKeys) {
     if (!in_regs) {
 #pragma unroll
@@ -1087,11 +1136,66 @@ __device__ __forceinline__ void for_keys(const uint32_t* keys, int j0, int j1, b
   }
 }
 
+// The bin holding the r-th largest of the counts in hs[0, nb) (bins above
+// it hold fewer than r keys): thread t owns bins [16 t, 16 t + 16); the
+// owner of the crossing bin writes its index, the remaining rank inside it
+// and its count.  Ends with a block barrier.
+__device__ __forceinline__ void topk_find_bin(const unsigned int* hs, int nb, int r, int2* wtot,
+                                              unsigned int* sh_bin, int* sh_rem, int* sh_cnt) {
+  constexpr int BPT = kTopkBins / kTopkThreads;
+  const int b0 = BPT * threadIdx.x;
+  unsigned int hv[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&hs[b0 + i]);
+    hv[i] = b0 + i < nb ? v.x : 0u;
+    hv[i + 1] = b0 + i + 1 < nb ? v.y : 0u;
+    hv[i + 2] = b0 + i + 2 < nb ? v.z : 0u;
+    hv[i + 3] = b0 + i + 3 < nb ? v.w : 0u;
+  }
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) local += (int)hv[i];
+  int tot, dummy;
+  const int excl = block_excl_scan2(local, 0, wtot, &tot, &dummy).x;
+  int above = tot - excl - local;  // keys in higher bins
+  if (above < r && above + local >= r) {
+    bool found = false;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (!found && above + (int)hv[i] >= r) {
+        *sh_bin = (unsigned int)(b0 + i);
+        *sh_rem = r - above;
+        *sh_cnt = (int)hv[i];
+        found = true;
+      }
+      above += (int)hv[i];
+    }
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, DecodeWs w,
                                                int32_t* __restrict__ topk_user,
                                                float* __restrict__ out) {
   const int u = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
+  const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
+  // the register run of a unit with at most kTopkThreads * kTopkRegKeys
+  // candidates, requested together with the unit state (the address is
+  // clamped into the unit's key buffer; a run that is used lies inside it)
+  uint32_t kr[kTopkRegKeys];
+  {
+    const int jr = min(tid * kTopkRegKeys, w.Lc_cap - kTopkRegKeys);
+#pragma unroll
+    for (int i = 0; i < kTopkRegKeys; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + jr + i);
+      kr[i] = v.x;
+      kr[i + 1] = v.y;
+      kr[i + 2] = v.z;
+      kr[i + 3] = v.w;
+    }
+  }
   const int32_t* si = w.stepinfo + 4 * u;
   const int k = d.k;
   if (si[2]) {
@@ -1111,12 +1215,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   if (topk_user)
     for (int i = kk + tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
   if (kk <= 0) return;
-  __shared__ unsigned int hs[kHistBins];
-  __shared__ int wtot[kTopkThreads / 64];
-  __shared__ unsigned int wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
-  __shared__ unsigned int sh_bin;
+  __shared__ __attribute__((aligned(16))) unsigned int hs[kTopkBins];
+  __shared__ uint2 cand[kTopkCap];  // candidates (key, position), position order
+  __shared__ int2 wtot[kTopkThreads / 64];
+  __shared__ unsigned int wlo[kTopkThreads / 64], whi[kTopkThreads / 64];
+  __shared__ unsigned int sh_bin, sh_kmin, sh_kmax;
   __shared__ int sh_rem, sh_cnt;
-  const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
   // runs of `per` keys, whole batches of kTopkRegKeys (vector reads stay
   // aligned); reads past the unit's candidates land in the next unit's keys
   // or in the kKeyPad entries of slack at the end of the buffer and are ignored
@@ -1124,114 +1228,171 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
                   kTopkRegKeys;
   const int j0 = tid * per, j1 = min(j0 + per, nc);
   const bool in_regs = per == kTopkRegKeys;
-  uint32_t kr[kTopkRegKeys];
-  if (in_regs) {
-#pragma unroll
-    for (int i = 0; i < kTopkRegKeys; i += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0, nc) + i);
-      kr[i] = v.x;
-      kr[i + 1] = v.y;
-      kr[i + 2] = v.z;
-      kr[i + 3] = v.w;
-    }
+  for (int i = tid; i < kTopkBins; i += kTopkThreads) hs[i] = 0u;
+  if (tid == 0) {
+    sh_kmin = 0xFFFFFFFFu;
+    sh_kmax = 0u;
   }
-  for (int i = tid; i < kHistBins; i += kTopkThreads) hs[i] = 0u;
-  // key range present
+  // key range present; per-thread maximum
   unsigned int kmin = 0xFFFFFFFFu, kmax = 0u;
   for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
     kmin = min(kmin, key);
     kmax = max(kmax, key);
   });
-  {
-    unsigned int a = kmin, b2 = kmax;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      a = min(a, (unsigned int)__shfl_xor((int)a, o));
-      b2 = max(b2, (unsigned int)__shfl_xor((int)b2, o));
-    }
-    if (lane == 0) {
-      wmin[wid] = a;
-      wmax[wid] = b2;
-    }
+  const unsigned int tmax = kmax;
+  wave_minmax_u(kmin, kmax);
+  if (lane == 0) {
+    wlo[wid] = kmin;
+    whi[wid] = kmax;
   }
   __syncthreads();
-  unsigned int lo = wmin[0], hi = wmax[0];
+  unsigned int lo = wlo[0], hi = whi[0];
 #pragma unroll
   for (int i = 1; i < kTopkThreads / 64; ++i) {
-    lo = min(lo, wmin[i]);
-    hi = max(hi, wmax[i]);
+    lo = min(lo, wlo[i]);
+    hi = max(hi, whi[i]);
   }
-  const unsigned int range = hi - lo;
-  const int bits = range == 0u ? 0 : 32 - __clz((int)range);
-  int shift = max(bits - 12, 0);
-  // level 1 over the range
-  for_keys(keys, j0, j1, in_regs, kr,
-           [&](uint32_t key, int) { atomicAdd(&hs[(key - lo) >> shift], 1u); });
-  __syncthreads();
-  int tot;
-  {  // thread t owns bins [BPT t, BPT t + BPT)
-    constexpr int BPT = kHistBins / kTopkThreads;
-    const int b0 = BPT * tid;
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) local += (int)hs[b0 + i];
-    const int excl = block_excl_scan(local, wtot, &tot);
-    int above = tot - excl - local;  // keys in higher bins
-    if (above < kk && above + local >= kk) {
-      for (int bb = b0 + BPT - 1; bb >= b0; --bb) {
-        if (above + (int)hs[bb] >= kk) {
-          sh_bin = (unsigned int)bb;
-          sh_rem = kk - above;
-          sh_cnt = (int)hs[bb];
-          break;
-        }
-        above += (int)hs[bb];
+  auto range_shift = [](unsigned int base, unsigned int top) {
+    const unsigned int rg = top - base;
+    const int bits = rg == 0u ? 0 : 32 - __clz((int)rg);
+    return max(bits - kTopkBinBits, 0);
+  };
+  // 1. floor from the per-thread maxima: wave w's q-th largest maximum m_w
+  //    (q = ceil(kk / 16)); every wave has q runs holding a key >= min_w m_w,
+  //    so at least 16 q >= kk keys are >= that minimum
+  if (kk <= kTopkThreads) {
+    // bitwise radix select over the lanes: the answer's bits from the top;
+    // `need` counts down the rank still to find below the decided prefix
+    int need = (kk + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
+    unsigned int mw = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const unsigned int want = (mw >> b) | 1u;
+      const int cnt = __popcll(__ballot((tmax >> b) == want));
+      if (cnt >= need) {
+        mw |= 1u << b;
+      } else {
+        need -= cnt;
       }
     }
+    if (lane == 0) wlo[wid] = mw;
     __syncthreads();
+    unsigned int fl = wlo[0];
+#pragma unroll
+    for (int i = 1; i < kTopkThreads / 64; ++i) fl = min(fl, wlo[i]);
+    lo = max(lo, fl);
   }
-  // the selected bin, as a prefix of (key - lo) at resolution `shift`
+  // 2. candidates: keys >= lo, counted, then listed in position order
+  int ccount = 0;
+  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) { ccount += key >= lo; });
+  int ntot, dummy;
+  const int coff = block_excl_scan2(ccount, 0, wtot, &ntot, &dummy).x;
+  const bool listed = ntot <= kTopkCap;
+  if (listed) {
+    int o = coff;
+    for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
+      if (key >= lo) cand[o++] = make_uint2(key, (unsigned int)j);
+    });
+  }
+  __syncthreads();
+  // candidates of this thread in position order: a contiguous share of the
+  // list (neighbouring lanes hold different stretches, so the equal keys of
+  // a pooled run do not collide in one atomic), or its run filtered to
+  // keys >= lo
+  const int cpt = (ntot + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(tid * cpt, ntot), i1 = min(i0 + cpt, ntot);
+  auto visit_ordered = [&](auto&& f) {
+    if (listed) {
+      for (int i = i0; i < i1; ++i) {
+        const uint2 e = cand[i];
+        f(e.x, (int)e.y);
+      }
+    } else {
+      for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
+        if (key >= lo) f(key, j);
+      });
+    }
+  };
+  // histogram of f(key) over the thread's candidates with pred(key); equal
+  // consecutive bins cost one atomic
+  auto histo = [&](auto&& pred, auto&& binof) {
+    unsigned int pb = 0xFFFFFFFFu, pc = 0u;
+    visit_ordered([&](uint32_t key, int) {
+      if (!pred(key)) return;
+      const unsigned int bn = binof(key);
+      if (bn != pb) {
+        if (pc) atomicAdd(&hs[pb], pc);
+        pb = bn;
+        pc = 0u;
+      }
+      ++pc;
+    });
+    if (pc) atomicAdd(&hs[pb], pc);
+  };
+  // 3. threshold
+  int shift = range_shift(lo, hi);
+  histo([](uint32_t) { return true; }, [&](uint32_t key) { return (key - lo) >> shift; });
+  __syncthreads();
+  topk_find_bin(hs, kTopkBins, kk, wtot, &sh_bin, &sh_rem, &sh_cnt);
   unsigned int bin = sh_bin;
   int rem = sh_rem, cnt_bin = sh_cnt;
   while (shift > 0 && rem < cnt_bin) {
-    const int nsh = max(shift - kTopkRefineBits, 0);
+    const int nsh = max(shift - kTopkBinBits, 0);
     const unsigned int nb = 1u << (shift - nsh);
-    if (tid < (int)nb) hs[tid] = 0u;
+    for (int i = tid; i < (int)nb; i += kTopkThreads) hs[i] = 0u;
     __syncthreads();
-    for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
-      const unsigned int rk = key - lo;
-      if ((rk >> shift) == bin) atomicAdd(&hs[(rk >> nsh) & (nb - 1u)], 1u);
-    });
-    __syncthreads();
-    const int local = tid < (int)nb ? (int)hs[tid] : 0;
-    const int excl = block_excl_scan(local, wtot, &tot);
-    const int above = tot - excl - local;
-    if (tid < (int)nb && above < rem && above + local >= rem) {
-      sh_bin = (bin << (shift - nsh)) | (unsigned int)tid;
-      sh_rem = rem - above;
-      sh_cnt = local;
+    unsigned int bmin = 0xFFFFFFFFu, bmax = 0u;
+    histo(
+        [&](uint32_t key) {
+          const bool in = ((key - lo) >> shift) == bin;
+          if (in) {
+            bmin = min(bmin, key);
+            bmax = max(bmax, key);
+          }
+          return in;
+        },
+        [&](uint32_t key) { return ((key - lo) >> nsh) & (nb - 1u); });
+    wave_minmax_u(bmin, bmax);
+    if (lane == 0) {
+      if (bmin != 0xFFFFFFFFu) atomicMin(&sh_kmin, bmin);
+      if (bmax != 0u) atomicMax(&sh_kmax, bmax);
     }
     __syncthreads();
-    bin = sh_bin;
+    if (sh_kmin == sh_kmax) {  // one value: it is the threshold
+      bin = sh_kmin - lo;
+      shift = 0;
+      break;
+    }
+    topk_find_bin(hs, (int)nb, rem, wtot, &sh_bin, &sh_rem, &sh_cnt);
+    const unsigned int sub = sh_bin;
     rem = sh_rem;
     cnt_bin = sh_cnt;
+    bin = (bin << (shift - nsh)) | sub;
     shift = nsh;
+    if (tid == 0) {
+      sh_kmin = 0xFFFFFFFFu;
+      sh_kmax = 0u;
+    }
+    __syncthreads();
   }
-  // compaction: keys with (key - lo) >> shift above `bin`, then the first
-  // `rem` keys of the bin in position order
-  const int need_eq = rem;
+  // 4. compaction in position order: keys with (key - lo) >> shift above
+  // `bin`, then the first `rem` keys of the bin; the in-bin keys taken
+  // before thread t number min(rem, in-bin keys before t)
   int c_gt = 0, c_eq = 0;
-  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
+  visit_ordered([&](uint32_t key, int) {
     const unsigned int bn = (key - lo) >> shift;
     c_gt += bn > bin;
     c_eq += bn == bin;
   });
-  const int eq_base = block_excl_scan(c_eq, wtot, &tot);
-  const int take_eq = max(0, min(need_eq - eq_base, c_eq));
-  int off = block_excl_scan(c_gt + take_eq, wtot, &tot);
+  int tgt, teq;
+  const int2 base = block_excl_scan2(c_gt, c_eq, wtot, &tgt, &teq);
+  const int take_eq = max(0, min(rem - base.y, c_eq));
+  int off = base.x + min(rem, base.y);
+  // the picks go through LDS (the histogram is free now) and leave in one
+  // coalesced pass; units with more than kTopkBins picks write directly
+  const bool stage = kk <= kTopkBins;
   int32_t* sel = w.topk + (int64_t)u * k;
   int seen = 0;
-  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
+  visit_ordered([&](uint32_t key, int j) {
     const unsigned int bn = (key - lo) >> shift;
     bool take = bn > bin;
     if (bn == bin) {
@@ -1239,11 +1400,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
       ++seen;
     }
     if (take) {
-      sel[off] = s + j;
-      if (topk_user) topk_user[(int64_t)u * k + off] = s + j;
+      if (stage) {
+        hs[off] = (unsigned int)(s + j);
+      } else {
+        sel[off] = s + j;
+        if (topk_user) topk_user[(int64_t)u * k + off] = s + j;
+      }
       ++off;
     }
   });
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kk; i += kTopkThreads) {
+      const int v = (int)hs[i];
+      sel[i] = v;
+      if (topk_user) topk_user[(int64_t)u * k + i] = v;
+    }
+  }
 }
 
 hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
