@@ -197,3 +197,39 @@ def test_repeatable(gpu_lib):
             res.append(out.clone())
         outs.append(torch.stack(res))
     assert torch.equal(outs[0], outs[1])
+
+
+_SMALL_BF16 = dict(n_q_heads=4, n_kv_heads=1, head_dim=64, rank=32, q_window=4, n_recent=16,
+                   n_sample=256, model="power", exponents=(0.8,))
+
+
+@pytest.mark.parametrize("top_k", [64, 1500])
+def test_long_context_key_runs_bf16(gpu_lib, top_k):
+    """More than 32 768 candidates: top-k threads own runs longer than their
+    register batch (re-read per pass); top_k = 1500 > 1024 also skips the
+    floor from the run maxima and selects over the runs themselves."""
+    w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=top_k)
+    st = _run(w, 34000, 1, 3)
+    assert st.n_checked == 3
+
+
+def test_flat_scores_tie_order_bf16(gpu_lib):
+    """Zero queries make every latent logit 0, so all pooled scores tie and
+    more than 8192 keys pass the floor (the selection runs over the thread
+    runs, not the candidate list): the picks are the first top_k candidates,
+    ties going to the lower position."""
+    kvlr = _kvlr()
+    w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=64)
+    L, steps = 10000, 3
+    prompt = synth.make_prompt(w, L=L, batch=1)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=1)
+    dec.q.zero_()
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps + 8)
+    topk = torch.empty(1, w.top_k, dtype=torch.int32, device="cuda")
+    out = torch.empty(1, w.n_q_heads, w.head_dim, device="cuda")
+    for t in range(steps):
+        print(f"  step {t}", flush=True)
+        kvlr.decode_step(kc, dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), out, topk)
+        torch.cuda.synchronize()
+        expect = np.arange(w.n_sink, w.n_sink + w.top_k)
+        assert np.array_equal(topk[0].cpu().numpy(), expect), topk[0][:8]
