@@ -2149,6 +2149,188 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
   }
 }
 
+// --------------------------------------------------------------------------
+// merge for bf16 storage: grid (H_kv, U), 256 threads.  Same combination as
+// k_merge; the selected-row partials are read as 16-byte vectors (thread t:
+// coefficients 4 (t % 64) .. + 3 of heads t / 64 and t / 64 + 4), and
+// B^V_h (sum_sel f ylat) runs on MFMA 16x16x32: A = 16 channels of B^V_h
+// straight from memory (K = coefficient index), B = the G head vectors as
+// bf16 hi + lo pairs (two MFMAs, ~16 mantissa bits), D = channels x heads.
+// Wave w takes the channel tiles w, w + 4, ...
+// --------------------------------------------------------------------------
+constexpr int kMergeCT = 4;  // channel tiles per wave (head_dim <= 256)
+__global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeWs w,
+                                                    float* __restrict__ out) {
+  const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int l = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = l & 15, kq = l >> 4;
+  const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
+  const int nst = w.nsl + w.nse;
+  const int nks = r / 32, nct = (dh + 15) / 16;
+  extern __shared__ __attribute__((aligned(16))) float smf[];
+  float* ys = smf;                 // [G][r]
+  float* oe = ys + G * r;          // [G][dh] exact-row part of the output
+  float* fs = oe + G * dh;         // [G][nst]
+  float* Lg = fs + G * nst;        // [8]
+  float* stl = Lg + 8;             // [G][nst][2]
+  // ---- loads that do not need the unit state go out first
+  const int32_t* si = w.stepinfo + 4 * u;
+  const int full = si[2], Lcur = si[0];
+  const float* stb = w.astat + ((int64_t)u * nst * Hq + h * G) * 2;
+  float2 stv[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int x = min(tid + 256 * t, G * nst - 1);
+    stv[t] = *reinterpret_cast<const float2*>(stb + ((int64_t)(x % nst) * Hq + x / nst) * 2);
+  }
+  // selected-row partials: coefficients i4 .. i4 + 3 of heads gq and gq + 4,
+  // first 8 splits
+  const int i4 = min(4 * l, r - 4), gq = tid >> 6;
+  const float* ylb = w.ylat + ((int64_t)u * w.nsl * Hq + h * G) * r + i4;
+  const int nsl1 = max(w.nsl, 1);
+  f32x4 yv[8][2];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      yv[t][e] = *reinterpret_cast<const f32x4*>(
+          ylb + ((int64_t)min(t, nsl1 - 1) * Hq + min(gq + 4 * e, G - 1)) * r);
+  const float* yeb = w.yex + ((int64_t)u * w.nse * Hq + h * G) * dh;
+  float ev[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int x = min(tid + 256 * m, G * dh - 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ev[m][e] = yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh];
+  }
+  // B^V_h fragments: channel tile ct = wv + 4 m, rows clamped into the head
+  const uint16_t* bbase = (const uint16_t*)c.basis_v + ((int64_t)u * d.D + (int64_t)h * dh) * r;
+  bf16x8 bfr[kMergeCT][8];
+#pragma unroll
+  for (int m = 0; m < kMergeCT; ++m) {
+    const int ch = min((wv + 4 * m) * 16 + n16, dh - 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      if (wv + 4 * m < nct && ks < nks) bfr[m][ks] = ld_bf16x8(bbase + (int64_t)ch * r + 32 * ks + 8 * kq);
+  }
+  if (full) return;  // the top-k kernel wrote zeros
+  const int nc = Lcur + 1 - d.nrec - d.s;
+  const int kk = max(0, min(d.k, nc));
+  const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
+  for (int t = 0; t * 256 < G * nst; ++t) {
+    const int x = tid + 256 * t;
+    if (x < G * nst) {
+      const int sp = x % nst;
+      const bool ran = sp < nl || sp >= w.nsl;
+      float2 v = t < 2 ? stv[t] : *reinterpret_cast<const float2*>(stb + ((int64_t)sp * Hq + x / nst) * 2);
+      stl[2 * ((x / nst) * nst + sp)] = ran ? v.x : -INFINITY;
+      stl[2 * ((x / nst) * nst + sp) + 1] = ran ? v.y : 0.f;
+    }
+  }
+  __syncthreads();
+  // per head (a wave each): M = max over splits, f = 2^(m - M), L = sum f S
+  for (int g = wv; g < G; g += 4) {
+    float mx[1] = {-INFINITY};
+    for (int sp = l; sp < nst; sp += 64) mx[0] = fmaxf(mx[0], stl[2 * (g * nst + sp)]);
+    wave_max_n<1>(mx);
+    float L[1] = {0.f};
+    for (int sp = l; sp < nst; sp += 64) {
+      const float m = stl[2 * (g * nst + sp)];
+      const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx[0]);
+      fs[g * nst + sp] = f;
+      L[0] += f * stl[2 * (g * nst + sp) + 1];
+    }
+    wave_sum_n<1>(L);
+    if (l == 0) Lg[g] = L[0];
+  }
+  __syncthreads();
+  // selected-row part: ys[g][i] = sum over splits of f * ylat (coefficient
+  // groups past 64 * 4 loop; splits past 8 are read here)
+  for (int ib = 4 * l; ib < r; ib += 256) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int g = gq + 4 * e;
+      if (g >= G) continue;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const float* yp = w.ylat + ((int64_t)u * w.nsl * Hq + h * G + g) * r + ib;
+      int sp0 = 0;
+      if (ib == 4 * l && ib == i4) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (t < nl) acc += fs[g * nst + t] * yv[t][e];
+        sp0 = 8;
+      }
+      for (int sp = sp0; sp < nl; ++sp)
+        acc += fs[g * nst + sp] * *reinterpret_cast<const f32x4*>(yp + (int64_t)sp * Hq * r);
+      *reinterpret_cast<f32x4*>(ys + g * r + ib) = acc;
+    }
+  }
+  // exact-row part: oe[g][ch] = sum over exact splits of f * yex
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int x = tid + 256 * m;
+    if (x < G * dh) {
+      const int g = x / dh;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < w.nse) acc += fs[g * nst + w.nsl + e] * ev[m][e];
+      for (int e = 4; e < w.nse; ++e)
+        acc += fs[g * nst + w.nsl + e] * yeb[((int64_t)e * Hq + g) * dh + x % dh];
+      oe[x] = acc;
+    }
+  }
+  for (int x = tid + 1024; x < G * dh; x += 256) {
+    const int g = x / dh;
+    float acc = 0.f;
+    for (int e = 0; e < w.nse; ++e)
+      acc += fs[g * nst + w.nsl + e] * yeb[((int64_t)e * Hq + g) * dh + x % dh];
+    oe[x] = acc;
+  }
+  __syncthreads();
+  // B operands (shared by the wave's channel tiles): head n16's coefficients
+  // 32 ks + 8 kq .. + 7 as bf16 hi / lo
+  bf16x8 bh[8], bl[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks < nks && n16 < G) {
+      const float* yr = ys + n16 * r + 32 * ks + 8 * kq;
+      split8(*reinterpret_cast<const f32x4*>(yr), *reinterpret_cast<const f32x4*>(yr + 4), &bh[ks], &bl[ks]);
+    } else {
+      bh[ks] = __builtin_bit_cast(bf16x8, u16x8{});
+      bl[ks] = bh[ks];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kMergeCT; ++m) {
+    const int ct = wv + 4 * m;
+    if (ct >= nct) break;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < nks) {
+        acc = mfma16x16x32(bfr[m][ks], bh[ks], acc);
+        acc = mfma16x16x32(bfr[m][ks], bl[ks], acc);
+      }
+    }
+    // lane: channels ct * 16 + 4 kq + i, head n16
+    const int ch0 = ct * 16 + 4 * kq;
+    if (n16 < G && ch0 < dh) {
+      const float inv = 1.f / Lg[n16];
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (acc[i] + oe[n16 * dh + ch0 + i]) * inv;
+      float* op = out + ((int64_t)u * Hq + h * G + n16) * dh + ch0;
+      if (ch0 + 4 <= dh) {
+        *reinterpret_cast<f32x4*>(op) = o;
+      } else {
+        for (int i = 0; i < dh - ch0; ++i) op[i] = o[i];
+      }
+    }
+  }
+}
+
 static size_t merge_lds(const Dims& d, const DecodeWs& w) {
   return ((size_t)d.G * (d.r + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
@@ -2218,7 +2400,12 @@ static hipError_t launch_merge_t(const Dims& d, int U, const CachePtrs& c, const
 hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, float* out,
                         hipStream_t st) {
   if (d.dtype == 0) return launch_merge_t<float>(d, U, c, w, out, st);
-  return launch_merge_t<uint16_t>(d, U, c, w, out, st);
+  static size_t done = 0;
+  const size_t lds = merge_lds(d, w);
+  hipError_t e = allow_lds(&k_merge_mfma, lds, &done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_merge_mfma, dim3(d.Hkv, U), dim3(256), lds, st, d, c, w, out);
+  return hipGetLastError();
 }
 
 }  // namespace kvlr
