@@ -1807,6 +1807,148 @@ __device__ __forceinline__ void split8(f32x4 p0, f32x4 p1, bf16x8* hi, bf16x8* l
   *lo = __builtin_bit_cast(bf16x8, pl);
 }
 
+// Exact rows for bf16 storage: the logits on MFMA 16x16x32 (A = the G
+// query rows of KV head h, bf16 and exact, zero past G; B = the K rows,
+// K = channels, read straight from memory; D = heads x rows), the softmax
+// reduced over each 16-lane row of the wave, the values as in attend_exact.
+__device__ __forceinline__ void attend_exact_mfma(const Dims& d, const CachePtrs& c, const DecodeWs& w,
+                                                  const uint16_t* __restrict__ q, float ascale, int be,
+                                                  int u, int tid, float* smf) {
+  const int wv = tid >> 6, l = tid & 63, Hq = d.Hq;
+  const int n16 = l & 15, kq = l >> 4;
+  const int nhq = (d.Hkv + 3) >> 2;
+  const int e = be / nhq, h = (be % nhq) * 4 + wv;
+  const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
+  const int row0 = e * w.rse;
+  const int nrow = min(w.rse, s + nrec - row0);
+  if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
+  constexpr int VEC = 8;
+  const int ldv = dh + VEC;                        // padded LDS row (storage elements)
+  float* pw = smf + wv * exact_wave_floats(G, dh, 2) + G * dh;  // [32][8] probabilities
+  uint16_t* vs = reinterpret_cast<uint16_t*>(pw + 32 * 8);       // [32][ldv] value rows
+  auto rowptr = [&](const void* sink, const void* ring, int rr) {
+    const int64_t roff = rr < s ? ((int64_t)u * s + rr) * D : ((int64_t)u * nrec + (rr - s)) * D;
+    return (rr < s ? (const uint16_t*)sink : (const uint16_t*)ring) + roff + (int64_t)h * dh;
+  };
+  const int nks = dh / 32;  // head_dim multiple of 32 here
+  // B: K row 16 t + n16 (clamped to the last row), channels 32 ks + 8 kq
+  bf16x8 kb[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* kr = rowptr(c.sink_k, c.ring_k, row0 + min(16 * t + n16, nrow - 1));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      if (ks < nks) kb[t][ks] = ld_bf16x8(kr + 32 * ks + 8 * kq);
+  }
+  // A: query head h G + n16 (zero past G)
+  bf16x8 qa[8];
+  {
+    const uint16_t* qh = q + ((int64_t)u * Hq + h * G + min(n16, G - 1)) * dh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      if (ks < nks) qa[ks] = n16 < G ? ld_bf16x8(qh + 32 * ks + 8 * kq) : __builtin_bit_cast(bf16x8, u16x8{});
+  }
+  // V rows to LDS: piece x = l + 64 i of (row, 16-byte chunk); all loads
+  // first (clamped), then the stores (rows <= 32, d_h <= 256: <= 16 each)
+  const int npc = dh / VEC;
+  u16x8 vp[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int x = min(l + 64 * i, nrow * npc - 1);
+    vp[i] = *reinterpret_cast<const u16x8*>(rowptr(c.sink_v, c.ring_v, row0 + x / npc) + (x % npc) * VEC);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int x = l + 64 * i;
+    if (x < nrow * npc) *reinterpret_cast<u16x8*>(vs + (x / npc) * ldv + (x % npc) * VEC) = vp[i];
+  }
+  // logits: lane holds heads 4 kq + i, rows 16 t + n16
+  f32x4 z[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    z[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      if (ks < nks) z[t] = mfma16x16x32(qa[ks], kb[t][ks], z[t]);
+  }
+  float m[4], S[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float z0 = n16 < nrow ? z[0][i] * ascale : -INFINITY;
+    const float z1 = 16 + n16 < nrow ? z[1][i] * ascale : -INFINITY;
+    float mx = fmaxf(z0, z1);
+    mx = fmaxf(mx, dpp_f<0xB1>(mx));
+    mx = fmaxf(mx, dpp_f<0x4E>(mx));
+    mx = fmaxf(mx, dpp_f<0x141>(mx));
+    mx = fmaxf(mx, dpp_f<0x140>(mx));
+    m[i] = mx;
+    const float p0 = n16 < nrow ? __builtin_amdgcn_exp2f(z0 - mx) : 0.f;
+    const float p1 = 16 + n16 < nrow ? __builtin_amdgcn_exp2f(z1 - mx) : 0.f;
+    if (kq < 2) {
+      pw[n16 * 8 + 4 * kq + i] = p0;
+      pw[(16 + n16) * 8 + 4 * kq + i] = p1;
+    }
+    float sm = p0 + p1;
+    sm += dpp_f<0xB1>(sm);
+    sm += dpp_f<0x4E>(sm);
+    sm += dpp_f<0x141>(sm);
+    sm += dpp_f<0x140>(sm);
+    S[i] = sm;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // V rows and probabilities are in LDS
+  __builtin_amdgcn_wave_barrier();
+  // values: lane l holds channel pairs c = 2 l + 128 i, i < 2 (d_h <= 256)
+  float o[8][4];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[g][i] = 0.f;
+  const int c0 = min(2 * l, dh - 2), c1 = min(2 * l + 128, dh - 2);
+#pragma unroll 4
+  for (int j = 0; j < nrow; ++j) {
+    const uint16_t* vj = vs + j * ldv;
+    const float v0 = bf2f(vj[c0]), v1 = bf2f(vj[c0 + 1]);
+    const float v2 = bf2f(vj[c1]), v3 = bf2f(vj[c1 + 1]);
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(pw + j * 8);
+    const f32x4 pb = G > 4 ? *reinterpret_cast<const f32x4*>(pw + j * 8 + 4) : f32x4{};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float p = g < 4 ? pa[g] : pb[g - 4];
+      o[g][0] += p * v0;
+      o[g][1] += p * v1;
+      o[g][2] += p * v2;
+      o[g][3] += p * v3;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      const int a = h * G + g;
+      float* yo = w.yex + (((int64_t)u * w.nse + e) * Hq + a) * dh;
+      if (2 * l < dh) {
+        yo[2 * l] = o[g][0];
+        yo[2 * l + 1] = o[g][1];
+      }
+      if (2 * l + 128 < dh) {
+        yo[2 * l + 128] = o[g][2];
+        yo[2 * l + 129] = o[g][3];
+      }
+    }
+  }
+  // statistics: lane (n16 = 0, kq) holds heads 4 kq + i
+  if (n16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kq + i;
+      if (g < G) {
+        float* stp = w.astat + (((int64_t)u * (w.nsl + w.nse) + w.nsl + e) * Hq + h * G + g) * 2;
+        stp[0] = m[i];
+        stp[1] = S[i];
+      }
+    }
+  }
+}
+
 template <int R>
 __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, DecodeWs w,
                                                      const uint16_t* __restrict__ q, float ascale) {
@@ -1819,7 +1961,10 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   extern __shared__ __attribute__((aligned(16))) float smf[];
   if (b >= w.nsl * w.nhg) {
-    attend_exact<uint16_t>(d, c, w, q, ascale, b - w.nsl * w.nhg, u, tid, smf);
+    if (d.dh % 32 == 0)
+      attend_exact_mfma(d, c, w, q, ascale, b - w.nsl * w.nhg, u, tid, smf);
+    else
+      attend_exact<uint16_t>(d, c, w, q, ascale, b - w.nsl * w.nhg, u, tid, smf);
     return;
   }
   uint8_t* lds = reinterpret_cast<uint8_t*>(smf);
@@ -1836,6 +1981,13 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
     const int j = min(tid + 256 * i, NPC - 1) / KC;
     selv[i] = w.topk[(int64_t)u * d.k + min(row0 + j, d.k - 1)];
   }
+  // V pieces: lane l of wave wv takes rows 4 (l % 16) + {0..3} and chunks
+  // 4 wv + l / 16 + 16 p, so the transposed stores below are 8-byte writes
+  // of four rows that spread over the banks
+  const int vjg = l & 15, vcl = l >> 4;
+  int selr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) selr[q] = w.topk[(int64_t)u * d.k + min(row0 + 4 * vjg + q, d.k - 1)];
   const int ht = wv >> 1, rt0 = 2 * (wv & 1);
   const int ah = min(a0 + 16 * ht + n16, Hq - 1);  // heads past H_q repeat the last one
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(w.qlat) + ((int64_t)u * Hq + ah) * 2 * R;
@@ -1854,14 +2006,23 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
   {
     const uint16_t* cks = (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * R;
     const uint16_t* cvs = (const uint16_t*)c.coef_v + (int64_t)u * c.Lmax * R;
-    u16x8 xk[NP], xv[NP];
+    constexpr int NVP = (KC + 15) / 16;  // V chunk passes
+    u16x8 xk[NP], xv[NVP][4];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int e = min(tid + 256 * i, NPC - 1);
       const int cc = e % KC;
       const int64_t pos = min(max((int64_t)selv[i], (int64_t)0), c.Lmax - 1);
       xk[i] = *reinterpret_cast<const u16x8*>(cks + pos * R + cc * 8);
-      xv[i] = *reinterpret_cast<const u16x8*>(cvs + pos * R + cc * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < NVP; ++p) {
+      const int cc = min(4 * wv + vcl + 16 * p, KC - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t pos = min(max((int64_t)selr[q], (int64_t)0), c.Lmax - 1);
+        xv[p][q] = *reinterpret_cast<const u16x8*>(cvs + pos * R + cc * 8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -1869,10 +2030,21 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
       if (e < NPC) {
         const int j = e / KC, cc = e % KC;
         *reinterpret_cast<u16x8*>(lds + Lay::ck + j * Lay::CKB + cc * 16) = xk[i];
-        const u16x8 v = j < nrow ? xv[i] : u16x8{};
+      }
+    }
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          *reinterpret_cast<uint16_t*>(lds + Lay::cv + (cc * 8 + x) * Lay::CVB + j * 2) = v[x];
+    for (int p = 0; p < NVP; ++p) {
+      const int cc = 4 * wv + vcl + 16 * p;
+      if (cc < KC) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * vjg + q >= nrow) xv[p][q] = u16x8{};
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const uint32_t lo = (uint32_t)xv[p][0][x] | ((uint32_t)xv[p][1][x] << 16);
+          const uint32_t hi = (uint32_t)xv[p][2][x] | ((uint32_t)xv[p][3][x] << 16);
+          *reinterpret_cast<uint2*>(lds + Lay::cv + (cc * 8 + x) * Lay::CVB + 8 * vjg) = make_uint2(lo, hi);
+        }
       }
     }
   }
