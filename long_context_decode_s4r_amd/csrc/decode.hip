@@ -1778,15 +1778,19 @@ struct AttnTile {
   static constexpr int CKB = R * 2 + 16;           // bytes per staged K row
   static constexpr int CVB = kAttnRows * 2 + 16;   // bytes per transposed V row
   static constexpr int ZLD = kAttnRows + 1, PLD = kAttnRows + 4;  // fp32 strides
+  // the logits and probabilities reuse the K rows' space once the logit
+  // MFMAs are done (a block barrier separates them), so two blocks fit a CU
   static constexpr int ck = 0;
-  static constexpr int cv = ck + kAttnRows * CKB;
-  static constexpr int zs = cv + R * CVB;
+  static constexpr int zs = 0;
   static constexpr int pz = zs + ((32 * ZLD * 4 + 15) & ~15);
-  static constexpr int bytes = pz + 32 * PLD * 4;
+  static constexpr int kz = kAttnRows * CKB > pz + 32 * PLD * 4 ? kAttnRows * CKB : pz + 32 * PLD * 4;
+  static constexpr int cv = (kz + 15) & ~15;
+  static constexpr int bytes = cv + R * CVB;
 };
 static int attn_tile_bytes(int r) {
-  return kAttnRows * (r * 2 + 16) + r * (kAttnRows * 2 + 16) + ((32 * (kAttnRows + 1) * 4 + 15) & ~15) +
-         32 * (kAttnRows + 4) * 4;
+  const int kb = kAttnRows * (r * 2 + 16);
+  const int zp = ((32 * (kAttnRows + 1) * 4 + 15) & ~15) + 32 * (kAttnRows + 4) * 4;
+  return ((kb > zp ? kb : zp) + 15) / 16 * 16 + r * (kAttnRows * 2 + 16);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -2064,6 +2068,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
       acc0 = mfma16x16x32(alo[ks], b0, acc0);
       acc1 = mfma16x16x32(alo[ks], b1, acc1);
     }
+    __syncthreads();  // every wave is done with the K rows: zs takes their space
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       zs[(16 * ht + 4 * kg + i) * Lay::ZLD + 16 * rt0 + n16] = acc0[i];
