@@ -242,7 +242,10 @@ def main():
         ms_graph = timed(lambda n: [g.replay() for _ in range(n)], reps) / graph_steps
     except Exception as ex:  # graph capture unavailable: eager numbers only
         log(f"[bench] graph capture failed: {ex}")
-    ms = ms_graph if ms_graph is not None else ms_eager
+    # the faster of the two launch modes is the step time (both are reported);
+    # on this ROCm a replayed graph leaves ~5 us between kernel nodes
+    use_graph = ms_graph is not None and ms_graph < ms_eager
+    ms = ms_graph if use_graph else ms_eager
     # (c) stage timing: HIP events recorded by the library between its launches
     kvlr.profile_enable(True)
     for i in range(args.steps):
@@ -275,7 +278,7 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
-        "timing": "hip_graph_replay" if ms_graph is not None else "eager",
+        "timing": "hip_graph_replay" if use_graph else "eager",
         "algorithmic_bytes": {"scan_per_launch": int(scan_bytes), "step": int(step_bytes)},
     }
     if not args.no_prefill:

@@ -1257,29 +1257,28 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
     const int bits = rg == 0u ? 0 : 32 - __clz((int)rg);
     return max(bits - kTopkBinBits, 0);
   };
-  // 1. floor from the per-thread maxima: wave w's q-th largest maximum m_w
-  //    (q = ceil(kk / 16)); every wave has q runs holding a key >= min_w m_w,
-  //    so at least 16 q >= kk keys are >= that minimum
+  // 1. floor: with kk <= 1024, the kk-th largest per-thread maximum is <=
+  //    the kk-th largest key (kk runs each hold a key at least that large),
+  //    and so is the lower edge of its histogram bin.  Maxima that cluster
+  //    in a bin would serialize on its atomic, so each wave first peels off
+  //    up to four groups of lanes sharing a bin (one ballot and one atomic
+  //    each); the remaining lanes add their own.
   if (kk <= kTopkThreads) {
-    // bitwise radix select over the lanes: the answer's bits from the top;
-    // `need` counts down the rank still to find below the decided prefix
-    int need = (kk + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
-    unsigned int mw = 0u;
-    for (int b = 31; b >= 0; --b) {
-      const unsigned int want = (mw >> b) | 1u;
-      const int cnt = __popcll(__ballot((tmax >> b) == want));
-      if (cnt >= need) {
-        mw |= 1u << b;
-      } else {
-        need -= cnt;
-      }
+    const int vsh = range_shift(lo, hi);
+    const unsigned int vb = (tmax > lo ? tmax - lo : 0u) >> vsh;
+    uint64_t rest = __ballot(true);
+    for (int it = 0; it < 4 && rest; ++it) {
+      const int ld = __builtin_ctzll(rest);
+      const unsigned int bl = (unsigned int)__builtin_amdgcn_readlane((int)vb, ld);
+      const uint64_t m = __ballot(vb == bl) & rest;
+      if (lane == ld) atomicAdd(&hs[bl], (unsigned int)__popcll(m));
+      rest &= ~m;
     }
-    if (lane == 0) wlo[wid] = mw;
+    if ((rest >> lane) & 1u) atomicAdd(&hs[vb], 1u);  // the spread remainder
     __syncthreads();
-    unsigned int fl = wlo[0];
-#pragma unroll
-    for (int i = 1; i < kTopkThreads / 64; ++i) fl = min(fl, wlo[i]);
-    lo = max(lo, fl);
+    topk_find_bin(hs, kTopkBins, kk, wtot, &sh_bin, &sh_rem, &sh_cnt);
+    lo = lo + (sh_bin << vsh);
+    for (int i = tid; i < kTopkBins; i += kTopkThreads) hs[i] = 0u;
   }
   // 2. candidates: keys >= lo, counted, then listed in position order
   int ccount = 0;
