@@ -101,6 +101,22 @@ void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
 }
 
 __device__ __forceinline__ int wrap_slot(int x, int W) { return ((x % W) + W) % W; }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Kernels that may need more than the default 64 KB of dynamic LDS get the
+// limit raised once (gfx950 has 160 KB of LDS per CU).
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t lds, size_t* done) {
+  if (lds <= 65536 || lds <= *done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) *done = lds;
+  return e;
+}
+
 __device__ __forceinline__ int wv_of(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
 __device__ __forceinline__ int l_of(int tid) { return tid & 63; }
 
@@ -137,6 +153,72 @@ template <> struct Vec16<uint16_t> {
 // reads 16 bytes of a basis row per iteration (rows rg, rg + 64, ...);
 // partial sums are reduced over row groups with lane shuffles and LDS.
 // --------------------------------------------------------------------------
+// state block of the prologue: exact ring push of k and v; the older window
+// rows' (m, S) updated with the candidate entering the compressed set
+template <typename T>
+__device__ __forceinline__ void prologue_state(const Dims& d, const CachePtrs& c, const T* __restrict__ kn,
+                                               const T* __restrict__ vn, float qscale, int u, int tid,
+                                               int32_t Lcur, int32_t steps, float* sm) {
+  constexpr int VEC = Vec16<T>::N;
+  const int D = d.D, r = d.r, G = d.G, W = d.W;
+  const int64_t p = Lcur;
+  {  // exact ring push, 16-byte pieces, loads before stores
+    const int rs = (int)(p % d.nrec);
+    constexpr int NP = (4096 / VEC + 255) / 256;  // D <= 4096
+    u16x8 bk[NP], bv[NP];
+    const int np = D / VEC;
+    const u16x8* sk = reinterpret_cast<const u16x8*>(kn + (int64_t)u * D);
+    const u16x8* sv = reinterpret_cast<const u16x8*>(vn + (int64_t)u * D);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = min(tid + 256 * i, np - 1);
+      bk[i] = sk[pc];
+      bv[i] = sv[pc];
+    }
+    u16x8* dk = reinterpret_cast<u16x8*>((T*)c.ring_k + ((int64_t)u * d.nrec + rs) * D);
+    u16x8* dv = reinterpret_cast<u16x8*>((T*)c.ring_v + ((int64_t)u * d.nrec + rs) * D);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + 256 * i;
+      if (pc < np) {
+        dk[pc] = bk[i];
+        dv[pc] = bv[i];
+      }
+    }
+  }
+  const int weff = min(steps + 1, W);
+  const int nold = (weff - 1) * G;
+  if (nold <= 0) return;
+  float* ce = sm;  // [r]
+  const int64_t pe = (int64_t)Lcur - d.nrec;  // candidate entering the compressed set
+  const T* cep = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pe) * r;
+  for (int i = tid; i < r; i += 256) ce[i] = Elem<T>::ld(cep, i);
+  __syncthreads();
+  for (int o0 = 0; o0 < nold; o0 += 64) {
+    const int o = o0 + (tid >> 2), part = tid & 3;
+    float z = 0.f;
+    int sl = 0, g = 0;
+    if (o < nold) {
+      const int i = 1 + o / G;
+      g = o % G;
+      sl = wrap_slot(steps - i, W);
+      const float* qr = c.qwin + (((int64_t)u * W + sl) * G + g) * r;
+#pragma unroll 16
+      for (int kk = part; kk < r; kk += 4) z += qr[kk] * ce[kk];
+    }
+    z += __shfl_xor(z, 1);
+    z += __shfl_xor(z, 2);
+    if (o < nold && part == 0) {
+      z *= qscale;
+      float* rsp = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
+      const float m = rsp[0], S = rsp[1];
+      const float mn = fmaxf(m, z);
+      rsp[0] = mn;
+      rsp[1] = S * exp2f(m - mn) + exp2f(z - mn);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* __restrict__ q,
                                                   const T* __restrict__ kn,
@@ -362,62 +444,200 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
     }
     return;
   }
-  // ---- state block ----
-  {  // exact ring push, 16-byte pieces, loads before stores
-    const int rs = (int)(p % d.nrec);
-    constexpr int NP = (4096 / VEC + 255) / 256;  // D <= 4096
-    u16x8 bk[NP], bv[NP];
-    const int np = D / VEC;
-    const u16x8* sk = reinterpret_cast<const u16x8*>(kn + (int64_t)u * D);
-    const u16x8* sv = reinterpret_cast<const u16x8*>(vn + (int64_t)u * D);
+  prologue_state<T>(d, c, kn, vn, qscale, u, tid, Lcur, steps, sm);
+}
+
+// --------------------------------------------------------------------------
+// prologue for bf16 storage: the same blocks as k_prologue, the products on
+// MFMA 16x16x32.  The inputs (k, v and the query heads) are bf16 and so exact
+// as operands; A = up to 16 input vectors straight from memory (K = basis
+// row index), B = basis columns, which are staged through LDS transposed
+// ([column][row], four rows per 8-byte write) so an operand is one 16-byte
+// read.  The unit state is needed only by the stores, so its load overlaps
+// the whole computation.
+//   GEMV block (32 columns of B^K or B^V): rows in chunks of kProRows; wave
+//     w takes k-steps 8 w .. 8 w + 7 of each chunk, the four waves' partial
+//     sums meet in LDS;
+//   projected-query block (KV head h): the d_h rows of head h, all r
+//     columns; wave w takes column tiles w, w + 4, ...
+// --------------------------------------------------------------------------
+constexpr int kProRows = 1024;
+constexpr int kProLdb = kProRows + 8;  // staged column length (bf16), padded
+
+__device__ __forceinline__ void stage_quad_t(uint16_t* bt, int ldb, int col, int row, const u16x8 (&v)[4]) {
+  // rows row .. row + 3 of the 8 columns col .. col + 7, written transposed
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pc = min(tid + 256 * i, np - 1);
-      bk[i] = sk[pc];
-      bv[i] = sv[pc];
+  for (int x = 0; x < 8; ++x) {
+    const uint32_t lo = (uint32_t)v[0][x] | ((uint32_t)v[1][x] << 16);
+    const uint32_t hi = (uint32_t)v[2][x] | ((uint32_t)v[3][x] << 16);
+    *reinterpret_cast<uint2*>(bt + (col + x) * ldb + row) = make_uint2(lo, hi);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ kn,
+                                                       const uint16_t* __restrict__ vn, DecodeWs w,
+                                                       float qscale, float ascale, int ncb) {
+  const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int l = tid & 63, wv = tid >> 6, n16 = l & 15, kq = l >> 4;
+  const int D = d.D, r = d.r, G = d.G, W = d.W, dh = d.dh, Hq = d.Hq;
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
+  if (b == 0 && tid == 0) {
+    w.stepinfo[4 * u + 0] = Lcur;
+    w.stepinfo[4 * u + 1] = steps;
+    w.stepinfo[4 * u + 2] = (int64_t)Lcur >= c.Lmax ? 1 : 0;
+    w.stepinfo[4 * u + 3] = 0;
+  }
+  if (b == 2 * ncb) {
+    if ((int64_t)Lcur >= c.Lmax) return;
+    prologue_state<uint16_t>(d, c, kn, vn, qscale, u, tid, Lcur, steps, sm);
+    return;
+  }
+  uint16_t* bt = reinterpret_cast<uint16_t*>(sm);
+  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u16x8{});
+  if (b < 2 * ncb) {
+    const int kind = b >= ncb ? 1 : 0;
+    const int col0 = (kind ? b - ncb : b) * 32;
+    const int nvec = kind == 0 ? 1 + G : 1;
+    const uint16_t* B = (const uint16_t*)(kind ? c.basis_v : c.basis_k) + (int64_t)u * D * r;
+    float* red = sm + 32 * kProLdb / 2;  // [4 waves][16][32]
+    const int cq = tid & 3, a4 = 4 * (tid >> 2);
+    const int colq = min(col0 + 8 * cq, r - 8);  // columns past r: computed, not stored
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int r0 = 0; r0 < D; r0 += kProRows) {
+      u16x8 pc[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          pc[j][qq] = *reinterpret_cast<const u16x8*>(
+              B + (int64_t)min(r0 + a4 + 256 * j + qq, D - 1) * r + colq);
+      // A: input vector n16 (0: k or v, 1 + g: the query heads of group g,
+      // concatenated over the KV heads), elements kk .. kk + 7
+      bf16x8 xa[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int kk = r0 + 32 * (8 * wv + ks) + 8 * kq;
+        xa[ks] = zero8;
+        if (n16 < nvec && kk < D) {
+          const uint16_t* src = n16 == 0 ? (kind ? vn : kn) + (int64_t)u * D + kk
+                                         : q + ((int64_t)u * Hq + (kk / dh) * G + (n16 - 1)) * dh + kk % dh;
+          xa[ks] = ld_bf16x8(src);
+        }
+      }
+      if (r0 > 0) __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+      for (int j = 0; j < 4; ++j) stage_quad_t(bt, kProLdb, 8 * cq, a4 + 256 * j, pc[j]);
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int kr = 32 * (8 * wv + ks);
+        if (r0 + kr < D) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * t + n16) * kProLdb + kr + 8 * kq);
+            acc[t] = mfma16x16x32(xa[ks], bo, acc[t]);
+          }
+        }
+      }
     }
-    u16x8* dk = reinterpret_cast<u16x8*>((T*)c.ring_k + ((int64_t)u * d.nrec + rs) * D);
-    u16x8* dv = reinterpret_cast<u16x8*>((T*)c.ring_v + ((int64_t)u * d.nrec + rs) * D);
+    // the waves' partial sums: lane holds vectors 4 kq + i, columns 16 t + n16
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pc = tid + 256 * i;
-      if (pc < np) {
-        dk[pc] = bk[i];
-        dv[pc] = bv[i];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wv * 16 + 4 * kq + i) * 32 + 16 * t + n16] = acc[t][i];
+    __syncthreads();
+    if ((int64_t)Lcur >= c.Lmax) return;
+    const int64_t p = Lcur;
+    for (int o = tid; o < nvec * 32; o += 256) {
+      const int v = o >> 5, cc = o & 31, cl = col0 + cc;
+      if (cl >= r) continue;
+      const float sum = (red[v * 32 + cc] + red[(16 + v) * 32 + cc]) +
+                        (red[(32 + v) * 32 + cc] + red[(48 + v) * 32 + cc]);
+      if (v == 0) {
+        uint16_t* C = (uint16_t*)(kind == 0 ? c.coef_k : c.coef_v);
+        C[((int64_t)u * c.Lmax + p) * r + cl] = f2bf(sum);
+      } else {
+        const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
+        c.qwin[row * r + cl] = sum;
+        const float x = sum * qscale;  // MFMA operands of the latent scoring
+        const uint16_t hb = f2bf(x);
+        c.qsplit[(row * 2 + 0) * r + cl] = hb;
+        c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
+      }
+    }
+    return;
+  }
+  // ---- projected queries: qlat[h G + g] = ascale * q[h G + g] . B^K rows of head h
+  const int h = b - 2 * ncb - 1;
+  const int ldq = dh + 8;
+  const uint16_t* B = (const uint16_t*)c.basis_k + ((int64_t)u * D + (int64_t)h * dh) * r;
+  const int nqc = (dh / 4) * (r / 8);  // (row quad, column chunk) items
+  for (int i0 = 0; i0 < nqc; i0 += 4 * 256) {
+    u16x8 pc[4][4];
+    // item it: row quad 8 (it / (8 ncc)) + it % 8, column chunk (it / 8) % ncc
+    // (eight lanes read 128 contiguous bytes of a row; the transposed writes
+    // of a wave spread over the banks)
+    const int ncc = r / 8;
+    auto quad = [&](int it) { return 4 * ((it % 8) + 8 * (it / (8 * ncc))); };
+    auto chunk = [&](int it) { return 8 * ((it / 8) % ncc); };
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int it = min(i0 + tid + 256 * m, nqc - 1);
+      const int rq = quad(it), cc = chunk(it);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        pc[m][qq] = *reinterpret_cast<const u16x8*>(B + (int64_t)(rq + qq) * r + cc);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int it = i0 + tid + 256 * m;
+      if (it < nqc) stage_quad_t(bt, ldq, chunk(it), quad(it), pc[m]);
+    }
+  }
+  // A: query head h G + n16 (zero past G), channels 32 ks + 8 kq
+  const int nks = dh / 32;
+  bf16x8 qa[8];
+  {
+    const uint16_t* qh = q + ((int64_t)u * Hq + h * G + min(n16, G - 1)) * dh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qa[ks] = (n16 < G && ks < nks) ? ld_bf16x8(qh + 32 * ks + 8 * kq) : zero8;
+  }
+  __syncthreads();
+  const bool live = (int64_t)Lcur < c.Lmax;
+  for (int tile = wv; tile < r / 16; tile += 4) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < nks) {
+        const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * tile + n16) * ldq + 32 * ks + 8 * kq);
+        acc = mfma16x16x32(qa[ks], bo, acc);
+      }
+    }
+    // lane: heads 4 kq + i, column 16 tile + n16
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * kq + i;
+        if (g < G) {
+          const float x = acc[i] * ascale;
+          uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + ((int64_t)u * Hq + h * G + g) * 2 * r + 16 * tile + n16;
+          const uint16_t hb = f2bf(x);
+          ql[0] = hb;
+          ql[r] = f2bf(x - bf2f(hb));
+        }
       }
     }
   }
-  const int weff = min(steps + 1, W);
-  const int nold = (weff - 1) * G;
-  if (nold <= 0) return;
-  float* ce = sm;  // [r]
-  const int64_t pe = (int64_t)Lcur - d.nrec;  // candidate entering the compressed set
-  const T* cep = (const T*)c.coef_k + ((int64_t)u * c.Lmax + pe) * r;
-  for (int i = tid; i < r; i += 256) ce[i] = Elem<T>::ld(cep, i);
-  __syncthreads();
-  for (int o0 = 0; o0 < nold; o0 += 64) {
-    const int o = o0 + (tid >> 2), part = tid & 3;
-    float z = 0.f;
-    int sl = 0, g = 0;
-    if (o < nold) {
-      const int i = 1 + o / G;
-      g = o % G;
-      sl = wrap_slot(steps - i, W);
-      const float* qr = c.qwin + (((int64_t)u * W + sl) * G + g) * r;
-#pragma unroll 16
-      for (int kk = part; kk < r; kk += 4) z += qr[kk] * ce[kk];
-    }
-    z += __shfl_xor(z, 1);
-    z += __shfl_xor(z, 2);
-    if (o < nold && part == 0) {
-      z *= qscale;
-      float* rsp = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
-      const float m = rsp[0], S = rsp[1];
-      const float mn = fmaxf(m, z);
-      rsp[0] = mn;
-      rsp[1] = S * exp2f(m - mn) + exp2f(z - mn);
-    }
-  }
+}
+
+static size_t prologue_mfma_lds(const Dims& d) {
+  const size_t gemv = (size_t)32 * kProLdb * 2 + (size_t)4 * 16 * 32 * 4;
+  const size_t qlat = (size_t)d.r * (d.dh + 8) * 2;
+  const size_t state = (size_t)d.r * 4;
+  size_t m = gemv > qlat ? gemv : qlat;
+  return m > state ? m : state;
 }
 
 hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_new,
@@ -433,12 +653,20 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
   dim3 grid(2 * ncb + 1 + d.Hkv, U);
   const float qscale = kLog2e / sqrtf((float)d.r);
   const float ascale = kLog2e / sqrtf((float)d.dh);
-  if (d.dtype == 0)
+  if (d.dtype == 0) {
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
                        (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb);
-  else
+  } else if (d.dh % 32 == 0) {
+    static size_t done = 0;
+    const size_t lm = prologue_mfma_lds(d);
+    hipError_t e = allow_lds(&k_prologue_mfma, lm, &done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_prologue_mfma, grid, dim3(256), lm, st, d, c, (const uint16_t*)q,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
+  } else {
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
+  }
   return hipGetLastError();
 }
 
@@ -1792,9 +2020,6 @@ static int attn_tile_bytes(int r) {
   return ((kb > zp ? kb : zp) + 15) / 16 * 16 + r * (kAttnRows * 2 + 16);
 }
 
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // bf16 hi / lo pair of 8 fp32 values as MFMA operands
 __device__ __forceinline__ void split8(f32x4 p0, f32x4 p1, bf16x8* hi, bf16x8* lo) {
@@ -2511,16 +2736,6 @@ static size_t merge_lds(const Dims& d, const DecodeWs& w) {
   return ((size_t)d.G * (d.r + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
 
-// Kernels that may need more than the default 64 KB of dynamic LDS get the
-// limit raised once (gfx950 has 160 KB of LDS per CU).
-template <typename K>
-static hipError_t allow_lds(K kernel, size_t lds, size_t* done) {
-  if (lds <= 65536 || lds <= *done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e == hipSuccess) *done = lds;
-  return e;
-}
 
 template <typename T>
 static hipError_t launch_attend_t(const Dims& d, int U, const void* q, const CachePtrs& c,
