@@ -1116,21 +1116,21 @@ __device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s
 __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
                                               float* __restrict__ scores_user) {
   const int blk = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int32_t* si = w.stepinfo + 4 * u;
-  if (si[2]) return;
-  const int Lcur = si[0], steps = si[1];
   const int G = d.G, s = d.s;
-  const int nc = Lcur + 1 - d.nrec - s;
-  const int c0 = blk * kPoolChunk;
-  if (c0 >= nc && blk != 0) return;
-  const int c1 = min(c0 + kPoolChunk, nc);
   const int h = d.kappa >> 1;
+  const int c0 = blk * kPoolChunk;
+  // scores are computed in groups of 8 positions over the chunk plus the
+  // pooling halo, rounded out to whole groups: [base, base + 8 ng)
+  const int hg = (h + 7) >> 3;
+  const int base = c0 - 8 * hg, ng = kPoolChunk / 8 + 2 * hg;
   __shared__ float Mg[8], Ig[8];
   __shared__ float wm[4][8], wsum[4][8];
-  __shared__ float sc[kPoolChunk + 256];
+  __shared__ __attribute__((aligned(16))) float sc[kPoolChunk + 256];
   const int lane = tid & 63, wv = tid >> 6;
-  // the split statistics of the current rows and this block's score inputs
-  // are requested together (both need only the unit state)
+  // the split statistics of the current rows and this thread's first group
+  // of score inputs (16-byte loads, clamped to the buffer; the candidate
+  // count only masks them afterwards) go out before the unit state is read
+  const int32_t* si = w.stepinfo + 4 * u;
   const float* tp = w.tilestat + (int64_t)u * w.nsplit * G * 2;
   float2 tv[8];
   {
@@ -1139,19 +1139,27 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
     for (int g = 0; g < 8; ++g)
       tv[g] = *reinterpret_cast<const float2*>(tp + (sp * G + min(g, G - 1)) * 2);
   }
-  const bool have = c0 < nc;
   const float* part = w.partial + (int64_t)u * w.Lc_cap;
   const float* spill = w.spill + (int64_t)u * G * w.Lc_cap;
-  const int lo = max(c0 - h, 0), hi = max(min(c1 + h, nc), lo + 1);
-  constexpr int NIT = (kPoolChunk + 256) / 256;
-  float pv[NIT], sv[NIT][8];
+  auto gstart = [&](int gi) { return min(max(base + 8 * gi, 0), w.Lc_cap - 8); };
+  f32x4 pv[2], sv[8][2];
+  {
+    const int j = gstart(tid);
+    pv[0] = *reinterpret_cast<const f32x4*>(part + j);
+    pv[1] = *reinterpret_cast<const f32x4*>(part + j + 4);
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {  // clamped, unconditional loads
-    const int j = min(lo + tid + 256 * it, hi - 1);
-    pv[it] = part[j];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) sv[it][g] = spill[(int64_t)min(g, G - 1) * w.Lc_cap + j];
+    for (int g = 0; g < 8; ++g) {
+      if (g < G) {
+        sv[g][0] = *reinterpret_cast<const f32x4*>(spill + (int64_t)g * w.Lc_cap + j);
+        sv[g][1] = *reinterpret_cast<const f32x4*>(spill + (int64_t)g * w.Lc_cap + j + 4);
+      }
+    }
   }
+  if (si[2]) return;
+  const int Lcur = si[0], steps = si[1];
+  const int nc = Lcur + 1 - d.nrec - s;
+  if (c0 >= nc && blk != 0) return;
+  const int c1 = min(c0 + kPoolChunk, nc);
   {  // 1. current rows' softmax statistics over all splits: max, then the
      //    rescaled sums (splits past nsplit contribute nothing)
     const bool ok = tid < w.nsplit;
@@ -1187,35 +1195,58 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
     }
     __syncthreads();
   }
-  if (!have) return;
-  float vals[NIT];
+  if (c0 >= nc) return;
+  // 2. scores of group gi -> sc[8 gi ..]; positions outside [0, nc) are
+  //    never read as candidates
+  auto score_group = [&](int gi, const f32x4 (&p2)[2], const f32x4 (&s2)[8][2]) {
+    const int j0 = base + 8 * gi;
+    const int shift = j0 - gstart(gi);  // 0 except where the load was clamped
+    float v[8];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    float v = pv[it];
+    for (int e = 0; e < 8; ++e) {
+      float x = e < 4 ? p2[0][e] : p2[1][e - 4];
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < G) v += __builtin_amdgcn_exp2f(sv[it][g] - Mg[g]) * Ig[g];
-    vals[it] = v;
-  }
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int j = lo + tid + 256 * it;
-    if (j < hi) {
-      sc[j - lo] = vals[it];
-      if (scores_user && j >= c0 && j < c1) scores_user[(int64_t)u * c.Lmax + s + j] = vals[it];
+      for (int g = 0; g < 8; ++g)
+        if (g < G) x += __builtin_amdgcn_exp2f((e < 4 ? s2[g][0][e] : s2[g][1][e - 4]) - Mg[g]) * Ig[g];
+      v[e] = x;
     }
+    if (shift == 0) {
+      *reinterpret_cast<f32x4*>(sc + 8 * gi) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(sc + 8 * gi + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    if (scores_user && shift == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e >= c0 && j0 + e < c1) scores_user[(int64_t)u * c.Lmax + s + j0 + e] = v[e];
+    }
+  };
+  score_group(tid, pv, sv);
+  for (int gi = tid + 256; gi < ng; gi += 256) {  // the halo groups past 256
+    const int j = gstart(gi);
+    f32x4 p2[2], s2[8][2];
+    p2[0] = *reinterpret_cast<const f32x4*>(part + j);
+    p2[1] = *reinterpret_cast<const f32x4*>(part + j + 4);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g < G) {
+        s2[g][0] = *reinterpret_cast<const f32x4*>(spill + (int64_t)g * w.Lc_cap + j);
+        s2[g][1] = *reinterpret_cast<const f32x4*>(spill + (int64_t)g * w.Lc_cap + j + 4);
+      }
+    }
+    score_group(gi, p2, s2);
   }
   __syncthreads();
   uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
-  // thread t: candidates c0 + 8t .. c0 + 8t + 7 (kPoolChunk = 8 * 256)
+  // 3. thread t: candidates c0 + 8t .. c0 + 8t + 7 (kPoolChunk = 8 * 256);
+  //    sc index of position j is j - base
   const int jb = c0 + 8 * tid;
   if (jb < c1) {
     if (h <= 4) {
-      float win[16];  // sc at jb - 4 .. jb + 11, -inf outside the candidates
+      float win[16];  // scores at jb - 4 .. jb + 11, -inf outside the candidates
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = jb - 4 + e;
-        win[e] = (j >= 0 && j < nc) ? sc[min(max(j - lo, 0), kPoolChunk + 255)] : -INFINITY;
+        win[e] = (j >= 0 && j < nc) ? sc[min(max(j - base, 0), kPoolChunk + 255)] : -INFINITY;
       }
       uint32_t kv[8];
 #pragma unroll
@@ -1226,15 +1257,20 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
           if (dd <= h) mx = fmaxf(mx, fmaxf(win[e + 4 - dd], win[e + 4 + dd]));
         kv[e] = __float_as_uint(mx);
       }
+      if (jb + 8 <= c1) {
+        *reinterpret_cast<uint4*>(keys + jb) = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+        *reinterpret_cast<uint4*>(keys + jb + 4) = make_uint4(kv[4], kv[5], kv[6], kv[7]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (jb + e < c1) keys[jb + e] = kv[e];
+        for (int e = 0; e < 8; ++e)
+          if (jb + e < c1) keys[jb + e] = kv[e];
+      }
     } else {
       for (int j = jb; j < min(jb + 8, c1); ++j) {
-        float mx = sc[j - lo];
+        float mx = sc[j - base];
         for (int dd = 1; dd <= h; ++dd) {
-          if (j - dd >= 0) mx = fmaxf(mx, sc[j - dd - lo]);
-          if (j + dd < nc) mx = fmaxf(mx, sc[j + dd - lo]);
+          if (j - dd >= 0) mx = fmaxf(mx, sc[j - dd - base]);
+          if (j + dd < nc) mx = fmaxf(mx, sc[j + dd - base]);
         }
         keys[j] = __float_as_uint(mx);
       }
