@@ -149,7 +149,8 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
 }
 
 struct DecodeLayout {
-  size_t stepinfo, partial, spill, tilestat, keys, topk, qlat, ylat, yex, astat, total;
+  size_t stepinfo, partial, spill, tilestat, keys, topk, qlat, ylat, yex, astat, gmax, cslot,
+      total;
   DecodeWs t;  // tiling fields
 };
 
@@ -167,12 +168,14 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   L.partial = take((size_t)U * L.t.Lc_cap * sizeof(float));
   L.spill = take((size_t)U * d.G * L.t.Lc_cap * sizeof(float));
   L.tilestat = take((size_t)U * L.t.nsplit * d.G * 2 * sizeof(float));
-  L.keys = take(((size_t)U * L.t.Lc_cap + kKeyPad) * sizeof(uint32_t));
+  L.keys = take((size_t)U * L.t.Lc_cap * sizeof(uint32_t));
   L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
   L.qlat = take((size_t)U * d.Hq * d.r * sizeof(float));
   L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.r * sizeof(float));
   L.yex = take((size_t)U * L.t.nse * d.Hq * d.dh * sizeof(float));
   L.astat = take((size_t)U * (L.t.nsl + L.t.nse) * d.Hq * 2 * sizeof(float));
+  L.gmax = take((size_t)U * (L.t.Lc_cap / 8) * sizeof(uint32_t));
+  L.cslot = take((size_t)U * L.t.Lc_cap * 8);
   L.total = off;
   return L;
 }
@@ -370,6 +373,8 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   dw.ylat = (float*)(w + dl.ylat);
   dw.yex = (float*)(w + dl.yex);
   dw.astat = (float*)(w + dl.astat);
+  dw.gmax = (uint32_t*)(w + dl.gmax);
+  dw.cslot = (uint2*)(w + dl.cslot);
   const CachePtrs cp = cache_ptrs(cache);
   const int U = (int)n_units;
 

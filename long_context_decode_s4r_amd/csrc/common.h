@@ -191,14 +191,14 @@ hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K
 // decode
 constexpr int kHistBins = 4096;  // selection histogram over the top 12 key bits
 constexpr int kPoolChunk = 2048; // candidates per block of the pooling kernel
-constexpr int kKeyPad = 128;     // entries of slack after the last unit's keys
+constexpr int kTopkGroupCap = 8192;  // group maxima per unit read by the top-k kernel
 
 struct DecodeWs {
   int32_t* stepinfo;  // [U][4]     {tokens cached, steps taken, unit full, -}
   float* partial;     // [U][Lc_cap] score contribution of the older window rows
   float* spill;       // [U][G][Lc_cap] base-2 logits of the current rows
   float* tilestat;    // [U][nsplit][G][2] per-split (max, sum) of the current rows
-  uint32_t* keys;     // [U][Lc_cap] (+ kKeyPad slack) pooled scores as ordered bit patterns
+  uint32_t* keys;     // [U][Lc_cap] pooled scores as ordered bit patterns
   int32_t* topk;      // [U][k] selected positions, ascending
   float* qlat;        // [U][Hq][r] query heads projected onto their KV head's
                       //            slice of B^K, times log2(e)/sqrt(d_h)
@@ -206,8 +206,11 @@ struct DecodeWs {
   float* yex;         // [U][nse][Hq][dh] per split: sum_j p_j v_j (exact rows)
   float* astat;       // [U][nsl + nse][Hq][2] per split: (max, sum) of the
                       //            base-2 attention logits
+  uint32_t* gmax;     // [U][Lc_cap / 8] largest key of each group of 8 << gsh candidates
+  uint2* cslot;       // [U][Lc_cap] top-k scratch: (key, position) candidates
   // tiling (decode_tiling)
   int Lc_cap, nsplit, chunk;  // scoring: candidate capacity, splits, split length
+  int gsh;                    // top-k: groups of 8 << gsh candidates, at most kTopkGroupCap
   int nsl, nhg, hb, rsl;      // attention over selected rows: row splits, head
                               // groups, heads per group, rows per split
   int nse, rse;               // attention over exact rows: splits, rows per split

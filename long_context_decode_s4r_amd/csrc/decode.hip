@@ -92,6 +92,9 @@ void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
   // attention: selected rows in splits of rsl rows x hb heads, exact rows in
   // splits of at most 32 rows
   attend_tile(d, &w->hb, &w->rsl);
+  // top-k floor: at most kTopkGroupCap group maxima per unit
+  w->gsh = 0;
+  while (((lc + (8 << w->gsh) - 1) >> (3 + w->gsh)) > kTopkGroupCap) ++w->gsh;
   w->nhg = (d.Hq + w->hb - 1) / w->hb;
   w->nsl = (d.k + w->rsl - 1) / w->rsl;
   const int nex = d.s + d.nrec;
@@ -157,8 +160,8 @@ template <> struct Vec16<uint16_t> {
 // rows' (m, S) updated with the candidate entering the compressed set
 template <typename T>
 __device__ __forceinline__ void prologue_state(const Dims& d, const CachePtrs& c, const T* __restrict__ kn,
-                                               const T* __restrict__ vn, float qscale, int u, int tid,
-                                               int32_t Lcur, int32_t steps, float* sm) {
+                                               const T* __restrict__ vn, const DecodeWs& w, float qscale,
+                                               int u, int tid, int32_t Lcur, int32_t steps, float* sm) {
   constexpr int VEC = Vec16<T>::N;
   const int D = d.D, r = d.r, G = d.G, W = d.W;
   const int64_t p = Lcur;
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
     }
     return;
   }
-  prologue_state<T>(d, c, kn, vn, qscale, u, tid, Lcur, steps, sm);
+  prologue_state<T>(d, c, kn, vn, w, qscale, u, tid, Lcur, steps, sm);
 }
 
 // --------------------------------------------------------------------------
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, cons
   }
   if (b == 2 * ncb) {
     if ((int64_t)Lcur >= c.Lmax) return;
-    prologue_state<uint16_t>(d, c, kn, vn, qscale, u, tid, Lcur, steps, sm);
+    prologue_state<uint16_t>(d, c, kn, vn, w, qscale, u, tid, Lcur, steps, sm);
     return;
   }
   uint16_t* bt = reinterpret_cast<uint16_t*>(sm);
@@ -1101,6 +1104,22 @@ hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs
 //   3. pooled key = max over |d| <= kappa/2 inside the candidates, stored as
 //      the float's bit pattern (scores are >= 0, so bits order like values).
 // --------------------------------------------------------------------------
+// min and max over the wave (xor-pattern DPP, then the four rows), in every lane
+__device__ __forceinline__ void wave_minmax_u(unsigned int& mn, unsigned int& mx) {
+#define KVLR_MM(CTRL)                                                                          \
+  mn = min(mn, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mn, CTRL, 0xF, 0xF, false)); \
+  mx = max(mx, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mx, CTRL, 0xF, 0xF, false));
+  KVLR_MM(0xB1)
+  KVLR_MM(0x4E)
+  KVLR_MM(0x141)
+  KVLR_MM(0x140)
+#undef KVLR_MM
+  mn = min(min((unsigned int)__builtin_amdgcn_readlane((int)mn, 0), (unsigned int)__builtin_amdgcn_readlane((int)mn, 16)),
+           min((unsigned int)__builtin_amdgcn_readlane((int)mn, 32), (unsigned int)__builtin_amdgcn_readlane((int)mn, 48)));
+  mx = max(max((unsigned int)__builtin_amdgcn_readlane((int)mx, 0), (unsigned int)__builtin_amdgcn_readlane((int)mx, 16)),
+           max((unsigned int)__builtin_amdgcn_readlane((int)mx, 32), (unsigned int)__builtin_amdgcn_readlane((int)mx, 48)));
+}
+
 __device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
   if (!(s2 > 0.f)) return;
   if (!(s > 0.f)) {
@@ -1240,6 +1259,7 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
   // 3. thread t: candidates c0 + 8t .. c0 + 8t + 7 (kPoolChunk = 8 * 256);
   //    sc index of position j is j - base
   const int jb = c0 + 8 * tid;
+  unsigned int tmx = 0u;  // the largest of this thread's keys
   if (jb < c1) {
     if (h <= 4) {
       float win[16];  // scores at jb - 4 .. jb + 11, -inf outside the candidates
@@ -1256,6 +1276,9 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
         for (int dd = 1; dd <= 4; ++dd)
           if (dd <= h) mx = fmaxf(mx, fmaxf(win[e + 4 - dd], win[e + 4 + dd]));
         kv[e] = __float_as_uint(mx);
+        if (jb + e < c1) {
+          tmx = max(tmx, kv[e]);
+        }
       }
       if (jb + 8 <= c1) {
         *reinterpret_cast<uint4*>(keys + jb) = make_uint4(kv[0], kv[1], kv[2], kv[3]);
@@ -1272,10 +1295,17 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
           if (j - dd >= 0) mx = fmaxf(mx, sc[j - dd - base]);
           if (j + dd < nc) mx = fmaxf(mx, sc[j + dd - base]);
         }
-        keys[j] = __float_as_uint(mx);
+        const unsigned int kv = __float_as_uint(mx);
+        keys[j] = kv;
+        tmx = max(tmx, kv);
       }
     }
   }
+  // 4. the maximum of each group of 8 << gsh candidates (2^gsh neighbouring
+  //    threads; c0 is a multiple of the group size), for the top-k floor
+  for (int o = 1; o < (1 << w.gsh); o <<= 1) tmx = max(tmx, (unsigned int)__shfl_xor((int)tmx, o));
+  if (jb < c1 && (tid & ((1 << w.gsh) - 1)) == 0)
+    w.gmax[(int64_t)u * (w.Lc_cap >> 3) + (jb >> (3 + w.gsh))] = tmx;
 }
 
 hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
@@ -1287,16 +1317,19 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 
 // --------------------------------------------------------------------------
 // top-k: one 1024-thread block per unit.
-//   Thread t owns a contiguous run of keys (pooled scores as ordered bit
-//   patterns), kept in registers while the run fits, else re-read per pass;
-//   the register run is requested before the unit state arrives.
-//   1. Floor: with kk <= 1024 picks, the kk-th largest per-thread maximum is
-//      at most the kk-th largest key (kk threads each hold a key at least
-//      that large), and so is the lower edge of its histogram bin.
-//   2. The keys >= floor (candidates) are compacted, in position order, into
-//      an LDS list; every later pass runs over that short list with full,
-//      mostly conflict-free LDS atomics.  (More than kTopkCap candidates, or
-//      kk > 1024: the passes run over the thread runs instead.)
+//   Keys are pooled scores as ordered bit patterns.  Wave w owns a
+//   contiguous stretch of whole 256-key tiles (split by the capacity), read
+//   with coalesced 16-byte loads, the first tiles and the group maxima
+//   requested before the unit state arrives.
+//   1. Floor: the pool kernel leaves the maximum of each group of 8
+//      candidates.  Sets of disjoint groups have maxima too; if kk of them
+//      are >= x, so is the kk-th largest key.  Each wave bounds the m_w-th
+//      largest of its values from below by a bitwise search (wave ballots
+//      only), with sum_w m_w >= kk; the floor is the least of the bounds.
+//   2. The keys >= floor (candidates) are compacted per wave, in position
+//      order (one ballot per key slot of a tile), into the wave's LDS list,
+//      entries past kTopkWaveCap into the workspace; every later pass runs
+//      over those short lists with full, mostly conflict-free LDS atomics.
 //   3. Threshold T = the kk-th largest key, by a radix select over
 //      [floor, max]: 2^14-bin histograms of (key - floor) >> shift, refined
 //      until the selected bin is one key value (also when the bin turns out
@@ -1310,11 +1343,11 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 //   (topk = -1, out = 0).
 // --------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024; // 16 waves; <= 128 VGPRs per thread
-constexpr int kTopkRegKeys = 32;   // keys per thread held in registers (32 768 candidates)
+constexpr int kTopkTileRegs = 12;  // key tiles per wave held in registers (+4 VGPRs each)
+constexpr int kTopkGroupRegs = kTopkGroupCap / kTopkThreads;  // group maxima per thread
 constexpr int kTopkBinBits = 14;   // histogram digits per pass
 constexpr int kTopkBins = 1 << kTopkBinBits;
-constexpr int kTopkCap = 8192;     // candidate list capacity
-static_assert(kKeyPad >= kTopkRegKeys, "key buffer padding must cover one register run");
+constexpr int kTopkWaveCap = 512;  // candidates per wave kept in LDS
 
 template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_i(int v) {
@@ -1332,21 +1365,6 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// min and max over the wave (xor-pattern DPP, then the four rows), in every lane
-__device__ __forceinline__ void wave_minmax_u(unsigned int& mn, unsigned int& mx) {
-#define KVLR_MM(CTRL)                                                                          \
-  mn = min(mn, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mn, CTRL, 0xF, 0xF, false)); \
-  mx = max(mx, (unsigned int)__builtin_amdgcn_update_dpp(0, (int)mx, CTRL, 0xF, 0xF, false));
-  KVLR_MM(0xB1)
-  KVLR_MM(0x4E)
-  KVLR_MM(0x141)
-  KVLR_MM(0x140)
-#undef KVLR_MM
-  mn = min(min((unsigned int)__builtin_amdgcn_readlane((int)mn, 0), (unsigned int)__builtin_amdgcn_readlane((int)mn, 16)),
-           min((unsigned int)__builtin_amdgcn_readlane((int)mn, 32), (unsigned int)__builtin_amdgcn_readlane((int)mn, 48)));
-  mx = max(max((unsigned int)__builtin_amdgcn_readlane((int)mx, 0), (unsigned int)__builtin_amdgcn_readlane((int)mx, 16)),
-           max((unsigned int)__builtin_amdgcn_readlane((int)mx, 32), (unsigned int)__builtin_amdgcn_readlane((int)mx, 48)));
-}
 
 // exclusive block prefix sums of two counters (a, b); totals in *ta, *tb
 __device__ __forceinline__ int2 block_excl_scan2(int a, int b, int2* wtot, int* ta, int* tb) {
@@ -1370,34 +1388,6 @@ __device__ __forceinline__ int2 block_excl_scan2(int a, int b, int2* wtot, int* 
   *ta = sa;
   *tb = sb;
   return make_int2(ba + ia - a, bb + ib - b);
-}
-
-// apply f(key, position) to the thread's run [j0, j1) in position order, in
-// batches of kTopkRegKeys held in kr; a run of one batch stays in kr across
-// passes (in_regs), longer runs reload every batch on every pass
-template <typename F>
-__device__ __forceinline__ void for_keys(const uint32_t* keys, int j0, int j1, bool in_regs,
-                                         uint32_t* kr, F&& f) {
-  if (in_regs && j1 - j0 == kTopkRegKeys) {  // a full register run: no bound checks
-#pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i) f(kr[i], j0 + i);
-    return;
-  }
-  for (int jb = j0; jb < j1; jb += kTopkRegKeys) {
-    if (!in_regs) {
-#pragma unroll
-      for (int i = 0; i < kTopkRegKeys; i += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + jb + i);
-        kr[i] = v.x;
-        kr[i + 1] = v.y;
-        kr[i + 2] = v.z;
-        kr[i + 3] = v.w;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kTopkRegKeys; ++i)
-      if (jb + i < j1) f(kr[i], jb + i);
-  }
 }
 
 // The bin holding the r-th largest of the counts in hs[0, nb) (bins above
@@ -1444,22 +1434,30 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
                                                float* __restrict__ out) {
   const int u = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
+  constexpr int NW = kTopkThreads / 64;
   const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
-  // the register run of a unit with at most kTopkThreads * kTopkRegKeys
-  // candidates, requested together with the unit state (the address is
-  // clamped into the unit's key buffer; a run that is used lies inside it)
-  uint32_t kr[kTopkRegKeys];
-  {
-    const int jr = min(tid * kTopkRegKeys, w.Lc_cap - kTopkRegKeys);
+  const uint32_t* gmx = w.gmax + (int64_t)u * (w.Lc_cap >> 3);
+  // Wave wid scans tiles [t0, t1) of 256 keys (lane l: keys 4 l .. 4 l + 3
+  // of a tile, one 16-byte load).  The split follows the capacity, so the
+  // first kTopkTileRegs tiles and the first kTopkGroupRegs group maxima per
+  // thread are requested before the unit state arrives (reads stay below
+  // Lc_cap; entries past the unit's candidates are masked later).
+  const int ncap = w.Lc_cap;
+  const int ntc = (ncap + 255) / 256;
+  const int tpw = (ntc + NW - 1) / NW;
+  const int t0 = wid * tpw;
+  const int t1 = min(t0 + tpw, ntc);
+  // (unconditional loads at clamped addresses, so no branch separates them
+  // from their first use)
+  const int gsz = 8 << w.gsh;
+  const int ngcap = (ncap + gsz - 1) / gsz;  // <= kTopkThreads * kTopkGroupRegs
+  uint32_t gv[kTopkGroupRegs];  // requested first: the floor needs them first
 #pragma unroll
-    for (int i = 0; i < kTopkRegKeys; i += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(keys + jr + i);
-      kr[i] = v.x;
-      kr[i + 1] = v.y;
-      kr[i + 2] = v.z;
-      kr[i + 3] = v.w;
-    }
-  }
+  for (int i = 0; i < kTopkGroupRegs; ++i) gv[i] = gmx[min(tid + kTopkThreads * i, ngcap - 1)];
+  uint4 kt[kTopkTileRegs];
+#pragma unroll
+  for (int i = 0; i < kTopkTileRegs; ++i)
+    kt[i] = *reinterpret_cast<const uint4*>(keys + min((t0 + i) * 256 + 4 * lane, ncap - 4));
   const int32_t* si = w.stepinfo + 4 * u;
   const int k = d.k;
   if (si[2]) {
@@ -1472,107 +1470,152 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   const int s = d.s;
   const int nc = Lcur + 1 - d.nrec - s;
   const int kk = min(k, nc);
-  if (tid == 0) {
-    c.lens[2 * u] = Lcur + 1;
-    c.lens[2 * u + 1] = steps + 1;
+  // (lens and the unused top-k slots are written at the end: a store here
+  // would stand between the prefetch and its first use)
+  if (kk <= 0) {
+    if (tid == 0) {
+      c.lens[2 * u] = Lcur + 1;
+      c.lens[2 * u + 1] = steps + 1;
+    }
+    if (topk_user)
+      for (int i = tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
+    return;
   }
-  if (topk_user)
-    for (int i = kk + tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
-  if (kk <= 0) return;
   __shared__ __attribute__((aligned(16))) unsigned int hs[kTopkBins];
-  __shared__ uint2 cand[kTopkCap];  // candidates (key, position), position order
-  __shared__ int2 wtot[kTopkThreads / 64];
-  __shared__ unsigned int wlo[kTopkThreads / 64], whi[kTopkThreads / 64];
+  __shared__ uint2 cand[NW * kTopkWaveCap];  // per wave: candidates (key, position), position order
+  __shared__ int2 wtot[NW];
+  __shared__ unsigned int wlo[NW], whi[NW];
   __shared__ unsigned int sh_bin, sh_kmin, sh_kmax;
   __shared__ int sh_rem, sh_cnt;
-  // runs of `per` keys, whole batches of kTopkRegKeys (vector reads stay
-  // aligned); reads past the unit's candidates land in the next unit's keys
-  // or in the kKeyPad entries of slack at the end of the buffer and are ignored
-  const int per = ((nc + kTopkThreads - 1) / kTopkThreads + kTopkRegKeys - 1) / kTopkRegKeys *
-                  kTopkRegKeys;
-  const int j0 = tid * per, j1 = min(j0 + per, nc);
-  const bool in_regs = per == kTopkRegKeys;
   for (int i = tid; i < kTopkBins; i += kTopkThreads) hs[i] = 0u;
   if (tid == 0) {
     sh_kmin = 0xFFFFFFFFu;
     sh_kmax = 0u;
   }
-  // key range present; per-thread maximum
-  unsigned int kmin = 0xFFFFFFFFu, kmax = 0u;
-  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) {
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
-  });
-  const unsigned int tmax = kmax;
-  wave_minmax_u(kmin, kmax);
-  if (lane == 0) {
-    wlo[wid] = kmin;
-    whi[wid] = kmax;
+  // 1. floor.  The pool kernel leaves the maximum of every group of 8 << gsh
+  //    candidates (at most kTopkGroupCap groups); register slot i of thread t
+  //    holds group t + 1024 i.  Wave w searches its own values for x_w, a lower bound (on a
+  //    grid of 2^-12 of its range) of their m_w-th largest, m_w =
+  //    ceil(kk n_w / n) for its n_w of the n values: every wave then holds
+  //    m_w values >= x_w, together >= kk values from disjoint key sets, so
+  //    floor = min_w x_w is at most the kk-th largest key.  (n < kk: no
+  //    floor.)  The values' maximum is also the keys' maximum.
+  const int ng = (nc + gsz - 1) / gsz;
+  const int nval = ng;
+  {
+    bool gok[kTopkGroupRegs];
+#pragma unroll
+    for (int i = 0; i < kTopkGroupRegs; ++i) gok[i] = tid + kTopkThreads * i < ng;
+    unsigned int mn = 0xFFFFFFFFu, mx = 0u;
+    int nw = 0;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kTopkGroupRegs; ++i) {
+      if (gok[i]) {
+        mn = min(mn, gv[i]);
+        mx = max(mx, gv[i]);
+      }
+      nw += __popcll(__ballot(gok[i]));
+    }
+    wave_minmax_u(mn, mx);
+    unsigned int xw = 0xFFFFFFFFu;  // no values: no bound from this wave
+    if (nw > 0 && nval >= kk) {
+      const int mw = (int)(((int64_t)kk * nw + nval - 1) / nval);
+      const unsigned int rg = mx - mn;
+      const int top = rg == 0u ? -1 : 31 - __clz((int)rg);
+      const int sh = max(top + 1 - 12, 0);
+      unsigned int dv[kTopkGroupRegs];  // offsets above mn; 0 (never counted) for no value
+#pragma unroll
+      for (int i = 0; i < kTopkGroupRegs; ++i) dv[i] = gok[i] ? gv[i] - mn : 0u;
+      unsigned int t = 0u;  // offset above mn with >= mw values at or above it
+      for (int bit = top; bit >= sh; --bit) {
+        const unsigned int cand_t = t | (1u << bit);  // >= 1
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkGroupRegs; ++i)  // lanes with dv[i] >= cand_t (35: unsigned >=)
+          cnt += __popcll(__builtin_amdgcn_uicmp(dv[i], cand_t, 35));
+        if (cnt >= mw) t = cand_t;
+      }
+      xw = mn + t;
+    }
+    if (lane == 0) {
+      wlo[wid] = xw;
+      whi[wid] = mx;
+    }
   }
   __syncthreads();
   unsigned int lo = wlo[0], hi = whi[0];
 #pragma unroll
-  for (int i = 1; i < kTopkThreads / 64; ++i) {
+  for (int i = 1; i < NW; ++i) {
     lo = min(lo, wlo[i]);
     hi = max(hi, whi[i]);
   }
+  if (nval < kk) lo = 0u;  // fewer values than picks: every key is a candidate
   auto range_shift = [](unsigned int base, unsigned int top) {
     const unsigned int rg = top - base;
     const int bits = rg == 0u ? 0 : 32 - __clz((int)rg);
     return max(bits - kTopkBinBits, 0);
   };
-  // 1. floor: with kk <= 1024, the kk-th largest per-thread maximum is <=
-  //    the kk-th largest key (kk runs each hold a key at least that large),
-  //    and so is the lower edge of its histogram bin.  Maxima that cluster
-  //    in a bin would serialize on its atomic, so each wave first peels off
-  //    up to four groups of lanes sharing a bin (one ballot and one atomic
-  //    each); the remaining lanes add their own.
-  if (kk <= kTopkThreads) {
-    const int vsh = range_shift(lo, hi);
-    const unsigned int vb = (tmax > lo ? tmax - lo : 0u) >> vsh;
-    uint64_t rest = __ballot(true);
-    for (int it = 0; it < 4 && rest; ++it) {
-      const int ld = __builtin_ctzll(rest);
-      const unsigned int bl = (unsigned int)__builtin_amdgcn_readlane((int)vb, ld);
-      const uint64_t m = __ballot(vb == bl) & rest;
-      if (lane == ld) atomicAdd(&hs[bl], (unsigned int)__popcll(m));
-      rest &= ~m;
+  // 2. candidates: keys >= lo, compacted per wave in position order (ballot
+  //    counts): the wave's first kTopkWaveCap go to its stretch of the LDS
+  //    list, any further ones to the wave's region of the unit's slot
+  //    buffer (indexed like the list, starting at the wave's first position,
+  //    so it never overflows).
+  uint2* wlist = cand + wid * kTopkWaveCap;
+  uint2* wslot = w.cslot + (int64_t)u * ncap + (int64_t)t0 * 256;
+  int wcount = 0;  // wave-uniform
+  auto take_tile = [&](const uint4& kv, int t) {
+    const int j = t * 256 + 4 * lane;
+    const uint32_t kx[4] = {kv.x, kv.y, kv.z, kv.w};
+    bool p[4];
+    uint64_t bl[4];
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // lane masks of j + e < nc (36: unsigned <) and key >= lo (35: >=)
+      bl[e] = __builtin_amdgcn_uicmp((unsigned int)(j + e), (unsigned int)nc, 36) &
+              __builtin_amdgcn_uicmp(kx[e], lo, 35);
+      p[e] = (bl[e] >> lane) & 1u;
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bl[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bl[e], 0u));
+      tot += __popcll(bl[e]);
     }
-    if ((rest >> lane) & 1u) atomicAdd(&hs[vb], 1u);  // the spread remainder
-    __syncthreads();
-    topk_find_bin(hs, kTopkBins, kk, wtot, &sh_bin, &sh_rem, &sh_cnt);
-    lo = lo + (sh_bin << vsh);
-    for (int i = tid; i < kTopkBins; i += kTopkThreads) hs[i] = 0u;
+    int o = wcount + before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (p[e]) {
+        const uint2 v = make_uint2(kx[e], (unsigned int)(j + e));
+        if (o < kTopkWaveCap)
+          wlist[o] = v;
+        else
+          wslot[o] = v;
+        ++o;
+      }
+    wcount += tot;
+  };
+  for (int r0 = 0; t0 + r0 < t1; r0 += kTopkTileRegs) {
+    if (r0 > 0) {
+#pragma unroll
+      for (int i = 0; i < kTopkTileRegs; ++i) {
+        const int j = (t0 + r0 + i) * 256 + 4 * lane;
+        kt[i] = *reinterpret_cast<const uint4*>(keys + min(j, ncap - 4));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTopkTileRegs; ++i)
+      if (t0 + r0 + i < t1 && (t0 + r0 + i) * 256 < nc) take_tile(kt[i], t0 + r0 + i);
   }
-  // 2. candidates: keys >= lo, counted, then listed in position order
-  int ccount = 0;
-  for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int) { ccount += key >= lo; });
-  int ntot, dummy;
-  const int coff = block_excl_scan2(ccount, 0, wtot, &ntot, &dummy).x;
-  const bool listed = ntot <= kTopkCap;
-  if (listed) {
-    int o = coff;
-    for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
-      if (key >= lo) cand[o++] = make_uint2(key, (unsigned int)j);
-    });
+  if (wcount > kTopkWaveCap) {
+    // the slot entries are read back by other lanes of the same wave
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  // candidates of this thread in position order: a contiguous share of the
-  // list (neighbouring lanes hold different stretches, so the equal keys of
-  // a pooled run do not collide in one atomic), or its run filtered to
-  // keys >= lo
-  const int cpt = (ntot + kTopkThreads - 1) / kTopkThreads;
-  const int i0 = min(tid * cpt, ntot), i1 = min(i0 + cpt, ntot);
+  // candidates of this thread, in position order: a contiguous share of its
+  // wave's list (neighbouring lanes hold different stretches, so the equal
+  // keys of a pooled run do not collide in one atomic)
+  const int cpl = (wcount + 63) / 64;
+  const int a0 = min(lane * cpl, wcount), a1 = min(a0 + cpl, wcount);
   auto visit_ordered = [&](auto&& f) {
-    if (listed) {
-      for (int i = i0; i < i1; ++i) {
-        const uint2 e = cand[i];
-        f(e.x, (int)e.y);
-      }
-    } else {
-      for_keys(keys, j0, j1, in_regs, kr, [&](uint32_t key, int j) {
-        if (key >= lo) f(key, j);
-      });
+    for (int i = a0; i < a1; ++i) {
+      const uint2 e = i < kTopkWaveCap ? wlist[i] : wslot[i];
+      f(e.x, (int)e.y);
     }
   };
   // histogram of f(key) over the thread's candidates with pred(key); equal
@@ -1680,6 +1723,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
       if (topk_user) topk_user[(int64_t)u * k + i] = v;
     }
   }
+  if (tid == 0) {
+    c.lens[2 * u] = Lcur + 1;
+    c.lens[2 * u + 1] = steps + 1;
+  }
+  if (topk_user)
+    for (int i = kk + tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
 }
 
 hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,

@@ -205,19 +205,36 @@ _SMALL_BF16 = dict(n_q_heads=4, n_kv_heads=1, head_dim=64, rank=32, q_window=4, 
 
 @pytest.mark.parametrize("top_k", [64, 1500])
 def test_long_context_key_runs_bf16(gpu_lib, top_k):
-    """More than 32 768 candidates: top-k threads own runs longer than their
-    register batch (re-read per pass); top_k = 1500 > 1024 also skips the
-    floor from the run maxima and selects over the runs themselves."""
+    """More than 32 768 candidates: every top-k wave scans more than eight key
+    tiles; top_k = 1500 also needs more than 1024 of the 4096 group maxima
+    above the floor."""
     w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=top_k)
     st = _run(w, 34000, 1, 3)
     assert st.n_checked == 3
 
 
+def test_few_groups_no_floor_bf16(gpu_lib):
+    """top_k = 1500 of about 2900 candidates: fewer group maxima (8 keys
+    each) than picks, so there is no floor and every key is a candidate."""
+    w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=1500)
+    st = _run(w, 3000, 1, 3)
+    assert st.n_checked == 3
+
+
+def test_very_long_context_coarse_groups_bf16(gpu_lib):
+    """140 000 tokens: the pool kernel merges its 8-candidate groups in fours
+    (at most 8192 group maxima per unit) and the top-k waves scan their
+    tiles in several register rounds."""
+    w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=512)
+    st = _run(w, 140000, 1, 2)
+    assert st.n_checked == 2
+
+
 def test_flat_scores_tie_order_bf16(gpu_lib):
     """Zero queries make every latent logit 0, so all pooled scores tie and
-    more than 8192 keys pass the floor (the selection runs over the thread
-    runs, not the candidate list): the picks are the first top_k candidates,
-    ties going to the lower position."""
+    every key passes the floor (each top-k wave holds more candidates than
+    its LDS list, the rest in the workspace): the picks are the first top_k
+    candidates, ties going to the lower position."""
     kvlr = _kvlr()
     w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=64)
     L, steps = 10000, 3
