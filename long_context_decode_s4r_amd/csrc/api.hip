@@ -296,6 +296,22 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
   const int max_sweeps = 30;
   const double tol = 1e-13;
   int cur = 0;
+  if (bjac_supported(n)) {
+    // block Jacobi, in place in A[0] and V[0]; A[1] holds the rounds' Q blocks
+    const int nb = n / 32;
+    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+      for (int rd = 0; rd < nb - 1; ++rd)
+        if ((he = launch_bjac_round(n, nmat, A[0], Vm[0], A[1], frozen, rd, st)) != hipSuccess)
+          return hip_fail(he, "block jacobi round");
+      if ((he = launch_jacobi_check(n, nmat, A[0], part, frozen, final_buf, 0, counter, tol, st)) != hipSuccess)
+        return hip_fail(he, "jacobi check");
+      int active = -1;
+      if ((he = hipMemcpyAsync(&active, counter, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
+        return hip_fail(he, "memcpy");
+      if ((he = hipStreamSynchronize(st)) != hipSuccess) return fail(KVLR_EDEVICE, "sync: %s", hipGetErrorString(he));
+      if (active == 0) break;
+    }
+  } else
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     for (int rd = 0; rd < n - 1; ++rd) {
       if ((he = launch_jacobi_round(n, nmat, A[cur], A[cur ^ 1], Vm[cur], Vm[cur ^ 1], frozen, st)) != hipSuccess)

@@ -171,6 +171,12 @@ hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double
 hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_dst,
                                const double* V_src, double* V_dst, const int* frozen,
                                hipStream_t st);
+// block Jacobi (n a multiple of 64, n >= 128): one outer round k of the
+// circle schedule over n / 32 blocks; Qbuf holds bjac_q_bytes(n, nmat)
+bool bjac_supported(int n);
+size_t bjac_q_bytes(int n, int nmat);
+hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,
+                             int k, hipStream_t st);
 hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
                                int* final_buf, int cur, int* n_active, double tol,
                                hipStream_t st);

@@ -352,6 +352,222 @@ hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, i
 }
 
 // --------------------------------------------------------------------------
+// 3b. block Jacobi (two-sided, fp64), for n a multiple of 64 and >= 128.
+//
+// The n indices form nb = n / 32 blocks of 32; an outer round pairs the
+// blocks by the circle method (block 0 fixed, the others rotating by one
+// place per round, so nb - 1 rounds meet every block pair once).  For pair
+// p = (I, J) the 64 x 64 submatrix S = A[I u J, I u J] is diagonalised in LDS
+// by cyclic Jacobi rotations (the same 2x2 Schur rotation as above, inner
+// rounds paired by the circle method over 64 indices), Q_p = the product of
+// those rotations, so Q_p^T S Q_p is diagonal.  Then, with Q the block
+// diagonal of the Q_p, A <- Q^T A Q and V <- V Q: tile (P, P') of A becomes
+// Q_P^T A[P, P'] Q_P' and row tile R of V's pair columns P becomes
+// V[R, P] Q_P.  Every tile reads only itself, so the update is in place.
+// Each outer round applies an orthogonal similarity, so A keeps its
+// eigenvalues and V its orthogonality; the rounds drive off(A) to zero as in
+// the scalar method (Golub & Van Loan, block Jacobi).
+// --------------------------------------------------------------------------
+constexpr int kBJ = 32;       // indices per block
+constexpr int kBJ2 = 2 * kBJ; // indices per pair (one subproblem)
+constexpr int kBJInner = 1;   // inner sweeps per subproblem
+
+__device__ __forceinline__ int bj_block(int slot, int k, int nb) {
+  return slot == 0 ? 0 : 1 + (slot - 1 + k) % (nb - 1);
+}
+// global index of local index li (< 64) of pair (I, J)
+__device__ __forceinline__ int bj_index(int li, int I, int J) {
+  return li < kBJ ? I * kBJ + li : J * kBJ + (li - kBJ);
+}
+
+// grid (nb / 2, nmat), kBJEigThreads threads: Q_p of every pair of outer
+// round k.  Inner round kr pairs local indices perm[kr][a] and
+// perm[kr][63 - a] (a < 32), the circle method over 64 indices, tabulated in
+// LDS once; thread t updates 2x2 block t of S and two entry pairs of Q.
+constexpr int kBJEigThreads = 1024;
+__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __restrict__ Aall,
+                                                            double* __restrict__ Qall,
+                                                            const int* __restrict__ frozen, int n,
+                                                            int k) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  constexpr int NT = kBJEigThreads, NP = kBJ2 / 2;
+  static_assert(NP * NP == NT && kBJ2 * NP == 2 * NT, "one 2x2 block and two Q pairs per thread");
+  const int nb = n / kBJ, p = blockIdx.x, tid = threadIdx.x;
+  const int I = bj_block(p, k, nb), J = bj_block(nb - 1 - p, k, nb);
+  const double* A = Aall + (int64_t)m * n * n;
+  __shared__ double S[kBJ2][kBJ2 + 1];
+  __shared__ double Q[kBJ2][kBJ2 + 1];
+  __shared__ double rc[NP], rs[NP], rt[NP];
+  __shared__ uint8_t perm[kBJ2 - 1][kBJ2];
+  for (int e = tid; e < kBJ2 * kBJ2; e += NT) {
+    const int i = e / kBJ2, j = e % kBJ2;
+    S[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I, J)];
+    Q[i][j] = i == j ? 1.0 : 0.0;
+  }
+  for (int e = tid; e < (kBJ2 - 1) * kBJ2; e += NT) {
+    const int kr = e / kBJ2, x = e % kBJ2;
+    perm[kr][x] = (uint8_t)(x == 0 ? 0 : 1 + (x - 1 + kr) % (kBJ2 - 1));
+  }
+  __syncthreads();
+  const int a = tid / NP, b = tid % NP;          // this thread's 2x2 block of S
+  const int qrow = tid / NP, qb = tid % NP;      // Q rows qrow and qrow + 32, pair qb
+  for (int sweep = 0; sweep < kBJInner; ++sweep) {
+    for (int kr = 0; kr < kBJ2 - 1; ++kr) {
+      if (tid < NP) {
+        const int ip = perm[kr][tid], iq = perm[kr][kBJ2 - 1 - tid];
+        const double app = S[ip][ip], aqq = S[iq][iq], apq = S[ip][iq];
+        double c = 1.0, sn = 0.0, t = 0.0;
+        if (apq != 0.0) {
+          // the rotation above with tau = d / (2 apq) multiplied through by
+          // |2 apq|: t = sgn(tau) 2|apq| / (|d| + sqrt(d^2 + 4 apq^2)), one
+          // square root and one division (the entries are Gram sums of unit
+          // vectors, far from overflow)
+          const double d = aqq - app, a2 = 2.0 * fabs(apq);
+          const bool neg = (d < 0.0) != (apq < 0.0) && d != 0.0;
+          t = a2 / (fabs(d) + sqrt(d * d + a2 * a2));
+          t = neg ? -t : t;
+          c = rsqrt(1.0 + t * t);
+          sn = t * c;
+        }
+        rc[tid] = c;
+        rs[tid] = sn;
+        rt[tid] = t;
+      }
+      __syncthreads();
+      // S <- J^T S J on block (a, b); Q <- Q J on its two entry pairs (the
+      // blocks and pairs are disjoint, so no thread reads another's stores)
+      const int pa = perm[kr][a], qa = perm[kr][kBJ2 - 1 - a];
+      const int pb = perm[kr][b], qbb = perm[kr][kBJ2 - 1 - b];
+      const int pq = perm[kr][qb], qq = perm[kr][kBJ2 - 1 - qb];
+      const double m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
+      const double v00 = Q[qrow][pq], v01 = Q[qrow][qq];
+      const double v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
+      const double cq = rc[qb], sq = rs[qb];
+      if (a == b) {
+        const double ta = rt[a];
+        S[pa][pa] = m00 - ta * m01;
+        S[qa][qa] = m11 + ta * m01;
+        S[pa][qa] = 0.0;
+        S[qa][pa] = 0.0;
+      } else {
+        const double ca = rc[a], sa = rs[a], cb = rc[b], sb = rs[b];
+        const double r00 = ca * m00 - sa * m10, r01 = ca * m01 - sa * m11;
+        const double r10 = sa * m00 + ca * m10, r11 = sa * m01 + ca * m11;
+        S[pa][pb] = cb * r00 - sb * r01;
+        S[pa][qbb] = sb * r00 + cb * r01;
+        S[qa][pb] = cb * r10 - sb * r11;
+        S[qa][qbb] = sb * r10 + cb * r11;
+      }
+      Q[qrow][pq] = cq * v00 - sq * v01;
+      Q[qrow][qq] = sq * v00 + cq * v01;
+      Q[qrow + NP][pq] = cq * v10 - sq * v11;
+      Q[qrow + NP][qq] = sq * v10 + cq * v11;
+      __syncthreads();
+    }
+  }
+  double* Qo = Qall + ((int64_t)m * (nb / 2) + p) * kBJ2 * kBJ2;
+  for (int e = tid; e < kBJ2 * kBJ2; e += NT) Qo[e] = Q[e / kBJ2][e % kBJ2];
+}
+
+// grid ((nb/2)^2 + (n/64)(nb/2), nmat), 256 threads: the in-place update of
+// A's tiles (P, P') and V's tiles (row tile R, pair P) of outer round k.
+// Thread (ti, tj) computes the 4 x 4 outputs at rows 4 ti, columns 4 tj.
+__global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
+                                                    double* __restrict__ Vall,
+                                                    const double* __restrict__ Qall,
+                                                    const int* __restrict__ frozen, int n, int k) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+  const int tile = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJ2];   // the tile (V: transposed)
+  __shared__ __attribute__((aligned(16))) double Q1[kBJ2][kBJ2];  // Q_P (then the second factor)
+  const double* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
+  double acc[4][4];
+  auto gemm = [&](const double (*Ak)[kBJ2], const double (*Bk)[kBJ2]) {
+    // acc[i][j] = sum_k Ak[k][4 ti + i] * Bk[k][4 tj + j]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+#pragma unroll 8
+    for (int kk = 0; kk < kBJ2; ++kk) {
+      double a[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = Ak[kk][4 * ti + i];
+        bv[i] = Bk[kk][4 * tj + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+    }
+  };
+  if (tile < np * np) {
+    const int P = tile / np, P2 = tile % np;
+    const int I = bj_block(P, k, nb), J = bj_block(nb - 1 - P, k, nb);
+    const int I2 = bj_block(P2, k, nb), J2 = bj_block(nb - 1 - P2, k, nb);
+    double* A = Aall + (int64_t)m * n * n;
+    const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
+    const double* QP2 = Qm + (int64_t)P2 * kBJ2 * kBJ2;
+    for (int e = tid; e < kBJ2 * kBJ2; e += 256) {
+      const int i = e / kBJ2, j = e % kBJ2;
+      X[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2)];
+      Q1[i][j] = QP[e];
+    }
+    __syncthreads();
+    gemm(Q1, X);  // T = Q_P^T X
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[4 * tj + j][4 * ti + i] = acc[i][j];  // X <- T^T
+    for (int e = tid; e < kBJ2 * kBJ2; e += 256) Q1[e / kBJ2][e % kBJ2] = QP2[e];
+    __syncthreads();
+    gemm(X, Q1);  // T Q_P2
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        A[(int64_t)bj_index(4 * ti + i, I, J) * n + bj_index(4 * tj + j, I2, J2)] = acc[i][j];
+  } else {
+    const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
+    const int I = bj_block(P, k, nb), J = bj_block(nb - 1 - P, k, nb);
+    double* V = Vall + (int64_t)m * n * n;
+    const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
+    for (int e = tid; e < kBJ2 * kBJ2; e += 256) {
+      const int i = e / kBJ2, j = e % kBJ2;
+      X[j][i] = V[(int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J)];
+      Q1[i][j] = QP[e];
+    }
+    __syncthreads();
+    gemm(X, Q1);  // V[R, P] Q_P
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        V[(int64_t)(kBJ2 * R + 4 * ti + i) * n + bj_index(4 * tj + j, I, J)] = acc[i][j];
+  }
+}
+
+bool bjac_supported(int n) { return n >= 2 * kBJ2 && n % kBJ2 == 0; }
+
+size_t bjac_q_bytes(int n, int nmat) { return (size_t)nmat * (n / kBJ2) * kBJ2 * kBJ2 * sizeof(double); }
+
+hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,
+                             int k, hipStream_t st) {
+  const int nb = n / kBJ, np = nb / 2;
+  hipLaunchKernelGGL(k_bjac_eig, dim3(np, nmat), dim3(kBJEigThreads), 0, st, A, Qbuf, frozen, n, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_bjac_apply, dim3(np * np + (n / kBJ2) * np, nmat), dim3(256), 0, st, A, V, Qbuf,
+                     frozen, n, k);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // 4. eigenvalues descending (bitonic sort of (lambda, slot) in LDS), basis =
 //    the first r eigenvector columns, rounded to storage.
 // --------------------------------------------------------------------------
