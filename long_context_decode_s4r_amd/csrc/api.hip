@@ -300,7 +300,7 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
     // block Jacobi, in place in A[0] and V[0]; A[1] holds the rounds' Q blocks
     const int nb = n / 32;
     for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-      for (int rd = 0; rd < nb - 1; ++rd)
+      for (int rd = -1; rd < nb - 1; ++rd)  // the self round, then the cross rounds
         if ((he = launch_bjac_round(n, nmat, A[0], Vm[0], A[1], frozen, rd, st)) != hipSuccess)
           return hip_fail(he, "block jacobi round");
       if ((he = launch_jacobi_check(n, nmat, A[0], part, frozen, final_buf, 0, counter, tol, st)) != hipSuccess)

@@ -171,8 +171,9 @@ hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double
 hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_dst,
                                const double* V_src, double* V_dst, const int* frozen,
                                hipStream_t st);
-// block Jacobi (n a multiple of 64, n >= 128): one outer round k of the
-// circle schedule over n / 32 blocks; Qbuf holds bjac_q_bytes(n, nmat)
+// block Jacobi (n a multiple of 64, n >= 128): round k of a sweep (k = -1:
+// rotations inside blocks; k = 0 .. n/32 - 2: between the blocks the circle
+// schedule pairs); Qbuf holds bjac_q_bytes(n, nmat)
 bool bjac_supported(int n);
 size_t bjac_q_bytes(int n, int nmat);
 hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,

@@ -354,36 +354,46 @@ hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, i
 // --------------------------------------------------------------------------
 // 3b. block Jacobi (two-sided, fp64), for n a multiple of 64 and >= 128.
 //
-// The n indices form nb = n / 32 blocks of 32; an outer round pairs the
-// blocks by the circle method (block 0 fixed, the others rotating by one
-// place per round, so nb - 1 rounds meet every block pair once).  For pair
-// p = (I, J) the 64 x 64 submatrix S = A[I u J, I u J] is diagonalised in LDS
-// by cyclic Jacobi rotations (the same 2x2 Schur rotation as above, inner
-// rounds paired by the circle method over 64 indices), Q_p = the product of
-// those rotations, so Q_p^T S Q_p is diagonal.  Then, with Q the block
-// diagonal of the Q_p, A <- Q^T A Q and V <- V Q: tile (P, P') of A becomes
-// Q_P^T A[P, P'] Q_P' and row tile R of V's pair columns P becomes
+// The n indices form nb = n / 32 blocks of 32.  A sweep is one "self" round
+// (k = -1: subproblem p = blocks (2p, 2p + 1), whose rotations pair indices
+// inside the same block) and nb - 1 "cross" rounds k = 0 .. nb - 2 (blocks
+// paired by the circle method, block 0 fixed and the others rotating by one
+// place per round; the rotations pair an index of I with one of J), so every
+// index pair is rotated once per sweep, as in scalar cyclic Jacobi.  For
+// subproblem p = (I, J) the 64 x 64 submatrix S = A[I u J, I u J] is rotated
+// in LDS (the 2x2 Schur rotation above; 31 self or 32 cross inner rounds of
+// 32 disjoint pairs) and Q_p accumulates the rotations.  Then, with Q the
+// block diagonal of the Q_p, A <- Q^T A Q and V <- V Q: tile (P, P') of A
+// becomes Q_P^T A[P, P'] Q_P' and row tile R of V's pair columns P becomes
 // V[R, P] Q_P.  Every tile reads only itself, so the update is in place.
-// Each outer round applies an orthogonal similarity, so A keeps its
-// eigenvalues and V its orthogonality; the rounds drive off(A) to zero as in
-// the scalar method (Golub & Van Loan, block Jacobi).
 // --------------------------------------------------------------------------
 constexpr int kBJ = 32;       // indices per block
 constexpr int kBJ2 = 2 * kBJ; // indices per pair (one subproblem)
-constexpr int kBJInner = 1;   // inner sweeps per subproblem
 
 __device__ __forceinline__ int bj_block(int slot, int k, int nb) {
   return slot == 0 ? 0 : 1 + (slot - 1 + k) % (nb - 1);
+}
+// blocks (I, J) of subproblem p in round k (k < 0: the self round)
+__device__ __forceinline__ void bj_pair(int p, int k, int nb, int* I, int* J) {
+  if (k < 0) {
+    *I = 2 * p;
+    *J = 2 * p + 1;
+  } else {
+    *I = bj_block(p, k, nb);
+    *J = bj_block(nb - 1 - p, k, nb);
+  }
 }
 // global index of local index li (< 64) of pair (I, J)
 __device__ __forceinline__ int bj_index(int li, int I, int J) {
   return li < kBJ ? I * kBJ + li : J * kBJ + (li - kBJ);
 }
 
-// grid (nb / 2, nmat), kBJEigThreads threads: Q_p of every pair of outer
-// round k.  Inner round kr pairs local indices perm[kr][a] and
-// perm[kr][63 - a] (a < 32), the circle method over 64 indices, tabulated in
-// LDS once; thread t updates 2x2 block t of S and two entry pairs of Q.
+// grid (nb / 2, nmat), kBJEigThreads threads: Q_p of every subproblem of
+// round k.  Inner round kr rotates the local index pairs (pi[kr][a],
+// qi[kr][a]), a < 32, tabulated in LDS once: self rounds pair indices inside
+// each half by the circle method over 32, cross rounds pair a with
+// 32 + (a + kr) % 32.  Thread t updates 2x2 block t of S and two entry pairs
+// of Q.
 constexpr int kBJEigThreads = 1024;
 __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __restrict__ Aall,
                                                             double* __restrict__ Qall,
@@ -394,28 +404,41 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   constexpr int NT = kBJEigThreads, NP = kBJ2 / 2;
   static_assert(NP * NP == NT && kBJ2 * NP == 2 * NT, "one 2x2 block and two Q pairs per thread");
   const int nb = n / kBJ, p = blockIdx.x, tid = threadIdx.x;
-  const int I = bj_block(p, k, nb), J = bj_block(nb - 1 - p, k, nb);
+  int I, J;
+  bj_pair(p, k, nb, &I, &J);
   const double* A = Aall + (int64_t)m * n * n;
   __shared__ double S[kBJ2][kBJ2 + 1];
   __shared__ double Q[kBJ2][kBJ2 + 1];
   __shared__ double rc[NP], rs[NP], rt[NP];
-  __shared__ uint8_t perm[kBJ2 - 1][kBJ2];
+  __shared__ uint8_t pi[kBJ][NP], qi[kBJ][NP];
   for (int e = tid; e < kBJ2 * kBJ2; e += NT) {
     const int i = e / kBJ2, j = e % kBJ2;
     S[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I, J)];
     Q[i][j] = i == j ? 1.0 : 0.0;
   }
-  for (int e = tid; e < (kBJ2 - 1) * kBJ2; e += NT) {
-    const int kr = e / kBJ2, x = e % kBJ2;
-    perm[kr][x] = (uint8_t)(x == 0 ? 0 : 1 + (x - 1 + kr) % (kBJ2 - 1));
+  const int nround = k < 0 ? kBJ - 1 : kBJ;
+  for (int e = tid; e < kBJ * NP; e += NT) {
+    const int kr = e / NP, a = e % NP;
+    int x, y;
+    if (k < 0) {  // circle method over the 32 indices of each half
+      const int h = a / (NP / 2), c = a % (NP / 2);
+      auto cs = [&](int z) { return z == 0 ? 0 : 1 + (z - 1 + kr) % (kBJ - 1); };
+      x = kBJ * h + cs(c);
+      y = kBJ * h + cs(kBJ - 1 - c);
+    } else {
+      x = a;
+      y = kBJ + (a + kr) % kBJ;
+    }
+    pi[kr][a] = (uint8_t)x;
+    qi[kr][a] = (uint8_t)y;
   }
   __syncthreads();
   const int a = tid / NP, b = tid % NP;          // this thread's 2x2 block of S
   const int qrow = tid / NP, qb = tid % NP;      // Q rows qrow and qrow + 32, pair qb
-  for (int sweep = 0; sweep < kBJInner; ++sweep) {
-    for (int kr = 0; kr < kBJ2 - 1; ++kr) {
+  {
+    for (int kr = 0; kr < nround; ++kr) {
       if (tid < NP) {
-        const int ip = perm[kr][tid], iq = perm[kr][kBJ2 - 1 - tid];
+        const int ip = pi[kr][tid], iq = qi[kr][tid];
         const double app = S[ip][ip], aqq = S[iq][iq], apq = S[ip][iq];
         double c = 1.0, sn = 0.0, t = 0.0;
         if (apq != 0.0) {
@@ -437,9 +460,9 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
       __syncthreads();
       // S <- J^T S J on block (a, b); Q <- Q J on its two entry pairs (the
       // blocks and pairs are disjoint, so no thread reads another's stores)
-      const int pa = perm[kr][a], qa = perm[kr][kBJ2 - 1 - a];
-      const int pb = perm[kr][b], qbb = perm[kr][kBJ2 - 1 - b];
-      const int pq = perm[kr][qb], qq = perm[kr][kBJ2 - 1 - qb];
+      const int pa = pi[kr][a], qa = qi[kr][a];
+      const int pb = pi[kr][b], qbb = qi[kr][b];
+      const int pq = pi[kr][qb], qq = qi[kr][qb];
       const double m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
       const double v00 = Q[qrow][pq], v01 = Q[qrow][qq];
       const double v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
@@ -507,8 +530,9 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
   };
   if (tile < np * np) {
     const int P = tile / np, P2 = tile % np;
-    const int I = bj_block(P, k, nb), J = bj_block(nb - 1 - P, k, nb);
-    const int I2 = bj_block(P2, k, nb), J2 = bj_block(nb - 1 - P2, k, nb);
+    int I, J, I2, J2;
+    bj_pair(P, k, nb, &I, &J);
+    bj_pair(P2, k, nb, &I2, &J2);
     double* A = Aall + (int64_t)m * n * n;
     const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
     const double* QP2 = Qm + (int64_t)P2 * kBJ2 * kBJ2;
@@ -534,7 +558,8 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
         A[(int64_t)bj_index(4 * ti + i, I, J) * n + bj_index(4 * tj + j, I2, J2)] = acc[i][j];
   } else {
     const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
-    const int I = bj_block(P, k, nb), J = bj_block(nb - 1 - P, k, nb);
+    int I, J;
+    bj_pair(P, k, nb, &I, &J);
     double* V = Vall + (int64_t)m * n * n;
     const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
     for (int e = tid; e < kBJ2 * kBJ2; e += 256) {
