@@ -118,6 +118,16 @@ def test_edge_cases_f32(gpu_lib, variant):
     assert st.n_checked == 18
 
 
+@pytest.mark.parametrize("head_dim", [64, 96])
+def test_block_jacobi_small_f32(gpu_lib, head_dim):
+    """D' = 128 and 192 (2 KV heads): the smallest block-Jacobi eigensolves
+    (4 and 6 blocks of 32 indices); bases and decode steps against the oracle."""
+    w = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=head_dim, rank=24,
+                               q_window=4, top_k=32, n_recent=8, n_sample=256)
+    st = _run(w, 600, 2, 4)
+    assert st.n_checked == 8
+
+
 def test_full_rank_all_selected_equals_full_attention(gpu_lib):
     """r = D' and k >= |J|: the GPU output equals plain full attention over
     every token (fp32 storage)."""
