@@ -172,6 +172,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the prefill leg (basis build + projection of one 64K sequence)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the compressed-KV path has no multi-GPU part "
@@ -180,6 +182,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
         copy_probe()
+        return
+    if args.prefill_only:
+        kvlr.load()
+        torch.cuda.set_device(0)
+        print(json.dumps({"prefill": run_prefill_leg(args)}), flush=True)
         return
     w = configs.by_name(args.workload)
     if w is None:
