@@ -1331,7 +1331,7 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 //      entries past kTopkWaveCap into the workspace; every later pass runs
 //      over those short lists with full, mostly conflict-free LDS atomics.
 //   3. Threshold T = the kk-th largest key, by a radix select over
-//      [floor, max]: 2^14-bin histograms of (key - floor) >> shift, refined
+//      [floor, max]: 2^12-bin histograms of (key - floor) >> shift, refined
 //      until the selected bin is one key value (also when the bin turns out
 //      to hold a single value) or is taken whole.
 //   4. Ordered compaction: every key above the threshold bin, and the first
@@ -1345,7 +1345,7 @@ hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs&
 constexpr int kTopkThreads = 1024; // 16 waves; <= 128 VGPRs per thread
 constexpr int kTopkTileRegs = 12;  // key tiles per wave held in registers (+4 VGPRs each)
 constexpr int kTopkGroupRegs = kTopkGroupCap / kTopkThreads;  // group maxima per thread
-constexpr int kTopkBinBits = 14;   // histogram digits per pass
+constexpr int kTopkBinBits = 12;   // histogram digits per pass
 constexpr int kTopkBins = 1 << kTopkBinBits;
 constexpr int kTopkWaveCap = 512;  // candidates per wave kept in LDS
 
