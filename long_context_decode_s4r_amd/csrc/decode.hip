@@ -2636,23 +2636,26 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
 }
 
 // --------------------------------------------------------------------------
-// merge for bf16 storage: grid (H_kv, U), 256 threads.  Same combination as
+// merge for bf16 storage: grid (nparts H_kv, U), 256 threads; block
+// (h, part) writes the part-th share of head h's channel tiles (every part
+// forms the split combination itself).  Same combination as
 // k_merge; the selected-row partials are read as 16-byte vectors (thread t:
 // coefficients 4 (t % 64) .. + 3 of heads t / 64 and t / 64 + 4), and
 // B^V_h (sum_sel f ylat) runs on MFMA 16x16x32: A = 16 channels of B^V_h
 // straight from memory (K = coefficient index), B = the G head vectors as
 // bf16 hi + lo pairs (two MFMAs, ~16 mantissa bits), D = channels x heads.
-// Wave w takes the channel tiles w, w + 4, ...
+// Wave w takes the part's channel tiles w, w + 4, ...
 // --------------------------------------------------------------------------
 constexpr int kMergeCT = 4;  // channel tiles per wave (head_dim <= 256)
-__global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeWs w,
+__global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeWs w, int nparts,
                                                     float* __restrict__ out) {
-  const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x / nparts, part = blockIdx.x % nparts, u = blockIdx.y, tid = threadIdx.x;
   const int l = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = l & 15, kq = l >> 4;
   const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
   const int nst = w.nsl + w.nse;
   const int nks = r / 32, nct = (dh + 15) / 16;
+  const int ctper = (nct + nparts - 1) / nparts;  // channel tiles of this block: part * ctper + ...
   extern __shared__ __attribute__((aligned(16))) float smf[];
   float* ys = smf;                 // [G][r]
   float* oe = ys + G * r;          // [G][dh] exact-row part of the output
@@ -2690,15 +2693,17 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
     for (int e = 0; e < 4; ++e)
       ev[m][e] = yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh];
   }
-  // B^V_h fragments: channel tile ct = wv + 4 m, rows clamped into the head
+  // B^V_h fragments: channel tile ct = part * ctper + wv + 4 m, rows clamped into the head
   const uint16_t* bbase = (const uint16_t*)c.basis_v + ((int64_t)u * d.D + (int64_t)h * dh) * r;
   bf16x8 bfr[kMergeCT][8];
 #pragma unroll
   for (int m = 0; m < kMergeCT; ++m) {
-    const int ch = min((wv + 4 * m) * 16 + n16, dh - 1);
+    const int ctm = part * ctper + wv + 4 * m;
+    const int ch = min(ctm * 16 + n16, dh - 1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      if (wv + 4 * m < nct && ks < nks) bfr[m][ks] = ld_bf16x8(bbase + (int64_t)ch * r + 32 * ks + 8 * kq);
+      if (wv + 4 * m < ctper && ctm < nct && ks < nks)
+        bfr[m][ks] = ld_bf16x8(bbase + (int64_t)ch * r + 32 * ks + 8 * kq);
   }
   if (full) return;  // the top-k kernel wrote zeros
   const int nc = Lcur + 1 - d.nrec - d.s;
@@ -2790,8 +2795,8 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
   }
 #pragma unroll
   for (int m = 0; m < kMergeCT; ++m) {
-    const int ct = wv + 4 * m;
-    if (ct >= nct) break;
+    const int ct = part * ctper + wv + 4 * m;
+    if (wv + 4 * m >= ctper || ct >= nct) break;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -2880,7 +2885,10 @@ hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs
   const size_t lds = merge_lds(d, w);
   hipError_t e = allow_lds(&k_merge_mfma, lds, &done);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge_mfma, dim3(d.Hkv, U), dim3(256), lds, st, d, c, w, out);
+  // two blocks per KV head (halves of its channel tiles): twice the blocks
+  // in flight for the same loads of the split partials
+  const int nparts = (d.dh + 15) / 16 >= 2 ? 2 : 1;
+  hipLaunchKernelGGL(k_merge_mfma, dim3(nparts * d.Hkv, U), dim3(256), lds, st, d, c, w, nparts, out);
   return hipGetLastError();
 }
 
