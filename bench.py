@@ -177,7 +177,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the compressed-KV path has no multi-GPU part "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+              "(units shard across GPUs without exchange); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
