@@ -150,7 +150,7 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
 
 struct DecodeLayout {
   size_t stepinfo, partial, spill, tilestat, keys, topk, qlat, ylat, yex, astat, gmax, cslot,
-      total;
+      tkpcnt, tkhint, total;
   DecodeWs t;  // tiling fields
 };
 
@@ -176,6 +176,8 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   L.astat = take((size_t)U * (L.t.nsl + L.t.nse) * d.Hq * 2 * sizeof(float));
   L.gmax = take((size_t)U * (L.t.Lc_cap / 8) * sizeof(uint32_t));
   L.cslot = take((size_t)U * L.t.Lc_cap * 8);
+  L.tkpcnt = take((size_t)U * L.t.tk_nbp * sizeof(int));
+  L.tkhint = take((size_t)U * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -391,6 +393,8 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   dw.astat = (float*)(w + dl.astat);
   dw.gmax = (uint32_t*)(w + dl.gmax);
   dw.cslot = (uint2*)(w + dl.cslot);
+  dw.tkpcnt = (int*)(w + dl.tkpcnt);
+  dw.tkhint = (uint32_t*)(w + dl.tkhint);
   const CachePtrs cp = cache_ptrs(cache);
   const int U = (int)n_units;
 

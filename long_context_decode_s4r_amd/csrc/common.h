@@ -215,9 +215,12 @@ struct DecodeWs {
                       //            base-2 attention logits
   uint32_t* gmax;     // [U][Lc_cap / 8] largest key of each group of 8 << gsh candidates
   uint2* cslot;       // [U][Lc_cap] top-k scratch: (key, position) candidates
+  int* tkpcnt;        // [U][tk_nbp] keys >= the hint per pooling block
+  uint32_t* tkhint;   // [U] selection hint carried from the previous step (any value is valid)
   // tiling (decode_tiling)
   int Lc_cap, nsplit, chunk;  // scoring: candidate capacity, splits, split length
   int gsh;                    // top-k: groups of 8 << gsh candidates, at most kTopkGroupCap
+  int tk_nbp;                 // pooling blocks per unit, ceil(Lc_cap / kPoolChunk)
   int nsl, nhg, hb, rsl;      // attention over selected rows: row splits, head
                               // groups, heads per group, rows per split
   int nse, rse;               // attention over exact rows: splits, rows per split

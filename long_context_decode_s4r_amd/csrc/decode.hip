@@ -95,6 +95,7 @@ void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
   // top-k floor: at most kTopkGroupCap group maxima per unit
   w->gsh = 0;
   while (((lc + (8 << w->gsh) - 1) >> (3 + w->gsh)) > kTopkGroupCap) ++w->gsh;
+  w->tk_nbp = (int)((lc + kPoolChunk - 1) / kPoolChunk);
   w->nhg = (d.Hq + w->hb - 1) / w->hb;
   w->nsl = (d.k + w->rsl - 1) / w->rsl;
   const int nex = d.s + d.nrec;
@@ -1104,6 +1105,22 @@ hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs
 //   3. pooled key = max over |d| <= kappa/2 inside the candidates, stored as
 //      the float's bit pattern (scores are >= 0, so bits order like values).
 // --------------------------------------------------------------------------
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+// inclusive prefix sum over the wave: row_shr 1, 2, 4, 8 within rows of 16,
+// then row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3)
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF>(x);
+  x += dpp_i<0x112, 0xF>(x);
+  x += dpp_i<0x114, 0xF>(x);
+  x += dpp_i<0x118, 0xF>(x);
+  x += dpp_i<0x142, 0xA>(x);
+  x += dpp_i<0x143, 0xC>(x);
+  return x;
+}
+
 // min and max over the wave (xor-pattern DPP, then the four rows), in every lane
 __device__ __forceinline__ void wave_minmax_u(unsigned int& mn, unsigned int& mx) {
 #define KVLR_MM(CTRL)                                                                          \
@@ -1260,6 +1277,7 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
   //    sc index of position j is j - base
   const int jb = c0 + 8 * tid;
   unsigned int tmx = 0u;  // the largest of this thread's keys
+  uint32_t kv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   if (jb < c1) {
     if (h <= 4) {
       float win[16];  // scores at jb - 4 .. jb + 11, -inf outside the candidates
@@ -1268,7 +1286,6 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
         const int j = jb - 4 + e;
         win[e] = (j >= 0 && j < nc) ? sc[min(max(j - base, 0), kPoolChunk + 255)] : -INFINITY;
       }
-      uint32_t kv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float mx = win[e + 4];
@@ -1289,15 +1306,18 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
           if (jb + e < c1) keys[jb + e] = kv[e];
       }
     } else {
-      for (int j = jb; j < min(jb + 8, c1); ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = jb + e;
+        if (j >= c1) break;
         float mx = sc[j - base];
         for (int dd = 1; dd <= h; ++dd) {
           if (j - dd >= 0) mx = fmaxf(mx, sc[j - dd - base]);
           if (j + dd < nc) mx = fmaxf(mx, sc[j + dd - base]);
         }
-        const unsigned int kv = __float_as_uint(mx);
-        keys[j] = kv;
-        tmx = max(tmx, kv);
+        kv[e] = __float_as_uint(mx);
+        keys[j] = kv[e];
+        tmx = max(tmx, kv[e]);
       }
     }
   }
@@ -1306,6 +1326,29 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
   for (int o = 1; o < (1 << w.gsh); o <<= 1) tmx = max(tmx, (unsigned int)__shfl_xor((int)tmx, o));
   if (jb < c1 && (tid & ((1 << w.gsh) - 1)) == 0)
     w.gmax[(int64_t)u * (w.Lc_cap >> 3) + (jb >> (3 + w.gsh))] = tmx;
+  // 5. the keys >= the selection hint (the previous top-k threshold with a
+  //    margin; any value is valid, the top-k kernel checks the count), as
+  //    (key, position) in position order into this block's stretch of the
+  //    top-k slot buffer, their count into tkpcnt
+  const uint32_t hint = w.tkhint[u];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cnt += (jb + e < c1 && kv[e] >= hint) ? 1 : 0;
+  const int incl = wave_incl_scan(cnt);
+  __shared__ int ptot[4];
+  if (lane == 63) ptot[wv] = incl;
+  __syncthreads();
+  int off = incl - cnt, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    off += i < wv ? ptot[i] : 0;
+    tot += ptot[i];
+  }
+  uint2* dst = w.cslot + (int64_t)u * w.Lc_cap + c0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (jb + e < c1 && kv[e] >= hint) dst[off++] = make_uint2(kv[e], (unsigned int)(jb + e));
+  if (tid == 0) w.tkpcnt[(int64_t)u * w.tk_nbp + blk] = tot;
 }
 
 hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
@@ -1348,23 +1391,8 @@ constexpr int kTopkGroupRegs = kTopkGroupCap / kTopkThreads;  // group maxima pe
 constexpr int kTopkBinBits = 12;   // histogram digits per pass
 constexpr int kTopkBins = 1 << kTopkBinBits;
 constexpr int kTopkWaveCap = 512;  // candidates per wave kept in LDS
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
-}
-// inclusive prefix sum over the wave: row_shr 1, 2, 4, 8 within rows of 16,
-// then row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3)
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += dpp_i<0x111, 0xF>(x);
-  x += dpp_i<0x112, 0xF>(x);
-  x += dpp_i<0x114, 0xF>(x);
-  x += dpp_i<0x118, 0xF>(x);
-  x += dpp_i<0x142, 0xA>(x);
-  x += dpp_i<0x143, 0xC>(x);
-  return x;
-}
-
+constexpr int kTopkCap = 16 * kTopkWaveCap;  // hint path: candidate list capacity
+constexpr float kTopkHintMargin = 0.85f;     // hint = this x the previous threshold
 
 // exclusive block prefix sums of two counters (a, b); totals in *ta, *tb
 __device__ __forceinline__ int2 block_excl_scan2(int a, int b, int2* wtot, int* ta, int* tb) {
@@ -1437,27 +1465,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   constexpr int NW = kTopkThreads / 64;
   const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
   const uint32_t* gmx = w.gmax + (int64_t)u * (w.Lc_cap >> 3);
-  // Wave wid scans tiles [t0, t1) of 256 keys (lane l: keys 4 l .. 4 l + 3
-  // of a tile, one 16-byte load).  The split follows the capacity, so the
-  // first kTopkTileRegs tiles and the first kTopkGroupRegs group maxima per
-  // thread are requested before the unit state arrives (reads stay below
-  // Lc_cap; entries past the unit's candidates are masked later).
   const int ncap = w.Lc_cap;
-  const int ntc = (ncap + 255) / 256;
-  const int tpw = (ntc + NW - 1) / NW;
-  const int t0 = wid * tpw;
-  const int t1 = min(t0 + tpw, ntc);
-  // (unconditional loads at clamped addresses, so no branch separates them
-  // from their first use)
-  const int gsz = 8 << w.gsh;
-  const int ngcap = (ncap + gsz - 1) / gsz;  // <= kTopkThreads * kTopkGroupRegs
-  uint32_t gv[kTopkGroupRegs];  // requested first: the floor needs them first
-#pragma unroll
-  for (int i = 0; i < kTopkGroupRegs; ++i) gv[i] = gmx[min(tid + kTopkThreads * i, ngcap - 1)];
-  uint4 kt[kTopkTileRegs];
-#pragma unroll
-  for (int i = 0; i < kTopkTileRegs; ++i)
-    kt[i] = *reinterpret_cast<const uint4*>(keys + min((t0 + i) * 256 + 4 * lane, ncap - 4));
+  // 0. the hint path: the pooling blocks left their keys >= the hint in
+  //    position order; when at least kk and at most kTopkCap keys passed,
+  //    the kk-th largest key is >= the hint and those keys are the whole
+  //    candidate list.  Otherwise the full scan below runs.
+  const int nbp = w.tk_nbp;
+  const int pc = w.tkpcnt[(int64_t)u * nbp + min(tid, nbp - 1)];
+  const uint32_t hint = w.tkhint[u];
   const int32_t* si = w.stepinfo + 4 * u;
   const int k = d.k;
   if (si[2]) {
@@ -1470,8 +1485,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   const int s = d.s;
   const int nc = Lcur + 1 - d.nrec - s;
   const int kk = min(k, nc);
-  // (lens and the unused top-k slots are written at the end: a store here
-  // would stand between the prefetch and its first use)
+  // (lens and the unused top-k slots are written at the end)
   if (kk <= 0) {
     if (tid == 0) {
       c.lens[2 * u] = Lcur + 1;
@@ -1482,7 +1496,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
     return;
   }
   __shared__ __attribute__((aligned(16))) unsigned int hs[kTopkBins];
-  __shared__ uint2 cand[NW * kTopkWaveCap];  // per wave: candidates (key, position), position order
+  __shared__ uint2 cand[NW * kTopkWaveCap];  // candidates (key, position), position order
+  __shared__ int roff[kTopkThreads + 1];     // hint path: the pooling blocks' list offsets
   __shared__ int2 wtot[NW];
   __shared__ unsigned int wlo[NW], whi[NW];
   __shared__ unsigned int sh_bin, sh_kmin, sh_kmax;
@@ -1492,129 +1507,199 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
     sh_kmin = 0xFFFFFFFFu;
     sh_kmax = 0u;
   }
-  // 1. floor.  The pool kernel leaves the maximum of every group of 8 << gsh
-  //    candidates (at most kTopkGroupCap groups); register slot i of thread t
-  //    holds group t + 1024 i.  Wave w searches its own values for x_w, a lower bound (on a
-  //    grid of 2^-12 of its range) of their m_w-th largest, m_w =
-  //    ceil(kk n_w / n) for its n_w of the n values: every wave then holds
-  //    m_w values >= x_w, together >= kk values from disjoint key sets, so
-  //    floor = min_w x_w is at most the kk-th largest key.  (n < kk: no
-  //    floor.)  The values' maximum is also the keys' maximum.
-  const int ng = (nc + gsz - 1) / gsz;
-  const int nval = ng;
-  {
-    bool gok[kTopkGroupRegs];
-#pragma unroll
-    for (int i = 0; i < kTopkGroupRegs; ++i) gok[i] = tid + kTopkThreads * i < ng;
-    unsigned int mn = 0xFFFFFFFFu, mx = 0u;
-    int nw = 0;  // wave-uniform
-#pragma unroll
-    for (int i = 0; i < kTopkGroupRegs; ++i) {
-      if (gok[i]) {
-        mn = min(mn, gv[i]);
-        mx = max(mx, gv[i]);
-      }
-      nw += __popcll(__ballot(gok[i]));
-    }
-    wave_minmax_u(mn, mx);
-    unsigned int xw = 0xFFFFFFFFu;  // no values: no bound from this wave
-    if (nw > 0 && nval >= kk) {
-      const int mw = (int)(((int64_t)kk * nw + nval - 1) / nval);
-      const unsigned int rg = mx - mn;
-      const int top = rg == 0u ? -1 : 31 - __clz((int)rg);
-      const int sh = max(top + 1 - 12, 0);
-      unsigned int dv[kTopkGroupRegs];  // offsets above mn; 0 (never counted) for no value
-#pragma unroll
-      for (int i = 0; i < kTopkGroupRegs; ++i) dv[i] = gok[i] ? gv[i] - mn : 0u;
-      unsigned int t = 0u;  // offset above mn with >= mw values at or above it
-      for (int bit = top; bit >= sh; --bit) {
-        const unsigned int cand_t = t | (1u << bit);  // >= 1
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < kTopkGroupRegs; ++i)  // lanes with dv[i] >= cand_t (35: unsigned >=)
-          cnt += __popcll(__builtin_amdgcn_uicmp(dv[i], cand_t, 35));
-        if (cnt >= mw) t = cand_t;
-      }
-      xw = mn + t;
-    }
-    if (lane == 0) {
-      wlo[wid] = xw;
-      whi[wid] = mx;
-    }
-  }
-  __syncthreads();
-  unsigned int lo = wlo[0], hi = whi[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) {
-    lo = min(lo, wlo[i]);
-    hi = max(hi, whi[i]);
-  }
-  if (nval < kk) lo = 0u;  // fewer values than picks: every key is a candidate
+  const int nbu = (nc + kPoolChunk - 1) / kPoolChunk;  // pooling blocks that ran
+  int ptot, pdummy;
+  const int poff = block_excl_scan2(tid < nbu && nbu <= kTopkThreads ? pc : 0, 0, wtot, &ptot, &pdummy).x;
+  const bool fast = nbu <= kTopkThreads && ptot >= kk && ptot <= kTopkCap;  // block-uniform
   auto range_shift = [](unsigned int base, unsigned int top) {
     const unsigned int rg = top - base;
     const int bits = rg == 0u ? 0 : 32 - __clz((int)rg);
     return max(bits - kTopkBinBits, 0);
   };
-  // 2. candidates: keys >= lo, compacted per wave in position order (ballot
-  //    counts): the wave's first kTopkWaveCap go to its stretch of the LDS
-  //    list, any further ones to the wave's region of the unit's slot
-  //    buffer (indexed like the list, starting at the wave's first position,
-  //    so it never overflows).
+  unsigned int lo, hi;
+  // full scan: wave wid's stretch of tiles and its candidate list
+  const int ntc = (ncap + 255) / 256;
+  const int tpw = (ntc + NW - 1) / NW;
+  const int t0 = wid * tpw;
+  const int t1 = min(t0 + tpw, ntc);
   uint2* wlist = cand + wid * kTopkWaveCap;
   uint2* wslot = w.cslot + (int64_t)u * ncap + (int64_t)t0 * 256;
   int wcount = 0;  // wave-uniform
-  auto take_tile = [&](const uint4& kv, int t) {
-    const int j = t * 256 + 4 * lane;
-    const uint32_t kx[4] = {kv.x, kv.y, kv.z, kv.w};
-    bool p[4];
-    uint64_t bl[4];
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // lane masks of j + e < nc (36: unsigned <) and key >= lo (35: >=)
-      bl[e] = __builtin_amdgcn_uicmp((unsigned int)(j + e), (unsigned int)nc, 36) &
-              __builtin_amdgcn_uicmp(kx[e], lo, 35);
-      p[e] = (bl[e] >> lane) & 1u;
-      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bl[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bl[e], 0u));
-      tot += __popcll(bl[e]);
-    }
-    int o = wcount + before;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p[e]) {
-        const uint2 v = make_uint2(kx[e], (unsigned int)(j + e));
-        if (o < kTopkWaveCap)
-          wlist[o] = v;
-        else
-          wslot[o] = v;
-        ++o;
+  if (fast) {
+    if (tid < nbu) roff[tid] = poff;
+    if (tid == 0) roff[nbu] = ptot;
+    __syncthreads();
+    // list entry i comes from pooling block r (roff[r] <= i < roff[r + 1]);
+    // four entries per thread and round, requested together
+    auto block_of = [&](int i) {
+      int a = 0, z = nbu;
+      while (z - a > 1) {
+        const int m = (a + z) >> 1;
+        if (roff[m] <= i) a = m; else z = m;
       }
-    wcount += tot;
-  };
-  for (int r0 = 0; t0 + r0 < t1; r0 += kTopkTileRegs) {
-    if (r0 > 0) {
+      return a;
+    };
+    const uint2* src = w.cslot + (int64_t)u * ncap;
+    unsigned int mx = 0u, mn = 0xFFFFFFFFu;
+    for (int i0 = 0; i0 < ptot; i0 += 4 * kTopkThreads) {
+      uint2 e[4];
 #pragma unroll
-      for (int i = 0; i < kTopkTileRegs; ++i) {
-        const int j = (t0 + r0 + i) * 256 + 4 * lane;
-        kt[i] = *reinterpret_cast<const uint4*>(keys + min(j, ncap - 4));
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * kTopkThreads + tid;
+        if (i < ptot) {
+          const int r = block_of(i);
+          e[q] = src[(int64_t)r * kPoolChunk + (i - roff[r])];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * kTopkThreads + tid;
+        if (i < ptot) {
+          cand[i] = e[q];
+          mx = max(mx, e[q].x);
+        }
       }
     }
+    wave_minmax_u(mn, mx);
+    if (lane == 0) whi[wid] = mx;
+    __syncthreads();
+    lo = hint;
+    hi = whi[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) hi = max(hi, whi[i]);
+  } else {
+    // Wave wid scans tiles [t0, t1) of 256 keys (lane l: keys 4 l .. 4 l + 3
+    // of a tile, one 16-byte load); the group maxima are requested first.
+    // Unconditional loads at clamped addresses (reads stay below Lc_cap;
+    // entries past the unit's candidates are masked later).
+    const int gsz = 8 << w.gsh;
+    const int ngcap = (ncap + gsz - 1) / gsz;  // <= kTopkThreads * kTopkGroupRegs
+    uint32_t gv[kTopkGroupRegs];
+#pragma unroll
+    for (int i = 0; i < kTopkGroupRegs; ++i) gv[i] = gmx[min(tid + kTopkThreads * i, ngcap - 1)];
+    uint4 kt[kTopkTileRegs];
 #pragma unroll
     for (int i = 0; i < kTopkTileRegs; ++i)
-      if (t0 + r0 + i < t1 && (t0 + r0 + i) * 256 < nc) take_tile(kt[i], t0 + r0 + i);
+      kt[i] = *reinterpret_cast<const uint4*>(keys + min((t0 + i) * 256 + 4 * lane, ncap - 4));
+    // 1. floor.  The pool kernel leaves the maximum of every group of 8 << gsh
+    //    candidates (at most kTopkGroupCap groups); register slot i of thread t
+    //    holds group t + 1024 i.  Wave w searches its own values for x_w, a lower bound (on a
+    //    grid of 2^-12 of its range) of their m_w-th largest, m_w =
+    //    ceil(kk n_w / n) for its n_w of the n values: every wave then holds
+    //    m_w values >= x_w, together >= kk values from disjoint key sets, so
+    //    floor = min_w x_w is at most the kk-th largest key.  (n < kk: no
+    //    floor.)  The values' maximum is also the keys' maximum.
+    const int ng = (nc + gsz - 1) / gsz;
+    const int nval = ng;
+    {
+      bool gok[kTopkGroupRegs];
+  #pragma unroll
+      for (int i = 0; i < kTopkGroupRegs; ++i) gok[i] = tid + kTopkThreads * i < ng;
+      unsigned int mn = 0xFFFFFFFFu, mx = 0u;
+      int nw = 0;  // wave-uniform
+  #pragma unroll
+      for (int i = 0; i < kTopkGroupRegs; ++i) {
+        if (gok[i]) {
+          mn = min(mn, gv[i]);
+          mx = max(mx, gv[i]);
+        }
+        nw += __popcll(__ballot(gok[i]));
+      }
+      wave_minmax_u(mn, mx);
+      unsigned int xw = 0xFFFFFFFFu;  // no values: no bound from this wave
+      if (nw > 0 && nval >= kk) {
+        const int mw = (int)(((int64_t)kk * nw + nval - 1) / nval);
+        const unsigned int rg = mx - mn;
+        const int top = rg == 0u ? -1 : 31 - __clz((int)rg);
+        const int sh = max(top + 1 - 12, 0);
+        unsigned int dv[kTopkGroupRegs];  // offsets above mn; 0 (never counted) for no value
+  #pragma unroll
+        for (int i = 0; i < kTopkGroupRegs; ++i) dv[i] = gok[i] ? gv[i] - mn : 0u;
+        unsigned int t = 0u;  // offset above mn with >= mw values at or above it
+        for (int bit = top; bit >= sh; --bit) {
+          const unsigned int cand_t = t | (1u << bit);  // >= 1
+          int cnt = 0;
+  #pragma unroll
+          for (int i = 0; i < kTopkGroupRegs; ++i)  // lanes with dv[i] >= cand_t (35: unsigned >=)
+            cnt += __popcll(__builtin_amdgcn_uicmp(dv[i], cand_t, 35));
+          if (cnt >= mw) t = cand_t;
+        }
+        xw = mn + t;
+      }
+      if (lane == 0) {
+        wlo[wid] = xw;
+        whi[wid] = mx;
+      }
+    }
+    __syncthreads();
+    lo = wlo[0];
+    hi = whi[0];
+  #pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      lo = min(lo, wlo[i]);
+      hi = max(hi, whi[i]);
+    }
+    if (nval < kk) lo = 0u;  // fewer values than picks: every key is a candidate
+    // 2. candidates: keys >= lo, compacted per wave in position order (ballot
+    //    counts): the wave's first kTopkWaveCap go to its stretch of the LDS
+    //    list, any further ones to the wave's region of the unit's slot
+    //    buffer (indexed like the list, starting at the wave's first position,
+    //    so it never overflows).
+    auto take_tile = [&](const uint4& kv, int t) {
+      const int j = t * 256 + 4 * lane;
+      const uint32_t kx[4] = {kv.x, kv.y, kv.z, kv.w};
+      bool p[4];
+      uint64_t bl[4];
+      int before = 0, tot = 0;
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) {  // lane masks of j + e < nc (36: unsigned <) and key >= lo (35: >=)
+        bl[e] = __builtin_amdgcn_uicmp((unsigned int)(j + e), (unsigned int)nc, 36) &
+                __builtin_amdgcn_uicmp(kx[e], lo, 35);
+        p[e] = (bl[e] >> lane) & 1u;
+        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bl[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bl[e], 0u));
+        tot += __popcll(bl[e]);
+      }
+      int o = wcount + before;
+  #pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p[e]) {
+          const uint2 v = make_uint2(kx[e], (unsigned int)(j + e));
+          if (o < kTopkWaveCap)
+            wlist[o] = v;
+          else
+            wslot[o] = v;
+          ++o;
+        }
+      wcount += tot;
+    };
+    for (int r0 = 0; t0 + r0 < t1; r0 += kTopkTileRegs) {
+      if (r0 > 0) {
+  #pragma unroll
+        for (int i = 0; i < kTopkTileRegs; ++i) {
+          const int j = (t0 + r0 + i) * 256 + 4 * lane;
+          kt[i] = *reinterpret_cast<const uint4*>(keys + min(j, ncap - 4));
+        }
+      }
+  #pragma unroll
+      for (int i = 0; i < kTopkTileRegs; ++i)
+        if (t0 + r0 + i < t1 && (t0 + r0 + i) * 256 < nc) take_tile(kt[i], t0 + r0 + i);
+    }
+    if (wcount > kTopkWaveCap) {
+      // the slot entries are read back by other lanes of the same wave
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
   }
-  if (wcount > kTopkWaveCap) {
-    // the slot entries are read back by other lanes of the same wave
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-  // candidates of this thread, in position order: a contiguous share of its
-  // wave's list (neighbouring lanes hold different stretches, so the equal
-  // keys of a pooled run do not collide in one atomic)
-  const int cpl = (wcount + 63) / 64;
-  const int a0 = min(lane * cpl, wcount), a1 = min(a0 + cpl, wcount);
+  // candidates of this thread in position order: a contiguous share of the
+  // list (hint path) or of its wave's list (neighbouring lanes hold
+  // different stretches, so the equal keys of a pooled run do not collide in
+  // one atomic)
+  const int cpt = fast ? (ptot + kTopkThreads - 1) / kTopkThreads : (wcount + 63) / 64;
+  const int nlist = fast ? ptot : wcount;
+  const int a0 = min((fast ? tid : lane) * cpt, nlist), a1 = min(a0 + cpt, nlist);
   auto visit_ordered = [&](auto&& f) {
     for (int i = a0; i < a1; ++i) {
-      const uint2 e = i < kTopkWaveCap ? wlist[i] : wslot[i];
+      const uint2 e = fast ? cand[i] : (i < kTopkWaveCap ? wlist[i] : wslot[i]);
       f(e.x, (int)e.y);
     }
   };
@@ -1679,6 +1764,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
       sh_kmax = 0u;
     }
     __syncthreads();
+  }
+  if (tid == 0) {  // the next step's hint: this threshold's bin edge, with a margin
+    const unsigned int edge = lo + (bin << shift);
+    w.tkhint[u] = __float_as_uint(__uint_as_float(edge) * kTopkHintMargin);
   }
   // 4. compaction in position order: keys with (key - lo) >> shift above
   // `bin`, then the first `rem` keys of the bin; the in-bin keys taken
