@@ -124,8 +124,9 @@ int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max,
  * L = prompt length for the prefill ops, the cache capacity L_max for
  * KVLR_OP_DECODE.  *bytes (host) is written on success.  The workspace holds
  * only scratch (sample, Gram/eigensolver matrices, transposed bases, partial
- * scores, spilled logits, attention partials); its contents between calls
- * are unspecified. */
+ * scores, spilled logits, attention partials) and, for decode, a top-k speed
+ * hint; its contents between calls are unspecified and never change a
+ * result. */
 int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units,
                          int64_t L, size_t* bytes);
 
@@ -176,6 +177,10 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
  *   scores    device, optional, [U][L_max] fp32: latent score of candidate
  *             position j at index j (before pooling); other entries untouched.
  *   ws        device workspace, ws_bytes >= kvlr_workspace_bytes(DECODE, L_max).
+ *             Reusing the same workspace for consecutive steps of the same
+ *             cache lets the top-k start from the previous step's threshold
+ *             (a speed hint only: any workspace content gives the same
+ *             result).
  * Candidates are positions [s, L_t - n_recent); ties in the pooled score go to
  * the lower position. */
 int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units,
