@@ -182,9 +182,12 @@ def run_prefill(kvlr, w, prompt, L_max, eig=True):
     return kc, K, V, ek, ev
 
 
-def run_checked_steps(kvlr, w, kc, dec, steps: int, units=None, check_every: int = 1):
+def run_checked_steps(kvlr, w, kc, dec, steps: int, units=None, check_every: int = 1,
+                      ws_fill=None):
     """Run `steps` decode steps on the GPU, checking the listed units stage
-    by stage.  Returns StepStats."""
+    by stage.  ws_fill(t, ws) may overwrite the decode workspace before step
+    t (its contents between calls must never change a result).  Returns
+    StepStats."""
     U = kc.n_units
     units = list(range(U)) if units is None else units
     out = torch.empty(U, w.n_q_heads, w.head_dim, device="cuda")
@@ -197,6 +200,8 @@ def run_checked_steps(kvlr, w, kc, dec, steps: int, units=None, check_every: int
         pre = [snapshot(kc, u, w) for u in units] if chk else None
         q, k, v = dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda()
         print(f"  step {t}", flush=True)
+        if ws_fill is not None:
+            ws_fill(t, ws)
         kvlr.decode_step(kc, q, k, v, out, topk, scores, ws)
         torch.cuda.synchronize()
         if chk:

@@ -240,6 +240,33 @@ def test_very_long_context_coarse_groups_bf16(gpu_lib):
     assert st.n_checked == 2
 
 
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_workspace_contents_never_matter(gpu_lib, fill):
+    """The decode workspace is overwritten before every step (all zero
+    bytes: a hint of 0 lets every key pass; all 0xFF bytes: no key passes;
+    random bytes): the top-k's hint path and full path must give the oracle's
+    selection either way."""
+    kvlr = _kvlr()
+    w = configs.LLAMA8B_32K.with_(**_SMALL_BF16, top_k=128)
+    L, steps = 6000, 4
+    prompt = synth.make_prompt(w, L=L, batch=2)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=2)
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps + 8)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+
+    def ws_fill(t, ws):
+        print(f"  fill {fill} before step {t}", flush=True)
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=gen))
+
+    st = run_checked_steps(kvlr, w, kc, dec, steps, ws_fill=ws_fill)
+    assert st.n_checked == 2 * steps
+
+
 def test_flat_scores_tie_order_bf16(gpu_lib):
     """Zero queries make every latent logit 0, so all pooled scores tie and
     every key passes the floor (each top-k wave holds more candidates than
