@@ -414,7 +414,7 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   if (ev) (void)hipEventRecord(ev[2], st);
   if ((he = launch_pool(d, U, cp, dw, scores, st)) != hipSuccess) return hip_fail(he, "pool");
   if (ev) (void)hipEventRecord(ev[3], st);
-  if ((he = launch_topk(d, U, cp, dw, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
+  if ((he = launch_topk(d, U, cp, dw, v_new, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
   if (ev) (void)hipEventRecord(ev[4], st);
   if ((he = launch_attend(d, U, q, cp, dw, st)) != hipSuccess) return hip_fail(he, "attend");
   if (ev) (void)hipEventRecord(ev[5], st);

@@ -243,7 +243,7 @@ hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs
                         hipStream_t st);
 hipError_t launch_pool(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                        float* scores_user, hipStream_t st);
-hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, const void* v_new,
                        int32_t* topk_user, float* out, hipStream_t st);
 hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
                          const DecodeWs& w, hipStream_t st);

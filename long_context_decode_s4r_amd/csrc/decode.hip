@@ -452,21 +452,31 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
 }
 
 // --------------------------------------------------------------------------
-// prologue for bf16 storage: the same blocks as k_prologue, the products on
-// MFMA 16x16x32.  The inputs (k, v and the query heads) are bf16 and so exact
-// as operands; A = up to 16 input vectors straight from memory (K = basis
-// row index), B = basis columns, which are staged through LDS transposed
-// ([column][row], four rows per 8-byte write) so an operand is one 16-byte
-// read.  The unit state is needed only by the stores, so its load overlaps
-// the whole computation.
-//   GEMV block (32 columns of B^K or B^V): rows in chunks of kProRows; wave
-//     w takes k-steps 8 w .. 8 w + 7 of each chunk, the four waves' partial
-//     sums meet in LDS;
-//   projected-query block (KV head h): the d_h rows of head h, all r
-//     columns; wave w takes column tiles w, w + 4, ...
+// prologue for bf16 storage when d_h divides 256: grid (ncb + 1, U), 256
+// threads, products on MFMA 16x16x32.
+//   blocks [0, ncb):  32 columns of B^K each.  A = up to 16 input vectors
+//     straight from memory (row 0: k, row 1 + g: query head g of every KV
+//     head, concatenated; K = basis row index), B = basis columns staged
+//     through LDS transposed ([column][row], four rows per 8-byte write) so
+//     an operand is one 16-byte read.  Rows in chunks of kProRows; wave w
+//     takes k-steps 8 w .. 8 w + 7 of a chunk, whole heads since d_h
+//     divides 256, and leaves each head's partial products in LDS.  A
+//     head's partial of row 1 + g is the projected query q[h G + g] . B^K
+//     rows of head h (attention in the coefficient space); the sum over
+//     heads gives c^K(new) (row 0) and the window query latents (rows
+//     1 .. G).  So B^K is read once for all three.
+//   block ncb:  exact ring push of k and v; the older window rows' (m, S)
+//     updated with the candidate entering the compressed set.
+// c^V(new) is first read when the new position leaves the exact ring, at
+// least one step later, so its GEMV runs beside the top-k selection (the
+// extra blocks of that launch), off this step's critical path.
 // --------------------------------------------------------------------------
 constexpr int kProRows = 1024;
 constexpr int kProLdb = kProRows + 8;  // staged column length (bf16), padded
+
+__host__ __device__ inline bool prologue_fused(const Dims& d) {
+  return d.dtype != 0 && d.dh % 32 == 0 && 256 % d.dh == 0 && d.G + 1 <= 16;
+}
 
 __device__ __forceinline__ void stage_quad_t(uint16_t* bt, int ldb, int col, int row, const u16x8 (&v)[4]) {
   // rows row .. row + 3 of the 8 columns col .. col + 7, written transposed
@@ -475,6 +485,91 @@ __device__ __forceinline__ void stage_quad_t(uint16_t* bt, int ldb, int col, int
     const uint32_t lo = (uint32_t)v[0][x] | ((uint32_t)v[1][x] << 16);
     const uint32_t hi = (uint32_t)v[2][x] | ((uint32_t)v[3][x] << 16);
     *reinterpret_cast<uint2*>(bt + (col + x) * ldb + row) = make_uint2(lo, hi);
+  }
+}
+
+// state block, bf16 storage: every load (the new k and v, the entering
+// candidate's key coefficients, the window rows' query latents and their
+// (m, S)) is requested before the first use, so the block costs about one
+// memory round trip.  Wave w takes window rows w, w + 4, ...; lane l holds
+// columns 4 l .. 4 l + 3 (rank <= 256).
+__device__ __forceinline__ void prologue_state_bf16(const Dims& d, const CachePtrs& c, const uint16_t* __restrict__ kn,
+                                                    const uint16_t* __restrict__ vn, float qscale, int u, int tid,
+                                                    int32_t Lcur, int32_t steps) {
+  const int D = d.D, r = d.r, G = d.G, W = d.W;
+  const int l = tid & 63, wv = tid >> 6;
+  const int64_t p = Lcur;
+  const int rs = (int)(p % d.nrec);
+  constexpr int NP = (4096 / 8 + 255) / 256;  // D <= 4096
+  const int np = D / 8;
+  u16x8 bk[NP], bv[NP];
+  const u16x8* sk = reinterpret_cast<const u16x8*>(kn + (int64_t)u * D);
+  const u16x8* sv = reinterpret_cast<const u16x8*>(vn + (int64_t)u * D);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pc = min(tid + 256 * i, np - 1);
+    bk[i] = sk[pc];
+    bv[i] = sv[pc];
+  }
+  const int weff = min(steps + 1, W);
+  const int nold = (weff - 1) * G;
+  const int c4 = min(4 * l, r - 4);
+  const bool cok = 4 * l < r;
+  const int64_t pe = (int64_t)Lcur - d.nrec;  // candidate entering the compressed set
+  const uint16_t* cep = (const uint16_t*)c.coef_k + ((int64_t)u * c.Lmax + max(pe, (int64_t)0)) * r + c4;
+  const uint2 cer = *reinterpret_cast<const uint2*>(cep);
+  constexpr int RB = 16;  // window rows per wave and batch
+  f32x4 qv[RB];
+  float2 st = make_float2(0.f, 0.f);
+  auto row_of = [&](int o, int* sl, int* g) {
+    const int i = 1 + o / G;
+    *g = o % G;
+    *sl = wrap_slot(steps - i, W);
+  };
+  auto issue = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      int sl, g;
+      row_of(min(wv + 4 * (m0 + i), max(nold - 1, 0)), &sl, &g);
+      qv[i] = *reinterpret_cast<const f32x4*>(c.qwin + (((int64_t)u * W + sl) * G + g) * r + c4);
+    }
+    int sl, g;
+    row_of(min(wv + 4 * (m0 + (l & (RB - 1))), max(nold - 1, 0)), &sl, &g);
+    st = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2);
+  };
+  if (nold > 0) issue(0);
+  u16x8* dk = reinterpret_cast<u16x8*>((uint16_t*)c.ring_k + ((int64_t)u * d.nrec + rs) * D);
+  u16x8* dv = reinterpret_cast<u16x8*>((uint16_t*)c.ring_v + ((int64_t)u * d.nrec + rs) * D);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pc = tid + 256 * i;
+    if (pc < np) {
+      dk[pc] = bk[i];
+      dv[pc] = bv[i];
+    }
+  }
+  if (nold <= 0) return;
+  const float ce0 = cok ? bf2f((uint16_t)(cer.x & 0xffffu)) : 0.f, ce1 = cok ? bf2f((uint16_t)(cer.x >> 16)) : 0.f;
+  const float ce2 = cok ? bf2f((uint16_t)(cer.y & 0xffffu)) : 0.f, ce3 = cok ? bf2f((uint16_t)(cer.y >> 16)) : 0.f;
+  for (int m0 = 0; wv + 4 * m0 < nold; m0 += RB) {
+    if (m0 > 0) issue(m0);
+    float zl = 0.f;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      float z = (qv[i][0] * ce0 + qv[i][1] * ce1) + (qv[i][2] * ce2 + qv[i][3] * ce3);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
+      if (l == i) zl = z;
+    }
+    const int o = wv + 4 * (m0 + l);
+    if (l < RB && o < nold) {
+      int sl, g;
+      row_of(o, &sl, &g);
+      const float z = zl * qscale;
+      const float mn = fmaxf(st.x, z);
+      *reinterpret_cast<float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2) =
+          make_float2(mn, st.y * exp2f(st.x - mn) + exp2f(z - mn));
+    }
   }
 }
 
@@ -487,161 +582,171 @@ __global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, cons
   const int D = d.D, r = d.r, G = d.G, W = d.W, dh = d.dh, Hq = d.Hq;
   extern __shared__ __attribute__((aligned(16))) float sm[];
   const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
+  const bool live = (int64_t)Lcur < c.Lmax;
   if (b == 0 && tid == 0) {
     w.stepinfo[4 * u + 0] = Lcur;
     w.stepinfo[4 * u + 1] = steps;
-    w.stepinfo[4 * u + 2] = (int64_t)Lcur >= c.Lmax ? 1 : 0;
+    w.stepinfo[4 * u + 2] = live ? 0 : 1;
     w.stepinfo[4 * u + 3] = 0;
   }
-  if (b == 2 * ncb) {
-    if ((int64_t)Lcur >= c.Lmax) return;
-    prologue_state<uint16_t>(d, c, kn, vn, w, qscale, u, tid, Lcur, steps, sm);
+  if (b == ncb) {
+    if (live) prologue_state_bf16(d, c, kn, vn, qscale, u, tid, Lcur, steps);
     return;
   }
   uint16_t* bt = reinterpret_cast<uint16_t*>(sm);
+  float* red = sm + 32 * kProLdb / 2;  // [heads of a chunk][16 vectors][32 columns]
   const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u16x8{});
-  if (b < 2 * ncb) {
-    const int kind = b >= ncb ? 1 : 0;
-    const int col0 = (kind ? b - ncb : b) * 32;
-    const int nvec = kind == 0 ? 1 + G : 1;
-    const uint16_t* B = (const uint16_t*)(kind ? c.basis_v : c.basis_k) + (int64_t)u * D * r;
-    float* red = sm + 32 * kProLdb / 2;  // [4 waves][16][32]
-    const int cq = tid & 3, a4 = 4 * (tid >> 2);
-    const int colq = min(col0 + 8 * cq, r - 8);  // columns past r: computed, not stored
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    for (int r0 = 0; r0 < D; r0 += kProRows) {
-      u16x8 pc[4][4];
+  const int col0 = b * 32;
+  const int nvec = 1 + G;
+  const uint16_t* B = (const uint16_t*)c.basis_k + (int64_t)u * D * r;
+  const int cq = tid & 3, a4 = 4 * (tid >> 2);
+  const int colq = min(col0 + 8 * cq, r - 8);  // columns past r: computed, not stored
+  float run[2] = {0.f, 0.f};                   // sums over heads of outputs tid, tid + 256
+  for (int r0 = 0; r0 < D; r0 += kProRows) {
+    u16x8 pc[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          pc[j][qq] = *reinterpret_cast<const u16x8*>(
-              B + (int64_t)min(r0 + a4 + 256 * j + qq, D - 1) * r + colq);
-      // A: input vector n16 (0: k or v, 1 + g: the query heads of group g,
-      // concatenated over the KV heads), elements kk .. kk + 7
-      bf16x8 xa[8];
+      for (int qq = 0; qq < 4; ++qq)
+        pc[j][qq] = *reinterpret_cast<const u16x8*>(B + (int64_t)min(r0 + a4 + 256 * j + qq, D - 1) * r + colq);
+    // A: vector n16, elements kk .. kk + 7
+    bf16x8 xa[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int kk = r0 + 32 * (8 * wv + ks) + 8 * kq;
-        xa[ks] = zero8;
-        if (n16 < nvec && kk < D) {
-          const uint16_t* src = n16 == 0 ? (kind ? vn : kn) + (int64_t)u * D + kk
-                                         : q + ((int64_t)u * Hq + (kk / dh) * G + (n16 - 1)) * dh + kk % dh;
-          xa[ks] = ld_bf16x8(src);
-        }
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kk = r0 + 32 * (8 * wv + ks) + 8 * kq;
+      xa[ks] = zero8;
+      if (n16 < nvec && kk < D) {
+        const uint16_t* src = n16 == 0 ? kn + (int64_t)u * D + kk
+                                       : q + ((int64_t)u * Hq + (kk / dh) * G + (n16 - 1)) * dh + kk % dh;
+        xa[ks] = ld_bf16x8(src);
       }
-      if (r0 > 0) __syncthreads();  // the previous chunk's operand reads are done
+    }
+    if (r0 > 0) __syncthreads();  // the previous chunk's operand and partial reads are done
 #pragma unroll
-      for (int j = 0; j < 4; ++j) stage_quad_t(bt, kProLdb, 8 * cq, a4 + 256 * j, pc[j]);
-      __syncthreads();
+    for (int j = 0; j < 4; ++j) stage_quad_t(bt, kProLdb, 8 * cq, a4 + 256 * j, pc[j]);
+    __syncthreads();
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int kr = 32 * (8 * wv + ks);
-        if (r0 + kr < D) {
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kr = 32 * (8 * wv + ks);
+      if (r0 + kr < D) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * t + n16) * kProLdb + kr + 8 * kq);
+          acc[t] = mfma16x16x32(xa[ks], bo, acc[t]);
+        }
+        if ((kr + 32) % dh == 0) {  // last k-step of head (r0 + kr) / dh: its partial, lane holds
+          const int hc = kr / dh;    // vectors 4 kq + i, columns 16 t + n16
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * t + n16) * kProLdb + kr + 8 * kq);
-            acc[t] = mfma16x16x32(xa[ks], bo, acc[t]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[(hc * 16 + 4 * kq + i) * 32 + 16 * t + n16] = acc[t][i];
+            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
     }
-    // the waves' partial sums: lane holds vectors 4 kq + i, columns 16 t + n16
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(wv * 16 + 4 * kq + i) * 32 + 16 * t + n16] = acc[t][i];
     __syncthreads();
-    if ((int64_t)Lcur >= c.Lmax) return;
-    const int64_t p = Lcur;
-    for (int o = tid; o < nvec * 32; o += 256) {
-      const int v = o >> 5, cc = o & 31, cl = col0 + cc;
-      if (cl >= r) continue;
-      const float sum = (red[v * 32 + cc] + red[(16 + v) * 32 + cc]) +
-                        (red[(32 + v) * 32 + cc] + red[(48 + v) * 32 + cc]);
-      if (v == 0) {
-        uint16_t* C = (uint16_t*)(kind == 0 ? c.coef_k : c.coef_v);
-        C[((int64_t)u * c.Lmax + p) * r + cl] = f2bf(sum);
-      } else {
-        const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
-        c.qwin[row * r + cl] = sum;
-        const float x = sum * qscale;  // MFMA operands of the latent scoring
-        const uint16_t hb = f2bf(x);
-        c.qsplit[(row * 2 + 0) * r + cl] = hb;
-        c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
-      }
-    }
-    return;
-  }
-  // ---- projected queries: qlat[h G + g] = ascale * q[h G + g] . B^K rows of head h
-  const int h = b - 2 * ncb - 1;
-  const int ldq = dh + 8;
-  const uint16_t* B = (const uint16_t*)c.basis_k + ((int64_t)u * D + (int64_t)h * dh) * r;
-  const int nqc = (dh / 4) * (r / 8);  // (row quad, column chunk) items
-  for (int i0 = 0; i0 < nqc; i0 += 4 * 256) {
-    u16x8 pc[4][4];
-    // item it: row quad 8 (it / (8 ncc)) + it % 8, column chunk (it / 8) % ncc
-    // (eight lanes read 128 contiguous bytes of a row; the transposed writes
-    // of a wave spread over the banks)
-    const int ncc = r / 8;
-    auto quad = [&](int it) { return 4 * ((it % 8) + 8 * (it / (8 * ncc))); };
-    auto chunk = [&](int it) { return 8 * ((it / 8) % ncc); };
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int it = min(i0 + tid + 256 * m, nqc - 1);
-      const int rq = quad(it), cc = chunk(it);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        pc[m][qq] = *reinterpret_cast<const u16x8*>(B + (int64_t)(rq + qq) * r + cc);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int it = i0 + tid + 256 * m;
-      if (it < nqc) stage_quad_t(bt, ldq, chunk(it), quad(it), pc[m]);
-    }
-  }
-  // A: query head h G + n16 (zero past G), channels 32 ks + 8 kq
-  const int nks = dh / 32;
-  bf16x8 qa[8];
-  {
-    const uint16_t* qh = q + ((int64_t)u * Hq + h * G + min(n16, G - 1)) * dh;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qa[ks] = (n16 < G && ks < nks) ? ld_bf16x8(qh + 32 * ks + 8 * kq) : zero8;
-  }
-  __syncthreads();
-  const bool live = (int64_t)Lcur < c.Lmax;
-  for (int tile = wv; tile < r / 16; tile += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks < nks) {
-        const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * tile + n16) * ldq + 32 * ks + 8 * kq);
-        acc = mfma16x16x32(qa[ks], bo, acc);
-      }
-    }
-    // lane: heads 4 kq + i, column 16 tile + n16
+    const int nhc = min(kProRows, D - r0) / dh;  // heads of this chunk
     if (live) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int g = 4 * kq + i;
-        if (g < G) {
-          const float x = acc[i] * ascale;
-          uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + ((int64_t)u * Hq + h * G + g) * 2 * r + 16 * tile + n16;
+      for (int o = tid; o < nhc * G * 32; o += 256) {
+        const int cc = o & 31, hg = o >> 5, hc = hg / G, g = hg % G, cl = col0 + cc;
+        if (cl < r) {
+          const float x = red[(hc * 16 + 1 + g) * 32 + cc] * ascale;
+          const int h = r0 / dh + hc;
+          uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + ((int64_t)u * Hq + h * G + g) * 2 * r + cl;
           const uint16_t hb = f2bf(x);
           ql[0] = hb;
           ql[r] = f2bf(x - bf2f(hb));
         }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int o = tid + 256 * j;
+      if (o < nvec * 32) {
+        const int v = o >> 5, cc = o & 31;
+        float s = 0.f;
+        for (int hc = 0; hc < nhc; ++hc) s += red[(hc * 16 + v) * 32 + cc];
+        run[j] += s;
+      }
+    }
+  }
+  if (!live) return;
+  const int64_t p = Lcur;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int o = tid + 256 * j;
+    const int v = o >> 5, cc = o & 31, cl = col0 + cc;
+    if (o >= nvec * 32 || cl >= r) continue;
+    const float sum = run[j];
+    if (v == 0) {
+      uint16_t* C = (uint16_t*)c.coef_k;
+      C[((int64_t)u * c.Lmax + p) * r + cl] = f2bf(sum);
+    } else {
+      const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
+      c.qwin[row * r + cl] = sum;
+      const float x = sum * qscale;  // MFMA operands of the latent scoring
+      const uint16_t hb = f2bf(x);
+      c.qsplit[(row * 2 + 0) * r + cl] = hb;
+      c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
+    }
   }
 }
 
 static size_t prologue_mfma_lds(const Dims& d) {
-  const size_t gemv = (size_t)32 * kProLdb * 2 + (size_t)4 * 16 * 32 * 4;
-  const size_t qlat = (size_t)d.r * (d.dh + 8) * 2;
-  const size_t state = (size_t)d.r * 4;
-  size_t m = gemv > qlat ? gemv : qlat;
-  return m > state ? m : state;
+  const int nh = (d.D < kProRows ? d.D : kProRows) / d.dh;
+  return (size_t)32 * kProLdb * 2 + (size_t)nh * 16 * 32 * 4;
+}
+
+// c^V(new) = v_cat . B^V, 32 columns per block of 1024 threads: thread
+// (row group tid / 4, column octet tid % 4) takes rows rg, rg + 256, ...;
+// row-group sums meet over lanes, then over the 16 waves in LDS.  Blocks
+// of the top-k launch (see the prologue).
+__device__ __forceinline__ void value_coef_block(const Dims& d, const CachePtrs& c, const DecodeWs& w,
+                                                 const uint16_t* __restrict__ vn, int u, int vb, int tid) {
+  __shared__ float vred[16 * 32];
+  const int32_t* si = w.stepinfo + 4 * u;
+  if (si[2]) return;  // no append
+  const int64_t p = si[0];
+  const int D = d.D, r = d.r;
+  const int cq = tid & 3, rg = tid >> 2;
+  const int col = min(32 * vb + 8 * cq, r - 8);
+  const uint16_t* B = (const uint16_t*)c.basis_v + (int64_t)u * D * r;
+  const uint16_t* x = vn + (int64_t)u * D;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r0 = 0; r0 < D; r0 += 1024) {
+    u16x8 bw[4];
+    float xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + rg + 256 * i;
+      bw[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)min(row, D - 1) * r + col);
+      xv[i] = row < D ? bf2f(x[row]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv[i], bf2f(bw[i][e]), acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int m = 4; m < 64; m <<= 1) acc[e] += __shfl_xor(acc[e], m);
+  const int l = tid & 63, wv = tid >> 6;
+  if (l < 4)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vred[wv * 32 + 8 * l + e] = acc[e];
+  __syncthreads();
+  if (tid < 32) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += vred[i * 32 + tid];
+    const int cl = 32 * vb + tid;
+    if (cl < r) ((uint16_t*)c.coef_v)[((int64_t)u * c.Lmax + p) * r + cl] = f2bf(s);
+  }
 }
 
 hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_new,
@@ -660,12 +765,12 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
   if (d.dtype == 0) {
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
                        (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb);
-  } else if (d.dh % 32 == 0) {
+  } else if (prologue_fused(d)) {
     static size_t done = 0;
     const size_t lm = prologue_mfma_lds(d);
     hipError_t e = allow_lds(&k_prologue_mfma, lm, &done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prologue_mfma, grid, dim3(256), lm, st, d, c, (const uint16_t*)q,
+    hipLaunchKernelGGL(k_prologue_mfma, dim3(ncb + 1, U), dim3(256), lm, st, d, c, (const uint16_t*)q,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
   } else {
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
@@ -1458,9 +1563,14 @@ __device__ __forceinline__ void topk_find_bin(const unsigned int* hs, int nb, in
 }
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, DecodeWs w,
+                                               const uint16_t* __restrict__ vn,
                                                int32_t* __restrict__ topk_user,
                                                float* __restrict__ out) {
-  const int u = blockIdx.x, tid = threadIdx.x;
+  const int u = blockIdx.y, tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    value_coef_block(d, c, w, vn, u, blockIdx.x - 1, tid);
+    return;
+  }
   const int lane = tid & 63, wid = tid >> 6;
   constexpr int NW = kTopkThreads / 64;
   const uint32_t* keys = w.keys + (int64_t)u * w.Lc_cap;
@@ -1820,9 +1930,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
     for (int i = kk + tid; i < k; i += kTopkThreads) topk_user[(int64_t)u * k + i] = -1;
 }
 
-hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
+hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, const void* v_new,
                        int32_t* topk_user, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3(U), dim3(kTopkThreads), 0, st, d, c, w, topk_user, out);
+  const int nvb = prologue_fused(d) ? d.r / 32 : 0;  // c^V(new) blocks, see the prologue
+  hipLaunchKernelGGL(k_topk, dim3(1 + nvb, U), dim3(kTopkThreads), 0, st, d, c, w,
+                     (const uint16_t*)v_new, topk_user, out);
   return hipGetLastError();
 }
 

@@ -240,6 +240,20 @@ def test_very_long_context_coarse_groups_bf16(gpu_lib):
     assert st.n_checked == 2
 
 
+@pytest.mark.parametrize("heads", [(8, 4, 32), (4, 2, 96), (12, 12, 128)],
+                         ids=["dh32", "dh96", "D1536"])
+def test_prologue_head_shapes_bf16(gpu_lib, heads):
+    """bf16 prologue shapes: d_h = 32 (eight heads per wave of the fused B^K
+    pass), d_h = 96 (does not divide 256: the general prologue, with c^V(new)
+    in the prologue) and D' = 1536 (the fused pass in two row chunks)."""
+    Hq, Hkv, dh = heads
+    w = configs.LLAMA8B_32K.with_(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh, rank=64, q_window=4,
+                                  n_recent=16, n_sample=256, model="power", exponents=(0.8,),
+                                  top_k=64)
+    st = _run(w, 3000, 2, 3)
+    assert st.n_checked == 6
+
+
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
 def test_workspace_contents_never_matter(gpu_lib, fill):
     """The decode workspace is overwritten before every step (all zero
