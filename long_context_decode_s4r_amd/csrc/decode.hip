@@ -781,7 +781,8 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
 
 // --------------------------------------------------------------------------
 // latent scoring, bf16 storage: grid (nsplit, U), 512 threads (8 waves, two
-// per SIMD).
+// per SIMD).  A unit's 64-position tiles are dealt round-robin over its
+// nsplit blocks.
 //
 // Key coefficients stream through a 4-stage LDS ring, 64 positions per tile,
 // filled by direct global->LDS loads (global_load_lds_dwordx4), three tiles
@@ -804,8 +805,8 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
 // bits) and the column blocks w / NG + (8 / NG) j of every tile.  The
 // K-index permutation gives lane (n, kq) of both operands the chunks
 // 4 ks + kq.  Per position, a group's probability sum over its rows lands in
-// an LDS segment buffer; every 256 positions the block sums the groups and
-// stores the segment, together with the current rows' logits.
+// an LDS segment buffer; every 8 tiles the block sums the groups and stores
+// the segment, together with the current rows' logits.
 // --------------------------------------------------------------------------
 constexpr int kScoreTP = 64;     // positions per tile
 constexpr int kScoreSeg = 512;   // positions per output segment (buffered in LDS)
@@ -861,12 +862,11 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
   const int nrb = (W * G + 15) / 16;
   const int ngr = (nrb + RBW - 1) / RBW;       // groups holding row blocks
   const int64_t cend = (int64_t)Lcur + 1 - d.nrec;
-  // the unit's candidates split evenly over the grid, in whole tiles
-  const int64_t per = (max(cend - s, (int64_t)0) + w.nsplit - 1) / w.nsplit;
-  const int64_t chunk = (per + kScoreTP - 1) / kScoreTP * kScoreTP;
-  const int64_t j0 = s + (int64_t)split * chunk;
-  const int64_t j1 = min(j0 + chunk, cend);
-  const int npos = (int)max(j1 - j0, (int64_t)0);
+  // the unit's candidate tiles dealt round-robin over the splits: tile t of
+  // this block is the unit's tile t * nsplit + split, so at any moment the
+  // unit's blocks stream neighbouring tiles
+  const int64_t ntu = (max(cend - s, (int64_t)0) + kScoreTP - 1) / kScoreTP;
+  const int ntl = ntu > split ? (int)((ntu - split + w.nsplit - 1) / w.nsplit) : 0;
 
   // ---- DMA of one tile into a stage ----------------------------------------
   // Piece q of this lane: LDS row pl, slot sl holds global chunk sl ^ (pl & SWZ);
@@ -901,10 +901,11 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
       }
     }
   };
-  // the block's tiles: t covers positions j0 + t * TP + [0, TP); requests past
-  // the last tile re-read it (harmless, keeps the ring's count uniform)
-  const int ntl = (npos + kScoreTP - 1) / kScoreTP;
-  auto tp = [&](int t) { return j0 + (int64_t)min(t, max(ntl - 1, 0)) * kScoreTP; };
+  // the block's tiles: t covers positions tp(t) + [0, TP); requests past the
+  // last tile re-read it (harmless, keeps the ring's count uniform)
+  auto tp = [&](int t) {
+    return (int64_t)s + ((int64_t)min(t, max(ntl - 1, 0)) * w.nsplit + split) * kScoreTP;
+  };
   if (ntl > 0) {  // prime the ring before the operand loads below
     issue(tp(0), st0.b);
     issue(tp(1), st1.b);
@@ -955,7 +956,7 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
   // positions this lane flushes
   float nm = -INFINITY, ns = 0.f;
 
-  // tile t of the block (positions j0 + t*TP + pl; segment slot (t % SEGT)*TP + pl)
+  // tile t of the block (positions tp(t) + pl; segment slot (t % SEGT)*TP + pl)
   auto compute = [&](int t, const uint8_t* stage) {
     if (!wact) return;
     const uint32_t sbase = lds_offset(stage);
@@ -1007,29 +1008,30 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
     }
   };
 
-  float* partial = w.partial + (int64_t)u * w.Lc_cap + (j0 - s);
-  float* spill = w.spill + (int64_t)u * G * w.Lc_cap + (j0 - s);
-  // flush of segment sg, four positions per lane and one 16-byte store per
-  // wave: the last wave stores the group sums, wave g < G the current row g's
-  // logits (and folds them into its running max and sum)
+  float* partial = w.partial + (int64_t)u * w.Lc_cap - s;           // [position]
+  float* spill = w.spill + (int64_t)u * G * w.Lc_cap - s;            // [row][position]
+  // flush of segment sg (the block's tiles SEGT sg ..), four positions per
+  // lane and one 16-byte store per wave: the last wave stores the group sums,
+  // wave g < G the current row g's logits (and folds them into its running
+  // max and sum); positions from cend on are not stored
   auto flush = [&](int sg) {
-    const int seg0 = sg * kScoreSeg;
-    const int segn = min(kScoreSeg, npos - seg0);
 #pragma unroll
     for (int e0 = 4 * l; e0 < kScoreSeg; e0 += 256) {
-    if (wv == kScoreWaves - 1 && e0 < segn) {
+    const int t = sg * SEGT + e0 / kScoreTP;
+    const int64_t pos = tp(t) + e0 % kScoreTP;
+    const int ne = t < ntl ? (int)min((int64_t)4, cend - pos) : 0;
+    if (wv == kScoreWaves - 1 && ne > 0) {
       f32x4 sum = *reinterpret_cast<const f32x4*>(&segred[0][e0]);
       for (int q2 = 1; q2 < ngr; ++q2) sum += *reinterpret_cast<const f32x4*>(&segred[q2][e0]);
-      if (e0 + 4 <= segn) {
-        *reinterpret_cast<f32x4*>(partial + seg0 + e0) = sum;
+      if (ne == 4) {
+        *reinterpret_cast<f32x4*>(partial + pos) = sum;
       } else {
-        for (int e = 0; e < segn - e0; ++e) partial[seg0 + e0 + e] = sum[e];
+        for (int e = 0; e < ne; ++e) partial[pos + e] = sum[e];
       }
     }
-    if (wv < G && e0 < segn) {
+    if (wv < G && ne > 0) {
       const f32x4 z = *reinterpret_cast<const f32x4*>(&segspill[wv][e0]);
-      float* dst = spill + (int64_t)wv * w.Lc_cap + seg0 + e0;
-      const int ne = min(4, segn - e0);
+      float* dst = spill + (int64_t)wv * w.Lc_cap + pos;
       if (ne == 4) {
         *reinterpret_cast<f32x4*>(dst) = z;
       } else {
