@@ -495,39 +495,47 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
 
 // grid ((nb/2)^2 + (n/64)(nb/2), nmat), 256 threads: the in-place update of
 // A's tiles (P, P') and V's tiles (row tile R, pair P) of outer round k.
-// Thread (ti, tj) computes the 4 x 4 outputs at rows 4 ti, columns 4 tj.
+// The 64 x 64 x 64 products run on fp64 MFMA 16x16x4 (lane l: A[l % 16][l / 16],
+// B[l / 16][l % 16]; D element v at row l / 16 + 4 v, column l % 16); wave w
+// computes the 32 x 32 quadrant (w / 2, w % 2), four 16 x 16 tiles, with
+// both operands read from LDS (row stride 65 doubles: the transposed stores
+// of 16 lanes land in distinct banks).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kBJLd = kBJ2 + 1;
+
 __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
                                                     double* __restrict__ Vall,
                                                     const double* __restrict__ Qall,
                                                     const int* __restrict__ frozen, int n, int k) {
   const int m = blockIdx.y;
   if (frozen[m]) return;
-  const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+  const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x;
+  const int l = tid & 63, w = tid >> 6, qi = w >> 1, qj = w & 1, c16 = l & 15, r4 = l >> 4;
   const int tile = blockIdx.x;
-  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJ2];   // the tile (V: transposed)
-  __shared__ __attribute__((aligned(16))) double Q1[kBJ2][kBJ2];  // Q_P (then the second factor)
+  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJLd];   // the tile (V: transposed)
+  __shared__ __attribute__((aligned(16))) double Q1[kBJ2][kBJLd];  // Q_P (then the second factor)
   const double* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
-  double acc[4][4];
-  auto gemm = [&](const double (*Ak)[kBJ2], const double (*Bk)[kBJ2]) {
-    // acc[i][j] = sum_k Ak[k][4 ti + i] * Bk[k][4 tj + j]
+  f64x4 acc[2][2];
+  // acc[ti][tj][v] = sum_k Ak[k][32 qi + 16 ti + r4 + 4 v] Bk[k][32 qj + 16 tj + c16]
+  auto gemm = [&](const double (*Ak)[kBJLd], const double (*Bk)[kBJLd]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-#pragma unroll 8
-    for (int kk = 0; kk < kBJ2; ++kk) {
-      double a[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = Ak[kk][4 * ti + i];
-        bv[i] = Bk[kk][4 * tj + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bv[j], acc[i][j]);
+      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int ks = 0; ks < kBJ2 / 4; ++ks) {
+      const int kr = 4 * ks + r4;
+      const double a0 = Ak[kr][32 * qi + c16], a1 = Ak[kr][32 * qi + 16 + c16];
+      const double b0 = Bk[kr][32 * qj + c16], b1 = Bk[kr][32 * qj + 16 + c16];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
   };
+  // output element (ti, tj, v) of this lane: row orow(ti, v), column ocol(tj)
+  auto orow = [&](int ti, int v) { return 32 * qi + 16 * ti + r4 + 4 * v; };
+  auto ocol = [&](int tj) { return 32 * qj + 16 * tj + c16; };
   if (tile < np * np) {
     const int P = tile / np, P2 = tile % np;
     int I, J, I2, J2;
@@ -536,44 +544,63 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
     double* A = Aall + (int64_t)m * n * n;
     const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
     const double* QP2 = Qm + (int64_t)P2 * kBJ2 * kBJ2;
-    for (int e = tid; e < kBJ2 * kBJ2; e += 256) {
-      const int i = e / kBJ2, j = e % kBJ2;
-      X[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2)];
-      Q1[i][j] = QP[e];
+    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
+      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+      const double2 x = *reinterpret_cast<const double2*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
+      const double2 q = *reinterpret_cast<const double2*>(QP + i * kBJ2 + j);
+      X[i][j] = x.x;
+      X[i][j + 1] = x.y;
+      Q1[i][j] = q.x;
+      Q1[i][j + 1] = q.y;
     }
     __syncthreads();
     gemm(Q1, X);  // T = Q_P^T X
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) X[4 * tj + j][4 * ti + i] = acc[i][j];  // X <- T^T
-    for (int e = tid; e < kBJ2 * kBJ2; e += 256) Q1[e / kBJ2][e % kBJ2] = QP2[e];
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) X[ocol(tj)][orow(ti, v)] = acc[ti][tj][v];  // X <- T^T
+    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
+      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+      const double2 q = *reinterpret_cast<const double2*>(QP2 + i * kBJ2 + j);
+      Q1[i][j] = q.x;
+      Q1[i][j + 1] = q.y;
+    }
     __syncthreads();
     gemm(X, Q1);  // T Q_P2
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        A[(int64_t)bj_index(4 * ti + i, I, J) * n + bj_index(4 * tj + j, I2, J2)] = acc[i][j];
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          A[(int64_t)bj_index(orow(ti, v), I, J) * n + bj_index(ocol(tj), I2, J2)] = acc[ti][tj][v];
   } else {
     const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
     int I, J;
     bj_pair(P, k, nb, &I, &J);
     double* V = Vall + (int64_t)m * n * n;
     const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
-    for (int e = tid; e < kBJ2 * kBJ2; e += 256) {
-      const int i = e / kBJ2, j = e % kBJ2;
-      X[j][i] = V[(int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J)];
-      Q1[i][j] = QP[e];
+    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
+      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+      const double2 x = *reinterpret_cast<const double2*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
+      const double2 q = *reinterpret_cast<const double2*>(QP + i * kBJ2 + j);
+      X[j][i] = x.x;
+      X[j + 1][i] = x.y;
+      Q1[i][j] = q.x;
+      Q1[i][j + 1] = q.y;
     }
     __syncthreads();
     gemm(X, Q1);  // V[R, P] Q_P
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        V[(int64_t)(kBJ2 * R + 4 * ti + i) * n + bj_index(4 * tj + j, I, J)] = acc[i][j];
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          V[(int64_t)(kBJ2 * R + orow(ti, v)) * n + bj_index(ocol(tj), I, J)] = acc[ti][tj][v];
   }
 }
 
