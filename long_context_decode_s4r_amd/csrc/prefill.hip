@@ -435,6 +435,13 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   __syncthreads();
   const int a = tid / NP, b = tid % NP;          // this thread's 2x2 block of S
   const int qrow = tid / NP, qb = tid % NP;      // Q rows qrow and qrow + 32, pair qb
+  // cross rounds keep Q in registers: pair qb of round kr is (qb, 32 + (qb +
+  // kr) % 32), so this thread holds x = Q[row][qb] and y = Q[row][32 + (qb +
+  // kr) % 32] for its two rows, and after each round takes y from the lane of
+  // pair qb + 1 (mod 32) of the same half-wave; self rounds use Q in LDS
+  const bool qreg = k >= 0;
+  double x0 = qrow == qb ? 1.0 : 0.0, y0 = 0.0, x1 = 0.0, y1 = x0;
+  const int ysrc = (tid & 32) | ((tid + 1) & 31);
   {
     for (int kr = 0; kr < nround; ++kr) {
       if (tid < NP) {
@@ -464,8 +471,6 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
       const int pb = pi[kr][b], qbb = qi[kr][b];
       const int pq = pi[kr][qb], qq = qi[kr][qb];
       const double m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
-      const double v00 = Q[qrow][pq], v01 = Q[qrow][qq];
-      const double v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
       const double cq = rc[qb], sq = rs[qb];
       if (a == b) {
         const double ta = rt[a];
@@ -482,15 +487,33 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
         S[qa][pb] = cb * r10 - sb * r11;
         S[qa][qbb] = sb * r10 + cb * r11;
       }
-      Q[qrow][pq] = cq * v00 - sq * v01;
-      Q[qrow][qq] = sq * v00 + cq * v01;
-      Q[qrow + NP][pq] = cq * v10 - sq * v11;
-      Q[qrow + NP][qq] = sq * v10 + cq * v11;
+      if (qreg) {
+        const double n0 = sq * x0 + cq * y0, n1 = sq * x1 + cq * y1;
+        x0 = cq * x0 - sq * y0;
+        x1 = cq * x1 - sq * y1;
+        y0 = kr + 1 < nround ? __shfl(n0, ysrc) : n0;
+        y1 = kr + 1 < nround ? __shfl(n1, ysrc) : n1;
+      } else {
+        const double v00 = Q[qrow][pq], v01 = Q[qrow][qq];
+        const double v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
+        Q[qrow][pq] = cq * v00 - sq * v01;
+        Q[qrow][qq] = sq * v00 + cq * v01;
+        Q[qrow + NP][pq] = cq * v10 - sq * v11;
+        Q[qrow + NP][qq] = sq * v10 + cq * v11;
+      }
       __syncthreads();
     }
   }
   double* Qo = Qall + ((int64_t)m * (nb / 2) + p) * kBJ2 * kBJ2;
-  for (int e = tid; e < kBJ2 * kBJ2; e += NT) Qo[e] = Q[e / kBJ2][e % kBJ2];
+  if (qreg) {
+    const int yc = kBJ + ((qb + nround - 1) & (kBJ - 1));
+    Qo[qrow * kBJ2 + qb] = x0;
+    Qo[qrow * kBJ2 + yc] = y0;
+    Qo[(qrow + NP) * kBJ2 + qb] = x1;
+    Qo[(qrow + NP) * kBJ2 + yc] = y1;
+  } else {
+    for (int e = tid; e < kBJ2 * kBJ2; e += NT) Qo[e] = Q[e / kBJ2][e % kBJ2];
+  }
 }
 
 // grid ((nb/2)^2 + (n/64)(nb/2), nmat), 256 threads: the in-place update of
