@@ -1388,10 +1388,22 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
   if (jb < c1) {
     if (h <= 4) {
       float win[16];  // scores at jb - 4 .. jb + 11, -inf outside the candidates
+      const int i0 = jb - 4 - base;  // = 8 tid + 8 hg - 4: a multiple of 4
+      if (i0 >= 0) {                 // four 16-byte reads
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(sc + i0 + 4 * x);
+#pragma unroll
+          for (int y = 0; y < 4; ++y) win[4 * x + y] = v4[y];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) win[e] = sc[max(i0 + e, 0)];
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = jb - 4 + e;
-        win[e] = (j >= 0 && j < nc) ? sc[min(max(j - base, 0), kPoolChunk + 255)] : -INFINITY;
+        win[e] = (j >= 0 && j < nc) ? win[e] : -INFINITY;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
