@@ -2872,8 +2872,9 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
   const int nks = r / 32, nct = (dh + 15) / 16;
   const int ctper = (nct + nparts - 1) / nparts;  // channel tiles of this block: part * ctper + ...
   extern __shared__ __attribute__((aligned(16))) float smf[];
-  float* ys = smf;                 // [G][r]
-  float* oe = ys + G * r;          // [G][dh] exact-row part of the output
+  const int ldy = r + 4;           // ys row stride: the heads' rows start 4 banks apart
+  float* ys = smf;                 // [G][ldy]
+  float* oe = ys + G * ldy;        // [G][dh] exact-row part of the output
   float* fs = oe + G * dh;         // [G][nst]
   float* Lg = fs + G * nst;        // [8]
   float* stl = Lg + 8;             // [G][nst][2]
@@ -2969,7 +2970,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
       }
       for (int sp = sp0; sp < nl; ++sp)
         acc += fs[g * nst + sp] * *reinterpret_cast<const f32x4*>(yp + (int64_t)sp * Hq * r);
-      *reinterpret_cast<f32x4*>(ys + g * r + ib) = acc;
+      *reinterpret_cast<f32x4*>(ys + g * ldy + ib) = acc;
     }
   }
   // exact-row part: oe[g][ch] = sum over exact splits of f * yex
@@ -3001,7 +3002,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     if (ks < nks && n16 < G) {
-      const float* yr = ys + n16 * r + 32 * ks + 8 * kq;
+      const float* yr = ys + n16 * ldy + 32 * ks + 8 * kq;
       split8(*reinterpret_cast<const f32x4*>(yr), *reinterpret_cast<const f32x4*>(yr + 4), &bh[ks], &bl[ks]);
     } else {
       bh[ks] = __builtin_bit_cast(bf16x8, u16x8{});
@@ -3037,8 +3038,8 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
   }
 }
 
-static size_t merge_lds(const Dims& d, const DecodeWs& w) {
-  return ((size_t)d.G * (d.r + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
+static size_t merge_lds(const Dims& d, const DecodeWs& w) {  // (k_merge_mfma pads ys rows by 4)
+  return ((size_t)d.G * (d.r + 4 + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
 
 
