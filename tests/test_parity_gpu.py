@@ -240,18 +240,21 @@ def test_very_long_context_coarse_groups_bf16(gpu_lib):
     assert st.n_checked == 2
 
 
-@pytest.mark.parametrize("heads", [(8, 4, 32), (4, 2, 96), (12, 12, 128)],
-                         ids=["dh32", "dh96", "D1536"])
+@pytest.mark.parametrize("heads", [(8, 4, 32, 4), (4, 2, 96, 4), (12, 12, 128, 4), (8, 1, 128, 16)],
+                         ids=["dh32", "dh96", "D1536", "G8W16"])
 def test_prologue_head_shapes_bf16(gpu_lib, heads):
     """bf16 prologue shapes: d_h = 32 (eight heads per wave of the fused B^K
     pass), d_h = 96 (does not divide 256: the general prologue, with c^V(new)
-    in the prologue) and D' = 1536 (the fused pass in two row chunks)."""
-    Hq, Hkv, dh = heads
-    w = configs.LLAMA8B_32K.with_(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh, rank=64, q_window=4,
+    in the prologue), D' = 1536 (the fused pass in two row chunks) and G = 8
+    with a 16-step window (nine input rows per MFMA tile; 120 older window
+    rows, two batches in the state block)."""
+    Hq, Hkv, dh, W = heads
+    w = configs.LLAMA8B_32K.with_(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=dh, rank=64, q_window=W,
                                   n_recent=16, n_sample=256, model="power", exponents=(0.8,),
                                   top_k=64)
-    st = _run(w, 3000, 2, 3)
-    assert st.n_checked == 6
+    steps = 3 if W == 4 else W + 2  # fill the whole window once
+    st = _run(w, 3000, 2, steps)
+    assert st.n_checked == 2 * steps
 
 
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
