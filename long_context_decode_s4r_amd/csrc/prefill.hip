@@ -520,9 +520,9 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
 // A's tiles (P, P') and V's tiles (row tile R, pair P) of outer round k.
 // The 64 x 64 x 64 products run on fp64 MFMA 16x16x4 (lane l: A[l % 16][l / 16],
 // B[l / 16][l % 16]; D element v at row l / 16 + 4 v, column l % 16); wave w
-// computes the 32 x 32 quadrant (w / 2, w % 2), four 16 x 16 tiles, with
-// both operands read from LDS (row stride 65 doubles: the transposed stores
-// of 16 lanes land in distinct banks).
+// computes the 32 x 32 quadrant (w / 2, w % 2), four 16 x 16 tiles; the
+// tile operand is read from LDS (row stride 65 doubles: the transposed
+// stores of 16 lanes land in distinct banks), the Q operands from memory.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kBJLd = kBJ2 + 1;
 
@@ -535,25 +535,49 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
   const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x;
   const int l = tid & 63, w = tid >> 6, qi = w >> 1, qj = w & 1, c16 = l & 15, r4 = l >> 4;
   const int tile = blockIdx.x;
-  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJLd];   // the tile (V: transposed)
-  __shared__ __attribute__((aligned(16))) double Q1[kBJ2][kBJLd];  // Q_P (then the second factor)
+  constexpr int NKS = kBJ2 / 4;  // MFMA k-steps
+  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJLd];  // the tile (V: transposed)
   const double* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
   f64x4 acc[2][2];
-  // acc[ti][tj][v] = sum_k Ak[k][32 qi + 16 ti + r4 + 4 v] Bk[k][32 qj + 16 tj + c16]
-  auto gemm = [&](const double (*Ak)[kBJLd], const double (*Bk)[kBJLd]) {
+  // the Q factors' MFMA operands come straight from memory (L2) into
+  // registers: lane (r4, c16) of k-step ks needs Q[4 ks + r4][col + c16]
+  auto qfrag = [&](const double* Qp, int col, double (&f0)[NKS], double (&f1)[NKS]) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f0[ks] = Qp[(4 * ks + r4) * kBJ2 + col + c16];
+      f1[ks] = Qp[(4 * ks + r4) * kBJ2 + col + 16 + c16];
+    }
+  };
+  auto zero = [&]() {
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int ks = 0; ks < kBJ2 / 4; ++ks) {
+  };
+  // acc[ti][tj][v] = sum_k A'[k][32 qi + 16 ti + r4 + 4 v] B'[k][32 qj + 16 tj + c16]
+  // with A' from registers (a0, a1) and B' = X, or A' = X and B' from registers
+  auto gemm_ra = [&](const double (&a0)[NKS], const double (&a1)[NKS]) {
+    zero();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       const int kr = 4 * ks + r4;
-      const double a0 = Ak[kr][32 * qi + c16], a1 = Ak[kr][32 * qi + 16 + c16];
-      const double b0 = Bk[kr][32 * qj + c16], b1 = Bk[kr][32 * qj + 16 + c16];
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+      const double b0 = X[kr][32 * qj + c16], b1 = X[kr][32 * qj + 16 + c16];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[ks], b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[ks], b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[ks], b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[ks], b1, acc[1][1], 0, 0, 0);
+    }
+  };
+  auto gemm_rb = [&](const double (&b0)[NKS], const double (&b1)[NKS]) {
+    zero();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kr = 4 * ks + r4;
+      const double a0 = X[kr][32 * qi + c16], a1 = X[kr][32 * qi + 16 + c16];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0[ks], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1[ks], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0[ks], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1[ks], acc[1][1], 0, 0, 0);
     }
   };
   // output element (ti, tj, v) of this lane: row orow(ti, v), column ocol(tj)
@@ -565,19 +589,18 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
     bj_pair(P, k, nb, &I, &J);
     bj_pair(P2, k, nb, &I2, &J2);
     double* A = Aall + (int64_t)m * n * n;
-    const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
-    const double* QP2 = Qm + (int64_t)P2 * kBJ2 * kBJ2;
+    double qa0[NKS], qa1[NKS];
+    qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qi, qa0, qa1);  // A' = Q_P (rows of Q_P^T)
     for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
       const double2 x = *reinterpret_cast<const double2*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
-      const double2 q = *reinterpret_cast<const double2*>(QP + i * kBJ2 + j);
       X[i][j] = x.x;
       X[i][j + 1] = x.y;
-      Q1[i][j] = q.x;
-      Q1[i][j + 1] = q.y;
     }
     __syncthreads();
-    gemm(Q1, X);  // T = Q_P^T X
+    gemm_ra(qa0, qa1);  // T = Q_P^T X
+    double qb0[NKS], qb1[NKS];
+    qfrag(Qm + (int64_t)P2 * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P2
     __syncthreads();
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
@@ -585,14 +608,8 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
       for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int v = 0; v < 4; ++v) X[ocol(tj)][orow(ti, v)] = acc[ti][tj][v];  // X <- T^T
-    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
-      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
-      const double2 q = *reinterpret_cast<const double2*>(QP2 + i * kBJ2 + j);
-      Q1[i][j] = q.x;
-      Q1[i][j + 1] = q.y;
-    }
     __syncthreads();
-    gemm(X, Q1);  // T Q_P2
+    gemm_rb(qb0, qb1);  // T Q_P2
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -605,18 +622,16 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
     int I, J;
     bj_pair(P, k, nb, &I, &J);
     double* V = Vall + (int64_t)m * n * n;
-    const double* QP = Qm + (int64_t)P * kBJ2 * kBJ2;
+    double qb0[NKS], qb1[NKS];
+    qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P
     for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
       const double2 x = *reinterpret_cast<const double2*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
-      const double2 q = *reinterpret_cast<const double2*>(QP + i * kBJ2 + j);
       X[j][i] = x.x;
       X[j + 1][i] = x.y;
-      Q1[i][j] = q.x;
-      Q1[i][j + 1] = q.y;
     }
     __syncthreads();
-    gemm(X, Q1);  // V[R, P] Q_P
+    gemm_rb(qb0, qb1);  // V[R, P] Q_P
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
