@@ -403,6 +403,7 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   if (frozen[m]) return;
   constexpr int NT = kBJEigThreads, NP = kBJ2 / 2;
   static_assert(NP * NP == NT && kBJ2 * NP == 2 * NT, "one 2x2 block and two Q pairs per thread");
+  static_assert((kBJ & (kBJ - 1)) == 0, "cross-round pairs use a power-of-two block");
   const int nb = n / kBJ, p = blockIdx.x, tid = threadIdx.x;
   int I, J;
   bj_pair(p, k, nb, &I, &J);
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   {
     for (int kr = 0; kr < nround; ++kr) {
       if (tid < NP) {
-        const int ip = pi[kr][tid], iq = qi[kr][tid];
+        const int ip = qreg ? tid : pi[kr][tid], iq = qreg ? kBJ + ((tid + kr) & (kBJ - 1)) : qi[kr][tid];
         const double app = S[ip][ip], aqq = S[iq][iq], apq = S[ip][iq];
         double c = 1.0, sn = 0.0, t = 0.0;
         if (apq != 0.0) {
@@ -467,9 +468,22 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
       __syncthreads();
       // S <- J^T S J on block (a, b); Q <- Q J on its two entry pairs (the
       // blocks and pairs are disjoint, so no thread reads another's stores)
-      const int pa = pi[kr][a], qa = qi[kr][a];
-      const int pb = pi[kr][b], qbb = qi[kr][b];
-      const int pq = pi[kr][qb], qq = qi[kr][qb];
+      int pa, qa, pb, qbb, pq, qq;  // cross rounds: the pairs by arithmetic, no table reads
+      if (qreg) {
+        pa = a;
+        qa = kBJ + ((a + kr) & (kBJ - 1));
+        pb = b;
+        qbb = kBJ + ((b + kr) & (kBJ - 1));
+        pq = pb;
+        qq = qbb;
+      } else {
+        pa = pi[kr][a];
+        qa = qi[kr][a];
+        pb = pi[kr][b];
+        qbb = qi[kr][b];
+        pq = pi[kr][qb];
+        qq = qi[kr][qb];
+      }
       const double m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
       const double cq = rc[qb], sq = rs[qb];
       if (a == b) {
