@@ -130,9 +130,10 @@ int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max,
 int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units,
                          int64_t L, size_t* bytes);
 
-/* Prefill part 1: bases ('What carries the argument': truncated SVD over the
- * sampled, token-wise-normalised non-sink states; 'Core claim': 7:3
- * recent-to-uniform sample of T' tokens).
+/* Prefill part 1: bases ('What carries the argument', Eqs. 1-2: leading right
+ * singular vectors of the per-token normalised sample of non-sink states;
+ * 'Core claim': the T'-token sample takes 7 parts from the end of the prompt
+ * to 3 parts spread evenly over the rest).
  *   K, V      device, [U][L][D'] storage: the prompt's keys and values.
  *   cache     basis_k / basis_v are written ([U][D'][r], top-r eigenvectors
  *             of S^T S, S = the rounded, row-normalised sample); other
@@ -161,9 +162,10 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
                  const void* K, const void* V, kvlr_cache* cache,
                  void* ws, size_t ws_bytes, void* stream);
 
-/* One decode step for every unit ('Referee Report' summary: sliding window of
- * query coefficients, latent scoring Eqs. 8-10, local window plus top-k
- * selection Eqs. 13-15, sparse reconstruction and exact attention Eqs. 16-18).
+/* One decode step for every unit ('Referee Report' summary: a window of the
+ * last W steps' query coefficients, latent scoring Eqs. 8-10, selection of the
+ * recent window and the top-k positions Eqs. 13-15, rebuilding of the chosen
+ * rows and exact attention Eqs. 16-18).
  *   q         device, [U][H_q][d_h] storage: the new token's queries.
  *   k_new     device, [U][H_kv][d_h] storage: its key; v_new likewise.
  *   cache     read and advanced: the token is appended at position L_t - 1

@@ -3,11 +3,12 @@
 // + exact attention (split over rows, splits merged by the last block).
 //
 // Method: S^4R review (pith.science/paper/2608.00528): 'What carries the
-// argument' (latent-space relevance scoring between a sliding window of query
-// coefficients and the cached key coefficients, Eqs. 8-10; sparse
-// reconstruction of the selected positions, Eqs. 13-16; exact attention with
-// the uncompressed sinks), 'Core claim' (queries projected into the key
-// subspace), 'Referee Report' major comment 2 (Z = C_Q C_K^T / sqrt(r)).
+// argument' (relevance of every cached position from a softmax of the last W
+// steps' query coefficients against its key coefficients, Eqs. 8-10; only
+// the chosen positions are rebuilt from their coefficients, Eqs. 13-16, and
+// attended exactly together with the exact sink tokens), 'Core claim' (the
+// queries are mapped onto the key basis), 'Referee Report' major comment 2
+// (Z = C_Q C_K^T / sqrt(r)).
 //
 // Latent softmax bookkeeping.  Each window row (one query coefficient vector
 // of one earlier step) keeps the running max m and sum S of its softmax over

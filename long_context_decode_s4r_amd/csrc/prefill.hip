@@ -3,9 +3,11 @@
 // every non-sink token onto the bases, exact sink / recent-window copies.
 //
 // Method: S^4R review (pith.science/paper/2608.00528), 'What carries the
-// argument' (truncated SVD over a sampled, token-wise-normalised subset,
-// Eqs. 1-2; coefficients c = s.B, Eq. 3) and 'Core claim' (s sinks kept in
-// full precision, 7:3 recent-to-uniform sample of T' tokens).
+// argument' (bases = leading right singular vectors of the per-token
+// normalised sample, Eqs. 1-2; every non-sink token kept as its coefficients
+// on the basis, Eq. 3) and 'Core claim' (the first s tokens stay exact; the
+// T'-token sample takes 7 parts from the end of the prompt to 3 parts spread
+// evenly over the rest).
 #include "common.h"
 
 #include <math.h>

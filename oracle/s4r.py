@@ -22,10 +22,16 @@ normalised SVD sample, the bases, the coefficient caches and the fp32 query
 window.  ``storage == "f64"`` disables rounding (used by the exactness pins).
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to something
-other than itself: exact-rank reconstruction, equality with full attention at
-r = D' and k >= |J|, the latent identity at r = D', library SVD, closed-form
-softmax cases, score invariants, pure-Python brute force on tiny inputs,
-sampling counts and the closed-form memory ratio.
+other than itself: exact-rank reconstruction (also with separate key and
+value ranks, and for a basis shared by several layers), equality with full
+attention at r = D' and k >= |J| (also with the recent window rebuilt from
+coefficients), the latent identity at r = D', library SVD (also of the
+stacked samples of a layer window), closed-form softmax cases, a hand-built
+window ring (with and without prompt-tail queries), score invariants,
+pure-Python brute force on tiny inputs with the test's own query window,
+sampling counts (7:3, 10:0 and the full prompt), the closed-form memory
+ratio and the rank it gives for a retention target.  A table of planted
+mistakes checks that each pin catches the error it is meant to catch.
 """
 from __future__ import annotations
 
@@ -65,14 +71,17 @@ def rnd(x, storage: str) -> np.ndarray:
 # --------------------------------------------------------------------------- #
 def sample_positions(L: int, n_sink: int, n_sample: int,
                      recent_num: int = 7, recent_den: int = 10) -> np.ndarray:
-    """Positions of the SVD sample ('Core claim': T' << T non-sink tokens,
-    split 7:3 between recent and uniformly spaced positions; 'Load-bearing
-    premise' and 'Assumptions & free parameters' name the 7:3 split).
+    """Positions of the SVD sample ('Core claim' and 'Load-bearing premise':
+    T' non-sink prompt tokens, seven tenths of them taken from the end of the
+    prompt and the remainder spread over the rest; the ratio is a free
+    parameter in 'Assumptions & free parameters', and 'If this is right'
+    compares it with an all-recent 10:0 sample).
 
-    Reading R2: the recent share is floor(7 T'/10) positions ending at the
-    last prompt token; the rest are evenly spaced (no RNG) over the
-    non-sink, non-recent range [s, L - n_r).  Returned in that order
-    (uniform part first, then recent), all distinct.
+    Reading R2: n_r = floor(num T' / den) positions ending at the last prompt
+    token; the other n_u = T' - n_r are evenly spaced (no RNG) over the
+    non-sink positions before them, [s, L - n_r).  num = den gives the
+    all-recent sample (n_u = 0).  Returned uniform part first, then the
+    recent run; all distinct.
     """
     n_r = (recent_num * n_sample) // recent_den
     n_u = n_sample - n_r
@@ -85,9 +94,9 @@ def sample_positions(L: int, n_sink: int, n_sample: int,
 
 
 def normalize_rows(Y: np.ndarray) -> np.ndarray:
-    """Token-wise normalisation of the sampled states ('What carries the
-    argument': the SVD is taken over a sampled, token-wise-normalised
-    subset).  Each row is divided by its Euclidean norm; zero rows stay 0."""
+    """Per-token normalisation of the sampled states before the SVD ('What
+    carries the argument', Eqs. 1-2; 'Core claim').  Each row is divided by
+    its Euclidean norm; an all-zero row stays zero."""
     Y = np.asarray(Y, dtype=np.float64)
     n = np.sqrt(np.sum(Y * Y, axis=1, keepdims=True))
     out = np.zeros_like(Y)
@@ -113,8 +122,9 @@ def eig_desc(A: np.ndarray):
 def build_basis(X: np.ndarray, n_sink: int, n_sample: int, rank: int,
                 storage: str, recent_num: int = 7, recent_den: int = 10):
     """Basis B (D' x r) of one state matrix X (L x D') of one layer and one
-    sequence ('What carries the argument': truncated SVD over the sampled,
-    normalised non-sink states; the top-r right singular vectors are B).
+    sequence ('What carries the argument', Eqs. 1-2: B holds the r leading
+    right singular vectors of the normalised sample, i.e. the r leading
+    eigenvectors of its Gram matrix).
 
     Returns (B, eigenvalues descending, S, positions).  S is the stored
     (rounded) normalised sample; B is rounded to the storage type.
@@ -126,6 +136,27 @@ def build_basis(X: np.ndarray, n_sink: int, n_sample: int, rank: int,
     lam, U = eig_desc(gram(S))
     B = rnd(U[:, :rank], storage)
     return B, lam, S, pos
+
+
+def build_basis_shared(Xs, n_sink: int, n_sample: int, rank: int, storage: str,
+                       recent_num: int = 7, recent_den: int = 10):
+    """One basis for a window of neighbouring layers (DepthWeave-KV page,
+    'Core claim' and Eq. 1: low-rank channel bases shared across a window of
+    adjacent layers, each layer keeping its own coefficients on the shared
+    basis; the learned router and residuals are not part of this).
+
+    Reading: the shared basis is the rank-r truncated SVD of the layers'
+    normalised samples stacked row-wise, i.e. the r leading eigenvectors of
+    the sum of the per-layer Gram matrices.  Xs: the window's state matrices
+    (each L x D', same sequence).  Returns (B, eigenvalues, [S per layer])."""
+    Ss = []
+    for X in Xs:
+        X = np.asarray(X, dtype=np.float64)
+        pos = sample_positions(X.shape[0], n_sink, n_sample, recent_num, recent_den)
+        Ss.append(rnd(normalize_rows(X[pos]), storage))
+    A = sum(gram(S) for S in Ss)
+    lam, U = eig_desc(A)
+    return rnd(U[:, :rank], storage), lam, Ss
 
 
 def project(X: np.ndarray, B: np.ndarray, storage: str) -> np.ndarray:
@@ -248,8 +279,17 @@ class Cache:
 
     Coefficient rows are indexed by absolute position (rows < n_sink unused).
     The recent ring holds the last n_recent tokens exactly; slot = pos mod
-    n_recent.  qwin holds the last W query-coefficient blocks; slot = step
-    mod W."""
+    n_recent.  qwin holds the last W query-coefficient blocks; the block
+    pushed as number p (counting from 0) sits in slot p mod W, and
+    ``pushes`` counts the blocks pushed so far (prompt-tail queries, if the
+    window was initialised from them, then one per decode step).
+
+    rank is the key rank r_K (latent scores use 1/sqrt(rank)); rank_v the
+    value rank r_V (defaults to rank; 'Reading between the lines' mentions a
+    1:1.5 key-to-value rank split).  local_exact False is the variant in
+    which the recent window is rebuilt from coefficients like the top-k rows
+    ('Core claim': only the local window and the top-k positions are
+    reconstructed) instead of being read from the exact ring."""
     n_q_heads: int
     n_kv_heads: int
     head_dim: int
@@ -270,18 +310,25 @@ class Cache:
     BV: np.ndarray
     qwin: np.ndarray
     L: int
-    steps: int = 0
+    pushes: int = 0
+    rank_v: int = 0
+    local_exact: bool = True
     last: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        if not self.rank_v:
+            self.rank_v = self.rank
 
     @property
     def G(self) -> int:
         return self.n_q_heads // self.n_kv_heads
 
     def window_rows(self) -> np.ndarray:
-        """The W_eff * G valid query-coefficient rows (reading R9: the window
-        starts empty and includes the current query)."""
-        w_eff = min(self.steps, self.q_window)
-        slots = [(self.steps - 1 - i) % self.q_window for i in range(w_eff)]
+        """The W_eff * G valid query-coefficient rows, newest block first,
+        W_eff = min(pushes, W) (reading R9: without prompt-tail queries the
+        window starts empty and always includes the current query)."""
+        w_eff = min(self.pushes, self.q_window)
+        slots = [(self.pushes - 1 - i) % self.q_window for i in range(w_eff)]
         if not slots:
             return np.zeros((0, self.rank))
         return np.concatenate([self.qwin[s] for s in slots], axis=0)
@@ -290,26 +337,55 @@ class Cache:
         """Compressed candidate positions J = [s, L_t - n_recent)."""
         return np.arange(self.n_sink, max(self.L - self.n_recent, self.n_sink))
 
+    def local_positions(self) -> np.ndarray:
+        """The recent window [L_t - n_recent, L_t) (never below the sinks)."""
+        return np.arange(max(self.L - self.n_recent, self.n_sink), self.L)
+
+
+def push_query(cache: Cache, q) -> np.ndarray:
+    """Project one token's queries into the key subspace ('Core claim':
+    queries are mapped onto the key basis) and push the G coefficient
+    vectors into the window ('What carries the argument': the window of
+    query coefficients).  The window is stored in fp32 (reading R13).
+    Returns the pushed block [G][r_K]."""
+    cq = rnd(query_concat(q, cache.n_kv_heads) @ cache.BK, "f32")
+    cache.qwin[cache.pushes % cache.q_window] = cq
+    cache.pushes += 1
+    return cq
+
 
 def prefill(K: np.ndarray, V: np.ndarray, *, n_q_heads: int, n_kv_heads: int,
             head_dim: int, rank: int, n_sink: int, n_sample: int, q_window: int,
             top_k: int, n_recent: int, pool_kernel: int, storage: str,
-            L_max: int | None = None, recent_num: int = 7, recent_den: int = 10):
+            L_max: int | None = None, recent_num: int = 7, recent_den: int = 10,
+            rank_v: int | None = None, tail_q=None, local_exact: bool = True,
+            BK=None, BV=None):
     """Prefill of one (layer, sequence): sinks and recent ring kept exact,
     bases from the sample, coefficients of every row in [s, L).
-    K, V: [L][D'] as stored.  Returns (Cache, info)."""
+    K, V: [L][D'] as stored.  rank_v: value rank (default: rank).
+    tail_q: optional [n][H_q][d_h] queries of the last n prompt tokens (oldest
+    first, n <= W): the window starts with their coefficients (the variant
+    that seeds the window from the prompt's last queries; reading R9 is the
+    default, an empty window).  BK, BV: bases to use instead of building
+    them (a depth-shared basis).  Returns (Cache, info)."""
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     L, Dp = K.shape
+    rank_v = rank if rank_v is None else rank_v
     if Dp != n_kv_heads * head_dim:
         raise ValueError("D' must equal n_kv_heads * head_dim")
     if L < n_sink + n_recent:
         raise ValueError("prompt shorter than sinks + recent window")
     L_max = L if L_max is None else L_max
-    BK, lamK, SK, pos = build_basis(K, n_sink, n_sample, rank, storage, recent_num, recent_den)
-    BV, lamV, SV, _ = build_basis(V, n_sink, n_sample, rank, storage, recent_num, recent_den)
+    info = dict(positions=sample_positions(L, n_sink, n_sample, recent_num, recent_den))
+    if BK is None:
+        BK, info["lam_k"], info["S_k"], _ = build_basis(K, n_sink, n_sample, rank, storage,
+                                                        recent_num, recent_den)
+    if BV is None:
+        BV, info["lam_v"], info["S_v"], _ = build_basis(V, n_sink, n_sample, rank_v, storage,
+                                                        recent_num, recent_den)
     CK = np.zeros((L_max, rank))
-    CV = np.zeros((L_max, rank))
+    CV = np.zeros((L_max, rank_v))
     CK[n_sink:L] = project(K[n_sink:L], BK, storage)
     CV[n_sink:L] = project(V[n_sink:L], BV, storage)
     ring_k = np.zeros((n_recent, Dp))
@@ -320,8 +396,13 @@ def prefill(K: np.ndarray, V: np.ndarray, *, n_q_heads: int, n_kv_heads: int,
     G = n_q_heads // n_kv_heads
     cache = Cache(n_q_heads, n_kv_heads, head_dim, rank, n_sink, q_window, top_k,
                   n_recent, pool_kernel, storage, K[:n_sink].copy(), V[:n_sink].copy(),
-                  ring_k, ring_v, CK, CV, BK, BV, np.zeros((q_window, G, rank)), L, 0)
-    info = dict(lam_k=lamK, lam_v=lamV, S_k=SK, S_v=SV, positions=pos)
+                  ring_k, ring_v, CK, CV, BK, BV, np.zeros((q_window, G, rank)), L, 0,
+                  rank_v, local_exact)
+    if tail_q is not None:
+        if len(tail_q) > q_window:
+            raise ValueError("more prompt-tail queries than the window holds")
+        for qt in tail_q:
+            push_query(cache, qt)
     return cache, info
 
 
@@ -330,11 +411,8 @@ def decode_append(cache: Cache, q, k_new, v_new):
 
     The new token's key/value coefficients are appended (Eq. 3 applied to the
     new token), its exact key/value enter the recent ring (evicting the
-    oldest, which then becomes a compressed candidate), and the queries are
-    projected into the key subspace ('Core claim': queries are projected into
-    the key subspace) and pushed into the query-coefficient window ('What
-    carries the argument': sliding window of query coefficients).
-    Mutates cache; returns the new query-coefficient block [G][r]."""
+    oldest, which then becomes a compressed candidate), and its queries go
+    through push_query.  Mutates cache; returns the pushed block [G][r_K]."""
     k_cat = np.asarray(k_new, np.float64).reshape(-1)
     v_cat = np.asarray(v_new, np.float64).reshape(-1)
     p = cache.L
@@ -345,10 +423,7 @@ def decode_append(cache: Cache, q, k_new, v_new):
     cache.ring_k[p % cache.n_recent] = k_cat
     cache.ring_v[p % cache.n_recent] = v_cat
     cache.L = p + 1
-    cq = rnd(query_concat(q, cache.n_kv_heads) @ cache.BK, "f32")  # fp32 window
-    cache.qwin[cache.steps % cache.q_window] = cq
-    cache.steps += 1
-    return cq
+    return push_query(cache, q)
 
 
 def decode_select(cache: Cache):
@@ -362,20 +437,28 @@ def decode_select(cache: Cache):
 
 
 def decode_attend(cache: Cache, q, positions) -> np.ndarray:
-    """Reconstruction of the selected positions and exact attention over
-    sinks + recent ring + reconstructed rows."""
+    """Reconstruction of the selected positions and exact attention over the
+    sinks, the recent window and the reconstructed rows.  The recent window
+    comes from the exact ring, or, with local_exact False, is rebuilt from
+    its coefficients together with the selected rows."""
     positions = np.asarray(positions, dtype=np.int64)
-    keys_exact = np.concatenate([cache.sink_k, cache.ring_k], axis=0)
-    vals_exact = np.concatenate([cache.sink_v, cache.ring_v], axis=0)
-    return sparse_attention(q, keys_exact, vals_exact, cache.CK[positions],
-                            cache.CV[positions], cache.BK, cache.BV, cache.n_kv_heads)
+    if cache.local_exact:
+        keys_exact = np.concatenate([cache.sink_k, cache.ring_k], axis=0)
+        vals_exact = np.concatenate([cache.sink_v, cache.ring_v], axis=0)
+        rebuilt = positions
+    else:
+        keys_exact, vals_exact = cache.sink_k, cache.sink_v
+        rebuilt = np.concatenate([positions, cache.local_positions()])
+    return sparse_attention(q, keys_exact, vals_exact, cache.CK[rebuilt],
+                            cache.CV[rebuilt], cache.BK, cache.BV, cache.n_kv_heads)
 
 
 def decode_step(cache: Cache, q, k_new, v_new) -> np.ndarray:
-    """One decode step for one (layer, sequence) (the three stages the
-    'Referee Report' summary lists: window of query coefficients and latent
-    scoring, selection of local window plus top-k, reconstruction and exact
-    attention).  q: [H_q][d_h], k_new/v_new: [H_kv][d_h].  Returns
+    """One decode step for one (layer, sequence), in the order the 'Referee
+    Report' summary gives: the query coefficients enter the window and score
+    the candidates (Eqs. 8-10), the recent window and the k best candidates
+    are chosen (Eqs. 13-15), and the chosen rows are rebuilt and attended
+    exactly (Eqs. 16-18).  q: [H_q][d_h], k_new/v_new: [H_kv][d_h].  Returns
     out [H_q][d_h]; cache.last holds positions, score and pooled."""
     decode_append(cache, q, k_new, v_new)
     positions, score, pooled = decode_select(cache)
@@ -388,14 +471,38 @@ def decode_step(cache: Cache, q, k_new, v_new) -> np.ndarray:
 # accounting
 # --------------------------------------------------------------------------- #
 def persistent_bytes(L: int, D: int, rank: int, n_sink: int, n_recent: int,
-                     elem_bytes: int) -> int:
+                     elem_bytes: int, rank_v: int | None = None) -> int:
     """Persistent cache bytes of one layer and sequence for K and V: exact
     sinks + exact recent ring + coefficients of the other tokens + bases
     ('If this is right': the persistent cache per layer tends to r/D' of the
     full cache for long contexts; memory analysis Eqs. 19-24)."""
+    rank_v = rank if rank_v is None else rank_v
     n_coef = max(L - n_sink, 0)
-    return 2 * elem_bytes * ((n_sink + n_recent) * D + n_coef * rank + D * rank)
+    return elem_bytes * (2 * (n_sink + n_recent) * D + (n_coef + D) * (rank + rank_v))
 
 
 def full_cache_bytes(L: int, D: int, elem_bytes: int) -> int:
     return 2 * elem_bytes * L * D
+
+
+def rank_for_ratio(eta: float, L: int, D: int, n_sink: int, n_recent: int,
+                   v_to_k: tuple = (1, 1), multiple: int = 8):
+    """Ranks (r_K, r_V) for a target retention ratio eta ('Referee Report'
+    major comment 3 and 'Assumptions & free parameters': r is solved from
+    the memory equation, Eq. 21, for a target eta).  The page does not print
+    Eq. 21; the accounting used here is persistent_bytes / full_cache_bytes
+    <= eta.  r_V / r_K = v_to_k[1] / v_to_k[0]; both are multiples of
+    ``multiple``.  Returns the largest such pair that meets the target (the
+    ratio is increasing in the ranks), or (0, 0) if even rank 0 exceeds it."""
+    a, b = v_to_k
+    best = (0, 0)
+    t = 1
+    while True:
+        rk, rv = a * t * multiple, b * t * multiple
+        if rk > D or rv > D:
+            break
+        if persistent_bytes(L, D, rk, n_sink, n_recent, 1, rv) > eta * full_cache_bytes(L, D, 1):
+            break
+        best = (rk, rv)
+        t += 1
+    return best

@@ -114,14 +114,14 @@ def check_decode_step(kc, w, u: int, pre: s4r.Cache, post: s4r.Cache, q, k, v, o
                np.abs(kn.reshape(-1)) @ np.abs(o.BK))
     check_rows(post.CV[p], o.CV[p], storage, f"unit {u} appended c^V",
                np.abs(vn.reshape(-1)) @ np.abs(o.BV))
-    slot = (o.steps - 1) % o.q_window
+    slot = (o.pushes - 1) % o.q_window
     qcat = s4r.query_concat(qn, w.n_kv_heads)
     scale = np.abs(qcat) @ np.abs(o.BK)
     assert np.all(np.abs(post.qwin[slot] - o.qwin[slot]) <= 1e-5 * scale + 1e-30), \
         f"unit {u}: query coefficients differ"
     assert np.array_equal(post.ring_k[p % o.n_recent], o.ring_k[p % o.n_recent])
     assert np.array_equal(post.ring_v[p % o.n_recent], o.ring_v[p % o.n_recent])
-    assert post.L == o.L and post.steps == o.steps
+    assert post.L == o.L and post.pushes == o.pushes
     # adopt the GPU's stored rows (stage isolation)
     o.CK[p] = post.CK[p]
     o.CV[p] = post.CV[p]

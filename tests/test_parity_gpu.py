@@ -39,7 +39,7 @@ def _prefill_checks(w, prompt, kc, ek, ev, units):
         for p in range(L - w.n_recent, L):
             assert np.array_equal(snap.ring_k[p % w.n_recent], Ku[p])
             assert np.array_equal(snap.ring_v[p % w.n_recent], Vu[p])
-        assert snap.L == L and snap.steps == 0
+        assert snap.L == L and snap.pushes == 0
 
 
 def _run(w, L, batch, steps, L_extra=8, units=None, check_every=1, n_layers=1):
