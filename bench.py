@@ -76,7 +76,8 @@ def oracle_cache_of(kc, u, w):
                      w.top_k, w.n_recent, w.pool_kernel, w.storage, f(kc.sink_k[u]),
                      f(kc.sink_v[u]), f(kc.ring_k[u]), f(kc.ring_v[u]), f(kc.coef_k[u]),
                      f(kc.coef_v[u]), f(kc.basis_k[u]), f(kc.basis_v[u]),
-                     f(kc.qwin[u]).reshape(w.q_window, w.G, w.rank), lens[0], lens[1])
+                     f(kc.qwin[u]).reshape(w.q_window, w.G, w.rank), lens[0], lens[1],
+                     w.rank_v or w.rank, w.local_window == 0)
 
 
 def cpu_baseline(kc, dec, w, U, budget_s: float):
@@ -146,6 +147,69 @@ def run_prefill_leg(args):
             "project_mfma_frac": flops / (t_p / 1e3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def _probe_lib():
+    import ctypes
+    lib = kvlr.load()
+    lib.kvlr_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvlr_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    return lib
+
+
+def run_probes(full: bool = True):
+    """Measured ceilings (include/kvlr_probe.h): streaming-read bandwidth over
+    a 4 GiB buffer (16x the 256 MB Infinity Cache) through the register path
+    and the direct global->LDS path, and the dense bf16 MFMA rate.  Each
+    configuration: one untimed launch, then the best of 5 timed launches
+    (HIP events on the launch stream)."""
+    lib = _probe_lib()
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(launch, reps=5):
+        launch()
+        best = float("inf")
+        for _ in range(reps):
+            e0.record(st)
+            launch()
+            e1.record(st)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    reads = []
+    configs_ = [(0, b, dpt) for b in ((1024, 2048) if not full else (256, 512, 1024, 2048, 4096))
+                for dpt in ((8,) if not full else (2, 4, 8, 16))] + [(1, 256, 0)]
+    for method, blocks, depth in configs_:
+        def launch():
+            rc = lib.kvlr_probe_read(buf.data_ptr(), nbytes, method, blocks, depth, sink.data_ptr(),
+                                     st.cuda_stream)
+            assert rc == 0, rc
+        ms = best_ms(launch)
+        reads.append({"method": ["register", "global_to_lds"][method], "blocks": blocks,
+                      "depth": depth, "gbps": round(nbytes / (ms / 1e3) / 1e9, 1)})
+    del buf
+    mfma = []
+    for shape, fl in ((0, 16384), (1, 32768)):
+        blocks, iters = 2048, 4000
+        def launch():
+            rc = lib.kvlr_probe_mfma(shape, iters, blocks, sink.data_ptr(), st.cuda_stream)
+            assert rc == 0, rc
+        ms = best_ms(launch)
+        flops = blocks * 4 * iters * 8 * fl
+        mfma.append({"shape": ["16x16x32_bf16", "32x32x16_bf16"][shape],
+                     "tflops": round(flops / (ms / 1e3) / 1e12, 1)})
+    best_read = max(reads, key=lambda r: r["gbps"])
+    return {"read": reads, "best_read_gbps": best_read["gbps"],
+            "best_read_config": {k: best_read[k] for k in ("method", "blocks", "depth")},
+            "mfma": mfma, "best_mfma_tflops": max(m["tflops"] for m in mfma)}
+
+
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -174,6 +238,8 @@ def main():
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill leg (basis build + projection of one 64K sequence)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the measured-ceiling probes (read bandwidth, bf16 MFMA rate)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the compressed-KV path has no multi-GPU part "
@@ -182,6 +248,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
         copy_probe()
+        return
+    if args.probe:
+        kvlr.load()
+        torch.cuda.set_device(0)
+        print(json.dumps({"probe": run_probes(full=True)}), flush=True)
         return
     if args.prefill_only:
         kvlr.load()

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = ["api.hip", "prefill.hip", "decode.hip"]
+SRC = ["api.hip", "prefill.hip", "decode.hip", "probe.hip"]
 LIB = os.path.join(HERE, "libkvlr.so")
 
 

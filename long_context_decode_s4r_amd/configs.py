@@ -41,6 +41,9 @@ class Workload:
     seed: int = 0
     sample_recent_num: int = 7
     sample_recent_den: int = 10
+    rank_v: int = 0            # value rank; 0 = the key rank
+    local_window: int = 0      # 0: exact recent window, 1: rebuilt from coefficients
+    eig_max_sweeps: int = 0    # 0: the library default
 
     @property
     def D(self) -> int:

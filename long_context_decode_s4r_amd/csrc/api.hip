@@ -42,13 +42,16 @@ size_t elem_bytes(const kvlr_config* c) { return c->dtype == KVLR_BF16 ? 2 : 4; 
 
 bool rank_supported_bf16(int r) { return r == 32 || r == 64 || r == 128 || r == 192 || r == 256; }
 
+constexpr int kDefaultEigSweeps = 24;
+
 Dims dims_of(const kvlr_config* c) {
   Dims d;
   d.Hq = c->n_q_heads;
   d.Hkv = c->n_kv_heads;
   d.dh = c->head_dim;
   d.D = c->n_kv_heads * c->head_dim;
-  d.r = c->rank;
+  d.r = c->rank_k;
+  d.rv = c->rank_v;
   d.G = c->n_q_heads / c->n_kv_heads;
   d.s = c->n_sink;
   d.T = c->n_sample;
@@ -59,13 +62,17 @@ Dims dims_of(const kvlr_config* c) {
   d.nrec = c->n_recent;
   d.kappa = c->pool_kernel;
   d.dtype = c->dtype;
+  d.local = c->local_window;
   return d;
 }
 
 int check_cfg(const kvlr_config* c) {
   if (!c) return fail(KVLR_EINVAL, "config is NULL");
-  if (c->reserved != 0) return fail(KVLR_EINVAL, "config.reserved must be 0");
   if (c->dtype != KVLR_F32 && c->dtype != KVLR_BF16) return fail(KVLR_EINVAL, "unknown dtype %d", c->dtype);
+  if (c->local_window != KVLR_LOCAL_EXACT && c->local_window != KVLR_LOCAL_RECONSTRUCTED)
+    return fail(KVLR_EINVAL, "unknown local_window %d", c->local_window);
+  if (c->eig_max_sweeps < 0 || c->eig_max_sweeps > 100)
+    return fail(KVLR_EINVAL, "eig_max_sweeps must be in [0, 100] (0 = default)");
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1)
     return fail(KVLR_EINVAL, "head counts and head_dim must be >= 1");
   if (c->n_q_heads % c->n_kv_heads != 0)
@@ -77,8 +84,16 @@ int check_cfg(const kvlr_config* c) {
   if (D % 2 != 0 || D > 4096) return fail(KVLR_EINVAL, "D' = %lld must be even and <= 4096", (long long)D);
   if ((1 + G) * D > 12288) return fail(KVLR_EINVAL, "(1 + G) * D' = %lld exceeds 12288", (long long)((1 + G) * D));
   if ((int64_t)G * c->head_dim > 1024) return fail(KVLR_EINVAL, "G * head_dim must be <= 1024");
-  if (c->rank < 1 || c->rank > D) return fail(KVLR_EINVAL, "rank %d must be in [1, D' = %lld]", c->rank, (long long)D);
-  if (c->rank % 8 != 0) return fail(KVLR_EINVAL, "rank %d must be a multiple of 8", c->rank);
+  if (c->rank_k < 1 || c->rank_k > D)
+    return fail(KVLR_EINVAL, "rank_k %d must be in [1, D' = %lld]", c->rank_k, (long long)D);
+  if (c->rank_v < 1 || c->rank_v > D)
+    return fail(KVLR_EINVAL, "rank_v %d must be in [1, D' = %lld]", c->rank_v, (long long)D);
+  if (c->rank_k % 8 != 0 || c->rank_v % 8 != 0)
+    return fail(KVLR_EINVAL, "ranks (%d, %d) must be multiples of 8", c->rank_k, c->rank_v);
+  if (c->rank_v != c->rank_k)
+    return fail(KVLR_EINVAL, "rank_v != rank_k is not supported by this build");
+  if (c->local_window != KVLR_LOCAL_EXACT)
+    return fail(KVLR_EINVAL, "a reconstructed local window is not supported by this build");
   if (c->head_dim % 8 != 0) return fail(KVLR_EINVAL, "head_dim %d must be a multiple of 8", c->head_dim);
   if (c->n_sink < 0) return fail(KVLR_EINVAL, "n_sink must be >= 0");
   if (c->n_sample < 1) return fail(KVLR_EINVAL, "n_sample must be >= 1");
@@ -90,11 +105,12 @@ int check_cfg(const kvlr_config* c) {
   if (c->pool_kernel < 1 || c->pool_kernel % 2 == 0 || c->pool_kernel > 255)
     return fail(KVLR_EINVAL, "pool_kernel must be odd and in [1, 255]");
   if (c->dtype == KVLR_BF16) {
-    if (!rank_supported_bf16(c->rank)) return fail(KVLR_EINVAL, "bf16 storage needs rank in {32, 64, 128, 192, 256}");
+    if (!rank_supported_bf16(c->rank_k) || !rank_supported_bf16(c->rank_v))
+      return fail(KVLR_EINVAL, "bf16 storage needs ranks in {32, 64, 128, 192, 256}");
     if (c->q_window * G > 128) return fail(KVLR_EINVAL, "bf16 storage needs q_window * G <= 128");
   } else {
-    if ((int64_t)c->q_window * G * c->rank > 8192)
-      return fail(KVLR_EINVAL, "fp32 storage needs q_window * G * rank <= 8192");
+    if ((int64_t)c->q_window * G * c->rank_k > 8192)
+      return fail(KVLR_EINVAL, "fp32 storage needs q_window * G * rank_k <= 8192");
   }
   if (attend_lds_bytes(dims_of(c)) == 0)
     return fail(KVLR_EINVAL, "rank / head shape too large for the attention tile (160 KB LDS)");
@@ -115,7 +131,7 @@ int check_sample_fits(const kvlr_config* c, int64_t L) {
 
 // ---- workspace layouts ------------------------------------------------------
 struct BuildLayout {
-  size_t S, A0, A1, V0, V1, part, frozen, final_buf, counter, total;
+  size_t S, A0, A1, V0, V1, part, frozen, final_buf, done, total;
   int nchunk;
 };
 
@@ -142,8 +158,8 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
   off = align_up(off + (size_t)nmat * sizeof(int));
   b.final_buf = off;
   off = align_up(off + (size_t)nmat * sizeof(int));
-  b.counter = off;
-  off = align_up(off + sizeof(int));
+  b.done = off;
+  off = align_up(off + (size_t)nmat * sizeof(int));
   b.total = off;
   return b;
 }
@@ -171,7 +187,7 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   L.keys = take((size_t)U * L.t.Lc_cap * sizeof(uint32_t));
   L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
   L.qlat = take((size_t)U * d.Hq * d.r * sizeof(float));
-  L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.r * sizeof(float));
+  L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.rv * sizeof(float));
   L.yex = take((size_t)U * L.t.nse * d.Hq * d.dh * sizeof(float));
   L.astat = take((size_t)U * (L.t.nsl + L.t.nse) * d.Hq * 2 * sizeof(float));
   L.gmax = take((size_t)U * (L.t.Lc_cap / 8) * sizeof(uint32_t));
@@ -188,15 +204,15 @@ int check_cache(const kvlr_cache* cache, bool need_state, int n_sink) {
   if (need_state) {
     if (n_sink > 0 && (!cache->sink_k || !cache->sink_v))
       return fail(KVLR_EINVAL, "sink buffers are NULL");
-    if (!cache->ring_k || !cache->ring_v || !cache->coef_k ||
-        !cache->coef_v || !cache->qwin || !cache->rowstat || !cache->lens || !cache->qsplit)
+    if (!cache->ring_k || !cache->ring_v || !cache->coef_k || !cache->coef_v || !cache->qwin ||
+        !cache->lens || !cache->state)
       return fail(KVLR_EINVAL, "a cache buffer is NULL");
     if (cache->L_max < 1) return fail(KVLR_EINVAL, "cache L_max must be >= 1");
   }
   return KVLR_OK;
 }
 
-CachePtrs cache_ptrs(const kvlr_cache* c) {
+CachePtrs cache_ptrs(const kvlr_cache* c, const Dims& d) {
   CachePtrs p;
   p.sink_k = c->sink_k;
   p.sink_v = c->sink_v;
@@ -207,9 +223,10 @@ CachePtrs cache_ptrs(const kvlr_cache* c) {
   p.basis_k = c->basis_k;
   p.basis_v = c->basis_v;
   p.qwin = c->qwin;
-  p.qsplit = (uint16_t*)c->qsplit;
-  p.rowstat = c->rowstat;
   p.lens = c->lens;
+  p.state = (uint8_t*)c->state;
+  p.state_stride = state_unit_bytes(d);
+  p.rowstat_off = state_rowstat_off(d);
   p.Lmax = c->L_max;
   return p;
 }
@@ -241,12 +258,13 @@ int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max, siz
   const int64_t G = cfg->n_q_heads / cfg->n_kv_heads;
   bytes[KVLR_BUF_SINK_K] = bytes[KVLR_BUF_SINK_V] = (size_t)n_units * cfg->n_sink * D * eb;
   bytes[KVLR_BUF_RING_K] = bytes[KVLR_BUF_RING_V] = (size_t)n_units * cfg->n_recent * D * eb;
-  bytes[KVLR_BUF_COEF_K] = bytes[KVLR_BUF_COEF_V] = (size_t)n_units * L_max * cfg->rank * eb;
-  bytes[KVLR_BUF_BASIS_K] = bytes[KVLR_BUF_BASIS_V] = (size_t)n_units * D * cfg->rank * eb;
-  bytes[KVLR_BUF_QWIN] = (size_t)n_units * cfg->q_window * G * cfg->rank * sizeof(float);
-  bytes[KVLR_BUF_ROWSTAT] = (size_t)n_units * cfg->q_window * G * 2 * sizeof(float);
+  bytes[KVLR_BUF_COEF_K] = (size_t)n_units * L_max * cfg->rank_k * eb;
+  bytes[KVLR_BUF_COEF_V] = (size_t)n_units * L_max * cfg->rank_v * eb;
+  bytes[KVLR_BUF_BASIS_K] = (size_t)n_units * D * cfg->rank_k * eb;
+  bytes[KVLR_BUF_BASIS_V] = (size_t)n_units * D * cfg->rank_v * eb;
+  bytes[KVLR_BUF_QWIN] = (size_t)n_units * cfg->q_window * G * cfg->rank_k * sizeof(float);
   bytes[KVLR_BUF_LENS] = (size_t)n_units * 2 * sizeof(int32_t);
-  bytes[KVLR_BUF_QSPLIT] = (size_t)n_units * cfg->q_window * G * 2 * cfg->rank * sizeof(uint16_t);
+  bytes[KVLR_BUF_STATE] = (size_t)n_units * state_unit_bytes(dims_of(cfg));
   return ok();
 }
 
@@ -266,7 +284,7 @@ int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units, int64_
 
 int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const void* K,
                      const void* V, kvlr_cache* cache, float* eigvals_k, float* eigvals_v,
-                     void* ws, size_t ws_bytes, void* stream) {
+                     int32_t* sweeps, void* ws, size_t ws_bytes, void* stream) {
   int e = check_cfg(cfg);
   if (e) return e;
   if (n_units < 1 || n_units > (1 << 20)) return fail(KVLR_EINVAL, "n_units out of range");
@@ -285,17 +303,18 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
   double* part = (double*)(w + bl.part);
   int* frozen = (int*)(w + bl.frozen);
   int* final_buf = (int*)(w + bl.final_buf);
-  int* counter = (int*)(w + bl.counter);
+  int* done = (int*)(w + bl.done);
   hipError_t he;
   if ((he = launch_sample_normalize(d, (int)n_units, L, K, V, w + bl.S, st)) != hipSuccess)
     return hip_fail(he, "sample/normalise");
   if ((he = launch_gram(d, nmat, w + bl.S, A[0], Vm[0], st)) != hipSuccess) return hip_fail(he, "gram");
-  if ((he = hipMemsetAsync(frozen, 0, (size_t)nmat * sizeof(int), st)) != hipSuccess)
-    return hip_fail(he, "memset");
-  if ((he = hipMemsetAsync(final_buf, 0, (size_t)nmat * sizeof(int), st)) != hipSuccess)
-    return hip_fail(he, "memset");
+  if ((he = launch_jacobi_init(nmat, frozen, final_buf, done, st)) != hipSuccess)
+    return hip_fail(he, "jacobi init");
+  // A fixed number of sweeps is enqueued; a matrix that has converged is
+  // frozen on the device and every later kernel returns at once for it, so
+  // nothing is read back and the call stays stream-ordered.
   const int n = d.D;
-  const int max_sweeps = 30;
+  const int max_sweeps = cfg->eig_max_sweeps > 0 ? cfg->eig_max_sweeps : kDefaultEigSweeps;
   const double tol = 1e-13;
   int cur = 0;
   if (bjac_supported(n)) {
@@ -305,36 +324,34 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
       for (int rd = -1; rd < nb - 1; ++rd)  // the self round, then the cross rounds
         if ((he = launch_bjac_round(n, nmat, A[0], Vm[0], A[1], frozen, rd, st)) != hipSuccess)
           return hip_fail(he, "block jacobi round");
-      if ((he = launch_jacobi_check(n, nmat, A[0], part, frozen, final_buf, 0, counter, tol, st)) != hipSuccess)
+      if ((he = launch_jacobi_check(n, nmat, A[0], part, frozen, final_buf, done, 0, sweep, tol, st)) !=
+          hipSuccess)
         return hip_fail(he, "jacobi check");
-      int active = -1;
-      if ((he = hipMemcpyAsync(&active, counter, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
-        return hip_fail(he, "memcpy");
-      if ((he = hipStreamSynchronize(st)) != hipSuccess) return fail(KVLR_EDEVICE, "sync: %s", hipGetErrorString(he));
-      if (active == 0) break;
     }
-  } else
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    for (int rd = 0; rd < n - 1; ++rd) {
-      if ((he = launch_jacobi_round(n, nmat, A[cur], A[cur ^ 1], Vm[cur], Vm[cur ^ 1], frozen, st)) != hipSuccess)
-        return hip_fail(he, "jacobi round");
-      cur ^= 1;
-    }
-    if (n <= 2) break;
-    if (sweep >= 2) {
-      if ((he = launch_jacobi_check(n, nmat, A[cur], part, frozen, final_buf, cur, counter, tol, st)) != hipSuccess)
+  } else if (n > 2) {
+    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+      for (int rd = 0; rd < n - 1; ++rd) {
+        if ((he = launch_jacobi_round(n, nmat, A[cur], A[cur ^ 1], Vm[cur], Vm[cur ^ 1], frozen, st)) !=
+            hipSuccess)
+          return hip_fail(he, "jacobi round");
+        cur ^= 1;
+      }
+      if ((he = launch_jacobi_check(n, nmat, A[cur], part, frozen, final_buf, done, cur, sweep, tol, st)) !=
+          hipSuccess)
         return hip_fail(he, "jacobi check");
-      int active = -1;
-      if ((he = hipMemcpyAsync(&active, counter, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
-        return hip_fail(he, "memcpy");
-      if ((he = hipStreamSynchronize(st)) != hipSuccess) return fail(KVLR_EDEVICE, "sync: %s", hipGetErrorString(he));
-      if (active == 0) break;
     }
+  } else {
+    // n = 2: one rotation diagonalises the matrix exactly
+    if ((he = launch_jacobi_round(n, nmat, A[0], A[1], Vm[0], Vm[1], frozen, st)) != hipSuccess)
+      return hip_fail(he, "jacobi round");
+    cur = 1;
+    if ((he = launch_jacobi_check(n, nmat, A[cur], part, frozen, final_buf, done, cur, 0, tol, st)) !=
+        hipSuccess)
+      return hip_fail(he, "jacobi check");
   }
-  if ((he = launch_extract(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, cur, cache->basis_k,
-                           cache->basis_v, eigvals_k, eigvals_v, st)) != hipSuccess)
+  if ((he = launch_extract(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, done, cur,
+                           cache->basis_k, cache->basis_v, eigvals_k, eigvals_v, sweeps, st)) != hipSuccess)
     return hip_fail(he, "extract");
-  if ((he = hipStreamSynchronize(st)) != hipSuccess) return fail(KVLR_EDEVICE, "sync: %s", hipGetErrorString(he));
   return ok();
 }
 
@@ -358,9 +375,7 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
   if ((he = launch_project(d, (int)n_units, L, cache->L_max, K, V, cache->basis_k, cache->basis_v,
                            cache->coef_k, cache->coef_v, ws, st)) != hipSuccess)
     return hip_fail(he, "project");
-  if ((he = launch_exact_and_reset(d, (int)n_units, L, K, V, cache->sink_k, cache->sink_v, cache->ring_k,
-                                   cache->ring_v, cache->qwin, cache->rowstat, cache->lens,
-                                   (uint16_t*)cache->qsplit, st)) != hipSuccess)
+  if ((he = launch_exact_and_reset(d, (int)n_units, L, K, V, cache_ptrs(cache, d), st)) != hipSuccess)
     return hip_fail(he, "exact/reset");
   return ok();
 }
@@ -395,7 +410,7 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   dw.cslot = (uint2*)(w + dl.cslot);
   dw.tkpcnt = (int*)(w + dl.tkpcnt);
   dw.tkhint = (uint32_t*)(w + dl.tkhint);
-  const CachePtrs cp = cache_ptrs(cache);
+  const CachePtrs cp = cache_ptrs(cache, d);
   const int U = (int)n_units;
 
   hipEvent_t* ev = nullptr;
@@ -420,6 +435,28 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   if (ev) (void)hipEventRecord(ev[5], st);
   if ((he = launch_merge(d, U, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
   if (ev) (void)hipEventRecord(ev[6], st);
+  return ok();
+}
+
+int kvlr_rank_for_ratio(double eta, int64_t L, int32_t d_kv, int32_t n_sink, int32_t n_recent,
+                        int32_t k_parts, int32_t v_parts, int32_t multiple, int32_t* rank_k,
+                        int32_t* rank_v) {
+  if (!rank_k || !rank_v) return fail(KVLR_EINVAL, "rank_k / rank_v is NULL");
+  if (!(eta > 0.0) || L < 1 || d_kv < 1 || n_sink < 0 || n_recent < 0 || k_parts < 1 ||
+      v_parts < 1 || multiple < 1 || (int64_t)n_sink > L)
+    return fail(KVLR_EINVAL, "eta, sizes, parts and multiple must be positive (n_sink <= L)");
+  // persistent bytes per element size: exact sinks and ring for K and V,
+  // coefficients of the other tokens and the bases
+  auto bytes = [&](int64_t rk, int64_t rv) {
+    return 2.0 * (double)(n_sink + n_recent) * d_kv + (double)(L - n_sink + d_kv) * (double)(rk + rv);
+  };
+  const double budget = eta * 2.0 * (double)L * d_kv;
+  int64_t t = 0;
+  while ((int64_t)k_parts * (t + 1) * multiple <= d_kv && (int64_t)v_parts * (t + 1) * multiple <= d_kv &&
+         bytes((int64_t)k_parts * (t + 1) * multiple, (int64_t)v_parts * (t + 1) * multiple) <= budget)
+    ++t;
+  *rank_k = (int32_t)(k_parts * t * multiple);
+  *rank_v = (int32_t)(v_parts * t * multiple);
   return ok();
 }
 

@@ -24,6 +24,24 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp64 -> bf16, round to nearest, ties to even, in one step (no rounding
+// through fp32 first, which can land on a bf16 tie and round again).
+// Finite values in the normal bf16 range are handled on the bits; zeros keep
+// their sign; anything else (NaN, inf, subnormal or overflowing results) goes
+// through fp32, whose double rounding cannot matter there.
+__device__ __forceinline__ uint16_t d2bf(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t sign = (u >> 63) << 15;
+  const uint64_t mag = u & 0x7fffffffffffffffull;
+  if (mag == 0) return (uint16_t)sign;
+  const int eb = (int)(mag >> 52) - 1023 + 127;  // bf16 biased exponent
+  if (eb <= 0 || eb >= 255) return f2bf((float)x);
+  // exponent and 52 fraction bits, rebiased; drop the low 45 fraction bits
+  const uint64_t t = ((uint64_t)eb << 52) | (mag & 0x000fffffffffffffull);
+  const uint64_t r = (t + 0x00000fffffffffffull + ((t >> 45) & 1ull)) >> 45;
+  return (uint16_t)(sign | r);  // a carry into the exponent is the right result
+}
+
 // storage element access, T = float (fp32) or uint16_t (bf16)
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -160,7 +178,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 namespace kvlr {
 
 struct Dims {
-  int Hq, Hkv, dh, D, r, G, s, T, rnum, rden, W, k, nrec, kappa, dtype;
+  int Hq, Hkv, dh, D;
+  int r;       // key rank r_K (the latent scores, the query window)
+  int rv;      // value rank r_V
+  int G, s, T, rnum, rden, W, k, nrec, kappa, dtype;
+  int local;   // recent window: 0 exact ring, 1 rebuilt from coefficients
 };
 
 // prefill
@@ -178,22 +200,23 @@ bool bjac_supported(int n);
 size_t bjac_q_bytes(int n, int nmat);
 hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,
                              int k, hipStream_t st);
+// convergence bookkeeping of the eigensolves, per matrix: frozen (converged,
+// later rounds skip it), final_buf (buffer holding its result, scalar path),
+// done_sweeps (sweep count at convergence, 0 = not yet)
+hipError_t launch_jacobi_init(int nmat, int* frozen, int* final_buf, int* done_sweeps, hipStream_t st);
 hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
-                               int* final_buf, int cur, int* n_active, double tol,
+                               int* final_buf, int* done_sweeps, int cur, int sweep, double tol,
                                hipStream_t st);
 hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
                           const double* V0, const double* V1, const int* frozen,
-                          const int* final_buf, int cur, void* basis_k, void* basis_v,
-                          float* eig_k, float* eig_v, hipStream_t st);
+                          const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
+                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
+                          hipStream_t st);
 hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
                           const void* V, const void* BK, const void* BV, void* CK, void* CV,
                           void* ws, hipStream_t st);
 // workspace bytes of launch_project (transposed bases; 0 when not used)
 size_t project_ws_bytes(const Dims& d, int64_t U);
-hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
-                                  void* sink_k, void* sink_v, void* ring_k, void* ring_v,
-                                  float* qwin, float* rowstat, int32_t* lens, uint16_t* qsplit,
-                                  hipStream_t st);
 
 // decode
 constexpr int kHistBins = 4096;  // selection histogram over the top 12 key bits
@@ -230,11 +253,32 @@ struct DecodeWs {
 struct CachePtrs {
   void *sink_k, *sink_v, *ring_k, *ring_v, *coef_k, *coef_v, *basis_k, *basis_v;
   float* qwin;
-  float* rowstat;
   int32_t* lens;
-  uint16_t* qsplit;  // [U][W][G][2][r] bf16 hi / lo of qwin * qscale
+  // per-unit opaque decode state, state_stride bytes per unit:
+  //   [W][G][2][r] bf16  hi / lo parts of qwin * log2(e)/sqrt(r) (scorer operands)
+  //   [W][G][2]    fp32  running (max, sum) of each window row's latent softmax
+  uint8_t* state;
+  int64_t state_stride, rowstat_off;
   int64_t Lmax;
 };
+__host__ __device__ inline uint16_t* qsplit_of(const CachePtrs& c, int64_t u) {
+  return reinterpret_cast<uint16_t*>(c.state + u * c.state_stride);
+}
+__host__ __device__ inline float* rowstat_of(const CachePtrs& c, int64_t u) {
+  return reinterpret_cast<float*>(c.state + u * c.state_stride + c.rowstat_off);
+}
+// state layout of one unit (bytes): the bf16 window operands, then the row
+// statistics, 256-byte aligned overall
+inline int64_t state_rowstat_off(const Dims& d) {
+  return ((int64_t)d.W * d.G * 2 * d.r * 2 + 15) / 16 * 16;
+}
+inline int64_t state_unit_bytes(const Dims& d) {
+  return (state_rowstat_off(d) + (int64_t)d.W * d.G * 2 * 4 + 255) / 256 * 256;
+}
+
+// prefill: exact sinks and ring, window and decode state cleared, lens = {L, 0}
+hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                                  const CachePtrs& c, hipStream_t st);
 
 hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_new,
                            const void* v_new, const CachePtrs& c, const DecodeWs& w,

@@ -215,7 +215,7 @@ __device__ __forceinline__ void prologue_state(const Dims& d, const CachePtrs& c
     z += __shfl_xor(z, 2);
     if (o < nold && part == 0) {
       z *= qscale;
-      float* rsp = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
+      float* rsp = rowstat_of(c, u) + (sl * G + g) * 2;
       const float m = rsp[0], S = rsp[1];
       const float mn = fmaxf(m, z);
       rsp[0] = mn;
@@ -369,8 +369,9 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
         c.qwin[row * r + cl] = sum;
         const float x = sum * qscale;  // MFMA operands of the latent scoring
         const uint16_t hb = f2bf(x);
-        c.qsplit[(row * 2 + 0) * r + cl] = hb;
-        c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
+        uint16_t* qs = qsplit_of(c, u) + ((steps % W) * G + (v - 1)) * 2 * r;
+        qs[cl] = hb;
+        qs[r + cl] = f2bf(x - bf2f(hb));
       }
     }
     return;
@@ -536,7 +537,7 @@ __device__ __forceinline__ void prologue_state_bf16(const Dims& d, const CachePt
     }
     int sl, g;
     row_of(min(wv + 4 * (m0 + (l & (RB - 1))), max(nold - 1, 0)), &sl, &g);
-    st = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2);
+    st = *reinterpret_cast<const float2*>(rowstat_of(c, u) + (sl * G + g) * 2);
   };
   if (nold > 0) issue(0);
   u16x8* dk = reinterpret_cast<u16x8*>((uint16_t*)c.ring_k + ((int64_t)u * d.nrec + rs) * D);
@@ -568,7 +569,7 @@ __device__ __forceinline__ void prologue_state_bf16(const Dims& d, const CachePt
       row_of(o, &sl, &g);
       const float z = zl * qscale;
       const float mn = fmaxf(st.x, z);
-      *reinterpret_cast<float2*>(c.rowstat + (((int64_t)u * W + sl) * G + g) * 2) =
+      *reinterpret_cast<float2*>(rowstat_of(c, u) + (sl * G + g) * 2) =
           make_float2(mn, st.y * exp2f(st.x - mn) + exp2f(z - mn));
     }
   }
@@ -689,8 +690,9 @@ __global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, cons
       c.qwin[row * r + cl] = sum;
       const float x = sum * qscale;  // MFMA operands of the latent scoring
       const uint16_t hb = f2bf(x);
-      c.qsplit[(row * 2 + 0) * r + cl] = hb;
-      c.qsplit[(row * 2 + 1) * r + cl] = f2bf(x - bf2f(hb));
+      uint16_t* qs = qsplit_of(c, u) + ((steps % W) * G + (v - 1)) * 2 * r;
+      qs[cl] = hb;
+      qs[r + cl] = f2bf(x - bf2f(hb));
     }
   }
 }
@@ -929,7 +931,7 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
     const int rv = valid ? rho : 0;
     const int i = rv / G, g = rv % G;
     const int sl = wrap_slot(steps - i, W);
-    const uint16_t* qh = c.qsplit + ((((int64_t)u * W + sl) * G + g) * 2) * r;
+    const uint16_t* qh = qsplit_of(c, u) + ((sl * G + g) * 2) * r;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const bf16x8 h = ld_bf16x8(qh + (4 * ks + kq) * 8);
@@ -944,7 +946,7 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
       const int rv2 = rr < nrows ? rr : 0;
       const int ii = rv2 / G, g2 = rv2 % G;
       const int sl2 = wrap_slot(steps - ii, W);
-      stv[i2] = *reinterpret_cast<const float2*>(c.rowstat + (((int64_t)u * W + sl2) * G + g2) * 2);
+      stv[i2] = *reinterpret_cast<const float2*>(rowstat_of(c, u) + (sl2 * G + g2) * 2);
     }
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs
   for (int rho = threadIdx.x; rho < nrows; rho += blockDim.x) {
     const int i = rho / G, g = rho % G;
     const int sl = wrap_slot(steps - i, W);
-    const float* rs = c.rowstat + (((int64_t)u * W + sl) * G + g) * 2;
+    const float* rs = rowstat_of(c, u) + (sl * G + g) * 2;
     rm[rho] = rs[0];
     ri[rho] = rho < G ? 0.f : 1.f / rs[1];
   }
@@ -1332,7 +1334,7 @@ __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
       Mg[tid] = mm;
       Ig[tid] = 1.f / ss;
       if (blk == 0) {
-        float* rs = c.rowstat + (((int64_t)u * d.W + steps % d.W) * G + tid) * 2;
+        float* rs = rowstat_of(c, u) + ((steps % d.W) * G + tid) * 2;
         rs[0] = mm;
         rs[1] = ss;
       }

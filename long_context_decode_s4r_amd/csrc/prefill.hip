@@ -15,7 +15,8 @@
 namespace kvlr {
 
 // --------------------------------------------------------------------------
-// 1. sample + normalise: S[m][i][:] = rnd(x_p / ||x_p||), m = 2u + (0 K | 1 V)
+// 1. sample + normalise: S[m][i][:] = rnd(x_p / ||x_p||), m = 2u + (0 K | 1 V),
+//    the quotient in fp64 and rounded once to the storage type
 //    sample position p(i): the first n_u entries are evenly spaced over
 //    [s, L - n_r), the last n_r are the most recent prompt positions.
 // --------------------------------------------------------------------------
@@ -50,11 +51,16 @@ __global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ 
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
-  const double tot = red[0];
-  const double inv = tot > 0.0 ? 1.0 / sqrt(tot) : 0.0;
+  const double nrm = sqrt(red[0]);
   T* out = S + ((int64_t)m * nT + i) * D;
-  for (int j = threadIdx.x; j < D; j += blockDim.x)
-    Elem<T>::st(out, j, (float)((double)Elem<T>::ld(row, j) * inv));
+  // x / ||x|| in fp64, rounded once to the storage type (a zero row stays 0)
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    const double x = nrm > 0.0 ? (double)Elem<T>::ld(row, j) / nrm : 0.0;
+    if constexpr (sizeof(T) == 2)
+      out[j] = d2bf(x);
+    else
+      out[j] = (float)x;
+  }
 }
 
 hipError_t launch_sample_normalize(const Dims& d, int U, int64_t L, const void* K, const void* V,
@@ -318,11 +324,8 @@ __global__ __launch_bounds__(256) void k_offnorm(const double* __restrict__ A,
 }
 
 __global__ void k_jacobi_check(const double* __restrict__ part, int* __restrict__ frozen,
-                               int* __restrict__ final_buf, int* __restrict__ n_active, int nmat,
-                               int nchunk, int cur, double tol) {
-  __shared__ int cnt;
-  if (threadIdx.x == 0) cnt = 0;
-  __syncthreads();
+                               int* __restrict__ final_buf, int* __restrict__ done_sweeps, int nmat,
+                               int nchunk, int cur, int sweep, double tol) {
   for (int m = threadIdx.x; m < nmat; m += blockDim.x) {
     if (frozen[m]) continue;
     double off = 0.0, tr = 0.0;
@@ -333,23 +336,38 @@ __global__ void k_jacobi_check(const double* __restrict__ part, int* __restrict_
     if (sqrt(off) <= tol * fabs(tr) || off == 0.0) {
       frozen[m] = 1;
       final_buf[m] = cur;
-    } else {
-      atomicAdd(&cnt, 1);
+      done_sweeps[m] = sweep + 1;
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) *n_active = cnt;
+}
+
+// matrices whose eigensolve reached the tolerance are frozen: every later
+// round and check kernel returns at once for them, so a fixed number of
+// sweeps can be enqueued without reading anything back
+__global__ void k_jacobi_init(int* __restrict__ frozen, int* __restrict__ final_buf,
+                              int* __restrict__ done_sweeps, int nmat) {
+  for (int m = threadIdx.x; m < nmat; m += blockDim.x) {
+    frozen[m] = 0;
+    final_buf[m] = 0;
+    done_sweeps[m] = 0;
+  }
+}
+
+hipError_t launch_jacobi_init(int nmat, int* frozen, int* final_buf, int* done_sweeps,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_jacobi_init, dim3(1), dim3(256), 0, st, frozen, final_buf, done_sweeps, nmat);
+  return hipGetLastError();
 }
 
 hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
-                               int* final_buf, int cur, int* n_active, double tol,
+                               int* final_buf, int* done_sweeps, int cur, int sweep, double tol,
                                hipStream_t st) {
   const int nchunk = (n + kJacRowsPerBlock - 1) / kJacRowsPerBlock;
   hipLaunchKernelGGL(k_offnorm, dim3(nchunk, nmat), dim3(256), 0, st, A, frozen, part, n, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_jacobi_check, dim3(1), dim3(256), 0, st, part, frozen, final_buf, n_active,
-                     nmat, nchunk, cur, tol);
+  hipLaunchKernelGGL(k_jacobi_check, dim3(1), dim3(256), 0, st, part, frozen, final_buf, done_sweeps,
+                     nmat, nchunk, cur, sweep, tol);
   return hipGetLastError();
 }
 
@@ -683,15 +701,19 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
                                                   const double* __restrict__ V0,
                                                   const double* __restrict__ V1,
                                                   const int* __restrict__ frozen,
-                                                  const int* __restrict__ final_buf, int cur,
-                                                  int n, int r, T* __restrict__ BK,
+                                                  const int* __restrict__ final_buf,
+                                                  const int* __restrict__ done_sweeps, int cur,
+                                                  int n, int rk, int rv, T* __restrict__ BK,
                                                   T* __restrict__ BV, float* __restrict__ eigK,
-                                                  float* __restrict__ eigV) {
+                                                  float* __restrict__ eigV,
+                                                  int32_t* __restrict__ sweeps) {
   extern __shared__ unsigned char smem_raw[];
   const int m = blockIdx.x, u = m >> 1, kind = m & 1;
+  const int r = kind ? rv : rk;
   const int buf = frozen[m] ? final_buf[m] : cur;
   const double* A = (buf ? A1 : A0) + (int64_t)m * n * n;
   const double* Vm = (buf ? V1 : V0) + (int64_t)m * n * n;
+  if (sweeps && threadIdx.x == 0) sweeps[m] = frozen[m] ? done_sweeps[m] : -1;
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
   double* key = reinterpret_cast<double*>(smem_raw);
@@ -727,26 +749,33 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
   if (eig)
     for (int i = threadIdx.x; i < n; i += blockDim.x) eig[(int64_t)u * n + i] = (float)key[i];
   T* B = (kind ? BV : BK) + (int64_t)u * n * r;
+  // eigenvector entries rounded once from fp64 to the storage type
   for (int64_t e = threadIdx.x; e < (int64_t)n * r; e += blockDim.x) {
     const int i = (int)(e / r), c = (int)(e % r);
-    Elem<T>::st(B, e, (float)Vm[(int64_t)i * n + idx[c]]);
+    const double x = Vm[(int64_t)i * n + idx[c]];
+    if constexpr (sizeof(T) == 2)
+      B[e] = d2bf(x);
+    else
+      B[e] = (float)x;
   }
 }
 
 hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
                           const double* V0, const double* V1, const int* frozen,
-                          const int* final_buf, int cur, void* basis_k, void* basis_v,
-                          float* eig_k, float* eig_v, hipStream_t st) {
+                          const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
+                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
+                          hipStream_t st) {
   int np2 = 1;
   while (np2 < d.D) np2 <<= 1;
   const size_t lds = (size_t)np2 * (sizeof(double) + sizeof(int));
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_extract<float>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
-                       final_buf, cur, d.D, d.r, (float*)basis_k, (float*)basis_v, eig_k, eig_v);
+                       final_buf, done_sweeps, cur, d.D, d.r, d.rv, (float*)basis_k,
+                       (float*)basis_v, eig_k, eig_v, sweeps);
   else
     hipLaunchKernelGGL(k_extract<uint16_t>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
-                       frozen, final_buf, cur, d.D, d.r, (uint16_t*)basis_k, (uint16_t*)basis_v,
-                       eig_k, eig_v);
+                       frozen, final_buf, done_sweeps, cur, d.D, d.r, d.rv, (uint16_t*)basis_k,
+                       (uint16_t*)basis_v, eig_k, eig_v, sweeps);
   return hipGetLastError();
 }
 
@@ -761,8 +790,9 @@ __global__ __launch_bounds__(256) void k_project_bf16(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ BV,
                                                       uint16_t* __restrict__ CK,
                                                       uint16_t* __restrict__ CV, int64_t L,
-                                                      int64_t Lmax, int D, int r, int s) {
+                                                      int64_t Lmax, int D, int rk, int rv, int s) {
   const int u = blockIdx.y >> 1, kind = blockIdx.y & 1;
+  const int r = kind ? rv : rk;
   const uint16_t* X = (kind ? V : K) + (int64_t)u * L * D;
   const uint16_t* B = (kind ? BV : BK) + (int64_t)u * D * r;
   uint16_t* C = (kind ? CV : CK) + (int64_t)u * Lmax * r;
@@ -841,13 +871,16 @@ constexpr int kProjRing = 4;     // X fragment ring depth (steps)
 
 __global__ __launch_bounds__(256) void k_basis_t(const uint16_t* __restrict__ BK,
                                                  const uint16_t* __restrict__ BV,
-                                                 uint16_t* __restrict__ BT, int D, int r) {
-  // tile of 32 channels x 32 columns; BT[u][kind][n][k] = B[u][kind][k][n]
+                                                 uint16_t* __restrict__ BT, int D, int rk, int rv) {
+  // tile of 32 channels x 32 columns; per unit BT holds B^K^T [rk][D'] then
+  // B^V^T [rv][D'], BT[n][k] = B[k][n]
   __shared__ uint16_t t[32][33];
   const int um = blockIdx.z, u = um >> 1, kind = um & 1;
+  const int r = kind ? rv : rk;
   const uint16_t* B = (kind ? BV : BK) + (int64_t)u * D * r;
-  uint16_t* T = BT + (int64_t)um * r * D;
+  uint16_t* T = BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0);
   const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  if (n0 >= r) return;
   for (int e = threadIdx.x; e < 1024; e += 256) {
     const int kk = e >> 5, nn = e & 31;
     if (k0 + kk < D && n0 + nn < r) t[kk][nn] = B[(int64_t)(k0 + kk) * r + n0 + nn];
@@ -865,7 +898,7 @@ template <int R, int NS>
 __global__ __launch_bounds__(kProjWaves * 64) void k_project_mfma(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ BT, uint16_t* __restrict__ CK, uint16_t* __restrict__ CV,
-    int64_t L, int64_t Lmax, int D, int s) {
+    int64_t L, int64_t Lmax, int D, int s, int kind_only, int rk, int rv) {
   constexpr int NT = kProjWaves * 64;
   constexpr int NCB = R / 32;
   constexpr int SB = R * kProjK * 2;         // stage bytes
@@ -873,10 +906,12 @@ __global__ __launch_bounds__(kProjWaves * 64) void k_project_mfma(
   constexpr int AR = kProjRing;
   static_assert(SB % (16 * NT) == 0, "rank must be a multiple of 64");
   __shared__ __attribute__((aligned(16))) uint8_t stg[2 * SB];
-  const int um = blockIdx.y, u = um >> 1, kind = um & 1;
+  // kind_only < 0: grid.y = 2 U (K and V share the rank R); else grid.y = U
+  const int u = kind_only < 0 ? blockIdx.y >> 1 : blockIdx.y;
+  const int kind = kind_only < 0 ? blockIdx.y & 1 : kind_only;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
   const uint16_t* X = (kind ? V : K) + (int64_t)u * L * D;
-  const uint16_t* Bt = BT + (int64_t)um * R * D;
+  const uint16_t* Bt = BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0);
   uint16_t* C = (kind ? CV : CK) + (int64_t)u * Lmax * R;
   const int64_t row0 = s + (int64_t)blockIdx.x * kProjRows;
   const int nsteps = NS > 0 ? NS : D / kProjK;
@@ -958,8 +993,10 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K
                                                      const float* __restrict__ BK,
                                                      const float* __restrict__ BV,
                                                      float* __restrict__ CK, float* __restrict__ CV,
-                                                     int64_t L, int64_t Lmax, int D, int r, int s) {
+                                                     int64_t L, int64_t Lmax, int D, int rk, int rv,
+                                                     int s) {
   const int u = blockIdx.y >> 1, kind = blockIdx.y & 1;
+  const int r = kind ? rv : rk;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nrow = L - s;
   if (e >= nrow * r) return;
@@ -974,17 +1011,15 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K
 
 template <int R>
 static hipError_t launch_project_mfma(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
-                                      const void* V, const void* BK, const void* BV, void* CK,
-                                      void* CV, uint16_t* BT, hipStream_t st) {
-  hipLaunchKernelGGL(k_basis_t, dim3((d.D + 31) / 32, R / 32, 2 * U), dim3(256), 0, st,
-                     (const uint16_t*)BK, (const uint16_t*)BV, BT, d.D, R);
+                                      const void* V, void* CK, void* CV, const uint16_t* BT,
+                                      int kind_only, hipStream_t st) {
   const int64_t nrow = L - d.s;
-  const dim3 grid((unsigned)((nrow + kProjRows - 1) / kProjRows), 2 * U);
+  const dim3 grid((unsigned)((nrow + kProjRows - 1) / kProjRows), kind_only < 0 ? 2 * U : U);
 #define KVLR_PROJ_LAUNCH(NS)                                                                     \
   hipLaunchKernelGGL((k_project_mfma<R, NS>), grid, dim3(kProjWaves * 64), 0, st,               \
                      (const uint16_t*)K,                                                        \
-                     (const uint16_t*)V, (const uint16_t*)BT, (uint16_t*)CK, (uint16_t*)CV, L,  \
-                     Lmax, d.D, d.s)
+                     (const uint16_t*)V, BT, (uint16_t*)CK, (uint16_t*)CV, L,                   \
+                     Lmax, d.D, d.s, kind_only, d.r, d.rv)
   switch (d.D / kProjK) {
     case 8: KVLR_PROJ_LAUNCH(8); break;
     case 16: KVLR_PROJ_LAUNCH(16); break;
@@ -994,9 +1029,26 @@ static hipError_t launch_project_mfma(const Dims& d, int U, int64_t L, int64_t L
   return hipGetLastError();
 }
 
+static hipError_t launch_project_rank(int R, const Dims& d, int U, int64_t L, int64_t Lmax,
+                                      const void* K, const void* V, void* CK, void* CV,
+                                      const uint16_t* BT, int kind_only, hipStream_t st) {
+  switch (R) {
+    case 64: return launch_project_mfma<64>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
+    case 128: return launch_project_mfma<128>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
+    case 192: return launch_project_mfma<192>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
+    case 256: return launch_project_mfma<256>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static bool project_mfma_ok(const Dims& d) {
+  auto ok = [](int r) { return r == 64 || r == 128 || r == 192 || r == 256; };
+  return d.dtype != 0 && ok(d.r) && ok(d.rv) && d.D % (kProjRing * kProjK) == 0;
+}
+
 size_t project_ws_bytes(const Dims& d, int64_t U) {
-  if (d.dtype == 0 || d.r % 64 != 0 || d.D % (kProjRing * kProjK) != 0) return 0;
-  return (size_t)U * 2 * d.r * d.D * sizeof(uint16_t);
+  if (!project_mfma_ok(d)) return 0;
+  return (size_t)U * (d.r + d.rv) * d.D * sizeof(uint16_t);
 }
 
 hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
@@ -1004,25 +1056,28 @@ hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const v
                           void* ws, hipStream_t st) {
   const int64_t nrow = L - d.s;
   if (nrow <= 0) return hipSuccess;
-  if (project_ws_bytes(d, U) > 0) {
+  if (project_mfma_ok(d)) {
     uint16_t* BT = (uint16_t*)ws;
-    switch (d.r) {
-      case 64: return launch_project_mfma<64>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
-      case 128: return launch_project_mfma<128>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
-      case 192: return launch_project_mfma<192>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
-      case 256: return launch_project_mfma<256>(d, U, L, Lmax, K, V, BK, BV, CK, CV, BT, st);
-      default: break;
-    }
+    const int rmax = d.r > d.rv ? d.r : d.rv;
+    hipLaunchKernelGGL(k_basis_t, dim3((d.D + 31) / 32, rmax / 32, 2 * U), dim3(256), 0, st,
+                       (const uint16_t*)BK, (const uint16_t*)BV, BT, d.D, d.r, d.rv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, BT, -1, st);
+    e = launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, BT, 0, st);
+    if (e != hipSuccess) return e;
+    return launch_project_rank(d.rv, d, U, L, Lmax, K, V, CK, CV, BT, 1, st);
   }
   if (d.dtype == 0) {
-    const int64_t tot = nrow * d.r;
+    const int64_t tot = nrow * (d.r > d.rv ? d.r : d.rv);
     hipLaunchKernelGGL(k_project_f32, dim3((unsigned)((tot + 255) / 256), 2 * U), dim3(256), 0, st,
                        (const float*)K, (const float*)V, (const float*)BK, (const float*)BV,
-                       (float*)CK, (float*)CV, L, Lmax, d.D, d.r, d.s);
+                       (float*)CK, (float*)CV, L, Lmax, d.D, d.r, d.rv, d.s);
   } else {
     hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)((nrow + 63) / 64), 2 * U), dim3(256), 0,
                        st, (const uint16_t*)K, (const uint16_t*)V, (const uint16_t*)BK,
-                       (const uint16_t*)BV, (uint16_t*)CK, (uint16_t*)CV, L, Lmax, d.D, d.r, d.s);
+                       (const uint16_t*)BV, (uint16_t*)CK, (uint16_t*)CV, L, Lmax, d.D, d.r, d.rv,
+                       d.s);
   }
   return hipGetLastError();
 }
@@ -1032,16 +1087,15 @@ hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const v
 // --------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
-                                                     const T* __restrict__ V, T* __restrict__ sk,
-                                                     T* __restrict__ sv, T* __restrict__ rk,
-                                                     T* __restrict__ rv, float* __restrict__ qwin,
-                                                     uint16_t* __restrict__ qsplit,
-                                                     float* __restrict__ rowstat,
-                                                     int32_t* __restrict__ lens, int64_t L, int D,
-                                                     int s, int nrec, int qw_per_unit,
-                                                     int rs_per_unit) {
+                                                     const T* __restrict__ V, CachePtrs c,
+                                                     int64_t L, int D, int s, int nrec,
+                                                     int qw_per_unit) {
   const int u = blockIdx.y;
   const int row = blockIdx.x;  // [0, s + nrec) exact rows, then one block for the reset
+  T* sk = (T*)c.sink_k;
+  T* sv = (T*)c.sink_v;
+  T* rk = (T*)c.ring_k;
+  T* rv = (T*)c.ring_v;
   if (row < s) {
     const T* src = K + ((int64_t)u * L + row) * D;
     const T* srcv = V + ((int64_t)u * L + row) * D;
@@ -1059,31 +1113,26 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
       rv[((int64_t)u * nrec + slot) * D + j] = srcv[j];
     }
   } else {
-    for (int j = threadIdx.x; j < qw_per_unit; j += blockDim.x) qwin[(int64_t)u * qw_per_unit + j] = 0.f;
-    for (int j = threadIdx.x; j < 2 * qw_per_unit; j += blockDim.x) qsplit[(int64_t)u * 2 * qw_per_unit + j] = 0;
-    for (int j = threadIdx.x; j < rs_per_unit; j += blockDim.x) rowstat[(int64_t)u * rs_per_unit + j] = 0.f;
+    for (int j = threadIdx.x; j < qw_per_unit; j += blockDim.x) c.qwin[(int64_t)u * qw_per_unit + j] = 0.f;
+    uint32_t* st = reinterpret_cast<uint32_t*>(c.state + u * c.state_stride);
+    for (int64_t j = threadIdx.x; j < c.state_stride / 4; j += blockDim.x) st[j] = 0u;
     if (threadIdx.x == 0) {
-      lens[2 * u] = (int32_t)L;
-      lens[2 * u + 1] = 0;
+      c.lens[2 * u] = (int32_t)L;
+      c.lens[2 * u + 1] = 0;
     }
   }
 }
 
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
-                                  void* sink_k, void* sink_v, void* ring_k, void* ring_v,
-                                  float* qwin, float* rowstat, int32_t* lens, uint16_t* qsplit,
-                                  hipStream_t st) {
+                                  const CachePtrs& c, hipStream_t st) {
   dim3 grid(d.s + d.nrec + 1, U);
-  const int qw = d.W * d.G * d.r, rs = d.W * d.G * 2;
+  const int qw = d.W * d.G * d.r;
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_exact_reset<float>, grid, dim3(256), 0, st, (const float*)K,
-                       (const float*)V, (float*)sink_k, (float*)sink_v, (float*)ring_k,
-                       (float*)ring_v, qwin, qsplit, rowstat, lens, L, d.D, d.s, d.nrec, qw, rs);
+                       (const float*)V, c, L, d.D, d.s, d.nrec, qw);
   else
     hipLaunchKernelGGL(k_exact_reset<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
-                       (const uint16_t*)V, (uint16_t*)sink_k, (uint16_t*)sink_v,
-                       (uint16_t*)ring_k, (uint16_t*)ring_v, qwin, qsplit, rowstat, lens, L, d.D, d.s,
-                       d.nrec, qw, rs);
+                       (const uint16_t*)V, c, L, d.D, d.s, d.nrec, qw);
   return hipGetLastError();
 }
 

@@ -1,0 +1,142 @@
+// Measurement probes: streaming reads (register path and direct
+// global->LDS path) and the dense bf16 MFMA issue rate.  Declared in
+// include/kvlr_probe.h.
+#include "../../include/kvlr_probe.h"
+#include "common.h"
+
+namespace kvlr {
+namespace {
+
+// register path: each thread keeps DEPTH 16-byte loads in flight per round
+template <int DEPTH>
+__global__ __launch_bounds__(256) void k_probe_read_reg(const uint4* __restrict__ src, int64_t n16,
+                                                        uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < n16; i0 += stride * DEPTH) {
+    uint4 v[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t i = i0 + d * stride;
+      v[d] = i < n16 ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // never for the probe's data
+}
+
+// LDS path: 512 threads, 4 stages of 32 KiB, 3 in flight; each lane moves
+// 16 bytes per request, each wave 1 KiB, 4 requests per wave per stage
+constexpr int kPrStage = 32768;
+__global__ __launch_bounds__(512) void k_probe_read_lds(const uint8_t* __restrict__ src, int64_t nstage,
+                                                        uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4 * kPrStage];
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  // this block's stages: b, b + grid, ...
+  const int64_t ns = nstage > blockIdx.x ? (nstage - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+  auto issue = [&](int64_t t, uint8_t* stage) {
+    const int64_t tt = t < ns ? t : ns - 1;  // requests past the end re-read the last stage
+    const uint8_t* base = src + ((int64_t)blockIdx.x + tt * gridDim.x) * kPrStage;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int off = (wvu * 4 + q) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(base + off + 16 * l),
+                                       (__attribute__((address_space(3))) void*)(stage + off), 16, 0, 0);
+    }
+  };
+  uint32_t acc = 0;
+  if (ns > 0) {
+    issue(0, ring);
+    issue(1, ring + kPrStage);
+    issue(2, ring + 2 * kPrStage);
+  }
+  for (int64_t t = 0; t < ns; ++t) {
+    // the wave's requests after stage t are stages t+1 and t+2: 8 requests
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(t + 3, ring + ((t + 3) & 3) * kPrStage);
+    acc ^= *reinterpret_cast<const uint32_t*>(ring + (t & 3) * kPrStage + 4 * tid);
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+template <int SHAPE>
+__global__ __launch_bounds__(256) void k_probe_mfma(int64_t iters, float* __restrict__ sink) {
+  const int l = threadIdx.x & 63;
+  bf16x8 a, b;
+  {
+    u16x8 ua, ub;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ua[e] = (uint16_t)(0x3c00 + ((l + e) & 7));  // small finite values
+      ub[e] = (uint16_t)(0x3c00 + ((l * 3 + e) & 7));
+    }
+    a = __builtin_bit_cast(bf16x8, ua);
+    b = __builtin_bit_cast(bf16x8, ub);
+  }
+  float s = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][3];
+  } else {
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][15];
+  }
+  if (s == -1.0f) sink[blockIdx.x] = s;  // sums of positive products: never -1
+}
+
+}  // namespace
+}  // namespace kvlr
+
+using namespace kvlr;
+
+extern "C" int kvlr_probe_read(const void* src, size_t bytes, int method, int blocks, int depth,
+                               uint32_t* sink, void* stream) {
+  if (!src || !sink || blocks < 1 || blocks > (1 << 20) || bytes == 0 || bytes % 16384 != 0) return 1;
+  hipStream_t st = (hipStream_t)stream;
+  if (method == 0) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    switch (depth) {
+#define KVLR_PR(D) \
+  case D: hipLaunchKernelGGL(k_probe_read_reg<D>, dim3(blocks), dim3(256), 0, st, (const uint4*)src, n16, sink); break;
+      KVLR_PR(1) KVLR_PR(2) KVLR_PR(4) KVLR_PR(8) KVLR_PR(16)
+#undef KVLR_PR
+      default: return 1;
+    }
+  } else if (method == 1) {
+    if (bytes % kPrStage != 0) return 1;
+    hipLaunchKernelGGL(k_probe_read_lds, dim3(blocks), dim3(512), 0, st, (const uint8_t*)src,
+                       (int64_t)(bytes / kPrStage), sink);
+  } else {
+    return 1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int kvlr_probe_mfma(int shape, int64_t iters, int blocks, float* sink, void* stream) {
+  if (!sink || iters < 1 || blocks < 1 || blocks > (1 << 20)) return 1;
+  hipStream_t st = (hipStream_t)stream;
+  if (shape == 0)
+    hipLaunchKernelGGL(k_probe_mfma<0>, dim3(blocks), dim3(256), 0, st, iters, sink);
+  else if (shape == 1)
+    hipLaunchKernelGGL(k_probe_mfma<1>, dim3(blocks), dim3(256), 0, st, iters, sink);
+  else
+    return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

@@ -21,7 +21,8 @@ F32, BF16 = 0, 1
 OK, EINVAL, EWORKSPACE, EDEVICE, ELAUNCH = 0, 1, 2, 3, 4
 OP_BUILD_BASES, OP_PROJECT, OP_DECODE = 0, 1, 2
 BUFFERS = ("sink_k", "sink_v", "ring_k", "ring_v", "coef_k", "coef_v", "basis_k", "basis_v",
-           "qwin", "rowstat", "lens", "qsplit")
+           "qwin", "lens", "state")
+LOCAL_EXACT, LOCAL_RECONSTRUCTED = 0, 1
 STAGES = ("prologue", "score", "pool", "topk", "attend", "merge")
 
 
@@ -33,15 +34,13 @@ class KvlrError(RuntimeError):
 
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "n_q_heads", "n_kv_heads", "head_dim", "rank", "n_sink", "n_sample",
+        "n_q_heads", "n_kv_heads", "head_dim", "rank_k", "rank_v", "n_sink", "n_sample",
         "sample_recent_num", "sample_recent_den", "q_window", "top_k", "n_recent",
-        "pool_kernel", "dtype", "reserved")]
+        "pool_kernel", "local_window", "eig_max_sweeps", "dtype")]
 
 
 class CacheStruct(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS[:8]] + [
-        ("qwin", ctypes.c_void_p), ("rowstat", ctypes.c_void_p), ("lens", ctypes.c_void_p),
-        ("qsplit", ctypes.c_void_p), ("L_max", ctypes.c_int64)]
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS] + [("L_max", ctypes.c_int64)]
 
 
 _lib = None
@@ -62,9 +61,11 @@ def load():
         "kvlr_check_config": (i32, [cfgp]),
         "kvlr_cache_bytes": (i32, [cfgp, i64, i64, ctypes.POINTER(sz)]),
         "kvlr_workspace_bytes": (i32, [cfgp, i32, i64, i64, ctypes.POINTER(sz)]),
-        "kvlr_build_bases": (i32, [cfgp, i64, i64, P, P, cachep, P, P, P, sz, P]),
+        "kvlr_build_bases": (i32, [cfgp, i64, i64, P, P, cachep, P, P, P, P, sz, P]),
         "kvlr_project": (i32, [cfgp, i64, i64, P, P, cachep, P, sz, P]),
         "kvlr_decode_step": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P, sz, P]),
+        "kvlr_rank_for_ratio": (i32, [ctypes.c_double, i64, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "kvlr_last_error": (ctypes.c_char_p, []),
         "kvlr_abi_version": (i32, []),
         "kvlr_build_info": (ctypes.c_char_p, []),
@@ -85,17 +86,30 @@ def _check(status: int):
 
 
 def make_config(n_q_heads, n_kv_heads, head_dim, rank, n_sink, n_sample, q_window, top_k,
-                n_recent, pool_kernel, storage, sample_recent_num=7, sample_recent_den=10) -> Config:
-    return Config(n_q_heads, n_kv_heads, head_dim, rank, n_sink, n_sample, sample_recent_num,
-                  sample_recent_den, q_window, top_k, n_recent, pool_kernel,
-                  {"f32": F32, "bf16": BF16}[storage], 0)
+                n_recent, pool_kernel, storage, sample_recent_num=7, sample_recent_den=10,
+                rank_v=None, local_window=LOCAL_EXACT, eig_max_sweeps=0) -> Config:
+    """rank is the key rank r_K; rank_v defaults to it."""
+    return Config(n_q_heads, n_kv_heads, head_dim, rank, rank if rank_v is None else rank_v,
+                  n_sink, n_sample, sample_recent_num, sample_recent_den, q_window, top_k,
+                  n_recent, pool_kernel, local_window, eig_max_sweeps,
+                  {"f32": F32, "bf16": BF16}[storage])
 
 
 def config_of(w) -> Config:
     """Config of a configs.Workload."""
     return make_config(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rank, w.n_sink, w.n_sample,
                        w.q_window, w.top_k, w.n_recent, w.pool_kernel, w.storage,
-                       w.sample_recent_num, w.sample_recent_den)
+                       w.sample_recent_num, w.sample_recent_den, w.rank_v or w.rank,
+                       w.local_window, w.eig_max_sweeps)
+
+
+def rank_for_ratio(eta: float, L: int, d_kv: int, n_sink: int, n_recent: int,
+                   k_parts: int = 1, v_parts: int = 1, multiple: int = 8):
+    """(r_K, r_V) for a retention target eta (host-side helper of the library)."""
+    rk, rv = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().kvlr_rank_for_ratio(eta, L, d_kv, n_sink, n_recent, k_parts, v_parts, multiple,
+                                      ctypes.byref(rk), ctypes.byref(rv)))
+    return rk.value, rv.value
 
 
 def storage_of(cfg: Config) -> torch.dtype:
@@ -142,9 +156,8 @@ class KVCache:
     basis_k: torch.Tensor
     basis_v: torch.Tensor
     qwin: torch.Tensor
-    rowstat: torch.Tensor
     lens: torch.Tensor
-    qsplit: torch.Tensor
+    state: torch.Tensor      # [U][bytes] opaque decode state of the library
 
     @staticmethod
     def allocate(cfg: Config, n_units: int, L_max: int, device="cuda") -> "KVCache":
@@ -152,20 +165,19 @@ class KVCache:
         dt = storage_of(cfg)
         D = cfg.n_kv_heads * cfg.head_dim
         G = cfg.n_q_heads // cfg.n_kv_heads
-        U, r = n_units, cfg.rank
+        U, rk, rv = n_units, cfg.rank_k, cfg.rank_v
+        sizes = cache_bytes(cfg, U, L_max)
         z = lambda *shape, dtype=dt: torch.zeros(*shape, dtype=dtype, device=device)
         c = KVCache(cfg, U, L_max,
                     z(U, cfg.n_sink, D), z(U, cfg.n_sink, D),
                     z(U, cfg.n_recent, D), z(U, cfg.n_recent, D),
-                    z(U, L_max, r), z(U, L_max, r), z(U, D, r), z(U, D, r),
-                    z(U, cfg.q_window, G, r, dtype=torch.float32),
-                    z(U, cfg.q_window, G, 2, dtype=torch.float32),
+                    z(U, L_max, rk), z(U, L_max, rv), z(U, D, rk), z(U, D, rv),
+                    z(U, cfg.q_window, G, rk, dtype=torch.float32),
                     z(U, 2, dtype=torch.int32),
-                    z(U, cfg.q_window, G, 2, r, dtype=torch.bfloat16))
-        want = cache_bytes(cfg, U, L_max)
+                    z(U, sizes["state"] // U, dtype=torch.uint8))
         for name in BUFFERS:
             t = getattr(c, name)
-            assert t.numel() * t.element_size() == want[name], name
+            assert t.numel() * t.element_size() == sizes[name], name
         return c
 
     def units(self, start: int, count: int) -> "KVCache":
@@ -202,7 +214,12 @@ def _check_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, shape):
 
 
 def build_bases(cache: KVCache, K: torch.Tensor, V: torch.Tensor, eig_k=None, eig_v=None,
-                ws: Optional[torch.Tensor] = None, stream=None) -> None:
+                ws: Optional[torch.Tensor] = None, stream=None, sweeps=None,
+                check_converged: bool = False) -> None:
+    """Enqueue the basis build.  sweeps: optional [U][2] int32 device tensor
+    for the eigensolves' sweep counts (-1 = not converged).  check_converged
+    (a convenience for callers that can wait) fills such a tensor, waits for
+    the stream and raises if any eigensolve did not converge."""
     cfg = cache.cfg
     U, L = K.shape[0], K.shape[1]
     D = cfg.n_kv_heads * cfg.head_dim
@@ -211,12 +228,23 @@ def build_bases(cache: KVCache, K: torch.Tensor, V: torch.Tensor, eig_k=None, ei
     for name, e in (("eig_k", eig_k), ("eig_v", eig_v)):
         if e is not None:
             _check_tensor(e, name, torch.float32, (U, D))
+    if sweeps is not None:
+        _check_tensor(sweeps, "sweeps", torch.int32, (U, 2))
+    elif check_converged:
+        sweeps = torch.empty(U, 2, dtype=torch.int32, device=K.device)
     need = workspace_bytes(cfg, OP_BUILD_BASES, U, L)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=K.device)
     st = cache.struct()
     _check(load().kvlr_build_bases(ctypes.byref(cfg), U, L, _ptr(K), _ptr(V), ctypes.byref(st),
-                                   _ptr(eig_k), _ptr(eig_v), _ptr(ws), ws.numel(), _stream(stream)))
+                                   _ptr(eig_k), _ptr(eig_v), _ptr(sweeps), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    if check_converged:
+        torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        bad = (sweeps < 0).nonzero().tolist()
+        if bad:
+            raise KvlrError(EDEVICE, f"eigensolve did not converge within the sweep limit for "
+                                     f"(unit, K=0|V=1) {bad}")
 
 
 def project(cache: KVCache, K: torch.Tensor, V: torch.Tensor, ws: Optional[torch.Tensor] = None,

@@ -47,7 +47,8 @@ def snapshot(kc, u: int, w) -> s4r.Cache:
         w.n_recent, w.pool_kernel, w.storage,
         np64(kc.sink_k[u]), np64(kc.sink_v[u]), np64(kc.ring_k[u]), np64(kc.ring_v[u]),
         np64(kc.coef_k[u]), np64(kc.coef_v[u]), np64(kc.basis_k[u]), np64(kc.basis_v[u]),
-        np64(kc.qwin[u]).reshape(w.q_window, G, w.rank), int(lens[0]), int(lens[1]))
+        np64(kc.qwin[u]).reshape(w.q_window, G, w.rank), int(lens[0]), int(lens[1]),
+        w.rank_v or w.rank, w.local_window == 0)
 
 
 def bf16_ulps(a: np.ndarray, b: np.ndarray) -> int:
@@ -99,7 +100,35 @@ class StepStats:
     worst_gap: float = 0.0
     max_out_err: float = 0.0
     max_score_err: float = 0.0
+    max_score_ratio: float = 0.0      # worst |error| / bound of the latent scores
+    max_score_err_near_tau: float = 0.0  # worst error within 1e-4 of the k-th pooled score
     notes: List[str] = field(default_factory=list)
+
+
+# Latent-score error bound.  bf16 storage: the GPU forms each base-2 logit
+# from the query coefficients as a bf16 hi + lo pair (hi = bf16(x), lo =
+# bf16(x - hi): together within 2^-18 of x, relative) times the stored
+# coefficients, accumulated by 2 r / 32 MFMAs into fp32 (each adds at most
+# 2^-24 of the sum of |terms|): |dz| <= (2^-18 + r/16 * 2^-24) A <= 2^-17 A
+# for r <= 256, A = sum_i |c_q,i c_k,i| log2(e)/sqrt(r).  fp32 storage: a
+# plain fp32 dot product, |dz| <= (r + 1) 2^-24 A.  A softmax probability
+# p = 2^(z - m) / S then moves by at most p (dz_j + max_j' dz_j') ln 2 (the
+# second term from the normaliser), and the score by the sum of that over
+# the window rows; 1.5x margin, plus 1e-6 relative and 1e-9 absolute for the
+# fp32 exp2 and sums.
+def score_bound(o: s4r.Cache, J: np.ndarray) -> np.ndarray:
+    rows = o.window_rows()
+    CK = o.CK[J]
+    scale = 1.0 / math.sqrt(o.rank)
+    Z = rows @ CK.T * scale
+    P = np.exp(Z - Z.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    A = np.abs(rows) @ np.abs(CK).T * scale * math.log2(math.e)
+    rel = 2.0 ** -17 if o.storage == "bf16" else (o.rank + 1) * 2.0 ** -24
+    dz = rel * A
+    per_row = P * (dz + dz.max(axis=1, keepdims=True)) * math.log(2.0)
+    score = P.sum(axis=0)
+    return 1.5 * per_row.sum(axis=0) + 1e-6 * score + 1e-9
 
 
 def check_decode_step(kc, w, u: int, pre: s4r.Cache, post: s4r.Cache, q, k, v, out_gpu,
@@ -128,10 +157,22 @@ def check_decode_step(kc, w, u: int, pre: s4r.Cache, post: s4r.Cache, q, k, v, o
     o.qwin[slot] = post.qwin[slot]
     pos_ref, score_ref, pooled_ref = s4r.decode_select(o)
     J = o.candidates()
-    if scores_gpu is not None:
+    if scores_gpu is not None and len(J):
         sg = np64(scores_gpu)[J]
-        err = float(np.max(np.abs(sg - score_ref))) if len(J) else 0.0
-        stats.max_score_err = max(stats.max_score_err, err)
+        err = np.abs(sg - score_ref)
+        bound = score_bound(o, J)
+        ratio = float(np.max(err / bound))
+        stats.max_score_err = max(stats.max_score_err, float(np.max(err)))
+        stats.max_score_ratio = max(stats.max_score_ratio, ratio)
+        kk = min(w.top_k, len(J))
+        if kk > 0:
+            tau = np.sort(pooled_ref)[::-1][kk - 1]
+            near = np.abs(score_ref - tau) < 1e-4
+            if np.any(near):
+                stats.max_score_err_near_tau = max(stats.max_score_err_near_tau,
+                                                   float(np.max(err[near])))
+        assert ratio <= 1.0, (f"unit {u}: latent score error {float(np.max(err)):.3g} exceeds its "
+                              f"bound (worst ratio {ratio:.3g})")
     kk = min(w.top_k, len(J))
     sel = np64(topk_gpu)[:kk].astype(np.int64)
     assert np.all(np64(topk_gpu)[kk:] == -1)
@@ -153,22 +194,26 @@ def check_bases(w, K_u: np.ndarray, B_gpu: np.ndarray, eig_gpu: np.ndarray, what
     """Bases of one unit and kind vs the oracle's: eigenvalues within
     1e-4 * lambda_1, captured sample energy of the GPU subspace within the
     rounding bound of its storage, orthonormal columns."""
-    B_ref, lam, S, _ = s4r.build_basis(K_u, w.n_sink, w.n_sample, w.rank, w.storage,
+    B_ref, lam, S, _ = s4r.build_basis(K_u, w.n_sink, w.n_sample, B_gpu.shape[1], w.storage,
                                        w.sample_recent_num, w.sample_recent_den)
     assert np.max(np.abs(eig_gpu - lam)) <= 1e-4 * lam[0], f"{what}: eigenvalues"
     Q, _ = np.linalg.qr(B_gpu)
     e_gpu = float(np.sum((S @ Q) ** 2))
-    e_ref = float(np.sum(lam[:w.rank]))
+    rank = B_gpu.shape[1]
+    e_ref = float(np.sum(lam[:rank]))
     # bf16 rounding turns the subspace by O(2^-8); the energy it loses is
     # second order, below 4 * 2^-16 of the captured energy
     tol = 6e-5 if w.storage == "bf16" else 1e-6
     assert abs(e_gpu - e_ref) <= tol * e_ref, f"{what}: energy {e_gpu} vs {e_ref}"
-    ortho = np.max(np.abs(B_gpu.T @ B_gpu - np.eye(w.rank)))
+    ortho = np.max(np.abs(B_gpu.T @ B_gpu - np.eye(rank)))
     assert ortho <= (0.05 if w.storage == "bf16" else 1e-5), f"{what}: orthonormality {ortho}"
     return B_ref, lam
 
 
-def run_prefill(kvlr, w, prompt, L_max, eig=True):
+def run_prefill(kvlr, w, prompt, L_max, eig=True, build_ws=None):
+    """Bases (convergence checked) and projection of a prompt.  build_ws: an
+    optional caller workspace for the basis build (its first bytes then hold
+    the normalised sample)."""
     cfg = kvlr.config_of(w)
     U, L = prompt.K.shape[0], prompt.K.shape[1]
     kc = kvlr.KVCache.allocate(cfg, U, L_max)
@@ -176,10 +221,42 @@ def run_prefill(kvlr, w, prompt, L_max, eig=True):
     ek = torch.zeros(U, D, device="cuda") if eig else None
     ev = torch.zeros(U, D, device="cuda") if eig else None
     K, V = prompt.K.cuda(), prompt.V.cuda()
-    kvlr.build_bases(kc, K, V, ek, ev)
+    kvlr.build_bases(kc, K, V, ek, ev, ws=build_ws, check_converged=True)
     kvlr.project(kc, K, V)
     torch.cuda.synchronize()
     return kc, K, V, ek, ev
+
+
+def sample_of_workspace(ws: torch.Tensor, w, U: int) -> torch.Tensor:
+    """The normalised sample the basis build leaves at the start of its
+    workspace: [U][2 (K, V)][T'][D'] in the storage type."""
+    dt = torch.bfloat16 if w.storage == "bf16" else torch.float32
+    n = U * 2 * w.n_sample * w.D
+    return ws[: n * (2 if w.storage == "bf16" else 4)].view(dt).view(U, 2, w.n_sample, w.D)
+
+
+def check_sample_bits(w, X_u: np.ndarray, S_gpu: torch.Tensor, what: str):
+    """The GPU's stored sample against rnd(normalize_rows(X[positions])):
+    bit-exact in bf16 (both sides round the fp64 quotient once).  In fp32 an
+    entry may differ by one fp32 step only where the fp64 quotient lies
+    within 2^-40 (relative) of an fp32 rounding midpoint, since the two
+    sides sum the squared norm in different orders."""
+    pos = s4r.sample_positions(X_u.shape[0], w.n_sink, w.n_sample, w.sample_recent_num,
+                               w.sample_recent_den)
+    exact = s4r.normalize_rows(X_u[pos])
+    ref = s4r.rnd(exact, w.storage)
+    got = np64(S_gpu)
+    if w.storage == "bf16":
+        bad = got != ref
+        assert not np.any(bad), f"{what}: {int(bad.sum())} sample entries differ from the oracle's"
+    else:
+        bad = got != ref
+        if np.any(bad):
+            ulp = np.spacing(np.abs(ref[bad]).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(got[bad] - ref[bad]) <= ulp), what
+            f32 = exact[bad].astype(np.float32).astype(np.float64)
+            mid = (f32 + np.where(exact[bad] > f32, ulp, -ulp) / 2)
+            assert np.all(np.abs(exact[bad] - mid) <= 2.0 ** -40 * np.abs(exact[bad])), what
 
 
 def run_checked_steps(kvlr, w, kc, dec, steps: int, units=None, check_every: int = 1,

@@ -18,8 +18,8 @@ def lib():
     return kvlr.load()
 
 
-def header_functions():
-    src = open(os.path.join(ROOT, "include", "kvlr.h")).read()
+def header_functions(header="kvlr.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(kvlr_[a-z_]+)\s*\(", src)))
 
@@ -29,13 +29,27 @@ def test_exports_every_declared_symbol(lib):
     assert len(names) >= 10
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kvlr_abi_version() == 1
+    assert lib.kvlr_abi_version() == 2
+    probes = header_functions("kvlr_probe.h")
+    assert probes == ["kvlr_probe_mfma", "kvlr_probe_read"]
+    for n in probes:
+        assert hasattr(lib, n), n
     assert b"gfx950" in lib.kvlr_build_info()
 
 
+def header_struct_fields(name):
+    """Field names of a struct in include/kvlr.h, in order."""
+    src = open(os.path.join(ROOT, "include", "kvlr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\}" % name, src, flags=re.S).group(1)
+    return re.findall(r"\b(\w+)\s*;", body)
+
+
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(kvlr.Config) == 14 * 4
-    assert ctypes.sizeof(kvlr.CacheStruct) == 12 * 8 + 8
+    assert [n for n, _ in kvlr.Config._fields_] == header_struct_fields("kvlr_config")
+    assert [n for n, _ in kvlr.CacheStruct._fields_] == header_struct_fields("kvlr_cache")
+    assert ctypes.sizeof(kvlr.Config) == 16 * 4
+    assert ctypes.sizeof(kvlr.CacheStruct) == 11 * 8 + 8
 
 
 @pytest.mark.parametrize("w", configs.ALL, ids=lambda w: w.name)
@@ -69,9 +83,12 @@ def test_config_rejected(lib, kw, msg):
     assert e.value.status == kvlr.EINVAL and msg in str(e.value)
 
 
-def test_reserved_and_dtype(lib):
+def test_enum_fields_and_dtype(lib):
     c = _cfg()
-    c.reserved = 1
+    c.local_window = 5
+    assert lib.kvlr_check_config(ctypes.byref(c)) == kvlr.EINVAL
+    c = _cfg()
+    c.eig_max_sweeps = -1
     assert lib.kvlr_check_config(ctypes.byref(c)) == kvlr.EINVAL
     c = _cfg()
     c.dtype = 7
@@ -86,7 +103,8 @@ def test_cache_and_workspace_sizes(lib):
     assert b["coef_k"] == 16 * 34000 * 256 * 2
     assert b["basis_v"] == 16 * 1024 * 256 * 2
     assert b["qwin"] == 16 * 16 * 4 * 256 * 4
-    assert b["rowstat"] == 16 * 16 * 4 * 2 * 4
+    # opaque decode state: at least the scorer's bf16 window copy and the row statistics
+    assert b["state"] >= 16 * (16 * 4 * 2 * 256 * 2 + 16 * 4 * 2 * 4) and b["state"] % (16 * 256) == 0
     assert b["lens"] == 16 * 2 * 4
     assert b["sink_k"] == 16 * 4 * 1024 * 2 and b["ring_v"] == 16 * 64 * 1024 * 2
     ws = kvlr.workspace_bytes(cfg, kvlr.OP_DECODE, 16, 34000)
@@ -104,11 +122,11 @@ def test_calls_reject_bad_arguments_without_device(lib):
     cache = kvlr.CacheStruct()
     # null inputs
     st = lib.kvlr_build_bases(ctypes.byref(cfg), 1, 32768, None, None, ctypes.byref(cache),
-                              None, None, None, 0, None)
+                              None, None, None, None, 0, None)
     assert st == kvlr.EINVAL
     # sample does not fit (needs 2048 rows in 100 tokens)
     st = lib.kvlr_build_bases(ctypes.byref(cfg), 1, 100, ctypes.c_void_p(16), ctypes.c_void_p(16),
-                              ctypes.byref(cache), None, None, None, 0, None)
+                              ctypes.byref(cache), None, None, None, None, 0, None)
     assert st == kvlr.EINVAL and b"does not fit" in lib.kvlr_last_error()
     # prompt shorter than sinks + recent window
     st = lib.kvlr_project(ctypes.byref(cfg), 1, 10, ctypes.c_void_p(16), ctypes.c_void_p(16),
@@ -135,3 +153,35 @@ def test_calls_reject_bad_arguments_without_device(lib):
 
 def test_profile_read_bad_args(lib):
     assert lib.kvlr_profile_read(None, 5, None) == kvlr.EINVAL
+
+
+@pytest.mark.parametrize("eta,L,D,s,n_rec,parts", [
+    (0.2, 32768, 1024, 4, 64, (1, 1)), (0.3, 65536, 512, 4, 64, (1, 1)),
+    (0.25, 131072, 1024, 4, 64, (2, 3)), (0.05, 4096, 1024, 4, 64, (1, 1)),
+    (0.5, 1024, 64, 4, 16, (1, 1)), (0.01, 100, 64, 4, 16, (1, 1))])
+def test_rank_for_ratio_matches_oracle(lib, eta, L, D, s, n_rec, parts):
+    """The library's host helper against the oracle's accounting."""
+    from oracle import s4r
+    assert kvlr.rank_for_ratio(eta, L, D, s, n_rec, *parts) == s4r.rank_for_ratio(
+        eta, L, D, s, n_rec, parts)
+
+
+def test_rank_for_ratio_rejects(lib):
+    with pytest.raises(kvlr.KvlrError):
+        kvlr.rank_for_ratio(0.0, 1000, 64, 4, 16)
+    with pytest.raises(kvlr.KvlrError):
+        kvlr.rank_for_ratio(0.2, 1000, 64, 4, 16, 0, 1)
+
+
+def test_probe_argument_errors(lib):
+    """Probe calls reject bad arguments before any launch."""
+    lib.kvlr_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvlr_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    assert lib.kvlr_probe_read(None, 1 << 20, 0, 256, 4, 16, None) == 1
+    assert lib.kvlr_probe_read(16, 1000, 0, 256, 4, 16, None) == 1       # not a multiple of 16 KiB
+    assert lib.kvlr_probe_read(16, 1 << 20, 0, 256, 3, 16, None) == 1    # unsupported depth
+    assert lib.kvlr_probe_read(16, 1 << 20, 2, 256, 4, 16, None) == 1    # unknown method
+    assert lib.kvlr_probe_mfma(2, 10, 256, 16, None) == 1
+    assert lib.kvlr_probe_mfma(0, 0, 256, 16, None) == 1

@@ -52,7 +52,8 @@ def _run(w, L, batch, steps, L_extra=8, units=None, check_every=1, n_layers=1):
     stats = run_checked_steps(_kvlr(), w, kc, dec, steps, units=units, check_every=check_every)
     print(f"  checked={stats.n_checked} topk_near_tie_diffs={stats.topk_diffs} "
           f"worst_gap={stats.worst_gap:.3g} max_out_err={stats.max_out_err:.3g} "
-          f"max_score_err={stats.max_score_err:.3g}", flush=True)
+          f"max_score_err={stats.max_score_err:.3g} score_err/bound={stats.max_score_ratio:.3g} "
+          f"score_err_near_tau={stats.max_score_err_near_tau:.3g}", flush=True)
     return stats
 
 
