@@ -90,10 +90,6 @@ int check_cfg(const kvlr_config* c) {
     return fail(KVLR_EINVAL, "rank_v %d must be in [1, D' = %lld]", c->rank_v, (long long)D);
   if (c->rank_k % 8 != 0 || c->rank_v % 8 != 0)
     return fail(KVLR_EINVAL, "ranks (%d, %d) must be multiples of 8", c->rank_k, c->rank_v);
-  if (c->rank_v != c->rank_k)
-    return fail(KVLR_EINVAL, "rank_v != rank_k is not supported by this build");
-  if (c->local_window != KVLR_LOCAL_EXACT)
-    return fail(KVLR_EINVAL, "a reconstructed local window is not supported by this build");
   if (c->head_dim % 8 != 0) return fail(KVLR_EINVAL, "head_dim %d must be a multiple of 8", c->head_dim);
   if (c->n_sink < 0) return fail(KVLR_EINVAL, "n_sink must be >= 0");
   if (c->n_sample < 1) return fail(KVLR_EINVAL, "n_sample must be >= 1");
@@ -105,9 +101,13 @@ int check_cfg(const kvlr_config* c) {
   if (c->pool_kernel < 1 || c->pool_kernel % 2 == 0 || c->pool_kernel > 255)
     return fail(KVLR_EINVAL, "pool_kernel must be odd and in [1, 255]");
   if (c->dtype == KVLR_BF16) {
-    if (!rank_supported_bf16(c->rank_k) || !rank_supported_bf16(c->rank_v))
-      return fail(KVLR_EINVAL, "bf16 storage needs ranks in {32, 64, 128, 192, 256}");
-    if (c->q_window * G > 128) return fail(KVLR_EINVAL, "bf16 storage needs q_window * G <= 128");
+    if (!rank_supported_bf16(c->rank_k))
+      return fail(KVLR_EINVAL, "bf16 storage needs rank_k in {32, 64, 128, 192, 256}");
+    if (!attend_ranks_supported(c->rank_k, c->rank_v))
+      return fail(KVLR_EINVAL, "bf16 storage needs rank_v = rank_k, or (rank_k, rank_v) = "
+                               "(64, 96) or (128, 192)");
+    if (c->q_window * G > (c->rank_k <= 128 ? 256 : 128))
+      return fail(KVLR_EINVAL, "bf16 storage needs q_window * G <= 256 (rank_k <= 128) or <= 128");
   } else {
     if ((int64_t)c->q_window * G * c->rank_k > 8192)
       return fail(KVLR_EINVAL, "fp32 storage needs q_window * G * rank_k <= 8192");
@@ -185,7 +185,7 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   L.spill = take((size_t)U * d.G * L.t.Lc_cap * sizeof(float));
   L.tilestat = take((size_t)U * L.t.nsplit * d.G * 2 * sizeof(float));
   L.keys = take((size_t)U * L.t.Lc_cap * sizeof(uint32_t));
-  L.topk = take((size_t)U * (c->top_k > 0 ? c->top_k : 1) * sizeof(int32_t));
+  L.topk = take((size_t)U * (L.t.ktot > 0 ? L.t.ktot : 1) * sizeof(int32_t));
   L.qlat = take((size_t)U * d.Hq * d.r * sizeof(float));
   L.ylat = take((size_t)U * (L.t.nsl > 0 ? L.t.nsl : 1) * d.Hq * d.rv * sizeof(float));
   L.yex = take((size_t)U * L.t.nse * d.Hq * d.dh * sizeof(float));

@@ -229,7 +229,8 @@ struct DecodeWs {
   float* spill;       // [U][G][Lc_cap] base-2 logits of the current rows
   float* tilestat;    // [U][nsplit][G][2] per-split (max, sum) of the current rows
   uint32_t* keys;     // [U][Lc_cap] pooled scores as ordered bit patterns
-  int32_t* topk;      // [U][k] selected positions, ascending
+  int32_t* topk;      // [U][ktot] rebuilt rows: the picks ascending, then the
+                      //            recent window's positions if it is rebuilt
   float* qlat;        // [U][Hq][r] query heads projected onto their KV head's
                       //            slice of B^K, times log2(e)/sqrt(d_h)
   float* ylat;        // [U][nsl][Hq][r] per split: sum_j p_j c^V_j (latent)
@@ -247,6 +248,7 @@ struct DecodeWs {
   int nsl, nhg, hb, rsl;      // attention over selected rows: row splits, head
                               // groups, heads per group, rows per split
   int nse, rse;               // attention over exact rows: splits, rows per split
+  int ktot;                   // length of the rebuilt-row list (k, + n_rec if rebuilt)
   int attend_lds;             // dynamic LDS of the attention kernel (bytes)
 };
 
@@ -299,5 +301,7 @@ hipError_t launch_merge(const Dims& d, int U, const CachePtrs& c, const DecodeWs
 void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w);
 // dynamic LDS bytes of the attention kernel for this shape (0 if it cannot fit)
 size_t attend_lds_bytes(const Dims& d);
+// bf16 storage: (key rank, value rank) pairs the attention kernel is built for
+bool attend_ranks_supported(int r, int rv);
 
 }  // namespace kvlr

@@ -40,7 +40,7 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 static size_t latent_lds(const Dims& d, int hb, int rsl) {
   const size_t el = d.dtype == 0 ? 4 : 2;
   return (size_t)hb * (d.r + 4) * 4 + (size_t)hb * (rsl + 1) * 4 + 16 + (size_t)rsl * hb * 4 +
-         (size_t)2 * rsl * (d.r * el + 16);
+         (size_t)rsl * (d.r * el + 16) + (size_t)rsl * (d.rv * el + 16);
 }
 // exact rows, per wave: queries [G][dh] fp32, probabilities [32][8] fp32,
 // value rows [32][dh + 16 bytes] storage type
@@ -50,7 +50,7 @@ __host__ __device__ inline int exact_wave_floats(int G, int dh, int el) {
 static size_t exact_lds(const Dims& d) {
   return (size_t)4 * exact_wave_floats(d.G, d.dh, d.dtype == 0 ? 4 : 2) * 4;
 }
-static int attn_tile_bytes(int r);
+static int attn_tile_bytes(int r, int rv);
 static void attend_tile(const Dims& d, int* hb, int* rsl) {
   if (d.dtype != 0) {  // bf16: MFMA tiles of 64 rows x 32 heads
     *hb = 32;
@@ -69,7 +69,7 @@ static void attend_tile(const Dims& d, int* hb, int* rsl) {
 size_t attend_lds_bytes(const Dims& d) {
   int hb, rsl;
   attend_tile(d, &hb, &rsl);
-  size_t a = d.dtype != 0 ? (size_t)attn_tile_bytes(d.r) : latent_lds(d, hb, rsl);
+  size_t a = d.dtype != 0 ? (size_t)attn_tile_bytes(d.r, d.rv) : latent_lds(d, hb, rsl);
   size_t b = exact_lds(d);
   a = a > b ? a : b;
   return a <= 160 * 1024 ? a : 0;
@@ -98,14 +98,28 @@ void decode_tiling(const Dims& d, int64_t U, int64_t Lmax, DecodeWs* w) {
   while (((lc + (8 << w->gsh) - 1) >> (3 + w->gsh)) > kTopkGroupCap) ++w->gsh;
   w->tk_nbp = (int)((lc + kPoolChunk - 1) / kPoolChunk);
   w->nhg = (d.Hq + w->hb - 1) / w->hb;
-  w->nsl = (d.k + w->rsl - 1) / w->rsl;
-  const int nex = d.s + d.nrec;
+  // rebuilt rows: the top-k picks, then (reconstructed local window) the
+  // recent window's positions; exact rows: the sinks, then (exact local
+  // window) the recent ring
+  w->ktot = d.k + (d.local ? d.nrec : 0);
+  w->nsl = (w->ktot + w->rsl - 1) / w->rsl;
+  const int nex = d.s + (d.local ? 0 : d.nrec);
   w->nse = (nex + 31) / 32;
-  w->rse = (nex + w->nse - 1) / w->nse;
+  w->rse = w->nse > 0 ? (nex + w->nse - 1) / w->nse : 0;
   w->attend_lds = (int)attend_lds_bytes(d);
 }
 
 __device__ __forceinline__ int wrap_slot(int x, int W) { return ((x % W) + W) % W; }
+
+// rows rebuilt from coefficients in this step (token count before the
+// append = Lcur): the min(k, |J|) picks, plus the recent window when it is
+// reconstructed rather than exact
+__device__ __forceinline__ int n_rebuilt(const Dims& d, int Lcur) {
+  const int kk = max(0, min(d.k, Lcur + 1 - d.nrec - d.s));
+  return kk + (d.local ? min(d.nrec, Lcur + 1 - d.s) : 0);
+}
+// exact rows: the sinks, plus the recent ring when it is attended exactly
+__host__ __device__ __forceinline__ int n_exact_rows(const Dims& d) { return d.s + (d.local ? 0 : d.nrec); }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -228,25 +242,27 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* __restrict__ q,
                                                   const T* __restrict__ kn,
                                                   const T* __restrict__ vn, DecodeWs w,
-                                                  float qscale, float ascale, int ncb) {
+                                                  float qscale, float ascale, int ncb, int ncbv) {
   constexpr int VEC = Vec16<T>::N;
   constexpr int NVMAX = 9;  // 1 + G, G <= 8
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int D = d.D, r = d.r, G = d.G, W = d.W;
+  const int D = d.D, G = d.G, W = d.W;
+  const int nkv = ncb + ncbv;  // K column blocks, then V column blocks
+  const int r = b >= ncb && b < nkv ? d.rv : d.r;  // rank of this block's basis
   const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
   // basis pieces of this thread are requested together with the unit state:
   // GEMV blocks rows rg + 64 i of their column slice, projected-query blocks
   // rows rg + 8 i of head h's slice (first column pass)
   constexpr int PF = 16;
   u16x8 bpre[PF];
-  if (b < 2 * ncb) {
+  if (b < nkv) {
     const T* B = (const T*)(b >= ncb ? c.basis_v : c.basis_k) + (int64_t)u * D * r;
     const int col = min((b >= ncb ? b - ncb : b) * 4 * VEC + (tid & 3) * VEC, r - VEC);
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       bpre[i] = *reinterpret_cast<const u16x8*>(B + (int64_t)min((tid >> 2) + 64 * i, D - 1) * r + col);
-  } else if (b > 2 * ncb) {
-    const int h = b - 2 * ncb - 1;
+  } else if (b > nkv) {
+    const int h = b - nkv - 1;
     const T* B = (const T*)c.basis_k + ((int64_t)u * D + (int64_t)h * d.dh) * r;
     const int col = min((tid & 31) * VEC, r - VEC);
 #pragma unroll
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
   if (full) return;
   const int64_t p = Lcur;
   extern __shared__ float sm[];
-  if (b < 2 * ncb) {
+  if (b < nkv) {
     const int kind = b >= ncb ? 1 : 0;
     const int cb = kind ? b - ncb : b;
     const int nvec = kind == 0 ? 1 + G : 1;
@@ -376,10 +392,10 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
     }
     return;
   }
-  if (b > 2 * ncb) {
+  if (b > nkv) {
     // qlat[h G + g] = ascale * q[h G + g] . B^K[h dh : (h + 1) dh, :]
     // (fp32 storage: fp32 rows; bf16 storage: bf16 hi and lo rows)
-    const int h = b - 2 * ncb - 1, dh = d.dh;
+    const int h = b - nkv - 1, dh = d.dh;
     float* qs = sm;                 // [G][dh]
     float* red = qs + G * dh;       // [4 waves][G][32 * VEC]
     const T* qh = q + ((int64_t)u * d.Hq + h * G) * dh;
@@ -712,7 +728,7 @@ __device__ __forceinline__ void value_coef_block(const Dims& d, const CachePtrs&
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;  // no append
   const int64_t p = si[0];
-  const int D = d.D, r = d.r;
+  const int D = d.D, r = d.rv;
   const int cq = tid & 3, rg = tid >> 2;
   const int col = min(32 * vb + 8 * cq, r - 8);
   const uint16_t* B = (const uint16_t*)c.basis_v + (int64_t)u * D * r;
@@ -757,17 +773,19 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
                            hipStream_t st) {
   const int vec = d.dtype == 0 ? 4 : 8;
   const int ncb = (d.r + 4 * vec - 1) / (4 * vec);
+  const int ncbv = (d.rv + 4 * vec - 1) / (4 * vec);
   const int nvec = 1 + d.G;
   size_t lds = ((size_t)nvec * d.D + 16 * nvec * 4 * vec) * sizeof(float);
   if (lds < (size_t)d.r * sizeof(float)) lds = (size_t)d.r * sizeof(float);
+  if (lds < (size_t)d.rv * sizeof(float)) lds = (size_t)d.rv * sizeof(float);
   const size_t lq = ((size_t)d.G * d.dh + (size_t)4 * d.G * 32 * vec) * sizeof(float);
   if (lds < lq) lds = lq;
-  dim3 grid(2 * ncb + 1 + d.Hkv, U);
+  dim3 grid(ncb + ncbv + 1 + d.Hkv, U);
   const float qscale = kLog2e / sqrtf((float)d.r);
   const float ascale = kLog2e / sqrtf((float)d.dh);
   if (d.dtype == 0) {
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
-                       (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb);
+                       (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb, ncbv);
   } else if (prologue_fused(d)) {
     static size_t done = 0;
     const size_t lm = prologue_mfma_lds(d);
@@ -777,7 +795,7 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
                        (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
   } else {
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb, ncbv);
   }
   return hipGetLastError();
 }
@@ -1181,8 +1199,12 @@ static hipError_t launch_score_bf16(const Dims& d, int U, const CachePtrs& c, co
     hipLaunchKernelGGL((k_score_bf16<KS, 2, 1>), grid, dim3(512), 0, st, d, c, w);
   else if (nrb <= 4)
     hipLaunchKernelGGL((k_score_bf16<KS, 2, 2>), grid, dim3(512), 0, st, d, c, w);
-  else
+  else if (nrb <= 8)
     hipLaunchKernelGGL((k_score_bf16<KS, 4, 2>), grid, dim3(512), 0, st, d, c, w);
+  else if constexpr (KS <= 8)  // up to 256 window rows: four row blocks per group
+    hipLaunchKernelGGL((k_score_bf16<KS, 4, 4>), grid, dim3(512), 0, st, d, c, w);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1613,6 +1635,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   const int nc = Lcur + 1 - d.nrec - s;
   const int kk = min(k, nc);
   // (lens and the unused top-k slots are written at the end)
+  // reconstructed local window: its positions follow the picks in the
+  // rebuilt-row list
+  const int nloc = d.local ? min(d.nrec, Lcur + 1 - s) : 0;
+  int32_t* sel = w.topk + (int64_t)u * w.ktot;
+  for (int i = tid; i < nloc; i += kTopkThreads) sel[max(kk, 0) + i] = Lcur + 1 - nloc + i;
   if (kk <= 0) {
     if (tid == 0) {
       c.lens[2 * u] = Lcur + 1;
@@ -1912,7 +1939,6 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
   // the picks go through LDS (the histogram is free now) and leave in one
   // coalesced pass; units with more than kTopkBins picks write directly
   const bool stage = kk <= kTopkBins;
-  int32_t* sel = w.topk + (int64_t)u * k;
   int seen = 0;
   visit_ordered([&](uint32_t key, int j) {
     const unsigned int bn = (key - lo) >> shift;
@@ -1949,7 +1975,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(Dims d, CachePtrs c, Deco
 
 hipError_t launch_topk(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, const void* v_new,
                        int32_t* topk_user, float* out, hipStream_t st) {
-  const int nvb = prologue_fused(d) ? d.r / 32 : 0;  // c^V(new) blocks, see the prologue
+  const int nvb = prologue_fused(d) ? d.rv / 32 : 0;  // c^V(new) blocks, see the prologue
   hipLaunchKernelGGL(k_topk, dim3(1 + nvb, U), dim3(kTopkThreads), 0, st, d, c, w,
                      (const uint16_t*)v_new, topk_user, out);
   return hipGetLastError();
@@ -2004,7 +2030,7 @@ __device__ __forceinline__ void attend_exact(const Dims& d, const CachePtrs& c, 
   const int e = be / nhq, h = (be % nhq) * 4 + wv;
   const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
   const int row0 = e * w.rse;
-  const int nrow = min(w.rse, s + nrec - row0);
+  const int nrow = min(w.rse, n_exact_rows(d) - row0);
   if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
   constexpr int VEC = Vec16<T>::N;
   const int ldv = dh + VEC;                        // padded LDS row (storage elements)
@@ -2139,9 +2165,8 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;  // full unit: the top-k kernel wrote zeros
   const int Lcur = si[0];
-  const int r = d.r, Hq = d.Hq;
-  const int nc = Lcur + 1 - d.nrec - d.s;
-  const int kk = max(0, min(d.k, nc));
+  const int r = d.r, rv = d.rv, Hq = d.Hq;  // key rank (logits), value rank (values)
+  const int kk = n_rebuilt(d, Lcur);
   const int wv = tid >> 6, l = tid & 63;
 
   {
@@ -2153,35 +2178,33 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
     const int hb = w.hb, a0 = hg * hb, na = min(hb, Hq - a0);
     constexpr int E = 16 / sizeof(T);                 // elements per 16-byte piece
     const int ldq = r + 4, ldz = w.rsl + 1, ldc = r + E, r4 = r / 4, rE = r / E;
+    const int ldcv = rv + E, rv4 = rv / 4, rvE = rv / E;
     float* qt = smf;                                  // [hb][ldq]
     float* zs = qt + hb * ldq;                        // [hb][ldz]
     T* ck = reinterpret_cast<T*>(zs + ((hb * ldz + 3) & ~3) + w.rsl * hb);  // [rsl][ldc]
-    T* cv = ck + w.rsl * ldc;
-    const int32_t* sel = w.topk + (int64_t)u * d.k + row0;
+    T* cv = ck + w.rsl * ldc;                         // [rsl][ldcv]
+    const int32_t* sel = w.topk + (int64_t)u * w.ktot + row0;
     {
       // every thread issues its loads (8 pieces of K and of V per round)
       // before it stores any of them
       const T* cks = (const T*)c.coef_k + (int64_t)u * c.Lmax * r;
-      const T* cvs = (const T*)c.coef_v + (int64_t)u * c.Lmax * r;
-      const int npc = nrow * rE;
+      const T* cvs = (const T*)c.coef_v + (int64_t)u * c.Lmax * rv;
+      const int npk = nrow * rE, npv = nrow * rvE, npc = npk > npv ? npk : npv;
       for (int e0 = 0; e0 < npc; e0 += 256 * 8) {
         u16x8 xk[8], xv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int e = min(e0 + tid + 256 * i, npc - 1);
-          const int j = e / rE, iE = e % rE;
-          const int64_t pos = min(max((int64_t)sel[j], (int64_t)0), c.Lmax - 1);
-          xk[i] = *reinterpret_cast<const u16x8*>(cks + pos * r + iE * E);
-          xv[i] = *reinterpret_cast<const u16x8*>(cvs + pos * r + iE * E);
+          const int ek = min(e0 + tid + 256 * i, npk - 1), ev = min(e0 + tid + 256 * i, npv - 1);
+          const int64_t pk = min(max((int64_t)sel[ek / rE], (int64_t)0), c.Lmax - 1);
+          const int64_t pv = min(max((int64_t)sel[ev / rvE], (int64_t)0), c.Lmax - 1);
+          xk[i] = *reinterpret_cast<const u16x8*>(cks + pk * r + (ek % rE) * E);
+          xv[i] = *reinterpret_cast<const u16x8*>(cvs + pv * rv + (ev % rvE) * E);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int e = e0 + tid + 256 * i;
-          if (e < npc) {
-            const int j = e / rE, iE = e % rE;
-            *reinterpret_cast<u16x8*>(ck + j * ldc + iE * E) = xk[i];
-            *reinterpret_cast<u16x8*>(cv + j * ldc + iE * E) = xv[i];
-          }
+          if (e < npk) *reinterpret_cast<u16x8*>(ck + (e / rE) * ldc + (e % rE) * E) = xk[i];
+          if (e < npv) *reinterpret_cast<u16x8*>(cv + (e / rvE) * ldcv + (e % rvE) * E) = xv[i];
         }
       }
       const float* qsrc = w.qlat + ((int64_t)u * Hq + a0) * r;
@@ -2259,12 +2282,12 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
     __syncthreads();
     // ylat[a] = sum_j p[a][j] c^V_j: item (8 heads, 4 coefficients)
     const int nag = (na + 7) >> 3;
-    for (int e = tid; e < nag * r4; e += 256) {
-      const int ag = e / r4, i4 = e % r4;
+    for (int e = tid; e < nag * rv4; e += 256) {
+      const int ag = e / rv4, i4 = e % rv4;
       f32x4 acc[8] = {};
 #pragma unroll 4
       for (int j = 0; j < nrow; ++j) {
-        const f32x4 v4 = Quad<T>::f(*reinterpret_cast<const QV*>(cv + j * ldc + 4 * i4));
+        const f32x4 v4 = Quad<T>::f(*reinterpret_cast<const QV*>(cv + j * ldcv + 4 * i4));
         const f32x4 pa = *reinterpret_cast<const f32x4*>(pT + j * hb + 8 * ag);
         const f32x4 pb = *reinterpret_cast<const f32x4*>(pT + j * hb + 8 * ag + 4);
         acc[0] += pa[0] * v4;
@@ -2280,7 +2303,7 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
       for (int aa = 0; aa < 8; ++aa) {
         const int a = 8 * ag + aa;
         if (a < na)
-          *reinterpret_cast<f32x4*>(w.ylat + (((int64_t)u * w.nsl + split) * Hq + a0 + a) * r +
+          *reinterpret_cast<f32x4*>(w.ylat + (((int64_t)u * w.nsl + split) * Hq + a0 + a) * rv +
                                     4 * i4) = acc[aa];
       }
     }
@@ -2302,9 +2325,9 @@ __global__ __launch_bounds__(256) void k_attend(Dims d, CachePtrs c, DecodeWs w,
 // fragments) are issued together with it.
 // --------------------------------------------------------------------------
 constexpr int kAttnRows = 64;
-template <int R>
+template <int R, int RV>
 struct AttnTile {
-  static constexpr int KC = R / 8;                 // 16-byte chunks per coefficient row
+  static constexpr int KC = R / 8;                 // 16-byte chunks per key coefficient row
   static constexpr int CKB = R * 2 + 16;           // bytes per staged K row
   static constexpr int CVB = kAttnRows * 2 + 16;   // bytes per transposed V row
   static constexpr int ZLD = kAttnRows + 1, PLD = kAttnRows + 4;  // fp32 strides
@@ -2315,12 +2338,12 @@ struct AttnTile {
   static constexpr int pz = zs + ((32 * ZLD * 4 + 15) & ~15);
   static constexpr int kz = kAttnRows * CKB > pz + 32 * PLD * 4 ? kAttnRows * CKB : pz + 32 * PLD * 4;
   static constexpr int cv = (kz + 15) & ~15;
-  static constexpr int bytes = cv + R * CVB;
+  static constexpr int bytes = cv + RV * CVB;      // V rows transposed: RV coefficient rows
 };
-static int attn_tile_bytes(int r) {
+static int attn_tile_bytes(int r, int rv) {
   const int kb = kAttnRows * (r * 2 + 16);
   const int zp = ((32 * (kAttnRows + 1) * 4 + 15) & ~15) + 32 * (kAttnRows + 4) * 4;
-  return ((kb > zp ? kb : zp) + 15) / 16 * 16 + r * (kAttnRows * 2 + 16);
+  return ((kb > zp ? kb : zp) + 15) / 16 * 16 + rv * (kAttnRows * 2 + 16);
 }
 
 
@@ -2351,7 +2374,7 @@ __device__ __forceinline__ void attend_exact_mfma(const Dims& d, const CachePtrs
   const int e = be / nhq, h = (be % nhq) * 4 + wv;
   const int s = d.s, nrec = d.nrec, G = d.G, dh = d.dh, D = d.D;
   const int row0 = e * w.rse;
-  const int nrow = min(w.rse, s + nrec - row0);
+  const int nrow = min(w.rse, n_exact_rows(d) - row0);
   if (nrow <= 0 || h >= d.Hkv) return;  // no block-wide barrier below
   constexpr int VEC = 8;
   const int ldv = dh + VEC;                        // padded LDS row (storage elements)
@@ -2480,15 +2503,15 @@ __device__ __forceinline__ void attend_exact_mfma(const Dims& d, const CachePtrs
   }
 }
 
-template <int R>
+template <int R, int RV>
 __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, DecodeWs w,
                                                      const uint16_t* __restrict__ q, float ascale) {
-  typedef AttnTile<R> Lay;
+  typedef AttnTile<R, RV> Lay;
   constexpr int NR = kAttnRows;
-  constexpr int KC = Lay::KC, KS = KC / 4, NT = R / 16;
-  constexpr int NPC = NR * KC;                 // pieces per staged matrix
+  constexpr int KC = Lay::KC, KS = KC / 4, NT = RV / 16, KCV = RV / 8;
+  constexpr int NPC = NR * KC;                 // pieces per staged K matrix
   constexpr int NP = (NPC + 255) / 256;        // pieces per thread
-  static_assert(KC % 4 == 0 && NT % 2 == 0, "rank must be a multiple of 32");
+  static_assert(KC % 4 == 0 && NT % 2 == 0, "ranks must be multiples of 32");
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   extern __shared__ __attribute__((aligned(16))) float smf[];
   if (b >= w.nsl * w.nhg) {
@@ -2510,7 +2533,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int j = min(tid + 256 * i, NPC - 1) / KC;
-    selv[i] = w.topk[(int64_t)u * d.k + min(row0 + j, d.k - 1)];
+    selv[i] = w.topk[(int64_t)u * w.ktot + min(row0 + j, w.ktot - 1)];
   }
   // V pieces: lane l of wave wv takes rows 4 (l % 16) + {0..3} and chunks
   // 4 wv + l / 16 + 16 p, so the transposed stores below are 8-byte writes
@@ -2518,7 +2541,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
   const int vjg = l & 15, vcl = l >> 4;
   int selr[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) selr[q] = w.topk[(int64_t)u * d.k + min(row0 + 4 * vjg + q, d.k - 1)];
+  for (int q = 0; q < 4; ++q) selr[q] = w.topk[(int64_t)u * w.ktot + min(row0 + 4 * vjg + q, w.ktot - 1)];
   const int ht = wv >> 1, rt0 = 2 * (wv & 1);
   const int ah = min(a0 + 16 * ht + n16, Hq - 1);  // heads past H_q repeat the last one
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(w.qlat) + ((int64_t)u * Hq + ah) * 2 * R;
@@ -2529,15 +2552,14 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
     alo[ks] = ld_bf16x8(qp + R + (4 * ks + kg) * 8);
   }
   if (full) return;  // the top-k kernel wrote zeros
-  const int nc = Lcur + 1 - d.nrec - d.s;
-  const int kk = max(0, min(d.k, nc));
+  const int kk = n_rebuilt(d, Lcur);
   const int nrow = min(NR, kk - row0);
   if (nrow <= 0) return;
   // ---- gather the rows: K row-major, V transposed (rows past nrow: V zeroed)
   {
     const uint16_t* cks = (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * R;
-    const uint16_t* cvs = (const uint16_t*)c.coef_v + (int64_t)u * c.Lmax * R;
-    constexpr int NVP = (KC + 15) / 16;  // V chunk passes
+    const uint16_t* cvs = (const uint16_t*)c.coef_v + (int64_t)u * c.Lmax * RV;
+    constexpr int NVP = (KCV + 15) / 16;  // V chunk passes
     u16x8 xk[NP], xv[NVP][4];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -2548,11 +2570,11 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
     }
 #pragma unroll
     for (int p = 0; p < NVP; ++p) {
-      const int cc = min(4 * wv + vcl + 16 * p, KC - 1);
+      const int cc = min(4 * wv + vcl + 16 * p, KCV - 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t pos = min(max((int64_t)selr[q], (int64_t)0), c.Lmax - 1);
-        xv[p][q] = *reinterpret_cast<const u16x8*>(cvs + pos * R + cc * 8);
+        xv[p][q] = *reinterpret_cast<const u16x8*>(cvs + pos * RV + cc * 8);
       }
     }
 #pragma unroll
@@ -2566,7 +2588,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
 #pragma unroll
     for (int p = 0; p < NVP; ++p) {
       const int cc = 4 * wv + vcl + 16 * p;
-      if (cc < KC) {
+      if (cc < KCV) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (4 * vjg + q >= nrow) xv[p][q] = u16x8{};
@@ -2642,7 +2664,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
     split8(*reinterpret_cast<const f32x4*>(prow + 32), *reinterpret_cast<const f32x4*>(prow + 36), &ph1,
            &pl1);
     const int hd = a0 + 16 * ht2 + 4 * kg;
-    float* yb = w.ylat + ((int64_t)u * w.nsl + split) * Hq * R;
+    float* yb = w.ylat + ((int64_t)u * w.nsl + split) * Hq * RV;
 #pragma unroll
     for (int t = 0; t < NT / 2; ++t) {
       const int it = (wv >> 1) * (NT / 2) + t;
@@ -2656,7 +2678,7 @@ __global__ __launch_bounds__(256) void k_attend_mfma(Dims d, CachePtrs c, Decode
       y = mfma16x16x32(pl1, b1, y);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (hd + i < Hq) yb[(int64_t)(hd + i) * R + 16 * it + n16] = y[i];
+        if (hd + i < Hq) yb[(int64_t)(hd + i) * RV + 16 * it + n16] = y[i];
     }
   }
 }
@@ -2671,7 +2693,7 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
                                                float* __restrict__ out) {
   const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int l = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
+  const int r = d.rv, Hq = d.Hq, G = d.G, dh = d.dh;  // everything here has the value rank
   const int nst = w.nsl + w.nse;
   extern __shared__ __attribute__((aligned(16))) float smf[];
   float* ys = smf;                 // [G][r]
@@ -2719,11 +2741,10 @@ __global__ __launch_bounds__(256) void k_merge(Dims d, CachePtrs c, DecodeWs w,
     const int x = min(tid + 256 * m, G * dh - 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      ev[m][e] = yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh];
+      ev[m][e] = w.nse > 0 ? yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh] : 0.f;
   }
   if (full) return;  // the top-k kernel wrote zeros
-  const int nc = Lcur + 1 - d.nrec - d.s;
-  const int kk = max(0, min(d.k, nc));
+  const int kk = n_rebuilt(d, Lcur);
   const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
   for (int t = 0; t * 256 < G * nst; ++t) {
     const int x = tid + 256 * t;
@@ -2870,7 +2891,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
   const int h = blockIdx.x / nparts, part = blockIdx.x % nparts, u = blockIdx.y, tid = threadIdx.x;
   const int l = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = l & 15, kq = l >> 4;
-  const int r = d.r, Hq = d.Hq, G = d.G, dh = d.dh;
+  const int r = d.rv, Hq = d.Hq, G = d.G, dh = d.dh;  // everything here has the value rank
   const int nst = w.nsl + w.nse;
   const int nks = r / 32, nct = (dh + 15) / 16;
   const int ctper = (nct + nparts - 1) / nparts;  // channel tiles of this block: part * ctper + ...
@@ -2910,7 +2931,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
     const int x = min(tid + 256 * m, G * dh - 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      ev[m][e] = yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh];
+      ev[m][e] = w.nse > 0 ? yeb[((int64_t)min(e, w.nse - 1) * Hq + x / dh) * dh + x % dh] : 0.f;
   }
   // B^V_h fragments: channel tile ct = part * ctper + wv + 4 m, rows clamped into the head
   const uint16_t* bbase = (const uint16_t*)c.basis_v + ((int64_t)u * d.D + (int64_t)h * dh) * r;
@@ -2925,8 +2946,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
         bfr[m][ks] = ld_bf16x8(bbase + (int64_t)ch * r + 32 * ks + 8 * kq);
   }
   if (full) return;  // the top-k kernel wrote zeros
-  const int nc = Lcur + 1 - d.nrec - d.s;
-  const int kk = max(0, min(d.k, nc));
+  const int kk = n_rebuilt(d, Lcur);
   const int nl = (kk + w.rsl - 1) / w.rsl;  // selected-row splits that ran
   for (int t = 0; t * 256 < G * nst; ++t) {
     const int x = tid + 256 * t;
@@ -3042,7 +3062,7 @@ __global__ __launch_bounds__(256) void k_merge_mfma(Dims d, CachePtrs c, DecodeW
 }
 
 static size_t merge_lds(const Dims& d, const DecodeWs& w) {  // (k_merge_mfma pads ys rows by 4)
-  return ((size_t)d.G * (d.r + 4 + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
+  return ((size_t)d.G * (d.rv + 4 + d.dh) + (size_t)3 * d.G * (w.nsl + w.nse) + 8) * sizeof(float);
 }
 
 
@@ -3060,30 +3080,42 @@ static hipError_t launch_attend_t(const Dims& d, int U, const void* q, const Cac
   return hipGetLastError();
 }
 
-template <int R>
+template <int R, int RV>
 static hipError_t launch_attend_mfma(const Dims& d, int U, const void* q, const CachePtrs& c,
                                      const DecodeWs& w, hipStream_t st) {
   static size_t done = 0;
   if (w.attend_lds <= 0) return hipErrorInvalidValue;
-  hipError_t e = allow_lds(&k_attend_mfma<R>, (size_t)w.attend_lds, &done);
+  hipError_t e = allow_lds(&k_attend_mfma<R, RV>, (size_t)w.attend_lds, &done);
   if (e != hipSuccess) return e;
   const float ascale = kLog2e / sqrtf((float)d.dh);
-  hipLaunchKernelGGL(k_attend_mfma<R>, dim3(w.nsl * w.nhg + w.nse * ((d.Hkv + 3) / 4), U),
+  hipLaunchKernelGGL((k_attend_mfma<R, RV>), dim3(w.nsl * w.nhg + w.nse * ((d.Hkv + 3) / 4), U),
                      dim3(256), w.attend_lds, st, d, c, w, (const uint16_t*)q, ascale);
   return hipGetLastError();
+}
+
+// bf16 rank pairs with a kernel: equal ranks, and values at 1.5x the keys
+// (the key-to-value split the review mentions) where that rank exists
+bool attend_ranks_supported(int r, int rv) {
+  if (r == rv) return r == 32 || r == 64 || r == 128 || r == 192 || r == 256;
+  return (r == 128 && rv == 192) || (r == 64 && rv == 96);
 }
 
 hipError_t launch_attend(const Dims& d, int U, const void* q, const CachePtrs& c,
                          const DecodeWs& w, hipStream_t st) {
   if (d.dtype == 0) return launch_attend_t<float>(d, U, q, c, w, st);
-  switch (d.r) {
-    case 32: return launch_attend_mfma<32>(d, U, q, c, w, st);
-    case 64: return launch_attend_mfma<64>(d, U, q, c, w, st);
-    case 128: return launch_attend_mfma<128>(d, U, q, c, w, st);
-    case 192: return launch_attend_mfma<192>(d, U, q, c, w, st);
-    case 256: return launch_attend_mfma<256>(d, U, q, c, w, st);
-    default: return hipErrorInvalidValue;
+  if (d.r == d.rv) {
+    switch (d.r) {
+      case 32: return launch_attend_mfma<32, 32>(d, U, q, c, w, st);
+      case 64: return launch_attend_mfma<64, 64>(d, U, q, c, w, st);
+      case 128: return launch_attend_mfma<128, 128>(d, U, q, c, w, st);
+      case 192: return launch_attend_mfma<192, 192>(d, U, q, c, w, st);
+      case 256: return launch_attend_mfma<256, 256>(d, U, q, c, w, st);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (d.r == 128 && d.rv == 192) return launch_attend_mfma<128, 192>(d, U, q, c, w, st);
+  if (d.r == 64 && d.rv == 96) return launch_attend_mfma<64, 96>(d, U, q, c, w, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename T>

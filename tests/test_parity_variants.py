@@ -1,0 +1,130 @@
+"""GPU parity of the method variants against the oracle: separate key and
+value ranks (the 1:1.5 key-to-value split), the recent window rebuilt from
+coefficients instead of read from the exact ring, the all-recent (10:0)
+sample and the full-prompt sample (T' = L - s, the full-prompt SVD
+baseline).  Same stage-wise protocol as tests/test_parity_gpu.py."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_decode_s4r_amd import configs, synth
+from oracle import s4r
+
+from gpu_helpers import (check_bases, check_rows, check_sample_bits, np64, run_checked_steps,
+                         run_prefill, sample_of_workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvlr():
+    from long_context_decode_s4r_amd import kvlr
+    kvlr.load()
+    return kvlr
+
+
+def _run(w, L, batch, steps, units=None, sample_bits=False):
+    print(f"case {w.name} rank_k={w.rank} rank_v={w.rank_v or w.rank} local={w.local_window} "
+          f"split={w.sample_recent_num}:{w.sample_recent_den - w.sample_recent_num} "
+          f"T'={w.n_sample} L={L} batch={batch} steps={steps}", flush=True)
+    kvlr = _kvlr()
+    prompt = synth.make_prompt(w, L=L, batch=batch)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=batch)
+    cfg = kvlr.config_of(w)
+    ws = torch.empty(kvlr.workspace_bytes(cfg, kvlr.OP_BUILD_BASES, batch, L), dtype=torch.uint8,
+                     device="cuda")
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps + 8, build_ws=ws)
+    S = sample_of_workspace(ws, w, batch)
+    for u in (range(batch) if units is None else units):
+        Ku, Vu = np64(prompt.K[u]), np64(prompt.V[u])
+        if sample_bits:
+            check_sample_bits(w, Ku, S[u, 0], f"unit {u} K sample")
+            check_sample_bits(w, Vu, S[u, 1], f"unit {u} V sample")
+        check_bases(w, Ku, np64(kc.basis_k[u]), np64(ek[u]), f"unit {u} K basis")
+        check_bases(w, Vu, np64(kc.basis_v[u]), np64(ev[u]), f"unit {u} V basis")
+        assert kc.basis_v.shape[2] == (w.rank_v or w.rank)
+        for X, B, C, what in ((Ku, kc.basis_k[u], kc.coef_k[u], "C^K"),
+                              (Vu, kc.basis_v[u], kc.coef_v[u], "C^V")):
+            Bn = np64(B)
+            ref = s4r.project(X[w.n_sink:L], Bn, w.storage)
+            check_rows(np64(C)[w.n_sink:L], ref, w.storage, f"unit {u} {what}",
+                       np.abs(X[w.n_sink:L]) @ np.abs(Bn))
+    st = run_checked_steps(kvlr, w, kc, dec, steps, units=units)
+    print(f"  checked={st.n_checked} topk_near_tie_diffs={st.topk_diffs} worst_gap={st.worst_gap:.3g} "
+          f"max_out_err={st.max_out_err:.3g} score_err/bound={st.max_score_ratio:.3g}", flush=True)
+    return st
+
+
+_F32 = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=32, rank=16, q_window=4,
+                              top_k=24, n_recent=8, n_sample=64)
+_QWEN = configs.QWEN7B_64K.with_(n_layers=1, batch=2, n_sample=512, top_k=96, exponents=(0.9,))
+_LLAMA = configs.LLAMA8B_32K.with_(batch=2, n_sample=512, top_k=128)
+
+
+@pytest.mark.parametrize("w", [
+    _F32.with_(rank_v=24), _F32.with_(rank=24, rank_v=16),
+    _QWEN.with_(rank_v=192), _QWEN.with_(rank=64, rank_v=96)],
+    ids=["f32_16_24", "f32_24_16", "bf16_128_192", "bf16_64_96"])
+def test_separate_key_value_ranks(gpu_lib, w):
+    st = _run(w, 3001 if w.storage == "bf16" else 700, 2, 10)
+    assert st.n_checked == 20
+
+
+@pytest.mark.parametrize("w", [
+    _F32.with_(local_window=1), _F32.with_(local_window=1, n_sink=0),
+    _LLAMA.with_(local_window=1), _QWEN.with_(local_window=1, rank_v=192),
+    _LLAMA.with_(local_window=1, top_k=0)],
+    ids=["f32", "f32_no_sink", "bf16_llama", "bf16_qwen_128_192", "bf16_k0"])
+def test_reconstructed_local_window(gpu_lib, w):
+    st = _run(w, 2500 if w.storage == "bf16" else 600, 2, 9)
+    assert st.n_checked == 18
+
+
+def test_reconstructed_local_window_full_rank_equals_full_attention(gpu_lib):
+    """Recent window rebuilt, r = D' and every candidate picked: the output is
+    plain full attention over all tokens (fp32 storage)."""
+    kvlr = _kvlr()
+    w = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=32, rank=64, q_window=4,
+                               top_k=100_000, n_recent=8, n_sample=96, model="power",
+                               exponents=(0.5,), local_window=1)
+    L, steps = 200, 5
+    prompt = synth.make_prompt(w, L=L, batch=1)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=1)
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps)
+    out = torch.empty(1, 4, 32, device="cuda")
+    Kall, Vall = np64(prompt.K[0]), np64(prompt.V[0])
+    for t in range(steps):
+        kvlr.decode_step(kc, dec.q[t].cuda(), dec.k[t].cuda(), dec.v[t].cuda(), out)
+        Kall = np.vstack([Kall, np64(dec.k[t][0]).reshape(1, -1)])
+        Vall = np.vstack([Vall, np64(dec.v[t][0]).reshape(1, -1)])
+        q = np64(dec.q[t][0])
+        ref = np.stack([s4r.softmax_attention(q[a], Kall[:, (a // 2) * 32:(a // 2 + 1) * 32],
+                                              Vall[:, (a // 2) * 32:(a // 2 + 1) * 32])
+                        for a in range(4)])
+        err = np.max(np.abs(np64(out[0]) - ref)) / np.max(np.abs(ref))
+        assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("w", [_F32.with_(sample_recent_num=10), _LLAMA.with_(sample_recent_num=10)],
+                         ids=["f32", "bf16"])
+def test_all_recent_sample(gpu_lib, w):
+    """10:0: the sample is the last T' prompt tokens (sample rows bit-exact)."""
+    st = _run(w, 2500 if w.storage == "bf16" else 600, 2, 4, sample_bits=True)
+    assert st.n_checked == 8
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_full_prompt_sample(gpu_lib, storage):
+    """T' = L - s: every non-sink prompt token is in the sample, the bases are
+    the full prompt's truncated SVD (the full-prompt baseline)."""
+    L = 2000 if storage == "bf16" else 600
+    w = (_LLAMA if storage == "bf16" else _F32).with_(n_sample=L - 4)
+    st = _run(w, L, 2, 4, sample_bits=True)
+    assert st.n_checked == 8
+
+
+def test_default_window_qwen_shape(gpu_lib):
+    """W = 32 (the review's default window) with G = 7: 224 window rows in
+    the bf16 scorer (rank 128), window filled and wrapped."""
+    w = _QWEN.with_(q_window=32, top_k=96)
+    st = _run(w, 3001, 2, 35, units=[1])
+    assert st.n_checked == 35
