@@ -218,6 +218,25 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units,
                      kvlr_cache* cache, float* out, int32_t* topk_idx,
                      float* scores, void* ws, size_t ws_bytes, void* stream);
 
+/* kvlr_decode_step for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step and the same results, with the workspace taken from a fixed scratch
+ * array of KVLR_NOALLOC_SCRATCH_BYTES that the library keeps in device memory,
+ * one copy per GPU, for the life of the process.  The call allocates nothing.
+ * Arguments as for kvlr_decode_step, without ws / ws_bytes.
+ * Errors: KVLR_EWORKSPACE if kvlr_workspace_bytes(DECODE) for this call
+ * exceeds the scratch (the message gives both sizes); KVLR_EDEVICE if the
+ * scratch of the current device cannot be located.
+ * Every call on one GPU shares that GPU's scratch, and the scratch keeps the
+ * last call's contents (only a speed hint of the top-k, which never changes a
+ * result): calls that overlap on one GPU (concurrent streams or threads)
+ * race and must be ordered by the caller. */
+#define KVLR_NOALLOC_SCRATCH_BYTES (32 << 20)
+int kvlr_decode_step_noalloc(const kvlr_config* cfg, int64_t n_units,
+                             const void* q, const void* k_new, const void* v_new,
+                             kvlr_cache* cache, float* out, int32_t* topk_idx,
+                             float* scores, void* stream);
+
 /* Ranks for a target retention ratio eta ('Referee Report' major comment 3 and
  * 'Assumptions & free parameters': the rank is solved from the memory
  * equation, Eq. 21, for a target eta; the page does not print Eq. 21, so the

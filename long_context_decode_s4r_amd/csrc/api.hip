@@ -239,6 +239,98 @@ bool g_prof_on = false;
 std::vector<hipEvent_t> g_prof_events;  // kMaxProfiled * (kStages + 1)
 int g_prof_steps = 0;
 
+// argument checks shared by the decode entry points; *dl gets the workspace
+// layout of the call
+int check_decode_args(const kvlr_config* cfg, int64_t n_units, const void* q, const void* k_new,
+                      const void* v_new, const kvlr_cache* cache, const float* out, DecodeLayout* dl) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (n_units < 1 || n_units > 65535) return fail(KVLR_EINVAL, "n_units must be in [1, 65535]");
+  if (!q || !k_new || !v_new || !out) return fail(KVLR_EINVAL, "q, k_new, v_new or out is NULL");
+  if ((e = check_cache(cache, true, cfg->n_sink))) return e;
+  if (cache->L_max > INT32_MAX - 1) return fail(KVLR_EINVAL, "L_max too large");
+  *dl = decode_layout(cfg, n_units, cache->L_max);
+  return KVLR_OK;
+}
+
+// the decode step's launches on a checked call with a workspace that fits
+int decode_launch(const kvlr_config* cfg, int64_t n_units, const void* q, const void* k_new,
+                  const void* v_new, const kvlr_cache* cache, float* out, int32_t* topk_idx,
+                  float* scores, const DecodeLayout& dl, void* ws, hipStream_t st) {
+  const Dims d = dims_of(cfg);
+  char* w = (char*)ws;
+  DecodeWs dw = dl.t;
+  dw.stepinfo = (int32_t*)(w + dl.stepinfo);
+  dw.partial = (float*)(w + dl.partial);
+  dw.spill = (float*)(w + dl.spill);
+  dw.tilestat = (float*)(w + dl.tilestat);
+  dw.keys = (uint32_t*)(w + dl.keys);
+  dw.topk = (int32_t*)(w + dl.topk);
+  dw.qlat = (float*)(w + dl.qlat);
+  dw.ylat = (float*)(w + dl.ylat);
+  dw.yex = (float*)(w + dl.yex);
+  dw.astat = (float*)(w + dl.astat);
+  dw.gmax = (uint32_t*)(w + dl.gmax);
+  dw.cslot = (uint2*)(w + dl.cslot);
+  dw.tkpcnt = (int*)(w + dl.tkpcnt);
+  dw.tkhint = (uint32_t*)(w + dl.tkhint);
+  const CachePtrs cp = cache_ptrs(cache, d);
+  const int U = (int)n_units;
+
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on && g_prof_steps < kMaxProfiled) {
+      ev = &g_prof_events[(size_t)g_prof_steps * (kStages + 1)];
+      ++g_prof_steps;
+    }
+  }
+  hipError_t he;
+  if (ev) (void)hipEventRecord(ev[0], st);
+  if ((he = launch_prologue(d, U, q, k_new, v_new, cp, dw, st)) != hipSuccess) return hip_fail(he, "prologue");
+  if (ev) (void)hipEventRecord(ev[1], st);
+  if ((he = launch_score(d, U, cp, dw, st)) != hipSuccess) return hip_fail(he, "score");
+  if (ev) (void)hipEventRecord(ev[2], st);
+  if ((he = launch_pool(d, U, cp, dw, scores, st)) != hipSuccess) return hip_fail(he, "pool");
+  if (ev) (void)hipEventRecord(ev[3], st);
+  if ((he = launch_topk(d, U, cp, dw, v_new, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
+  if (ev) (void)hipEventRecord(ev[4], st);
+  if ((he = launch_attend(d, U, q, cp, dw, st)) != hipSuccess) return hip_fail(he, "attend");
+  if (ev) (void)hipEventRecord(ev[5], st);
+  if ((he = launch_merge(d, U, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
+  if (ev) (void)hipEventRecord(ev[6], st);
+  return ok();
+}
+
+// ---- the decode step without a caller workspace -----------------------------
+// Its scratch is this file-scope device array: every GPU the library runs on
+// holds one copy (at its own address) until the process ends.  In host code
+// the array's name is only a stand-in for the symbol; the device address of
+// each GPU's copy comes from hipGetSymbolAddress with that GPU current and
+// is the only form ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[KVLR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(KVLR_EDEVICE, "hipGetDevice: %s", hipGetErrorString(he));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVLR_EDEVICE, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (he != hipSuccess || !p)
+      return fail(KVLR_EDEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(he));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVLR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,59 +475,30 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
 int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, const void* k_new,
                      const void* v_new, kvlr_cache* cache, float* out, int32_t* topk_idx,
                      float* scores, void* ws, size_t ws_bytes, void* stream) {
-  int e = check_cfg(cfg);
+  DecodeLayout dl;
+  int e = check_decode_args(cfg, n_units, q, k_new, v_new, cache, out, &dl);
   if (e) return e;
-  if (n_units < 1 || n_units > 65535) return fail(KVLR_EINVAL, "n_units must be in [1, 65535]");
-  if (!q || !k_new || !v_new || !out) return fail(KVLR_EINVAL, "q, k_new, v_new or out is NULL");
-  if ((e = check_cache(cache, true, cfg->n_sink))) return e;
-  if (cache->L_max > INT32_MAX - 1) return fail(KVLR_EINVAL, "L_max too large");
-  const DecodeLayout dl = decode_layout(cfg, n_units, cache->L_max);
   if (!ws || ws_bytes < dl.total)
     return fail(KVLR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", dl.total, ws_bytes);
-  hipStream_t st = (hipStream_t)stream;
-  const Dims d = dims_of(cfg);
-  char* w = (char*)ws;
-  DecodeWs dw = dl.t;
-  dw.stepinfo = (int32_t*)(w + dl.stepinfo);
-  dw.partial = (float*)(w + dl.partial);
-  dw.spill = (float*)(w + dl.spill);
-  dw.tilestat = (float*)(w + dl.tilestat);
-  dw.keys = (uint32_t*)(w + dl.keys);
-  dw.topk = (int32_t*)(w + dl.topk);
-  dw.qlat = (float*)(w + dl.qlat);
-  dw.ylat = (float*)(w + dl.ylat);
-  dw.yex = (float*)(w + dl.yex);
-  dw.astat = (float*)(w + dl.astat);
-  dw.gmax = (uint32_t*)(w + dl.gmax);
-  dw.cslot = (uint2*)(w + dl.cslot);
-  dw.tkpcnt = (int*)(w + dl.tkpcnt);
-  dw.tkhint = (uint32_t*)(w + dl.tkhint);
-  const CachePtrs cp = cache_ptrs(cache, d);
-  const int U = (int)n_units;
+  return decode_launch(cfg, n_units, q, k_new, v_new, cache, out, topk_idx, scores, dl, ws,
+                       (hipStream_t)stream);
+}
 
-  hipEvent_t* ev = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_prof_on && g_prof_steps < kMaxProfiled) {
-      ev = &g_prof_events[(size_t)g_prof_steps * (kStages + 1)];
-      ++g_prof_steps;
-    }
-  }
-  hipError_t he;
-  if (ev) (void)hipEventRecord(ev[0], st);
-  if ((he = launch_prologue(d, U, q, k_new, v_new, cp, dw, st)) != hipSuccess) return hip_fail(he, "prologue");
-  if (ev) (void)hipEventRecord(ev[1], st);
-  if ((he = launch_score(d, U, cp, dw, st)) != hipSuccess) return hip_fail(he, "score");
-  if (ev) (void)hipEventRecord(ev[2], st);
-  if ((he = launch_pool(d, U, cp, dw, scores, st)) != hipSuccess) return hip_fail(he, "pool");
-  if (ev) (void)hipEventRecord(ev[3], st);
-  if ((he = launch_topk(d, U, cp, dw, v_new, topk_idx, out, st)) != hipSuccess) return hip_fail(he, "topk");
-  if (ev) (void)hipEventRecord(ev[4], st);
-  if ((he = launch_attend(d, U, q, cp, dw, st)) != hipSuccess) return hip_fail(he, "attend");
-  if (ev) (void)hipEventRecord(ev[5], st);
-  if ((he = launch_merge(d, U, cp, dw, out, st)) != hipSuccess) return hip_fail(he, "merge");
-  if (ev) (void)hipEventRecord(ev[6], st);
-  return ok();
+int kvlr_decode_step_noalloc(const kvlr_config* cfg, int64_t n_units, const void* q,
+                             const void* k_new, const void* v_new, kvlr_cache* cache, float* out,
+                             int32_t* topk_idx, float* scores, void* stream) {
+  DecodeLayout dl;
+  int e = check_decode_args(cfg, n_units, q, k_new, v_new, cache, out, &dl);
+  if (e) return e;
+  if (dl.total > (size_t)KVLR_NOALLOC_SCRATCH_BYTES)
+    return fail(KVLR_EWORKSPACE,
+                "this decode step needs %zu bytes of workspace, more than the %d-byte fixed scratch of "
+                "kvlr_decode_step_noalloc; use kvlr_decode_step with a workspace",
+                dl.total, KVLR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((e = scratch_of_current_device(&ws))) return e;
+  return decode_launch(cfg, n_units, q, k_new, v_new, cache, out, topk_idx, scores, dl, ws,
+                       (hipStream_t)stream);
 }
 
 int kvlr_rank_for_ratio(double eta, int64_t L, int32_t d_kv, int32_t n_sink, int32_t n_recent,

@@ -64,6 +64,7 @@ def load():
         "kvlr_build_bases": (i32, [cfgp, i64, i64, P, P, cachep, P, P, P, P, sz, P]),
         "kvlr_project": (i32, [cfgp, i64, i64, P, P, cachep, P, sz, P]),
         "kvlr_decode_step": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P, sz, P]),
+        "kvlr_decode_step_noalloc": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P]),
         "kvlr_rank_for_ratio": (i32, [ctypes.c_double, i64, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "kvlr_last_error": (ctypes.c_char_p, []),
@@ -289,6 +290,31 @@ def decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: tor
     _check(load().kvlr_decode_step(ctypes.byref(cfg), U, _ptr(q), _ptr(k_new), _ptr(v_new),
                                    ctypes.byref(st), _ptr(out), _ptr(topk), _ptr(scores), _ptr(ws),
                                    ws.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # KVLR_NOALLOC_SCRATCH_BYTES
+
+
+def decode_step_noalloc(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        out: torch.Tensor, topk: Optional[torch.Tensor] = None,
+                        scores: Optional[torch.Tensor] = None, stream=None) -> None:
+    """decode_step without a workspace: the library's fixed per-GPU scratch
+    is used instead (kvlr_decode_step_noalloc)."""
+    cfg = cache.cfg
+    U = cache.n_units
+    dt = storage_of(cfg)
+    _check_tensor(q, "q", dt, (U, cfg.n_q_heads, cfg.head_dim))
+    _check_tensor(k_new, "k_new", dt, (U, cfg.n_kv_heads, cfg.head_dim))
+    _check_tensor(v_new, "v_new", dt, (U, cfg.n_kv_heads, cfg.head_dim))
+    _check_tensor(out, "out", torch.float32, (U, cfg.n_q_heads, cfg.head_dim))
+    if topk is not None:
+        _check_tensor(topk, "topk", torch.int32, (U, cfg.top_k))
+    if scores is not None:
+        _check_tensor(scores, "scores", torch.float32, (U, cache.L_max))
+    st = cache.struct()
+    _check(load().kvlr_decode_step_noalloc(ctypes.byref(cfg), U, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                           ctypes.byref(st), _ptr(out), _ptr(topk), _ptr(scores),
+                                           _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:
