@@ -130,7 +130,7 @@ enum {
   KVLR_BUF_QWIN, KVLR_BUF_LENS, KVLR_BUF_STATE, KVLR_BUF_COUNT
 };
 
-enum { KVLR_OP_BUILD_BASES = 0, KVLR_OP_PROJECT = 1, KVLR_OP_DECODE = 2 };
+enum { KVLR_OP_BUILD_BASES = 0, KVLR_OP_PROJECT = 1, KVLR_OP_DECODE = 2, KVLR_OP_INIT_WINDOW = 3 };
 
 /* Validate cfg.  Returns KVLR_OK or KVLR_EINVAL (message in last_error). */
 int kvlr_check_config(const kvlr_config* cfg);
@@ -177,6 +177,25 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L,
                      float* eigvals_k, float* eigvals_v, int32_t* sweeps,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* kvlr_build_bases with one basis per window of neighbouring layers
+ * (DepthWeave-KV page, 'Core claim' and Eq. 1: low-rank channel bases shared
+ * across a window of adjacent layers, each layer keeping its own coefficients;
+ * the router and residuals of that page are not part of this).
+ *   n_layers, batch  units are layer-major, unit = layer * batch + sequence;
+ *   depth_window     layers [w d, w d + d) share a basis (the last window may
+ *                    be shorter); 1 gives per-layer bases.
+ * The shared basis of a window and sequence is the rank-r truncated SVD of the
+ * layers' normalised samples stacked row-wise: the leading eigenvectors of
+ * the sum of their Gram matrices.  It is written to basis_k / basis_v of
+ * every unit of the window (copies, so the decode step is unchanged);
+ * eigvals and sweeps (optional) hold the window's values for every unit.
+ * Workspace: kvlr_workspace_bytes(BUILD, n_layers * batch, L).  Other
+ * arguments and errors as for kvlr_build_bases. */
+int kvlr_build_bases_shared(const kvlr_config* cfg, int64_t n_layers, int64_t batch,
+                            int32_t depth_window, int64_t L, const void* K, const void* V,
+                            kvlr_cache* cache, float* eigvals_k, float* eigvals_v,
+                            int32_t* sweeps, void* ws, size_t ws_bytes, void* stream);
+
 /* Prefill part 2: coefficients and exact buffers (Eq. 3: every non-sink token
  * kept as c = x.B; the sinks stay exact, 'Core claim').
  *   K, V      device, [U][L][D'] storage (same prompt as kvlr_build_bases).
@@ -189,6 +208,22 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L,
 int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
                  const void* K, const void* V, kvlr_cache* cache,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Seed the query-coefficient window with the queries of the prompt's last
+ * n_tail tokens (a variant of the window's start: by default it starts empty
+ * and the first decode step scores with its own query only).  Call after
+ * kvlr_project, before the first decode step.
+ *   n_tail    1 <= n_tail <= W.
+ *   q_tail    device, [U][n_tail][H_q][d_h] storage, oldest token first.
+ *   cache     each tail query's coefficients c_q[g] = q_cat[g].B^K are pushed
+ *             into qwin as a decode step would push them (lens[1] advances by
+ *             n_tail), and the pushed rows' softmax statistics over the
+ *             current candidates [s, L - n_recent) go into state.
+ *   ws        device workspace of ws_bytes >= kvlr_workspace_bytes(INIT_WINDOW,
+ *             U, L_max) (sized for n_tail = W). */
+int kvlr_init_window(const kvlr_config* cfg, int64_t n_units, int32_t n_tail,
+                     const void* q_tail, kvlr_cache* cache, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* One decode step for every unit ('Referee Report' summary: a window of the
  * last W steps' query coefficients, latent scoring Eqs. 8-10, selection of the

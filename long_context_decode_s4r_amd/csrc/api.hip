@@ -331,54 +331,14 @@ int scratch_of_current_device(void** ptr) {
   return KVLR_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int kvlr_check_config(const kvlr_config* cfg) {
-  const int e = check_cfg(cfg);
-  return e == KVLR_OK ? ok() : e;
-}
-
-int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max, size_t* bytes) {
+// basis build of n_layers x batch units (layer-major); depth > 1 shares one
+// basis over each window of `depth` neighbouring layers
+int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, int depth, int64_t L,
+                     const void* K, const void* V, kvlr_cache* cache, float* eigvals_k,
+                     float* eigvals_v, int32_t* sweeps, void* ws, size_t ws_bytes, void* stream) {
   int e = check_cfg(cfg);
   if (e) return e;
-  if (!bytes) return fail(KVLR_EINVAL, "bytes is NULL");
-  if (n_units < 1 || L_max < 1) return fail(KVLR_EINVAL, "n_units and L_max must be >= 1");
-  const size_t eb = elem_bytes(cfg);
-  const int64_t D = (int64_t)cfg->n_kv_heads * cfg->head_dim;
-  const int64_t G = cfg->n_q_heads / cfg->n_kv_heads;
-  bytes[KVLR_BUF_SINK_K] = bytes[KVLR_BUF_SINK_V] = (size_t)n_units * cfg->n_sink * D * eb;
-  bytes[KVLR_BUF_RING_K] = bytes[KVLR_BUF_RING_V] = (size_t)n_units * cfg->n_recent * D * eb;
-  bytes[KVLR_BUF_COEF_K] = (size_t)n_units * L_max * cfg->rank_k * eb;
-  bytes[KVLR_BUF_COEF_V] = (size_t)n_units * L_max * cfg->rank_v * eb;
-  bytes[KVLR_BUF_BASIS_K] = (size_t)n_units * D * cfg->rank_k * eb;
-  bytes[KVLR_BUF_BASIS_V] = (size_t)n_units * D * cfg->rank_v * eb;
-  bytes[KVLR_BUF_QWIN] = (size_t)n_units * cfg->q_window * G * cfg->rank_k * sizeof(float);
-  bytes[KVLR_BUF_LENS] = (size_t)n_units * 2 * sizeof(int32_t);
-  bytes[KVLR_BUF_STATE] = (size_t)n_units * state_unit_bytes(dims_of(cfg));
-  return ok();
-}
-
-int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units, int64_t L, size_t* bytes) {
-  int e = check_cfg(cfg);
-  if (e) return e;
-  if (!bytes) return fail(KVLR_EINVAL, "bytes is NULL");
-  if (n_units < 1 || L < 1) return fail(KVLR_EINVAL, "n_units and L must be >= 1");
-  switch (op) {
-    case KVLR_OP_BUILD_BASES: *bytes = build_layout(cfg, n_units).total; break;
-    case KVLR_OP_PROJECT: *bytes = project_ws_bytes(dims_of(cfg), n_units); break;
-    case KVLR_OP_DECODE: *bytes = decode_layout(cfg, n_units, L).total; break;
-    default: return fail(KVLR_EINVAL, "unknown op %d", op);
-  }
-  return ok();
-}
-
-int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const void* K,
-                     const void* V, kvlr_cache* cache, float* eigvals_k, float* eigvals_v,
-                     int32_t* sweeps, void* ws, size_t ws_bytes, void* stream) {
-  int e = check_cfg(cfg);
-  if (e) return e;
+  const int64_t n_units = n_layers * batch;
   if (n_units < 1 || n_units > (1 << 20)) return fail(KVLR_EINVAL, "n_units out of range");
   if ((e = check_sample_fits(cfg, L))) return e;
   if (!K || !V) return fail(KVLR_EINVAL, "K or V is NULL");
@@ -402,6 +362,9 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
   if ((he = launch_gram(d, nmat, w + bl.S, A[0], Vm[0], st)) != hipSuccess) return hip_fail(he, "gram");
   if ((he = launch_jacobi_init(nmat, frozen, final_buf, done, st)) != hipSuccess)
     return hip_fail(he, "jacobi init");
+  if (depth > 1 &&
+      (he = launch_gram_window_sum(d.D, (int)n_layers, (int)batch, depth, A[0], frozen, st)) != hipSuccess)
+    return hip_fail(he, "gram window sum");
   // A fixed number of sweeps is enqueued; a matrix that has converged is
   // frozen on the device and every later kernel returns at once for it, so
   // nothing is read back and the call stays stream-ordered.
@@ -442,8 +405,92 @@ int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const v
       return hip_fail(he, "jacobi check");
   }
   if ((he = launch_extract(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, done, cur,
-                           cache->basis_k, cache->basis_v, eigvals_k, eigvals_v, sweeps, st)) != hipSuccess)
+                           cache->basis_k, cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch,
+                           depth, st)) != hipSuccess)
     return hip_fail(he, "extract");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvlr_check_config(const kvlr_config* cfg) {
+  const int e = check_cfg(cfg);
+  return e == KVLR_OK ? ok() : e;
+}
+
+int kvlr_cache_bytes(const kvlr_config* cfg, int64_t n_units, int64_t L_max, size_t* bytes) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (!bytes) return fail(KVLR_EINVAL, "bytes is NULL");
+  if (n_units < 1 || L_max < 1) return fail(KVLR_EINVAL, "n_units and L_max must be >= 1");
+  const size_t eb = elem_bytes(cfg);
+  const int64_t D = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  const int64_t G = cfg->n_q_heads / cfg->n_kv_heads;
+  bytes[KVLR_BUF_SINK_K] = bytes[KVLR_BUF_SINK_V] = (size_t)n_units * cfg->n_sink * D * eb;
+  bytes[KVLR_BUF_RING_K] = bytes[KVLR_BUF_RING_V] = (size_t)n_units * cfg->n_recent * D * eb;
+  bytes[KVLR_BUF_COEF_K] = (size_t)n_units * L_max * cfg->rank_k * eb;
+  bytes[KVLR_BUF_COEF_V] = (size_t)n_units * L_max * cfg->rank_v * eb;
+  bytes[KVLR_BUF_BASIS_K] = (size_t)n_units * D * cfg->rank_k * eb;
+  bytes[KVLR_BUF_BASIS_V] = (size_t)n_units * D * cfg->rank_v * eb;
+  bytes[KVLR_BUF_QWIN] = (size_t)n_units * cfg->q_window * G * cfg->rank_k * sizeof(float);
+  bytes[KVLR_BUF_LENS] = (size_t)n_units * 2 * sizeof(int32_t);
+  bytes[KVLR_BUF_STATE] = (size_t)n_units * state_unit_bytes(dims_of(cfg));
+  return ok();
+}
+
+int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units, int64_t L, size_t* bytes) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (!bytes) return fail(KVLR_EINVAL, "bytes is NULL");
+  if (n_units < 1 || L < 1) return fail(KVLR_EINVAL, "n_units and L must be >= 1");
+  switch (op) {
+    case KVLR_OP_BUILD_BASES: *bytes = build_layout(cfg, n_units).total; break;
+    case KVLR_OP_PROJECT: *bytes = project_ws_bytes(dims_of(cfg), n_units); break;
+    case KVLR_OP_DECODE: *bytes = decode_layout(cfg, n_units, L).total; break;
+    case KVLR_OP_INIT_WINDOW: *bytes = window_init_ws_bytes(dims_of(cfg), n_units, L, cfg->q_window); break;
+    default: return fail(KVLR_EINVAL, "unknown op %d", op);
+  }
+  return ok();
+}
+
+int kvlr_build_bases(const kvlr_config* cfg, int64_t n_units, int64_t L, const void* K,
+                     const void* V, kvlr_cache* cache, float* eigvals_k, float* eigvals_v,
+                     int32_t* sweeps, void* ws, size_t ws_bytes, void* stream) {
+  return build_bases_impl(cfg, 1, n_units, 1, L, K, V, cache, eigvals_k, eigvals_v, sweeps, ws,
+                          ws_bytes, stream);
+}
+
+int kvlr_build_bases_shared(const kvlr_config* cfg, int64_t n_layers, int64_t batch,
+                            int32_t depth_window, int64_t L, const void* K, const void* V,
+                            kvlr_cache* cache, float* eigvals_k, float* eigvals_v, int32_t* sweeps,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (n_layers < 1 || batch < 1) return fail(KVLR_EINVAL, "n_layers and batch must be >= 1");
+  if (depth_window < 1 || depth_window > n_layers)
+    return fail(KVLR_EINVAL, "depth_window %d must be in [1, n_layers = %lld]", depth_window,
+                (long long)n_layers);
+  return build_bases_impl(cfg, n_layers, batch, depth_window, L, K, V, cache, eigvals_k, eigvals_v,
+                          sweeps, ws, ws_bytes, stream);
+}
+
+int kvlr_init_window(const kvlr_config* cfg, int64_t n_units, int32_t n_tail, const void* q_tail,
+                     kvlr_cache* cache, void* ws, size_t ws_bytes, void* stream) {
+  int e = check_cfg(cfg);
+  if (e) return e;
+  if (n_units < 1 || n_units > 65535) return fail(KVLR_EINVAL, "n_units must be in [1, 65535]");
+  if (n_tail < 1 || n_tail > cfg->q_window)
+    return fail(KVLR_EINVAL, "n_tail %d must be in [1, q_window = %d]", n_tail, cfg->q_window);
+  if (!q_tail) return fail(KVLR_EINVAL, "q_tail is NULL");
+  if ((e = check_cache(cache, true, cfg->n_sink))) return e;
+  if (cache->L_max > INT32_MAX - 1) return fail(KVLR_EINVAL, "L_max too large");
+  const Dims d = dims_of(cfg);
+  const size_t need = window_init_ws_bytes(d, n_units, cache->L_max, n_tail);
+  if (!ws || ws_bytes < need)
+    return fail(KVLR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hipError_t he = launch_window_init(d, (int)n_units, cache->L_max, n_tail, q_tail, cache_ptrs(cache, d), ws,
+                                     (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "window init");
   return ok();
 }
 

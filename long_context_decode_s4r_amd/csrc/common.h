@@ -210,8 +210,12 @@ hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, i
 hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
                           const double* V0, const double* V1, const int* frozen,
                           const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
-                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
-                          hipStream_t st);
+                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps, int batch,
+                          int depth, hipStream_t st);
+// bases shared over windows of `depth` layers: Grams summed into each
+// window's first layer, the other layers' matrices frozen
+hipError_t launch_gram_window_sum(int n, int n_layers, int batch, int depth, double* A, int* frozen,
+                                  hipStream_t st);
 hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
                           const void* V, const void* BK, const void* BV, void* CK, void* CV,
                           void* ws, hipStream_t st);
@@ -277,6 +281,11 @@ inline int64_t state_rowstat_off(const Dims& d) {
 inline int64_t state_unit_bytes(const Dims& d) {
   return (state_rowstat_off(d) + (int64_t)d.W * d.G * 2 * 4 + 255) / 256 * 256;
 }
+
+// prefill: the window seeded with the prompt's last n_tail queries
+size_t window_init_ws_bytes(const Dims& d, int64_t U, int64_t L, int n_tail);
+hipError_t launch_window_init(const Dims& d, int U, int64_t L, int n_tail, const void* q_tail,
+                              const CachePtrs& c, void* ws, hipStream_t st);
 
 // prefill: exact sinks and ring, window and decode state cleared, lens = {L, 0}
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,

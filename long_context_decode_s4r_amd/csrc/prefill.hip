@@ -706,14 +706,19 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
                                                   int n, int rk, int rv, T* __restrict__ BK,
                                                   T* __restrict__ BV, float* __restrict__ eigK,
                                                   float* __restrict__ eigV,
-                                                  int32_t* __restrict__ sweeps) {
+                                                  int32_t* __restrict__ sweeps, int batch, int depth) {
   extern __shared__ unsigned char smem_raw[];
   const int m = blockIdx.x, u = m >> 1, kind = m & 1;
   const int r = kind ? rv : rk;
-  const int buf = frozen[m] ? final_buf[m] : cur;
-  const double* A = (buf ? A1 : A0) + (int64_t)m * n * n;
-  const double* Vm = (buf ? V1 : V0) + (int64_t)m * n * n;
-  if (sweeps && threadIdx.x == 0) sweeps[m] = frozen[m] ? done_sweeps[m] : -1;
+  // the matrix whose eigensolve serves this unit: its own, or, with bases
+  // shared over a window of `depth` layers (units layer-major, `batch`
+  // sequences per layer), the window's first layer's
+  const int layer = u / batch, seq = u % batch;
+  const int ms = 2 * ((layer - layer % depth) * batch + seq) + kind;
+  const int buf = frozen[ms] ? final_buf[ms] : cur;
+  const double* A = (buf ? A1 : A0) + (int64_t)ms * n * n;
+  const double* Vm = (buf ? V1 : V0) + (int64_t)ms * n * n;
+  if (sweeps && threadIdx.x == 0) sweeps[m] = done_sweeps[ms] > 0 ? done_sweeps[ms] : -1;
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
   double* key = reinterpret_cast<double*>(smem_raw);
@@ -763,19 +768,19 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
 hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
                           const double* V0, const double* V1, const int* frozen,
                           const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
-                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
-                          hipStream_t st) {
+                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps, int batch,
+                          int depth, hipStream_t st) {
   int np2 = 1;
   while (np2 < d.D) np2 <<= 1;
   const size_t lds = (size_t)np2 * (sizeof(double) + sizeof(int));
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_extract<float>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
                        final_buf, done_sweeps, cur, d.D, d.r, d.rv, (float*)basis_k,
-                       (float*)basis_v, eig_k, eig_v, sweeps);
+                       (float*)basis_v, eig_k, eig_v, sweeps, batch, depth);
   else
     hipLaunchKernelGGL(k_extract<uint16_t>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
                        frozen, final_buf, done_sweeps, cur, d.D, d.r, d.rv, (uint16_t*)basis_k,
-                       (uint16_t*)basis_v, eig_k, eig_v, sweeps);
+                       (uint16_t*)basis_v, eig_k, eig_v, sweeps, batch, depth);
   return hipGetLastError();
 }
 
@@ -1133,6 +1138,197 @@ hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K
   else
     hipLaunchKernelGGL(k_exact_reset<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
                        (const uint16_t*)V, c, L, d.D, d.s, d.nrec, qw);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 7. window seeded with the prompt's last queries (the variant that starts
+//    decoding with a full query-coefficient window): every tail query's
+//    coefficients are pushed like a decode step's, and the pushed rows'
+//    running softmax statistics are computed over the current candidates
+//    [s, L - n_rec), so the first decode step scores with them as with rows
+//    of earlier steps.
+// --------------------------------------------------------------------------
+// grid (n_tail, U), 256 threads: c_q[g] = q_cat[g] . B^K for tail query j
+template <typename T>
+__global__ __launch_bounds__(256) void k_window_push(Dims d, CachePtrs c, const T* __restrict__ qt,
+                                                     int n_tail, float qscale) {
+  const int j = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int D = d.D, r = d.r, G = d.G, W = d.W, dh = d.dh;
+  extern __shared__ float xs[];  // [G][D'] concatenated queries
+  const T* qj = qt + ((int64_t)u * n_tail + j) * d.Hq * dh;
+  for (int e = tid; e < d.Hq * dh; e += 256) {
+    const int a = e / dh, i = e % dh, h = a / G, g = a % G;
+    xs[g * D + h * dh + i] = Elem<T>::ld(qj, e);
+  }
+  __syncthreads();
+  const int slot = (c.lens[2 * u + 1] + j) % W;
+  const T* B = (const T*)c.basis_k + (int64_t)u * D * r;
+  uint16_t* qs = qsplit_of(c, u);
+  for (int col = tid; col < r; col += 256) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < D; ++k) {
+      const float b = Elem<T>::ld(B, (int64_t)k * r + col);
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g < G) acc[g] += xs[g * D + k] * b;
+    }
+    for (int g = 0; g < G; ++g) {
+      const int row = slot * G + g;
+      c.qwin[((int64_t)u * W * G + row) * r + col] = acc[g];
+      const float x = acc[g] * qscale;  // the scorer's operands: bf16 hi + lo
+      const uint16_t hb = f2bf(x);
+      qs[(row * 2 + 0) * r + col] = hb;
+      qs[(row * 2 + 1) * r + col] = f2bf(x - bf2f(hb));
+    }
+  }
+}
+
+constexpr int kWinRows = 8;      // window rows per block of the statistics pass
+constexpr int kWinTile = 256;    // candidates per block
+
+// grid (ntile, ceil(nrows / 8), U), 256 threads: partial (max, sum) of the
+// base-2 logits of 8 pushed rows over one tile of candidates; thread (row
+// tid / 32, lane tid % 32) takes candidates lane, lane + 32, ...
+template <typename T>
+__global__ __launch_bounds__(256) void k_window_stats(Dims d, CachePtrs c, int n_tail, float qscale,
+                                                      float2* __restrict__ part, int ntile) {
+  const int tile = blockIdx.x, rg = blockIdx.y, u = blockIdx.z, tid = threadIdx.x;
+  const int r = d.r, G = d.G, W = d.W;
+  const int nrows = n_tail * G;
+  const int row = rg * kWinRows + tid / 32, lane = tid % 32;
+  extern __shared__ float qrow[];  // [8][r] window rows, scaled to base 2
+  const int pushed0 = c.lens[2 * u + 1];
+  for (int e = tid; e < kWinRows * r; e += 256) {
+    const int rr = rg * kWinRows + e / r;
+    float v = 0.f;
+    if (rr < nrows) {
+      const int slot = (pushed0 + rr / G) % W;
+      v = c.qwin[(((int64_t)u * W + slot) * G + rr % G) * r + e % r] * qscale;
+    }
+    qrow[e] = v;
+  }
+  __syncthreads();
+  const int64_t L = c.lens[2 * u];
+  const int64_t j0 = d.s, j1 = L - d.nrec;  // candidates
+  const T* CK = (const T*)c.coef_k + (int64_t)u * c.Lmax * r;
+  float m = -INFINITY, S = 0.f;
+  if (row < nrows) {
+    for (int t = lane; t < kWinTile; t += 32) {
+      const int64_t j = j0 + (int64_t)tile * kWinTile + t;
+      if (j >= j1) break;
+      const T* cj = CK + j * r;
+      float z = 0.f;
+      for (int i = 0; i < r; ++i) z += qrow[(tid / 32) * r + i] * Elem<T>::ld(cj, i);
+      const float mn = fmaxf(m, z);
+      S = (m == -INFINITY ? 0.f : S * exp2f(m - mn)) + exp2f(z - mn);
+      m = mn;
+    }
+  }
+  // combine the 32 lanes of the row (fixed order)
+  for (int o = 1; o < 32; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), S2 = __shfl_xor(S, o);
+    const float mn = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.f : S * exp2f(m - mn);
+    const float b = m2 == -INFINITY ? 0.f : S2 * exp2f(m2 - mn);
+    S = a + b;
+    m = mn;
+  }
+  if (lane == 0 && row < nrows) part[((int64_t)u * nrows + row) * ntile + tile] = make_float2(m, S);
+}
+
+// grid (1, U), 256 threads: merge the tiles of every pushed row into its
+// running statistics, then count the pushes
+__global__ __launch_bounds__(256) void k_window_merge(Dims d, CachePtrs c, int n_tail,
+                                                      const float2* __restrict__ part, int ntile) {
+  const int u = blockIdx.y, tid = threadIdx.x;
+  const int G = d.G, W = d.W, nrows = n_tail * G;
+  const int pushed0 = c.lens[2 * u + 1];
+  float* rs = rowstat_of(c, u);
+  for (int row = tid; row < nrows; row += 256) {
+    float m = -INFINITY, S = 0.f;
+    for (int t = 0; t < ntile; ++t) {
+      const float2 p = part[((int64_t)u * nrows + row) * ntile + t];
+      if (p.y == 0.f) continue;
+      const float mn = fmaxf(m, p.x);
+      S = (m == -INFINITY ? 0.f : S * exp2f(m - mn)) + p.y * exp2f(p.x - mn);
+      m = mn;
+    }
+    const int slot = (pushed0 + row / G) % W;
+    rs[(slot * G + row % G) * 2 + 0] = m;
+    rs[(slot * G + row % G) * 2 + 1] = S;
+  }
+  __syncthreads();
+  if (tid == 0) c.lens[2 * u + 1] = pushed0 + n_tail;
+}
+
+int64_t window_init_tiles(const Dims& d, int64_t L) {
+  const int64_t nc = L - d.s - d.nrec;
+  return nc > 0 ? (nc + kWinTile - 1) / kWinTile : 1;
+}
+
+size_t window_init_ws_bytes(const Dims& d, int64_t U, int64_t L, int n_tail) {
+  return (size_t)U * n_tail * d.G * window_init_tiles(d, L) * sizeof(float2);
+}
+
+hipError_t launch_window_init(const Dims& d, int U, int64_t L, int n_tail, const void* q_tail,
+                              const CachePtrs& c, void* ws, hipStream_t st) {
+  const float qscale = kLog2e / sqrtf((float)d.r);
+  const size_t lds = (size_t)d.G * d.D * sizeof(float);
+  if (d.dtype == 0)
+    hipLaunchKernelGGL(k_window_push<float>, dim3(n_tail, U), dim3(256), lds, st, d, c,
+                       (const float*)q_tail, n_tail, qscale);
+  else
+    hipLaunchKernelGGL(k_window_push<uint16_t>, dim3(n_tail, U), dim3(256), lds, st, d, c,
+                       (const uint16_t*)q_tail, n_tail, qscale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = n_tail * d.G;
+  const int ntile = (int)window_init_tiles(d, L);
+  float2* part = (float2*)ws;
+  const dim3 grid(ntile, (nrows + kWinRows - 1) / kWinRows, U);
+  const size_t lq = (size_t)kWinRows * d.r * sizeof(float);
+  if (d.dtype == 0)
+    hipLaunchKernelGGL(k_window_stats<float>, grid, dim3(256), lq, st, d, c, n_tail, qscale, part, ntile);
+  else
+    hipLaunchKernelGGL(k_window_stats<uint16_t>, grid, dim3(256), lq, st, d, c, n_tail, qscale, part, ntile);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_window_merge, dim3(1, U), dim3(256), 0, st, d, c, n_tail, part, ntile);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// 8. bases shared over a window of neighbouring layers: the Gram matrices of
+//    the layers of a window (same sequence) are summed into the window's
+//    first layer, whose eigensolve then serves the whole window; the other
+//    layers' matrices are frozen so the sweeps skip them, and the basis
+//    extraction copies the first layer's result to them.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gram_window_sum(double* __restrict__ A, int* __restrict__ frozen,
+                                                         int n, int n_layers, int batch, int depth) {
+  // grid (ceil(n * n / 256), 2 * batch * ceil(n_layers / depth)): one
+  // (window, sequence, K | V) per blockIdx.y
+  const int nwin = (n_layers + depth - 1) / depth;
+  const int y = blockIdx.y, kind = y & 1, wb = y >> 1, win = wb / batch, b = wb % batch;
+  const int l0 = win * depth, l1 = min(l0 + depth, n_layers);
+  if (win >= nwin) return;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int m0 = 2 * (l0 * batch + b) + kind;
+  if (e < (int64_t)n * n) {
+    double acc = A[(int64_t)m0 * n * n + e];
+    for (int l = l0 + 1; l < l1; ++l) acc += A[(int64_t)(2 * (l * batch + b) + kind) * n * n + e];
+    A[(int64_t)m0 * n * n + e] = acc;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (int l = l0 + 1; l < l1; ++l) frozen[2 * (l * batch + b) + kind] = 1;
+}
+
+hipError_t launch_gram_window_sum(int n, int n_layers, int batch, int depth, double* A, int* frozen,
+                                  hipStream_t st) {
+  const int nwin = (n_layers + depth - 1) / depth;
+  const int64_t n2 = (int64_t)n * n;
+  hipLaunchKernelGGL(k_gram_window_sum, dim3((unsigned)((n2 + 255) / 256), 2 * batch * nwin), dim3(256), 0,
+                     st, A, frozen, n, n_layers, batch, depth);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libkvlr.so")
 
 F32, BF16 = 0, 1
 OK, EINVAL, EWORKSPACE, EDEVICE, ELAUNCH = 0, 1, 2, 3, 4
-OP_BUILD_BASES, OP_PROJECT, OP_DECODE = 0, 1, 2
+OP_BUILD_BASES, OP_PROJECT, OP_DECODE, OP_INIT_WINDOW = 0, 1, 2, 3
 BUFFERS = ("sink_k", "sink_v", "ring_k", "ring_v", "coef_k", "coef_v", "basis_k", "basis_v",
            "qwin", "lens", "state")
 LOCAL_EXACT, LOCAL_RECONSTRUCTED = 0, 1
@@ -62,6 +62,8 @@ def load():
         "kvlr_cache_bytes": (i32, [cfgp, i64, i64, ctypes.POINTER(sz)]),
         "kvlr_workspace_bytes": (i32, [cfgp, i32, i64, i64, ctypes.POINTER(sz)]),
         "kvlr_build_bases": (i32, [cfgp, i64, i64, P, P, cachep, P, P, P, P, sz, P]),
+        "kvlr_build_bases_shared": (i32, [cfgp, i64, i64, i32, i64, P, P, cachep, P, P, P, P, sz, P]),
+        "kvlr_init_window": (i32, [cfgp, i64, i32, P, cachep, P, sz, P]),
         "kvlr_project": (i32, [cfgp, i64, i64, P, P, cachep, P, sz, P]),
         "kvlr_decode_step": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P, sz, P]),
         "kvlr_decode_step_noalloc": (i32, [cfgp, i64, P, P, P, cachep, P, P, P, P]),
@@ -246,6 +248,49 @@ def build_bases(cache: KVCache, K: torch.Tensor, V: torch.Tensor, eig_k=None, ei
         if bad:
             raise KvlrError(EDEVICE, f"eigensolve did not converge within the sweep limit for "
                                      f"(unit, K=0|V=1) {bad}")
+
+
+def build_bases_shared(cache: KVCache, n_layers: int, depth_window: int, K: torch.Tensor,
+                       V: torch.Tensor, eig_k=None, eig_v=None, ws: Optional[torch.Tensor] = None,
+                       stream=None, sweeps=None) -> None:
+    """Bases shared over windows of depth_window neighbouring layers (units
+    layer-major: unit = layer * batch + sequence)."""
+    cfg = cache.cfg
+    U, L = K.shape[0], K.shape[1]
+    if U % n_layers:
+        raise ValueError("n_units must be n_layers * batch")
+    D = cfg.n_kv_heads * cfg.head_dim
+    _check_tensor(K, "K", storage_of(cfg), (cache.n_units, L, D))
+    _check_tensor(V, "V", storage_of(cfg), (cache.n_units, L, D))
+    for name, e in (("eig_k", eig_k), ("eig_v", eig_v)):
+        if e is not None:
+            _check_tensor(e, name, torch.float32, (U, D))
+    if sweeps is not None:
+        _check_tensor(sweeps, "sweeps", torch.int32, (U, 2))
+    if ws is None:
+        ws = torch.empty(workspace_bytes(cfg, OP_BUILD_BASES, U, L), dtype=torch.uint8, device=K.device)
+    st = cache.struct()
+    _check(load().kvlr_build_bases_shared(ctypes.byref(cfg), n_layers, U // n_layers, depth_window, L,
+                                          _ptr(K), _ptr(V), ctypes.byref(st), _ptr(eig_k), _ptr(eig_v),
+                                          _ptr(sweeps), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def init_window(cache: KVCache, q_tail: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Seed the query window with the prompt's last queries, q_tail
+    [U][n_tail][H_q][d_h] (oldest first); call after project()."""
+    cfg = cache.cfg
+    U = cache.n_units
+    if q_tail.dim() != 4:
+        raise ValueError("q_tail must be [U][n_tail][H_q][d_h]")
+    n_tail = q_tail.shape[1]
+    _check_tensor(q_tail, "q_tail", storage_of(cfg), (U, n_tail, cfg.n_q_heads, cfg.head_dim))
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes(cfg, OP_INIT_WINDOW, U, cache.L_max), 1),
+                         dtype=torch.uint8, device=q_tail.device)
+    st = cache.struct()
+    _check(load().kvlr_init_window(ctypes.byref(cfg), U, n_tail, _ptr(q_tail), ctypes.byref(st),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def project(cache: KVCache, K: torch.Tensor, V: torch.Tensor, ws: Optional[torch.Tensor] = None,

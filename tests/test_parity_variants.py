@@ -128,3 +128,83 @@ def test_default_window_qwen_shape(gpu_lib):
     w = _QWEN.with_(q_window=32, top_k=96)
     st = _run(w, 3001, 2, 35, units=[1])
     assert st.n_checked == 35
+
+
+@pytest.mark.parametrize("storage,n_tail", [("f32", 3), ("bf16", 16), ("bf16", 5)])
+def test_prompt_tail_window(gpu_lib, storage, n_tail):
+    """The window seeded with the prompt's last n_tail queries: the pushed
+    query coefficients against the oracle's, then decode steps checked
+    stage by stage (their scores use the seeded rows' statistics)."""
+    kvlr = _kvlr()
+    w = _F32.with_(q_window=4) if storage == "f32" else _LLAMA
+    L, batch, steps = (600 if storage == "f32" else 2500), 2, 6
+    print(f"case prompt-tail window {storage} n_tail={n_tail}", flush=True)
+    prompt = synth.make_prompt(w, L=L, batch=batch)
+    dec = synth.make_decode_inputs(w, prompt, steps + n_tail, batch=batch)
+    tail = dec.q[steps:steps + n_tail].transpose(0, 1).contiguous()   # [U][n_tail][H_q][d_h]
+    kc, K, V, ek, ev = run_prefill(kvlr, w, prompt, L + steps + 8)
+    kvlr.init_window(kc, tail.cuda())
+    torch.cuda.synchronize()
+    assert kc.lens[:, 1].tolist() == [n_tail] * batch
+    for u in range(batch):
+        o = s4r.Cache(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rank, w.n_sink, w.q_window, w.top_k,
+                      w.n_recent, w.pool_kernel, w.storage, None, None, None, None, None, None,
+                      np64(kc.basis_k[u]), np64(kc.basis_v[u]),
+                      np.zeros((w.q_window, w.G, w.rank)), L, 0)
+        for j in range(n_tail):
+            s4r.push_query(o, np64(tail[u, j]))
+        qcat = [s4r.query_concat(np64(tail[u, j]), w.n_kv_heads) for j in range(n_tail)]
+        for j in range(n_tail):
+            slot = j % w.q_window
+            scale = np.abs(qcat[j]) @ np.abs(o.BK)
+            assert np.all(np.abs(np64(kc.qwin[u, slot]) - o.qwin[slot]) <= 1e-5 * scale + 1e-30)
+    st = run_checked_steps(kvlr, w, kc, dec, steps)
+    assert st.n_checked == batch * steps
+
+
+@pytest.mark.parametrize("storage,n_layers,depth", [("f32", 3, 2), ("bf16", 4, 3), ("bf16", 2, 2)])
+def test_depth_shared_bases(gpu_lib, storage, n_layers, depth):
+    """Bases shared over windows of neighbouring layers: every unit of a
+    window holds the same basis, whose eigenvalues and captured energy match
+    the oracle's for the window's stacked samples; decode steps then checked
+    per unit."""
+    kvlr = _kvlr()
+    if storage == "f32":
+        w = _F32.with_(n_layers=n_layers, model="power", exponents=tuple(0.6 + 0.2 * l for l in range(n_layers)))
+        L = 600
+    else:
+        w = _QWEN.with_(n_layers=n_layers, batch=2, exponents=tuple(0.6 + 0.2 * l for l in range(n_layers)))
+        L = 2000
+    batch = w.batch
+    U = n_layers * batch
+    print(f"case depth-shared bases {storage} layers={n_layers} depth={depth}", flush=True)
+    prompt = synth.make_prompt(w, L=L)
+    dec = synth.make_decode_inputs(w, prompt, 4)
+    cfg = kvlr.config_of(w)
+    kc = kvlr.KVCache.allocate(cfg, U, L + 12)
+    K, V = prompt.K.cuda(), prompt.V.cuda()
+    ek = torch.zeros(U, w.D, device="cuda")
+    evv = torch.zeros(U, w.D, device="cuda")
+    sw = torch.zeros(U, 2, dtype=torch.int32, device="cuda")
+    kvlr.build_bases_shared(kc, n_layers, depth, K, V, ek, evv, sweeps=sw)
+    kvlr.project(kc, K, V)
+    torch.cuda.synchronize()
+    assert bool((sw > 0).all()), sw
+    for l0 in range(0, n_layers, depth):
+        layers = range(l0, min(l0 + depth, n_layers))
+        for b in range(batch):
+            units = [l * batch + b for l in layers]
+            for kind, basis, eig, X in ((0, kc.basis_k, ek, prompt.K), (1, kc.basis_v, evv, prompt.V)):
+                B0 = basis[units[0]]
+                for u in units[1:]:
+                    assert torch.equal(basis[u], B0) and torch.equal(eig[u], eig[units[0]])
+                Bref, lam, Ss = s4r.build_basis_shared([np64(X[u]) for u in units], w.n_sink, w.n_sample,
+                                                       w.rank, w.storage)
+                assert np.max(np.abs(np64(eig[units[0]]) - lam)) <= 1e-4 * lam[0], (units, kind)
+                Q, _ = np.linalg.qr(np64(B0))
+                e_gpu = sum(float(np.sum((S @ Q) ** 2)) for S in Ss)
+                e_ref = float(np.sum(lam[:w.rank]))
+                tol = 6e-5 if storage == "bf16" else 1e-6
+                assert abs(e_gpu - e_ref) <= tol * e_ref, (units, kind, e_gpu, e_ref)
+    st = run_checked_steps(kvlr, w, kc, dec, 4, units=[0, U - 1])
+    assert st.n_checked == 8
