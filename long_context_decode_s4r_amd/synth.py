@@ -119,22 +119,27 @@ class Prompt:
 
 
 def make_prompt(w: Workload, device="cpu", L: Optional[int] = None,
-                batch: Optional[int] = None, n_layers: Optional[int] = None) -> Prompt:
-    """Prompt K, V for every (layer, sequence) unit, unit = layer*batch + seq."""
+                batch: Optional[int] = None, n_layers: Optional[int] = None,
+                first_layer: int = 0) -> Prompt:
+    """Prompt K, V for every (layer, sequence) unit, unit = layer*batch + seq,
+    for layers [first_layer, first_layer + n_layers) (unit numbering starts
+    at the first of them; a layer's draws do not depend on which others are
+    generated with it)."""
     L = w.L if L is None else L
     batch = w.batch if batch is None else batch
-    n_layers = w.n_layers if n_layers is None else n_layers
+    n_layers = w.n_layers - first_layer if n_layers is None else n_layers
     dt = storage_dtype(w.storage)
     U = n_layers * batch
     K = torch.empty(U, L, w.D, dtype=dt, device=device)
     V = torch.empty(U, L, w.D, dtype=dt, device=device)
     models = []
-    for layer in range(n_layers):
+    for li in range(n_layers):
+        layer = first_layer + li
         mk = state_model(w, layer, _STREAM_K, device)
         mv = state_model(w, layer, _STREAM_V, device)
         models += [mk, mv]
         for b in range(batch):
-            u = layer * batch + b
+            u = li * batch + b
             plant = planted_positions(w, b, L).to(device)
             for kind, m, out in ((_STREAM_K, mk, K), (_STREAM_V, mv, V)):
                 g = _gen(device, w.seed, kind, layer, b)
@@ -155,18 +160,22 @@ class DecodeInputs:
 
 
 def make_decode_inputs(w: Workload, prompt: Prompt, steps: int, device="cpu",
-                       batch: Optional[int] = None, n_layers: Optional[int] = None) -> DecodeInputs:
+                       batch: Optional[int] = None, n_layers: Optional[int] = None,
+                       first_layer: int = 0) -> DecodeInputs:
+    """Decode-step queries, keys and values for the layers of `prompt`
+    (generated with the same first_layer and n_layers)."""
     batch = w.batch if batch is None else batch
-    n_layers = w.n_layers if n_layers is None else n_layers
+    n_layers = len(prompt.models) // 2 if n_layers is None else n_layers
     dt = storage_dtype(w.storage)
     U = n_layers * batch
     q = torch.empty(steps, U, w.n_q_heads, w.head_dim, dtype=dt, device=device)
     k = torch.empty(steps, U, w.n_kv_heads, w.head_dim, dtype=dt, device=device)
     v = torch.empty(steps, U, w.n_kv_heads, w.head_dim, dtype=dt, device=device)
-    for layer in range(n_layers):
-        mk, mv = prompt.models[2 * layer], prompt.models[2 * layer + 1]
+    for li in range(n_layers):
+        layer = first_layer + li
+        mk, mv = prompt.models[2 * li], prompt.models[2 * li + 1]
         for b in range(batch):
-            u = layer * batch + b
+            u = li * batch + b
             gq = _gen(device, w.seed, _STREAM_Q, layer, b)
             q[:, u] = torch.randn(steps, w.n_q_heads, w.head_dim, generator=gq,
                                   device=device).to(dt)

@@ -51,3 +51,15 @@ def test_qwen_exponents():
     w = configs.QWEN7B_64K
     assert w.exponent(0) == pytest.approx(0.5) and w.exponent(27) == pytest.approx(1.2)
     assert w.G == 7 and w.D == 512
+
+
+def test_layer_slices_match_whole_model():
+    """A layer generated on its own equals the same layer generated with the
+    others (the 28-layer workload is built one layer at a time)."""
+    w = configs.QWEN7B_64K
+    a = synth.make_prompt(w, L=64, batch=2, n_layers=3)
+    b = synth.make_prompt(w, L=64, batch=2, n_layers=1, first_layer=2)
+    assert torch.equal(a.K[4:6], b.K) and torch.equal(a.V[4:6], b.V)
+    da = synth.make_decode_inputs(w, a, 2, batch=2)
+    db = synth.make_decode_inputs(w, b, 2, batch=2, first_layer=2)
+    assert torch.equal(da.q[:, 4:6], db.q) and torch.equal(da.v[:, 4:6], db.v)
