@@ -1112,6 +1112,258 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
   }
 }
 
+// --------------------------------------------------------------------------
+// latent scoring, bf16 storage, products on MFMA 32x32x16 (on gfx950 this
+// shape runs at the full bf16 rate, twice the flops per cycle of 16x16x32).
+// grid (nsplit, U), 512 threads (8 waves, two per SIMD); the unit's tiles,
+// the 4-stage LDS ring and its direct global->LDS loads, the waits and the
+// one barrier per tile are those of k_score_bf16 above.
+//
+// Work of a tile (64 positions): combos (row block rb of 32 window rows,
+// column block cb of 32 positions), 2 NRB of them (6 or 8), one per wave.  A
+// wave keeps its row block's query operands for all k-steps in registers
+// (bf16 hi + lo, ~16 mantissa bits) and reads the B operands (the
+// positions' key coefficients, K-contiguous 16-byte chunks of the swizzled
+// rows) from the tile's stage.  Lane l's accumulator i holds row
+// 8 (i / 4) + 4 (l / 32) + i % 4 of the row block for position l % 32.  The
+// wave turns the older rows into probabilities with their running
+// (max, sum), sums them over its rows (the lane halves meet through a
+// permlane32 swap) into the segment buffer, and, for row block 0, writes
+// the current rows' logits to the spill buffer.  Every kScoreSeg positions
+// the block adds the row blocks' sums, stores the segment and folds the
+// current rows' logits into their running (max, sum).
+//
+// Splitting the rank of a combo over several waves (for W G <= 64) was
+// measured slower than k_score_bf16, and with a full-rank share per wave
+// r = 256 spills; the dispatch below takes this kernel only for 3 or 4 row
+// blocks and r <= 192.
+// --------------------------------------------------------------------------
+template <int NKS, int NRB, int GM>
+__global__ __launch_bounds__(512) void k_score_mfma32(Dims d, CachePtrs c, DecodeWs w) {
+  constexpr int r = NKS * 16;
+  constexpr int ROWB = r * 2;
+  constexpr int TILEB = kScoreTP * ROWB;
+  constexpr int NCH = r / 8;
+  constexpr int SWZ = (NCH % 16 == 0) ? 15 : (NCH % 8 == 0) ? 7 : (NCH % 4 == 0) ? 3 : 1;
+  constexpr int DW = TILEB / 1024 < kScoreWaves ? TILEB / 1024 : kScoreWaves;
+  constexpr int PW = TILEB / (DW * 1024);
+  constexpr int SEGT = kScoreSeg / kScoreTP;
+  constexpr int COMBOS = 2 * NRB;
+  constexpr int KB = NKS % 4 == 0 ? 4 : NKS % 2 == 0 ? 2 : 1;
+  static_assert(TILEB % (DW * 1024) == 0, "tile must split into 1 KB pieces per wave");
+  static_assert(COMBOS <= kScoreWaves, "one combo per wave");
+  __shared__ ScoreStage<NKS> st0, st1, st2, st3;
+  __shared__ __attribute__((aligned(16))) float segred[NRB][kScoreSeg];   // row blocks' partial scores
+  __shared__ __attribute__((aligned(16))) float segspill[GM][kScoreSeg];  // current rows' logits
+  static_assert(sizeof(ScoreStage<NKS>) == TILEB, "stage size");
+
+  const int split = blockIdx.x, u = blockIdx.y;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int32_t* si = w.stepinfo + 4 * u;
+  if (si[2]) return;
+  const int Lcur = si[0], steps = si[1];
+  const int G = d.G, W = d.W, s = d.s;
+  const int weff = min(steps + 1, W);
+  const int nrows = weff * G;
+  const int64_t cend = (int64_t)Lcur + 1 - d.nrec;
+  const int64_t ntu = (max(cend - s, (int64_t)0) + kScoreTP - 1) / kScoreTP;
+  const int ntl = ntu > split ? (int)((ntu - split + w.nsplit - 1) / w.nsplit) : 0;
+
+  // ---- DMA of one tile into a stage (as in k_score_bf16)
+  const uint8_t* cbase = reinterpret_cast<const uint8_t*>(
+      (const uint16_t*)c.coef_k + (int64_t)u * c.Lmax * r);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  uint32_t qoff[PW];
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    const int Q = (wvu * PW + q) * 64 + l;
+    const int pl = Q / NCH, slot = Q % NCH;
+    qoff[q] = (uint32_t)(pl * ROWB + ((slot ^ (pl & SWZ)) << 4));
+  }
+  auto issue = [&](int64_t p0, uint8_t* stage) {
+    if (DW < kScoreWaves && wvu >= DW) return;
+    const uint8_t* tb = cbase + p0 * ROWB;
+    if (p0 + kScoreTP <= c.Lmax) {
+#pragma unroll
+      for (int q = 0; q < PW; ++q)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(tb + qoff[q]),
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+    } else {  // last tile of the buffer: clamp rows
+#pragma unroll
+      for (int q = 0; q < PW; ++q) {
+        const int pl = ((wvu * PW + q) * 64 + l) / NCH;
+        const int64_t pos = min(p0 + pl, c.Lmax - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(cbase + pos * ROWB + (qoff[q] - pl * ROWB)),
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+      }
+    }
+  };
+  auto tp = [&](int t) {
+    return (int64_t)s + ((int64_t)min(t, max(ntl - 1, 0)) * w.nsplit + split) * kScoreTP;
+  };
+  if (ntl > 0) {
+    issue(tp(0), st0.b);
+    issue(tp(1), st1.b);
+    issue(tp(2), st2.b);
+  }
+
+  // ---- this wave's combo
+  const int combo = wv;
+  const bool wact = wv < COMBOS;
+  const int rb = combo >> 1, cb = combo & 1;
+  const int p = l & 31, hk = l >> 5;
+  bf16x8 ahi[NKS], alo[NKS];
+  float mrow[16];
+  {
+    const int rho = 32 * rb + p;
+    const bool valid = wact && rho < nrows;
+    const int rv = valid ? rho : 0;
+    const int sl = wrap_slot(steps - rv / G, W);
+    const uint16_t* qh = qsplit_of(c, u) + ((sl * G + rv % G) * 2) * r;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+      const bf16x8 h = ld_bf16x8(qh + 16 * k + 8 * hk);
+      const bf16x8 lo = ld_bf16x8(qh + r + 16 * k + 8 * hk);
+      ahi[k] = valid ? h : __builtin_bit_cast(bf16x8, u16x8{});
+      alo[k] = valid ? lo : __builtin_bit_cast(bf16x8, u16x8{});
+    }
+    const float* rst = rowstat_of(c, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 32 * rb + acc_row32(i, l);
+      const bool old_row = wact && rr >= G && rr < nrows;
+      const int r2 = old_row ? rr : G;
+      const float2 stv = *reinterpret_cast<const float2*>(rst + (wrap_slot(steps - r2 / G, W) * G + r2 % G) * 2);
+      mrow[i] = old_row ? stv.x + log2f(stv.y) : FLT_MAX;
+    }
+  }
+  // current row g (< G <= GM): accumulator g % 4 of the lanes with hk = g / 4
+  // in the waves of row block 0; wave g < G keeps the row's running
+  // (max, sum) over the positions it flushes
+  float nm = -INFINITY, ns = 0.f;
+  float* partial = w.partial + (int64_t)u * w.Lc_cap - s;
+  float* spill = w.spill + (int64_t)u * G * w.Lc_cap - s;
+
+  auto compute = [&](int t, const uint8_t* stage) {
+    f32x16 acc = f32x16{};
+    if (wact) {
+      const uint32_t rbase = lds_offset(stage) + (32 * cb + p) * ROWB;
+      const int sw = (32 * cb + p) & SWZ;
+#pragma unroll
+      for (int k0 = 0; k0 < NKS; k0 += KB) {
+        uint32_t ad[4];
+        bf16x8 bb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          ad[kk] = rbase + (((2 * min(k0 + kk, NKS - 1) + hk) ^ sw) << 4);
+        lds_read4(ad, bb);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          acc = mfma32x32x16(ahi[k0 + kk], bb[kk], acc);
+          acc = mfma32x32x16(alo[k0 + kk], bb[kk], acc);
+        }
+      }
+    }
+    if (!wact) return;
+    // arguments are <= 0 (or -huge for excluded rows): the hardware exp2
+    // is exact enough and its flush of tiny results is harmless here
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(acc[i] - mrow[i]);
+    {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+      ps = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+    }
+    const int sp = (t % SEGT) * kScoreTP + 32 * cb + p;  // position within the segment
+    if (hk == 0) segred[rb][sp] = ps;
+    if (rb == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * hk + i < G) segspill[4 * hk + i][sp] = acc[i];
+    }
+  };
+
+  // flush of segment sg, four positions per lane and one 16-byte store per
+  // wave: the last wave stores the row blocks' summed scores, wave g < G the
+  // current row g's logits (and folds them into its running max and sum);
+  // positions from cend on are not stored
+  auto flush = [&](int sg) {
+#pragma unroll
+    for (int e0 = 4 * l; e0 < kScoreSeg; e0 += 256) {
+      const int t = sg * SEGT + e0 / kScoreTP;
+      const int64_t pos = tp(t) + e0 % kScoreTP;
+      const int ne = t < ntl ? (int)min((int64_t)4, cend - pos) : 0;
+      if (wv == kScoreWaves - 1 && ne > 0) {
+        f32x4 sum = *reinterpret_cast<const f32x4*>(&segred[0][e0]);
+#pragma unroll
+        for (int q2 = 1; q2 < NRB; ++q2) sum += *reinterpret_cast<const f32x4*>(&segred[q2][e0]);
+        if (ne == 4) {
+          *reinterpret_cast<f32x4*>(partial + pos) = sum;
+        } else {
+          for (int e = 0; e < ne; ++e) partial[pos + e] = sum[e];
+        }
+      }
+      if (wv < G && ne > 0) {
+        const f32x4 z = *reinterpret_cast<const f32x4*>(&segspill[wv][e0]);
+        float* dst = spill + (int64_t)wv * w.Lc_cap + pos;
+        if (ne == 4) {
+          *reinterpret_cast<f32x4*>(dst) = z;
+        } else {
+          for (int e = 0; e < ne; ++e) dst[e] = z[e];
+        }
+        float mx = nm;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = e < ne ? fmaxf(mx, z[e]) : mx;
+        float acc = ns * __builtin_amdgcn_exp2f(nm - mx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += e < ne ? __builtin_amdgcn_exp2f(z[e] - mx) : 0.f;
+        nm = mx;
+        ns = acc;
+      }
+    }
+  };
+  constexpr int kWaitN = (kScoreNST - 2) * PW;
+  for (int t = 0; t < ntl; t += kScoreNST) {
+#define KVLR_SCORE32_STEP(k, SREAD, SNEXT)                                                  \
+    if (t + k >= ntl) break;                                                                \
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWaitN) : "memory");  \
+    if ((t + k) % SEGT == 0 && t + k > 0) {                                                 \
+      flush((t + k) / SEGT - 1);                                                            \
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                       \
+    }                                                                                       \
+    issue(tp(t + k + 3), SNEXT);                                                            \
+    compute(t + k, SREAD);
+    KVLR_SCORE32_STEP(0, st0.b, st3.b)
+    KVLR_SCORE32_STEP(1, st1.b, st0.b)
+    KVLR_SCORE32_STEP(2, st2.b, st1.b)
+    KVLR_SCORE32_STEP(3, st3.b, st2.b)
+#undef KVLR_SCORE32_STEP
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (ntl > 0) flush((ntl - 1) / SEGT);
+
+  // current row g's (max, sum) over this split, from the lanes of wave g
+  if (wv < G) {
+    float m = nm, sm = ns;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
+      const float mx = fmaxf(m, m2);
+      const float a = (m == -INFINITY) ? 0.f : sm * exp2f(m - mx);
+      const float b2 = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mx);
+      sm = a + b2;
+      m = mx;
+    }
+    if (l == 0) {
+      float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
+      tst[wv * 2 + 0] = m;
+      tst[wv * 2 + 1] = sm;
+    }
+  }
+}
+
 // latent scoring, fp32 storage: plain fp32 dot products, one position per
 // thread, window rows staged in LDS.
 __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs w, float qscale) {
@@ -1188,9 +1440,47 @@ __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs
   }
 }
 
+// LDS of k_score_mfma32<NKS, NRB, GM> (4 stages, segment buffers)
+constexpr size_t score32_lds(int nks, int nrb, int gm) {
+  return (size_t)4 * kScoreTP * nks * 32 + (size_t)(nrb + gm) * kScoreSeg * 4;
+}
+// the MFMA 32x32x16 scorer is used for 3 or 4 row blocks of 32 when its LDS
+// fits and a wave's query operands (bf16 hi + lo) stay within 12 k-steps
+// (96 registers; 16 k-steps spill)
+constexpr bool score32_ok(int nks, int nrb, int gm) {
+  return nrb >= 3 && nrb <= 4 && nks <= 12 && score32_lds(nks, nrb, gm) <= 160 * 1024;
+}
+
+template <int NKS, int NRB, int GM>
+static hipError_t launch_score32(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, hipStream_t st) {
+  if constexpr (score32_ok(NKS, NRB, GM)) {
+    hipLaunchKernelGGL((k_score_mfma32<NKS, NRB, GM>), dim3(w.nsplit, U), dim3(512), 0, st, d, c, w);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+// MFMA 32x32x16 scorer where it is the faster one (W G in 65..128, r <= 192)
+template <int KS>
+static bool try_score32(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w, hipStream_t st,
+                        hipError_t* e) {
+  const int nrb = (d.W * d.G + 31) / 32;
+  const int gm = d.G <= 4 ? 4 : 8;
+#define KVLR_S32(NRB, GM)                                              \
+  if (nrb == NRB && gm == GM && score32_ok(KS, NRB, GM)) {               \
+    *e = launch_score32<KS, NRB, GM>(d, U, c, w, st);                   \
+    return true;                                                        \
+  }
+  KVLR_S32(3, 4) KVLR_S32(3, 8) KVLR_S32(4, 4) KVLR_S32(4, 8)
+#undef KVLR_S32
+  return false;
+}
+
 template <int KS>
 static hipError_t launch_score_bf16(const Dims& d, int U, const CachePtrs& c, const DecodeWs& w,
                                     hipStream_t st) {
+  hipError_t e;
+  if (try_score32<KS>(d, U, c, w, st, &e)) return e;
   const int nrb = (d.W * d.G + 15) / 16;
   dim3 grid(w.nsplit, U);
   if (nrb <= 1)

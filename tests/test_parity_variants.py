@@ -69,6 +69,18 @@ def test_separate_key_value_ranks(gpu_lib, w):
     assert st.n_checked == 20
 
 
+@pytest.mark.parametrize("shape", [(16, 4, 192, 24), (24, 4, 64, 16), (32, 8, 128, 32), (28, 4, 192, 16)],
+                         ids=["G4W24_r192", "G6W16_r64", "G4W32_r128", "G7W16_r192"])
+def test_window_row_blocks_bf16(gpu_lib, shape):
+    """Window row counts W G of 65..128 (three or four 32-row blocks of the
+    latent scorer, with four or eight current rows), for ranks 64..192,
+    over more steps than the window holds."""
+    Hq, Hkv, r, W = shape
+    w = _LLAMA.with_(n_q_heads=Hq, n_kv_heads=Hkv, rank=r, q_window=W, top_k=96)
+    st = _run(w, 20000, 2, W + 2)
+    assert st.n_checked == 2 * (W + 2)
+
+
 @pytest.mark.parametrize("w", [
     _F32.with_(local_window=1), _F32.with_(local_window=1, n_sink=0),
     _LLAMA.with_(local_window=1), _QWEN.with_(local_window=1, rank_v=192),
