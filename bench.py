@@ -6,9 +6,12 @@ storage, rank 256, 4 sinks, 2048-row SVD sample, query window 16, top-k 512,
 exact recent window 64.  A step is one full decode step of every sequence:
 append + query coefficients, latent scoring, pooled top-k, reconstruction and
 exact attention, merge.  Inputs (caches, bases, queries) are resident in HBM
-before timing.  When one step's scan would fit the 256 MB Infinity Cache the
-caches rotate over several instances with identical contents, so a step
-cannot be served from what the previous one left there.
+before timing.  The caches rotate over several instances with identical
+contents (as the layers of a model would), enough that what one instance's
+step reads through the caches (bases, gathered rows, exact rows) totals twice
+the 256 MB Infinity Cache over a rotation: a step cannot be served from what
+the same instance's previous step left there.  (The scan itself is read
+non-temporally and leaves nothing behind.)
 
 Other workloads (``--workload``): the same layer at 128K context and batch 4
 (planted atypical norms); the 28-layer Qwen-2.5-7B-shaped model at 64K, batch
@@ -370,8 +373,13 @@ def run_layer_decode(w, args, ceiling):
     fp32 case): units = the batch's sequences of one layer."""
     U = w.n_units
     cfg = kvlr.config_of(w)
-    scan_one = U * (w.L - w.n_sink - w.n_recent) * w.rank * (2 if w.storage == "bf16" else 4)
-    n_inst = args.instances or max(1, min(8, math.ceil(2 * MALL_BYTES / scan_one)))
+    el = 2 if w.storage == "bf16" else 4
+    rv = w.rank_v or w.rank
+    # bytes a step reads with cached loads: B^K (its transposed copy), B^V,
+    # the gathered coefficient rows and the exact rows
+    reread = U * el * ((w.rank + rv) * w.D + w.top_k * (w.rank + rv)
+                       + 2 * (w.n_sink + w.n_recent) * w.D)
+    n_inst = args.instances or max(3, min(32, math.ceil(2 * MALL_BYTES / reread)))
     per_inst = w.q_window + math.ceil((args.warmup + 3 * args.steps + 6 * n_inst) / n_inst) + 8
     L_max = w.L + per_inst
     log(f"[bench] workload {w.name}: generating prompt on the GPU")

@@ -227,6 +227,7 @@ CachePtrs cache_ptrs(const kvlr_cache* c, const Dims& d) {
   p.state = (uint8_t*)c->state;
   p.state_stride = state_unit_bytes(d);
   p.rowstat_off = state_rowstat_off(d);
+  p.bkt_off = state_bkt_off(d);
   p.Lmax = c->L_max;
   return p;
 }

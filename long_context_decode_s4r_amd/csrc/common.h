@@ -263,8 +263,11 @@ struct CachePtrs {
   // per-unit opaque decode state, state_stride bytes per unit:
   //   [W][G][2][r] bf16  hi / lo parts of qwin * log2(e)/sqrt(r) (scorer operands)
   //   [W][G][2]    fp32  running (max, sum) of each window row's latent softmax
+  //   (bf16 storage) [r][D'] bf16  B^K transposed, one contiguous row per
+  //                  column of B^K (the prologue's operand; written by the
+  //                  projection call, not part of the window state)
   uint8_t* state;
-  int64_t state_stride, rowstat_off;
+  int64_t state_stride, rowstat_off, bkt_off;
   int64_t Lmax;
 };
 __host__ __device__ inline uint16_t* qsplit_of(const CachePtrs& c, int64_t u) {
@@ -273,13 +276,20 @@ __host__ __device__ inline uint16_t* qsplit_of(const CachePtrs& c, int64_t u) {
 __host__ __device__ inline float* rowstat_of(const CachePtrs& c, int64_t u) {
   return reinterpret_cast<float*>(c.state + u * c.state_stride + c.rowstat_off);
 }
+__host__ __device__ inline uint16_t* bkt_of(const CachePtrs& c, int64_t u) {
+  return reinterpret_cast<uint16_t*>(c.state + u * c.state_stride + c.bkt_off);
+}
 // state layout of one unit (bytes): the bf16 window operands, then the row
-// statistics, 256-byte aligned overall
+// statistics (together the window state, cleared by the projection call),
+// then for bf16 storage B^K transposed; 256-byte aligned parts
 inline int64_t state_rowstat_off(const Dims& d) {
   return ((int64_t)d.W * d.G * 2 * d.r * 2 + 15) / 16 * 16;
 }
-inline int64_t state_unit_bytes(const Dims& d) {
+inline int64_t state_bkt_off(const Dims& d) {
   return (state_rowstat_off(d) + (int64_t)d.W * d.G * 2 * 4 + 255) / 256 * 256;
+}
+inline int64_t state_unit_bytes(const Dims& d) {
+  return state_bkt_off(d) + (d.dtype != 0 ? ((int64_t)d.r * d.D * 2 + 255) / 256 * 256 : 0);
 }
 
 // prefill: the window seeded with the prompt's last n_tail queries
@@ -287,7 +297,8 @@ size_t window_init_ws_bytes(const Dims& d, int64_t U, int64_t L, int n_tail);
 hipError_t launch_window_init(const Dims& d, int U, int64_t L, int n_tail, const void* q_tail,
                               const CachePtrs& c, void* ws, hipStream_t st);
 
-// prefill: exact sinks and ring, window and decode state cleared, lens = {L, 0}
+// prefill: exact sinks and ring, window and decode state cleared, lens = {L, 0},
+// (bf16) B^K transposed into the unit state
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   const CachePtrs& c, hipStream_t st);
 

@@ -470,40 +470,29 @@ __global__ __launch_bounds__(256) void k_prologue(Dims d, CachePtrs c, const T* 
 }
 
 // --------------------------------------------------------------------------
-// prologue for bf16 storage when d_h divides 256: grid (ncb + 1, U), 256
-// threads, products on MFMA 16x16x32.
-//   blocks [0, ncb):  32 columns of B^K each.  A = up to 16 input vectors
-//     straight from memory (row 0: k, row 1 + g: query head g of every KV
-//     head, concatenated; K = basis row index), B = basis columns staged
-//     through LDS transposed ([column][row], four rows per 8-byte write) so
-//     an operand is one 16-byte read.  Rows in chunks of kProRows; wave w
-//     takes k-steps 8 w .. 8 w + 7 of a chunk, whole heads since d_h
-//     divides 256, and leaves each head's partial products in LDS.  A
-//     head's partial of row 1 + g is the projected query q[h G + g] . B^K
-//     rows of head h (attention in the coefficient space); the sum over
-//     heads gives c^K(new) (row 0) and the window query latents (rows
-//     1 .. G).  So B^K is read once for all three.
-//   block ncb:  exact ring push of k and v; the older window rows' (m, S)
-//     updated with the candidate entering the compressed set.
+// prologue for bf16 storage when d_h divides 256: grid (r_K / 16 + 1, U),
+// 256 threads, products on MFMA 16x16x32.
+//   blocks [0, r_K / 16):  16 columns of B^K each, read from the transposed
+//     copy in the unit state (one contiguous D'-element row per column, so
+//     a block's operand slab is a few whole rows: 32 KB at D' = 1024),
+//     straight into the B operands; A = up to 16 input vectors straight
+//     from memory (row 0: k, row 1 + g: query head g of every KV head,
+//     concatenated; K = channel).  Wave w takes the channels
+//     [256 w, 256 w + 256) of every 1024, whole heads since d_h divides
+//     256.  After a head's last k-step its accumulator holds the head's
+//     partial products: for row 1 + g that is the projected query
+//     q[h G + g] . B^K_h of the attention in coefficient space; the sums
+//     over heads (in the wave, then over the waves in LDS) give c^K(new)
+//     (row 0) and the window query latents (rows 1 .. G).  B^K is read once
+//     for all three.
+//   block r_K / 16:  exact ring push of k and v; the older window rows'
+//     (m, S) updated with the candidate entering the compressed set.
 // c^V(new) is first read when the new position leaves the exact ring, at
 // least one step later, so its GEMV runs beside the top-k selection (the
 // extra blocks of that launch), off this step's critical path.
 // --------------------------------------------------------------------------
-constexpr int kProRows = 1024;
-constexpr int kProLdb = kProRows + 8;  // staged column length (bf16), padded
-
 __host__ __device__ inline bool prologue_fused(const Dims& d) {
   return d.dtype != 0 && d.dh % 32 == 0 && 256 % d.dh == 0 && d.G + 1 <= 16;
-}
-
-__device__ __forceinline__ void stage_quad_t(uint16_t* bt, int ldb, int col, int row, const u16x8 (&v)[4]) {
-  // rows row .. row + 3 of the 8 columns col .. col + 7, written transposed
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const uint32_t lo = (uint32_t)v[0][x] | ((uint32_t)v[1][x] << 16);
-    const uint32_t hi = (uint32_t)v[2][x] | ((uint32_t)v[3][x] << 16);
-    *reinterpret_cast<uint2*>(bt + (col + x) * ldb + row) = make_uint2(lo, hi);
-  }
 }
 
 // state block, bf16 storage: every load (the new k and v, the entering
@@ -598,7 +587,6 @@ __global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, cons
   const int b = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6, n16 = l & 15, kq = l >> 4;
   const int D = d.D, r = d.r, G = d.G, W = d.W, dh = d.dh, Hq = d.Hq;
-  extern __shared__ __attribute__((aligned(16))) float sm[];
   const int32_t Lcur = c.lens[2 * u], steps = c.lens[2 * u + 1];
   const bool live = (int64_t)Lcur < c.Lmax;
   if (b == 0 && tid == 0) {
@@ -611,111 +599,72 @@ __global__ __launch_bounds__(256) void k_prologue_mfma(Dims d, CachePtrs c, cons
     if (live) prologue_state_bf16(d, c, kn, vn, qscale, u, tid, Lcur, steps);
     return;
   }
-  uint16_t* bt = reinterpret_cast<uint16_t*>(sm);
-  float* red = sm + 32 * kProLdb / 2;  // [heads of a chunk][16 vectors][32 columns]
+  __shared__ float red[4][16][17];  // the waves' sums over their heads
+  constexpr int KSW = 8;            // k-steps of 32 channels per wave and round
   const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u16x8{});
-  const int col0 = b * 32;
-  const int nvec = 1 + G;
-  const uint16_t* B = (const uint16_t*)c.basis_k + (int64_t)u * D * r;
-  const int cq = tid & 3, a4 = 4 * (tid >> 2);
-  const int colq = min(col0 + 8 * cq, r - 8);  // columns past r: computed, not stored
-  float run[2] = {0.f, 0.f};                   // sums over heads of outputs tid, tid + 256
-  for (int r0 = 0; r0 < D; r0 += kProRows) {
-    u16x8 pc[4][4];
+  const int col = 16 * b + n16;     // < r (r is a multiple of 32)
+  const uint16_t* bt = bkt_of(c, u) + (int64_t)col * D;
+  const int g1 = min(max(n16 - 1, 0), G - 1);  // query of A row n16 (rows past G: zero)
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 256 * wv; c0 < D; c0 += 1024) {
+    bf16x8 xa[KSW], xb[KSW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        pc[j][qq] = *reinterpret_cast<const u16x8*>(B + (int64_t)min(r0 + a4 + 256 * j + qq, D - 1) * r + colq);
-    // A: vector n16, elements kk .. kk + 7
-    bf16x8 xa[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int kk = r0 + 32 * (8 * wv + ks) + 8 * kq;
-      xa[ks] = zero8;
-      if (n16 < nvec && kk < D) {
-        const uint16_t* src = n16 == 0 ? kn + (int64_t)u * D + kk
-                                       : q + ((int64_t)u * Hq + (kk / dh) * G + (n16 - 1)) * dh + kk % dh;
-        xa[ks] = ld_bf16x8(src);
-      }
+    for (int ks = 0; ks < KSW; ++ks) {
+      const int kk = c0 + 32 * ks + 8 * kq;
+      const int kc = kk < D ? kk : 0;  // k-steps past D' are skipped below
+      xb[ks] = ld_bf16x8(bt + kc);
+      const uint16_t* src = n16 == 0 ? kn + (int64_t)u * D + kc
+                                     : q + ((int64_t)u * Hq + (kc / dh) * G + g1) * dh + kc % dh;
+      xa[ks] = ld_bf16x8(src);
     }
-    if (r0 > 0) __syncthreads();  // the previous chunk's operand and partial reads are done
+    if (n16 > G) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) stage_quad_t(bt, kProLdb, 8 * cq, a4 + 256 * j, pc[j]);
-    __syncthreads();
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int ks = 0; ks < KSW; ++ks) xa[ks] = zero8;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int kr = 32 * (8 * wv + ks);
-      if (r0 + kr < D) {
+    for (int ks = 0; ks < KSW; ++ks) {
+      if (c0 + 32 * ks >= D) break;
+      acc = mfma16x16x32(xa[ks], xb[ks], acc);
+      if ((32 * (ks + 1)) % dh == 0) {  // last k-step of head (c0 + 32 ks) / dh (c0 % d_h == 0)
+        // lane: rows 4 kq + i, column col; rows 1 .. G are the head's projected queries
+        if (live) {
+          const int h = (c0 + 32 * ks) / dh;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 bo = *reinterpret_cast<const bf16x8*>(bt + (16 * t + n16) * kProLdb + kr + 8 * kq);
-          acc[t] = mfma16x16x32(xa[ks], bo, acc[t]);
-        }
-        if ((kr + 32) % dh == 0) {  // last k-step of head (r0 + kr) / dh: its partial, lane holds
-          const int hc = kr / dh;    // vectors 4 kq + i, columns 16 t + n16
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[(hc * 16 + 4 * kq + i) * 32 + 16 * t + n16] = acc[t][i];
-            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int i = 0; i < 4; ++i) {
+            const int v = 4 * kq + i;
+            if (v >= 1 && v <= G) {
+              const float x = acc[i] * ascale;
+              uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + ((int64_t)u * Hq + h * G + v - 1) * 2 * r + col;
+              const uint16_t hb = f2bf(x);
+              ql[0] = hb;
+              ql[r] = f2bf(x - bf2f(hb));
+            }
           }
         }
-      }
-    }
-    __syncthreads();
-    const int nhc = min(kProRows, D - r0) / dh;  // heads of this chunk
-    if (live) {
-      for (int o = tid; o < nhc * G * 32; o += 256) {
-        const int cc = o & 31, hg = o >> 5, hc = hg / G, g = hg % G, cl = col0 + cc;
-        if (cl < r) {
-          const float x = red[(hc * 16 + 1 + g) * 32 + cc] * ascale;
-          const int h = r0 / dh + hc;
-          uint16_t* ql = reinterpret_cast<uint16_t*>(w.qlat) + ((int64_t)u * Hq + h * G + g) * 2 * r + cl;
-          const uint16_t hb = f2bf(x);
-          ql[0] = hb;
-          ql[r] = f2bf(x - bf2f(hb));
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int o = tid + 256 * j;
-      if (o < nvec * 32) {
-        const int v = o >> 5, cc = o & 31;
-        float s = 0.f;
-        for (int hc = 0; hc < nhc; ++hc) s += red[(hc * 16 + v) * 32 + cc];
-        run[j] += s;
+        run += acc;
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
-  if (!live) return;
-  const int64_t p = Lcur;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int o = tid + 256 * j;
-    const int v = o >> 5, cc = o & 31, cl = col0 + cc;
-    if (o >= nvec * 32 || cl >= r) continue;
-    const float sum = run[j];
-    if (v == 0) {
-      uint16_t* C = (uint16_t*)c.coef_k;
-      C[((int64_t)u * c.Lmax + p) * r + cl] = f2bf(sum);
-    } else {
-      const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
-      c.qwin[row * r + cl] = sum;
-      const float x = sum * qscale;  // MFMA operands of the latent scoring
-      const uint16_t hb = f2bf(x);
-      uint16_t* qs = qsplit_of(c, u) + ((steps % W) * G + (v - 1)) * 2 * r;
-      qs[cl] = hb;
-      qs[r + cl] = f2bf(x - bf2f(hb));
-    }
+  for (int i = 0; i < 4; ++i) red[wv][4 * kq + i][n16] = run[i];
+  __syncthreads();
+  if (!live || tid >= (1 + G) * 16) return;
+  // thread: row v, column cl
+  const int v = tid >> 4, cc = tid & 15, cl = 16 * b + cc;
+  const float sum = (red[0][v][cc] + red[1][v][cc]) + (red[2][v][cc] + red[3][v][cc]);
+  if (v == 0) {
+    ((uint16_t*)c.coef_k)[((int64_t)u * c.Lmax + Lcur) * r + cl] = f2bf(sum);
+  } else {
+    const int64_t row = ((int64_t)u * W + steps % W) * G + (v - 1);
+    c.qwin[row * r + cl] = sum;
+    const float x = sum * qscale;  // MFMA operands of the latent scoring
+    const uint16_t hb = f2bf(x);
+    uint16_t* qs = qsplit_of(c, u) + ((steps % W) * G + (v - 1)) * 2 * r;
+    qs[cl] = hb;
+    qs[r + cl] = f2bf(x - bf2f(hb));
   }
-}
-
-static size_t prologue_mfma_lds(const Dims& d) {
-  const int nh = (d.D < kProRows ? d.D : kProRows) / d.dh;
-  return (size_t)32 * kProLdb * 2 + (size_t)nh * 16 * 32 * 4;
 }
 
 // c^V(new) = v_cat . B^V, 32 columns per block of 1024 threads: thread
@@ -787,12 +736,9 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
     hipLaunchKernelGGL(k_prologue<float>, grid, dim3(256), lds, st, d, c, (const float*)q,
                        (const float*)k_new, (const float*)v_new, w, qscale, ascale, ncb, ncbv);
   } else if (prologue_fused(d)) {
-    static size_t done = 0;
-    const size_t lm = prologue_mfma_lds(d);
-    hipError_t e = allow_lds(&k_prologue_mfma, lm, &done);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prologue_mfma, dim3(ncb + 1, U), dim3(256), lm, st, d, c, (const uint16_t*)q,
-                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb);
+    const int ncb16 = d.r / 16;
+    hipLaunchKernelGGL(k_prologue_mfma, dim3(ncb16 + 1, U), dim3(256), 0, st, d, c, (const uint16_t*)q,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb16);
   } else {
     hipLaunchKernelGGL(k_prologue<uint16_t>, grid, dim3(256), lds, st, d, c, (const uint16_t*)q,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, w, qscale, ascale, ncb, ncbv);
@@ -829,6 +775,12 @@ hipError_t launch_prologue(const Dims& d, int U, const void* q, const void* k_ne
 // an LDS segment buffer; every 8 tiles the block sums the groups and stores
 // the segment, together with the current rows' logits.
 // --------------------------------------------------------------------------
+// cache policy of the scan's direct global->LDS loads: non-temporal.  The
+// key coefficients are read once per step; streamed this way they run
+// faster (7.0 against 6.4 TB/s measured on a plain 1 GiB stream) and do not
+// evict the step's other data (bases, gathered rows, partial scores) from
+// the L2 and Infinity Cache, which the kernels after the scan then hit.
+constexpr int kScanPolicy = 2;   // the instruction's nt bit
 constexpr int kScoreTP = 64;     // positions per tile
 constexpr int kScoreSeg = 512;   // positions per output segment (buffered in LDS)
 constexpr int kScoreNST = 4;     // LDS ring stages (3 tiles in flight)
@@ -910,7 +862,7 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
       for (int q = 0; q < PW; ++q)
         __builtin_amdgcn_global_load_lds(
             (const void*)(tb + qoff[q]),
-            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, kScanPolicy);
     } else {  // last tile of the buffer: clamp rows
 #pragma unroll
       for (int q = 0; q < PW; ++q) {
@@ -918,7 +870,7 @@ __global__ __launch_bounds__(512) void k_score_bf16(Dims d, CachePtrs c, DecodeW
         const int64_t pos = min(p0 + pl, c.Lmax - 1);
         __builtin_amdgcn_global_load_lds(
             (const void*)(cbase + pos * ROWB + (qoff[q] - pl * ROWB)),
-            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, kScanPolicy);
       }
     }
   };
@@ -1188,7 +1140,7 @@ __global__ __launch_bounds__(512) void k_score_mfma32(Dims d, CachePtrs c, Decod
       for (int q = 0; q < PW; ++q)
         __builtin_amdgcn_global_load_lds(
             (const void*)(tb + qoff[q]),
-            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, kScanPolicy);
     } else {  // last tile of the buffer: clamp rows
 #pragma unroll
       for (int q = 0; q < PW; ++q) {
@@ -1196,7 +1148,7 @@ __global__ __launch_bounds__(512) void k_score_mfma32(Dims d, CachePtrs c, Decod
         const int64_t pos = min(p0 + pl, c.Lmax - 1);
         __builtin_amdgcn_global_load_lds(
             (const void*)(cbase + pos * ROWB + (qoff[q] - pl * ROWB)),
-            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void*)(stage + (wvu * PW + q) * 1024), 16, 0, kScanPolicy);
       }
     }
   };

@@ -1120,7 +1120,7 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
   } else {
     for (int j = threadIdx.x; j < qw_per_unit; j += blockDim.x) c.qwin[(int64_t)u * qw_per_unit + j] = 0.f;
     uint32_t* st = reinterpret_cast<uint32_t*>(c.state + u * c.state_stride);
-    for (int64_t j = threadIdx.x; j < c.state_stride / 4; j += blockDim.x) st[j] = 0u;
+    for (int64_t j = threadIdx.x; j < c.bkt_off / 4; j += blockDim.x) st[j] = 0u;  // window state
     if (threadIdx.x == 0) {
       c.lens[2 * u] = (int32_t)L;
       c.lens[2 * u + 1] = 0;
@@ -1128,16 +1128,36 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
   }
 }
 
+// B^K transposed into the unit state (bf16): tile of 32 channels x 32 columns
+__global__ __launch_bounds__(256) void k_basis_kt_state(CachePtrs c, int D, int r) {
+  __shared__ uint16_t t[32][33];
+  const int u = blockIdx.z, k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  const uint16_t* B = (const uint16_t*)c.basis_k + (int64_t)u * D * r;
+  uint16_t* T = bkt_of(c, u);
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int kk = e >> 5, nn = e & 31;
+    if (k0 + kk < D && n0 + nn < r) t[kk][nn] = B[(int64_t)(k0 + kk) * r + n0 + nn];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int nn = e >> 5, kk = e & 31;
+    if (k0 + kk < D && n0 + nn < r) T[(int64_t)(n0 + nn) * D + k0 + kk] = t[kk][nn];
+  }
+}
+
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   const CachePtrs& c, hipStream_t st) {
   dim3 grid(d.s + d.nrec + 1, U);
   const int qw = d.W * d.G * d.r;
-  if (d.dtype == 0)
+  if (d.dtype == 0) {
     hipLaunchKernelGGL(k_exact_reset<float>, grid, dim3(256), 0, st, (const float*)K,
                        (const float*)V, c, L, d.D, d.s, d.nrec, qw);
-  else
+  } else {
     hipLaunchKernelGGL(k_exact_reset<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)K,
                        (const uint16_t*)V, c, L, d.D, d.s, d.nrec, qw);
+    hipLaunchKernelGGL(k_basis_kt_state, dim3((d.D + 31) / 32, (d.r + 31) / 32, U), dim3(256), 0,
+                       st, c, d.D, d.r);
+  }
   return hipGetLastError();
 }
 
