@@ -95,7 +95,8 @@ def _probe_lib():
 def run_probes(full: bool = True):
     """Measured ceilings (include/kvlr_probe.h): streaming-read bandwidth over
     a 4 GiB buffer (16x the Infinity Cache) through the register path and the
-    direct global->LDS path, and the dense bf16 MFMA rate.  Each
+    direct global->LDS path (plain and non-temporal, the latter being the
+    latent scan's loads), and the dense bf16 MFMA rate.  Each
     configuration: one untimed launch, then the best of 5 timed launches (HIP
     events on the launch stream).  full=False runs only the configurations
     that were best on this GPU."""
@@ -119,9 +120,9 @@ def run_probes(full: bool = True):
         return best
 
     if full:
-        cfgs = [(0, b, dp) for b in (256, 512, 1024, 2048, 4096) for dp in (2, 4, 8, 16)] + [(1, 256, 0)]
+        cfgs = [(0, b, dp) for b in (256, 512, 1024, 2048, 4096) for dp in (2, 4, 8, 16)] + [(1, 256, 0), (2, 256, 0)]
     else:
-        cfgs = [(0, 256, 8), (0, 512, 4), (1, 256, 0)]
+        cfgs = [(0, 256, 8), (0, 512, 4), (1, 256, 0), (2, 256, 0)]
     reads = []
     for method, blocks, depth in cfgs:
         def launch():
@@ -129,7 +130,7 @@ def run_probes(full: bool = True):
                                      st.cuda_stream)
             assert rc == 0, rc
         ms = best_ms(launch)
-        reads.append({"method": ["register", "global_to_lds"][method], "blocks": blocks,
+        reads.append({"method": ["register", "global_to_lds", "global_to_lds_nt"][method], "blocks": blocks,
                       "depth": depth, "gbps": round(nbytes / (ms / 1e3) / 1e9, 1)})
     del buf
     mfma = []
@@ -324,9 +325,19 @@ def _stage_profile(step, steps):
     return {k: v / max(n_prof, 1) for k, v in stage_ms.items()}
 
 
+def scorer_kernel(w):
+    """The latent-scoring kernel the library launches for this shape (its
+    dispatch rule: the MFMA 32x32x16 scorer for 65..128 window rows and key
+    rank <= 192 in bf16, else k_score_bf16; fp32 storage: k_score_f32)."""
+    if w.storage != "bf16":
+        return "k_score_f32"
+    rows = w.q_window * w.G
+    return "k_score_mfma32" if 64 < rows <= 128 and w.rank <= 192 else "k_score_bf16"
+
+
 def _roofline(scan_bytes, score_ms, w, ceiling):
     achieved = scan_bytes / (score_ms / 1e3) / 1e9
-    kern = "k_score_bf16" if w.storage == "bf16" else "k_score_f32"
+    kern = scorer_kernel(w)
     r = {"bound": "hbm", "kernel": f"{kern} (latent scoring)", "achieved": round(achieved, 1),
          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
          "traffic": stored_traffic(kern, w.name)}

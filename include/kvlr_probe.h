@@ -26,7 +26,9 @@ extern "C" {
  *   method 1: direct global -> LDS loads (16 bytes per lane) into a ring of
  *             4 LDS stages of 32 KiB, three stages in flight, 512 threads per
  *             block (the scheme of the latent scoring kernel, with no compute);
- *             `depth` is ignored.
+ *             `depth` is ignored;
+ *   method 2: method 1 with non-temporal loads (the cache policy of the
+ *             latent scan: streamed data is not kept in the caches).
  *   sink      device, >= blocks uint32: written only if an impossible value
  *             turns up, so the loads cannot be optimised away. */
 int kvlr_probe_read(const void* src, size_t bytes, int method, int blocks, int depth,

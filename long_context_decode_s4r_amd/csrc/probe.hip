@@ -27,8 +27,11 @@ __global__ __launch_bounds__(256) void k_probe_read_reg(const uint4* __restrict_
 }
 
 // LDS path: 512 threads, 4 stages of 32 KiB, 3 in flight; each lane moves
-// 16 bytes per request, each wave 1 KiB, 4 requests per wave per stage
+// 16 bytes per request, each wave 1 KiB, 4 requests per wave per stage;
+// AUX = the loads' cache-policy bits (0, or 2 = non-temporal as in the
+// latent scan)
 constexpr int kPrStage = 32768;
+template <int AUX>
 __global__ __launch_bounds__(512) void k_probe_read_lds(const uint8_t* __restrict__ src, int64_t nstage,
                                                         uint32_t* __restrict__ sink) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[4 * kPrStage];
@@ -43,7 +46,7 @@ __global__ __launch_bounds__(512) void k_probe_read_lds(const uint8_t* __restric
     for (int q = 0; q < 4; ++q) {
       const int off = (wvu * 4 + q) * 1024;
       __builtin_amdgcn_global_load_lds((const void*)(base + off + 16 * l),
-                                       (__attribute__((address_space(3))) void*)(stage + off), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(stage + off), 16, 0, AUX);
     }
   };
   uint32_t acc = 0;
@@ -119,10 +122,14 @@ extern "C" int kvlr_probe_read(const void* src, size_t bytes, int method, int bl
 #undef KVLR_PR
       default: return 1;
     }
-  } else if (method == 1) {
+  } else if (method == 1 || method == 2) {
     if (bytes % kPrStage != 0) return 1;
-    hipLaunchKernelGGL(k_probe_read_lds, dim3(blocks), dim3(512), 0, st, (const uint8_t*)src,
-                       (int64_t)(bytes / kPrStage), sink);
+    if (method == 1)
+      hipLaunchKernelGGL(k_probe_read_lds<0>, dim3(blocks), dim3(512), 0, st, (const uint8_t*)src,
+                         (int64_t)(bytes / kPrStage), sink);
+    else
+      hipLaunchKernelGGL(k_probe_read_lds<2>, dim3(blocks), dim3(512), 0, st, (const uint8_t*)src,
+                         (int64_t)(bytes / kPrStage), sink);
   } else {
     return 1;
   }
