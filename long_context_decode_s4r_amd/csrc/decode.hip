@@ -1317,9 +1317,27 @@ __global__ __launch_bounds__(512) void k_score_mfma32(Dims d, CachePtrs c, Decod
 }
 
 // latent scoring, fp32 storage: plain fp32 dot products, one position per
-// thread, window rows staged in LDS.
-__global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs w, float qscale) {
-  const int split = blockIdx.x, u = blockIdx.y;
+// thread.  The window rows (scaled) sit in LDS; the block's positions are
+// taken in runs of P, each run's key-coefficient rows first copied into LDS
+// with coalesced loads (rows padded by one float), so every product reads
+// LDS.  The G current rows keep their running (max, sum) in registers; the
+// block combines them with wave shuffles and one LDS exchange (ms_combine:
+// a (max, sum) pair of base-2 softmax statistics merged into (m, s); pairs
+// with no mass are skipped).
+__device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
+  if (!(s2 > 0.f)) return;
+  if (!(s > 0.f)) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mx = fmaxf(m, m2);
+  s = s * exp2f(m - mx) + s2 * exp2f(m2 - mx);
+  m = mx;
+}
+
+__global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs w, float qscale, int P) {
+  const int split = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int32_t* si = w.stepinfo + 4 * u;
   if (si[2]) return;
   const int Lcur = si[0], steps = si[1];
@@ -1333,62 +1351,78 @@ __global__ __launch_bounds__(256) void k_score_f32(Dims d, CachePtrs c, DecodeWs
   float* qs = sm;                   // [nrows][r]
   float* rm = qs + W * G * r;       // [nrows] max
   float* ri = rm + W * G;           // [nrows] 1/S
-  float* red = ri + W * G;          // [256][2] for the new-row stats
-  for (int e = threadIdx.x; e < nrows * r; e += blockDim.x) {
+  float* red = ri + W * G;          // [4 waves][8 rows][2]
+  float* cs = red + 64;             // [P][r + 1] key-coefficient rows of a run
+  for (int e = tid; e < nrows * r; e += blockDim.x) {
     const int rho = e / r, k = e % r, i = rho / G, g = rho % G;
     const int sl = wrap_slot(steps - i, W);
     qs[e] = c.qwin[(((int64_t)u * W + sl) * G + g) * r + k] * qscale;
   }
-  for (int rho = threadIdx.x; rho < nrows; rho += blockDim.x) {
+  for (int rho = tid; rho < nrows; rho += blockDim.x) {
     const int i = rho / G, g = rho % G;
     const int sl = wrap_slot(steps - i, W);
     const float* rs = rowstat_of(c, u) + (sl * G + g) * 2;
     rm[rho] = rs[0];
     ri[rho] = rho < G ? 0.f : 1.f / rs[1];
   }
-  __syncthreads();
   float nm[8], ns[8];
+#pragma unroll
   for (int g = 0; g < 8; ++g) {
     nm[g] = -INFINITY;
     ns[g] = 0.f;
   }
   const float* CK = (const float*)c.coef_k + (int64_t)u * c.Lmax * r;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += blockDim.x) {
-    const float* cj = CK + j * r;
-    float ps = 0.f;
-    for (int rho = 0; rho < nrows; ++rho) {
-      float z = 0.f;
-      for (int k = 0; k < r; ++k) z += qs[rho * r + k] * cj[k];
-      if (rho < G) {
-        w.spill[((int64_t)u * G + rho) * w.Lc_cap + (j - s)] = z;
-        const float mx = fmaxf(nm[rho], z);
-        ns[rho] = ns[rho] * exp2f(nm[rho] - mx) + exp2f(z - mx);
-        nm[rho] = mx;
-      } else {
+  const int ld = r + 1;
+  for (int64_t p0 = j0; p0 < j1; p0 += P) {
+    const int np = (int)min((int64_t)P, j1 - p0);
+    __syncthreads();  // the previous run's rows are done (and, first, qs / rm / ri are written)
+    for (int e = tid; e < np * r; e += blockDim.x) cs[(e / r) * ld + e % r] = CK[p0 * r + e];
+    __syncthreads();
+    if (tid < np) {
+      const int64_t j = p0 + tid;
+      const float* cj = cs + tid * ld;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {  // current rows: logits spilled, running (max, sum)
+        if (g < G) {
+          float z = 0.f;
+          for (int k = 0; k < r; ++k) z += qs[g * r + k] * cj[k];
+          w.spill[((int64_t)u * G + g) * w.Lc_cap + (j - s)] = z;
+          const float mx = fmaxf(nm[g], z);
+          ns[g] = ns[g] * exp2f(nm[g] - mx) + exp2f(z - mx);
+          nm[g] = mx;
+        }
+      }
+      float ps = 0.f;
+      for (int rho = G; rho < nrows; ++rho) {
+        float z = 0.f;
+        for (int k = 0; k < r; ++k) z += qs[rho * r + k] * cj[k];
         ps += exp2f(z - rm[rho]) * ri[rho];
       }
+      w.partial[(int64_t)u * w.Lc_cap + (j - s)] = ps;
     }
-    w.partial[(int64_t)u * w.Lc_cap + (j - s)] = ps;
   }
-  // new-row statistics: block reduction per row (fixed order)
-  float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
-  for (int g = 0; g < G; ++g) {
-    red[threadIdx.x * 2] = nm[g];
-    red[threadIdx.x * 2 + 1] = ns[g];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float m = -INFINITY, S = 0.f;
-      for (int t = 0; t < blockDim.x; ++t) {
-        const float m2 = red[2 * t], s2 = red[2 * t + 1];
-        if (s2 == 0.f) continue;
-        const float mx = fmaxf(m, m2);
-        S = (m == -INFINITY ? 0.f : S * exp2f(m - mx)) + s2 * exp2f(m2 - mx);
-        m = mx;
+  // current rows' (max, sum) over the block: waves by shuffles, then LDS
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < G) {
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(nm[g], o), s2 = __shfl_xor(ns[g], o);
+        ms_combine(nm[g], ns[g], m2, s2);
       }
-      tst[g * 2] = m;
-      tst[g * 2 + 1] = S;
+      if (lane == 0) {
+        red[(wv * 8 + g) * 2] = nm[g];
+        red[(wv * 8 + g) * 2 + 1] = ns[g];
+      }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = -INFINITY, S = 0.f;
+    for (int x = 0; x < 4; ++x) ms_combine(m, S, red[(x * 8 + tid) * 2], red[(x * 8 + tid) * 2 + 1]);
+    float* tst = w.tilestat + ((int64_t)u * w.nsplit + split) * G * 2;
+    tst[tid * 2] = m;
+    tst[tid * 2 + 1] = S;
   }
 }
 
@@ -1455,8 +1489,14 @@ hipError_t launch_score(const Dims& d, int U, const CachePtrs& c, const DecodeWs
   const float qscale = kLog2e / sqrtf((float)d.r);
   if (d.dtype == 0) {
     dim3 grid(w.nsplit, U);
-    const size_t lds = ((size_t)d.W * d.G * d.r + 2 * d.W * d.G + 512) * sizeof(float);
-    hipLaunchKernelGGL(k_score_f32, grid, dim3(256), lds, st, d, c, w, qscale);
+    // runs of P positions: up to 256 (one per thread), within 96 KB of rows
+    int P = (int)((96 * 1024 / sizeof(float)) / (d.r + 1));
+    P = P > 256 ? 256 : (P < 1 ? 1 : P);
+    const size_t lds = ((size_t)d.W * d.G * d.r + 2 * d.W * d.G + 64 + (size_t)P * (d.r + 1)) * sizeof(float);
+    static size_t done = 0;
+    hipError_t e = allow_lds(&k_score_f32, lds, &done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_score_f32, grid, dim3(256), lds, st, d, c, w, qscale, P);
     return hipGetLastError();
   }
   switch (d.r) {
@@ -1509,18 +1549,6 @@ __device__ __forceinline__ void wave_minmax_u(unsigned int& mn, unsigned int& mx
            min((unsigned int)__builtin_amdgcn_readlane((int)mn, 32), (unsigned int)__builtin_amdgcn_readlane((int)mn, 48)));
   mx = max(max((unsigned int)__builtin_amdgcn_readlane((int)mx, 0), (unsigned int)__builtin_amdgcn_readlane((int)mx, 16)),
            max((unsigned int)__builtin_amdgcn_readlane((int)mx, 32), (unsigned int)__builtin_amdgcn_readlane((int)mx, 48)));
-}
-
-__device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
-  if (!(s2 > 0.f)) return;
-  if (!(s > 0.f)) {
-    m = m2;
-    s = s2;
-    return;
-  }
-  const float mx = fmaxf(m, m2);
-  s = s * exp2f(m - mx) + s2 * exp2f(m2 - mx);
-  m = mx;
 }
 
 __global__ __launch_bounds__(256) void k_pool(Dims d, CachePtrs c, DecodeWs w,
