@@ -163,11 +163,15 @@ int kvlr_workspace_bytes(const kvlr_config* cfg, int op, int64_t n_units,
  *   eigvals_k, eigvals_v  device, optional (NULL = skip), [U][D'] fp32: all
  *             eigenvalues of S^T S, descending.
  *   sweeps    device, optional (NULL = skip), [U][2] int32: Jacobi sweeps
- *             the K and V eigensolves took to reach off(A)_F <= 1e-13 tr(A),
+ *             the K and V eigensolves took to reach off(A)_F <= tol tr(A),
  *             or -1 if they had not within cfg->eig_max_sweeps (the bases are
- *             then the current, unconverged iterate).  The call cannot
- *             return this as a status without synchronising; read it after
- *             the stream has reached the call.
+ *             then the current, unconverged iterate).  The eigensolve runs in
+ *             fp32 with tol = 1e-5 for bf16 storage and D' a multiple of 64
+ *             (>= 128): eigenvalues to ~1e-5 of the largest, far inside the
+ *             bf16 rounding of the stored basis; otherwise in fp64 with
+ *             tol = 1e-13.
+ *             The call cannot return this as a status without synchronising;
+ *             read it after the stream has reached the call.
  *   ws        device workspace of ws_bytes >= kvlr_workspace_bytes(BUILD).
  * Sample positions: floor(T'*num/den) most recent prompt positions plus
  * T' - that many evenly spaced over [s, L - recent); requires L >= s +

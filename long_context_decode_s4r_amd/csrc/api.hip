@@ -43,6 +43,11 @@ size_t elem_bytes(const kvlr_config* c) { return c->dtype == KVLR_BF16 ? 2 : 4; 
 bool rank_supported_bf16(int r) { return r == 32 || r == 64 || r == 128 || r == 192 || r == 256; }
 
 constexpr int kDefaultEigSweeps = 24;
+// convergence of the fp32 eigensolve (bf16 storage): off(A)_F <= tol tr(A)
+#ifndef KVLR_EIG_TOL_F32
+#define KVLR_EIG_TOL_F32 1e-5
+#endif
+constexpr double kEigTolF32 = KVLR_EIG_TOL_F32;
 
 Dims dims_of(const kvlr_config* c) {
   Dims d;
@@ -373,14 +378,37 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
   const int max_sweeps = cfg->eig_max_sweeps > 0 ? cfg->eig_max_sweeps : kDefaultEigSweeps;
   const double tol = 1e-13;
   int cur = 0;
+  if (d.dtype != 0 && bjac_supported(n)) {
+    // bf16 bases: the block Jacobi runs in fp32, whose accuracy (eigenvectors
+    // to ~1e-6) is far beyond the bf16 rounding of the stored basis (2^-9);
+    // A32 and V32 take the V buffers, the Q blocks A[1]
+    float* A32 = (float*)Vm[1];
+    float* V32 = (float*)Vm[0];
+    float* Q32 = (float*)A[1];
+    if ((he = launch_to_f32(n, nmat, A[0], A32, V32, st)) != hipSuccess) return hip_fail(he, "fp32 copy");
+    const int nb = n / 32;
+    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+      for (int rd = -1; rd < nb - 1; ++rd)
+        if ((he = launch_bjac_round<float>(n, nmat, A32, V32, Q32, frozen, rd, st)) != hipSuccess)
+          return hip_fail(he, "block jacobi round");
+      if ((he = launch_jacobi_check<float>(n, nmat, A32, part, frozen, final_buf, done, 0, sweep,
+                                           kEigTolF32, st)) != hipSuccess)
+        return hip_fail(he, "jacobi check");
+    }
+    if ((he = launch_extract<float>(d, nmat, A32, A32, V32, V32, frozen, final_buf, done, 0, cache->basis_k,
+                                    cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch, depth,
+                                    st)) != hipSuccess)
+      return hip_fail(he, "extract");
+    return ok();
+  }
   if (bjac_supported(n)) {
     // block Jacobi, in place in A[0] and V[0]; A[1] holds the rounds' Q blocks
     const int nb = n / 32;
     for (int sweep = 0; sweep < max_sweeps; ++sweep) {
       for (int rd = -1; rd < nb - 1; ++rd)  // the self round, then the cross rounds
-        if ((he = launch_bjac_round(n, nmat, A[0], Vm[0], A[1], frozen, rd, st)) != hipSuccess)
+        if ((he = launch_bjac_round<double>(n, nmat, A[0], Vm[0], A[1], frozen, rd, st)) != hipSuccess)
           return hip_fail(he, "block jacobi round");
-      if ((he = launch_jacobi_check(n, nmat, A[0], part, frozen, final_buf, done, 0, sweep, tol, st)) !=
+      if ((he = launch_jacobi_check<double>(n, nmat, A[0], part, frozen, final_buf, done, 0, sweep, tol, st)) !=
           hipSuccess)
         return hip_fail(he, "jacobi check");
     }
@@ -392,7 +420,7 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
           return hip_fail(he, "jacobi round");
         cur ^= 1;
       }
-      if ((he = launch_jacobi_check(n, nmat, A[cur], part, frozen, final_buf, done, cur, sweep, tol, st)) !=
+      if ((he = launch_jacobi_check<double>(n, nmat, A[cur], part, frozen, final_buf, done, cur, sweep, tol, st)) !=
           hipSuccess)
         return hip_fail(he, "jacobi check");
     }
@@ -401,11 +429,11 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
     if ((he = launch_jacobi_round(n, nmat, A[0], A[1], Vm[0], Vm[1], frozen, st)) != hipSuccess)
       return hip_fail(he, "jacobi round");
     cur = 1;
-    if ((he = launch_jacobi_check(n, nmat, A[cur], part, frozen, final_buf, done, cur, 0, tol, st)) !=
+    if ((he = launch_jacobi_check<double>(n, nmat, A[cur], part, frozen, final_buf, done, cur, 0, tol, st)) !=
         hipSuccess)
       return hip_fail(he, "jacobi check");
   }
-  if ((he = launch_extract(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, done, cur,
+  if ((he = launch_extract<double>(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, done, cur,
                            cache->basis_k, cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch,
                            depth, st)) != hipSuccess)
     return hip_fail(he, "extract");

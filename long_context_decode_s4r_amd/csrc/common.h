@@ -198,20 +198,25 @@ hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_d
 // schedule pairs); Qbuf holds bjac_q_bytes(n, nmat)
 bool bjac_supported(int n);
 size_t bjac_q_bytes(int n, int nmat);
-hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,
-                             int k, hipStream_t st);
+// (T = double, or float for the fp32 eigensolve of bf16 storage)
+template <typename T>
+hipError_t launch_bjac_round(int n, int nmat, T* A, T* V, T* Qbuf, const int* frozen, int k,
+                             hipStream_t st);
+// the Gram matrices rounded to fp32 and V32 = I (start of the fp32 eigensolve)
+hipError_t launch_to_f32(int n, int nmat, const double* A64, float* A32, float* V32, hipStream_t st);
 // convergence bookkeeping of the eigensolves, per matrix: frozen (converged,
 // later rounds skip it), final_buf (buffer holding its result, scalar path),
 // done_sweeps (sweep count at convergence, 0 = not yet)
 hipError_t launch_jacobi_init(int nmat, int* frozen, int* final_buf, int* done_sweeps, hipStream_t st);
-hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
+template <typename T>
+hipError_t launch_jacobi_check(int n, int nmat, const T* A, double* part, int* frozen,
                                int* final_buf, int* done_sweeps, int cur, int sweep, double tol,
                                hipStream_t st);
-hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
-                          const double* V0, const double* V1, const int* frozen,
-                          const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
-                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps, int batch,
-                          int depth, hipStream_t st);
+template <typename S>
+hipError_t launch_extract(const Dims& d, int nmat, const S* A0, const S* A1, const S* V0, const S* V1,
+                          const int* frozen, const int* final_buf, const int* done_sweeps, int cur,
+                          void* basis_k, void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
+                          int batch, int depth, hipStream_t st);
 // bases shared over windows of `depth` layers: Grams summed into each
 // window's first layer, the other layers' matrices frozen
 hipError_t launch_gram_window_sum(int n, int n_layers, int batch, int depth, double* A, int* frozen,

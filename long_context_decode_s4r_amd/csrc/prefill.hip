@@ -289,17 +289,18 @@ hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_d
 // then one thread per matrix sums them in a fixed order
 constexpr int kJacRowsPerBlock = 16;
 
-__global__ __launch_bounds__(256) void k_offnorm(const double* __restrict__ A,
+template <typename T>
+__global__ __launch_bounds__(256) void k_offnorm(const T* __restrict__ A,
                                                  const int* __restrict__ frozen,
                                                  double* __restrict__ part, int n, int nchunk) {
   const int m = blockIdx.y;
   if (frozen[m]) return;
-  const double* Am = A + (int64_t)m * n * n;
+  const T* Am = A + (int64_t)m * n * n;
   const int r0 = blockIdx.x * kJacRowsPerBlock;
   double off = 0.0, tr = 0.0;
   for (int r = r0; r < min(r0 + kJacRowsPerBlock, n); ++r) {
     for (int c = threadIdx.x; c < n; c += blockDim.x) {
-      const double x = Am[(int64_t)r * n + c];
+      const double x = (double)Am[(int64_t)r * n + c];
       if (c == r)
         tr += x;
       else
@@ -359,17 +360,22 @@ hipError_t launch_jacobi_init(int nmat, int* frozen, int* final_buf, int* done_s
   return hipGetLastError();
 }
 
-hipError_t launch_jacobi_check(int n, int nmat, const double* A, double* part, int* frozen,
+template <typename T>
+hipError_t launch_jacobi_check(int n, int nmat, const T* A, double* part, int* frozen,
                                int* final_buf, int* done_sweeps, int cur, int sweep, double tol,
                                hipStream_t st) {
   const int nchunk = (n + kJacRowsPerBlock - 1) / kJacRowsPerBlock;
-  hipLaunchKernelGGL(k_offnorm, dim3(nchunk, nmat), dim3(256), 0, st, A, frozen, part, n, nchunk);
+  hipLaunchKernelGGL(k_offnorm<T>, dim3(nchunk, nmat), dim3(256), 0, st, A, frozen, part, n, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_jacobi_check, dim3(1), dim3(256), 0, st, part, frozen, final_buf, done_sweeps,
                      nmat, nchunk, cur, sweep, tol);
   return hipGetLastError();
 }
+template hipError_t launch_jacobi_check<double>(int, int, const double*, double*, int*, int*, int*,
+                                                int, int, double, hipStream_t);
+template hipError_t launch_jacobi_check<float>(int, int, const float*, double*, int*, int*, int*,
+                                               int, int, double, hipStream_t);
 
 // --------------------------------------------------------------------------
 // 3b. block Jacobi (two-sided, fp64), for n a multiple of 64 and >= 128.
@@ -415,8 +421,13 @@ __device__ __forceinline__ int bj_index(int li, int I, int J) {
 // 32 + (a + kr) % 32.  Thread t updates 2x2 block t of S and two entry pairs
 // of Q.
 constexpr int kBJEigThreads = 1024;
-__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __restrict__ Aall,
-                                                            double* __restrict__ Qall,
+__device__ __forceinline__ double bj_sqrt(double x) { return sqrt(x); }
+__device__ __forceinline__ float bj_sqrt(float x) { return sqrtf(x); }
+__device__ __forceinline__ double bj_rsqrt(double x) { return rsqrt(x); }
+__device__ __forceinline__ float bj_rsqrt(float x) { return rsqrtf(x); }
+template <typename T>
+__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const T* __restrict__ Aall,
+                                                            T* __restrict__ Qall,
                                                             const int* __restrict__ frozen, int n,
                                                             int k) {
   const int m = blockIdx.y;
@@ -427,15 +438,15 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   const int nb = n / kBJ, p = blockIdx.x, tid = threadIdx.x;
   int I, J;
   bj_pair(p, k, nb, &I, &J);
-  const double* A = Aall + (int64_t)m * n * n;
-  __shared__ double S[kBJ2][kBJ2 + 1];
-  __shared__ double Q[kBJ2][kBJ2 + 1];
-  __shared__ double rc[NP], rs[NP], rt[NP];
+  const T* A = Aall + (int64_t)m * n * n;
+  __shared__ T S[kBJ2][kBJ2 + 1];
+  __shared__ T Q[kBJ2][kBJ2 + 1];
+  __shared__ T rc[NP], rs[NP], rt[NP];
   __shared__ uint8_t pi[kBJ][NP], qi[kBJ][NP];
   for (int e = tid; e < kBJ2 * kBJ2; e += NT) {
     const int i = e / kBJ2, j = e % kBJ2;
     S[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I, J)];
-    Q[i][j] = i == j ? 1.0 : 0.0;
+    Q[i][j] = i == j ? T(1) : T(0);
   }
   const int nround = k < 0 ? kBJ - 1 : kBJ;
   for (int e = tid; e < kBJ * NP; e += NT) {
@@ -461,24 +472,24 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
   // kr) % 32] for its two rows, and after each round takes y from the lane of
   // pair qb + 1 (mod 32) of the same half-wave; self rounds use Q in LDS
   const bool qreg = k >= 0;
-  double x0 = qrow == qb ? 1.0 : 0.0, y0 = 0.0, x1 = 0.0, y1 = x0;
+  T x0 = qrow == qb ? T(1) : T(0), y0 = T(0), x1 = T(0), y1 = x0;
   const int ysrc = (tid & 32) | ((tid + 1) & 31);
   {
     for (int kr = 0; kr < nround; ++kr) {
       if (tid < NP) {
         const int ip = qreg ? tid : pi[kr][tid], iq = qreg ? kBJ + ((tid + kr) & (kBJ - 1)) : qi[kr][tid];
-        const double app = S[ip][ip], aqq = S[iq][iq], apq = S[ip][iq];
-        double c = 1.0, sn = 0.0, t = 0.0;
-        if (apq != 0.0) {
+        const T app = S[ip][ip], aqq = S[iq][iq], apq = S[ip][iq];
+        T c = T(1), sn = T(0), t = T(0);
+        if (apq != T(0)) {
           // the rotation above with tau = d / (2 apq) multiplied through by
           // |2 apq|: t = sgn(tau) 2|apq| / (|d| + sqrt(d^2 + 4 apq^2)), one
           // square root and one division (the entries are Gram sums of unit
           // vectors, far from overflow)
-          const double d = aqq - app, a2 = 2.0 * fabs(apq);
-          const bool neg = (d < 0.0) != (apq < 0.0) && d != 0.0;
-          t = a2 / (fabs(d) + sqrt(d * d + a2 * a2));
+          const T d = aqq - app, a2 = T(2) * fabs(apq);
+          const bool neg = (d < T(0)) != (apq < T(0)) && d != T(0);
+          t = a2 / (fabs(d) + bj_sqrt(d * d + a2 * a2));
           t = neg ? -t : t;
-          c = rsqrt(1.0 + t * t);
+          c = bj_rsqrt(T(1) + t * t);
           sn = t * c;
         }
         rc[tid] = c;
@@ -504,32 +515,32 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
         pq = pi[kr][qb];
         qq = qi[kr][qb];
       }
-      const double m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
-      const double cq = rc[qb], sq = rs[qb];
+      const T m00 = S[pa][pb], m01 = S[pa][qbb], m10 = S[qa][pb], m11 = S[qa][qbb];
+      const T cq = rc[qb], sq = rs[qb];
       if (a == b) {
-        const double ta = rt[a];
+        const T ta = rt[a];
         S[pa][pa] = m00 - ta * m01;
         S[qa][qa] = m11 + ta * m01;
-        S[pa][qa] = 0.0;
-        S[qa][pa] = 0.0;
+        S[pa][qa] = T(0);
+        S[qa][pa] = T(0);
       } else {
-        const double ca = rc[a], sa = rs[a], cb = rc[b], sb = rs[b];
-        const double r00 = ca * m00 - sa * m10, r01 = ca * m01 - sa * m11;
-        const double r10 = sa * m00 + ca * m10, r11 = sa * m01 + ca * m11;
+        const T ca = rc[a], sa = rs[a], cb = rc[b], sb = rs[b];
+        const T r00 = ca * m00 - sa * m10, r01 = ca * m01 - sa * m11;
+        const T r10 = sa * m00 + ca * m10, r11 = sa * m01 + ca * m11;
         S[pa][pb] = cb * r00 - sb * r01;
         S[pa][qbb] = sb * r00 + cb * r01;
         S[qa][pb] = cb * r10 - sb * r11;
         S[qa][qbb] = sb * r10 + cb * r11;
       }
       if (qreg) {
-        const double n0 = sq * x0 + cq * y0, n1 = sq * x1 + cq * y1;
+        const T n0 = sq * x0 + cq * y0, n1 = sq * x1 + cq * y1;
         x0 = cq * x0 - sq * y0;
         x1 = cq * x1 - sq * y1;
         y0 = kr + 1 < nround ? __shfl(n0, ysrc) : n0;
         y1 = kr + 1 < nround ? __shfl(n1, ysrc) : n1;
       } else {
-        const double v00 = Q[qrow][pq], v01 = Q[qrow][qq];
-        const double v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
+        const T v00 = Q[qrow][pq], v01 = Q[qrow][qq];
+        const T v10 = Q[qrow + NP][pq], v11 = Q[qrow + NP][qq];
         Q[qrow][pq] = cq * v00 - sq * v01;
         Q[qrow][qq] = sq * v00 + cq * v01;
         Q[qrow + NP][pq] = cq * v10 - sq * v11;
@@ -538,7 +549,7 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
       __syncthreads();
     }
   }
-  double* Qo = Qall + ((int64_t)m * (nb / 2) + p) * kBJ2 * kBJ2;
+  T* Qo = Qall + ((int64_t)m * (nb / 2) + p) * kBJ2 * kBJ2;
   if (qreg) {
     const int yc = kBJ + ((qb + nround - 1) & (kBJ - 1));
     Qo[qrow * kBJ2 + qb] = x0;
@@ -560,22 +571,44 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const double* __rest
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kBJLd = kBJ2 + 1;
 
-__global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
-                                                    double* __restrict__ Vall,
-                                                    const double* __restrict__ Qall,
+// the 16x16x4 MFMA of the scalar type: fp64 (D element v of lane l at row
+// l / 16 + 4 v) or fp32 (row 4 (l / 16) + v); operands as above for both
+template <typename T> struct BjMfma;
+template <> struct BjMfma<double> {
+  typedef f64x4 acc;
+  typedef double2 pair;
+  static __device__ __forceinline__ acc mma(double a, double b, acc c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int r4, int v) { return r4 + 4 * v; }
+};
+template <> struct BjMfma<float> {
+  typedef f32x4 acc;
+  typedef float2 pair;
+  static __device__ __forceinline__ acc mma(float a, float b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int row(int r4, int v) { return 4 * r4 + v; }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
+                                                    T* __restrict__ Vall,
+                                                    const T* __restrict__ Qall,
                                                     const int* __restrict__ frozen, int n, int k) {
+  typedef BjMfma<T> Mf;
   const int m = blockIdx.y;
   if (frozen[m]) return;
   const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x;
   const int l = tid & 63, w = tid >> 6, qi = w >> 1, qj = w & 1, c16 = l & 15, r4 = l >> 4;
   const int tile = blockIdx.x;
   constexpr int NKS = kBJ2 / 4;  // MFMA k-steps
-  __shared__ __attribute__((aligned(16))) double X[kBJ2][kBJLd];  // the tile (V: transposed)
-  const double* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
-  f64x4 acc[2][2];
+  __shared__ __attribute__((aligned(16))) T X[kBJ2][kBJLd];  // the tile (V: transposed)
+  const T* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
+  typename Mf::acc acc[2][2];
   // the Q factors' MFMA operands come straight from memory (L2) into
   // registers: lane (r4, c16) of k-step ks needs Q[4 ks + r4][col + c16]
-  auto qfrag = [&](const double* Qp, int col, double (&f0)[NKS], double (&f1)[NKS]) {
+  auto qfrag = [&](const T* Qp, int col, T (&f0)[NKS], T (&f1)[NKS]) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       f0[ks] = Qp[(4 * ks + r4) * kBJ2 + col + c16];
@@ -586,54 +619,54 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = typename Mf::acc{T(0), T(0), T(0), T(0)};
   };
   // acc[ti][tj][v] = sum_k A'[k][32 qi + 16 ti + r4 + 4 v] B'[k][32 qj + 16 tj + c16]
   // with A' from registers (a0, a1) and B' = X, or A' = X and B' from registers
-  auto gemm_ra = [&](const double (&a0)[NKS], const double (&a1)[NKS]) {
+  auto gemm_ra = [&](const T (&a0)[NKS], const T (&a1)[NKS]) {
     zero();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kr = 4 * ks + r4;
-      const double b0 = X[kr][32 * qj + c16], b1 = X[kr][32 * qj + 16 + c16];
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[ks], b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[ks], b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[ks], b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[ks], b1, acc[1][1], 0, 0, 0);
+      const T b0 = X[kr][32 * qj + c16], b1 = X[kr][32 * qj + 16 + c16];
+      acc[0][0] = Mf::mma(a0[ks], b0, acc[0][0]);
+      acc[0][1] = Mf::mma(a0[ks], b1, acc[0][1]);
+      acc[1][0] = Mf::mma(a1[ks], b0, acc[1][0]);
+      acc[1][1] = Mf::mma(a1[ks], b1, acc[1][1]);
     }
   };
-  auto gemm_rb = [&](const double (&b0)[NKS], const double (&b1)[NKS]) {
+  auto gemm_rb = [&](const T (&b0)[NKS], const T (&b1)[NKS]) {
     zero();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int kr = 4 * ks + r4;
-      const double a0 = X[kr][32 * qi + c16], a1 = X[kr][32 * qi + 16 + c16];
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0[ks], acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1[ks], acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0[ks], acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1[ks], acc[1][1], 0, 0, 0);
+      const T a0 = X[kr][32 * qi + c16], a1 = X[kr][32 * qi + 16 + c16];
+      acc[0][0] = Mf::mma(a0, b0[ks], acc[0][0]);
+      acc[0][1] = Mf::mma(a0, b1[ks], acc[0][1]);
+      acc[1][0] = Mf::mma(a1, b0[ks], acc[1][0]);
+      acc[1][1] = Mf::mma(a1, b1[ks], acc[1][1]);
     }
   };
   // output element (ti, tj, v) of this lane: row orow(ti, v), column ocol(tj)
-  auto orow = [&](int ti, int v) { return 32 * qi + 16 * ti + r4 + 4 * v; };
+  auto orow = [&](int ti, int v) { return 32 * qi + 16 * ti + Mf::row(r4, v); };
   auto ocol = [&](int tj) { return 32 * qj + 16 * tj + c16; };
   if (tile < np * np) {
     const int P = tile / np, P2 = tile % np;
     int I, J, I2, J2;
     bj_pair(P, k, nb, &I, &J);
     bj_pair(P2, k, nb, &I2, &J2);
-    double* A = Aall + (int64_t)m * n * n;
-    double qa0[NKS], qa1[NKS];
+    T* A = Aall + (int64_t)m * n * n;
+    T qa0[NKS], qa1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qi, qa0, qa1);  // A' = Q_P (rows of Q_P^T)
     for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
-      const double2 x = *reinterpret_cast<const double2*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
+      const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
       X[i][j] = x.x;
       X[i][j + 1] = x.y;
     }
     __syncthreads();
     gemm_ra(qa0, qa1);  // T = Q_P^T X
-    double qb0[NKS], qb1[NKS];
+    T qb0[NKS], qb1[NKS];
     qfrag(Qm + (int64_t)P2 * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P2
     __syncthreads();
 #pragma unroll
@@ -655,12 +688,12 @@ __global__ __launch_bounds__(256) void k_bjac_apply(double* __restrict__ Aall,
     const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
     int I, J;
     bj_pair(P, k, nb, &I, &J);
-    double* V = Vall + (int64_t)m * n * n;
-    double qb0[NKS], qb1[NKS];
+    T* V = Vall + (int64_t)m * n * n;
+    T qb0[NKS], qb1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P
     for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
-      const double2 x = *reinterpret_cast<const double2*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
+      const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
       X[j][i] = x.x;
       X[j + 1][i] = x.y;
     }
@@ -680,14 +713,36 @@ bool bjac_supported(int n) { return n >= 2 * kBJ2 && n % kBJ2 == 0; }
 
 size_t bjac_q_bytes(int n, int nmat) { return (size_t)nmat * (n / kBJ2) * kBJ2 * kBJ2 * sizeof(double); }
 
-hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf, const int* frozen,
-                             int k, hipStream_t st) {
+template <typename T>
+hipError_t launch_bjac_round(int n, int nmat, T* A, T* V, T* Qbuf, const int* frozen, int k,
+                             hipStream_t st) {
   const int nb = n / kBJ, np = nb / 2;
-  hipLaunchKernelGGL(k_bjac_eig, dim3(np, nmat), dim3(kBJEigThreads), 0, st, A, Qbuf, frozen, n, k);
+  hipLaunchKernelGGL(k_bjac_eig<T>, dim3(np, nmat), dim3(kBJEigThreads), 0, st, A, Qbuf, frozen, n, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bjac_apply, dim3(np * np + (n / kBJ2) * np, nmat), dim3(256), 0, st, A, V, Qbuf,
+  hipLaunchKernelGGL(k_bjac_apply<T>, dim3(np * np + (n / kBJ2) * np, nmat), dim3(256), 0, st, A, V, Qbuf,
                      frozen, n, k);
+  return hipGetLastError();
+}
+template hipError_t launch_bjac_round<double>(int, int, double*, double*, double*, const int*, int,
+                                              hipStream_t);
+template hipError_t launch_bjac_round<float>(int, int, float*, float*, float*, const int*, int,
+                                             hipStream_t);
+
+// the Gram matrices rounded to fp32 (A32) and V32 = I: the start of the fp32
+// eigensolve
+__global__ void k_to_f32(const double* __restrict__ A64, float* __restrict__ A32,
+                         float* __restrict__ V32, int D) {
+  const int m = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)D * D) return;
+  A32[(int64_t)m * D * D + e] = (float)A64[(int64_t)m * D * D + e];
+  V32[(int64_t)m * D * D + e] = (e / D == e % D) ? 1.f : 0.f;
+}
+
+hipError_t launch_to_f32(int n, int nmat, const double* A64, float* A32, float* V32, hipStream_t st) {
+  const int64_t n2 = (int64_t)n * n;
+  hipLaunchKernelGGL(k_to_f32, dim3((unsigned)((n2 + 255) / 256), nmat), dim3(256), 0, st, A64, A32, V32, n);
   return hipGetLastError();
 }
 
@@ -695,11 +750,11 @@ hipError_t launch_bjac_round(int n, int nmat, double* A, double* V, double* Qbuf
 // 4. eigenvalues descending (bitonic sort of (lambda, slot) in LDS), basis =
 //    the first r eigenvector columns, rounded to storage.
 // --------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
-                                                  const double* __restrict__ A1,
-                                                  const double* __restrict__ V0,
-                                                  const double* __restrict__ V1,
+template <typename T, typename S>
+__global__ __launch_bounds__(1024) void k_extract(const S* __restrict__ A0,
+                                                  const S* __restrict__ A1,
+                                                  const S* __restrict__ V0,
+                                                  const S* __restrict__ V1,
                                                   const int* __restrict__ frozen,
                                                   const int* __restrict__ final_buf,
                                                   const int* __restrict__ done_sweeps, int cur,
@@ -716,15 +771,15 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
   const int layer = u / batch, seq = u % batch;
   const int ms = 2 * ((layer - layer % depth) * batch + seq) + kind;
   const int buf = frozen[ms] ? final_buf[ms] : cur;
-  const double* A = (buf ? A1 : A0) + (int64_t)ms * n * n;
-  const double* Vm = (buf ? V1 : V0) + (int64_t)ms * n * n;
+  const S* A = (buf ? A1 : A0) + (int64_t)ms * n * n;
+  const S* Vm = (buf ? V1 : V0) + (int64_t)ms * n * n;
   if (sweeps && threadIdx.x == 0) sweeps[m] = done_sweeps[ms] > 0 ? done_sweeps[ms] : -1;
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
   double* key = reinterpret_cast<double*>(smem_raw);
   int* idx = reinterpret_cast<int*>(key + np2);
   for (int i = threadIdx.x; i < np2; i += blockDim.x) {
-    key[i] = i < n ? A[(int64_t)i * n + i] : -INFINITY;
+    key[i] = i < n ? (double)A[(int64_t)i * n + i] : -INFINITY;
     idx[i] = i;
   }
   __syncthreads();
@@ -754,10 +809,10 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
   if (eig)
     for (int i = threadIdx.x; i < n; i += blockDim.x) eig[(int64_t)u * n + i] = (float)key[i];
   T* B = (kind ? BV : BK) + (int64_t)u * n * r;
-  // eigenvector entries rounded once from fp64 to the storage type
+  // eigenvector entries rounded once to the storage type
   for (int64_t e = threadIdx.x; e < (int64_t)n * r; e += blockDim.x) {
     const int i = (int)(e / r), c = (int)(e % r);
-    const double x = Vm[(int64_t)i * n + idx[c]];
+    const double x = (double)Vm[(int64_t)i * n + idx[c]];
     if constexpr (sizeof(T) == 2)
       B[e] = d2bf(x);
     else
@@ -765,24 +820,30 @@ __global__ __launch_bounds__(1024) void k_extract(const double* __restrict__ A0,
   }
 }
 
-hipError_t launch_extract(const Dims& d, int nmat, const double* A0, const double* A1,
-                          const double* V0, const double* V1, const int* frozen,
-                          const int* final_buf, const int* done_sweeps, int cur, void* basis_k,
-                          void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps, int batch,
-                          int depth, hipStream_t st) {
+template <typename S>
+hipError_t launch_extract(const Dims& d, int nmat, const S* A0, const S* A1, const S* V0, const S* V1,
+                          const int* frozen, const int* final_buf, const int* done_sweeps, int cur,
+                          void* basis_k, void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
+                          int batch, int depth, hipStream_t st) {
   int np2 = 1;
   while (np2 < d.D) np2 <<= 1;
   const size_t lds = (size_t)np2 * (sizeof(double) + sizeof(int));
   if (d.dtype == 0)
-    hipLaunchKernelGGL(k_extract<float>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
+    hipLaunchKernelGGL((k_extract<float, S>), dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
                        final_buf, done_sweeps, cur, d.D, d.r, d.rv, (float*)basis_k,
                        (float*)basis_v, eig_k, eig_v, sweeps, batch, depth);
   else
-    hipLaunchKernelGGL(k_extract<uint16_t>, dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
+    hipLaunchKernelGGL((k_extract<uint16_t, S>), dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
                        frozen, final_buf, done_sweeps, cur, d.D, d.r, d.rv, (uint16_t*)basis_k,
                        (uint16_t*)basis_v, eig_k, eig_v, sweeps, batch, depth);
   return hipGetLastError();
 }
+template hipError_t launch_extract<double>(const Dims&, int, const double*, const double*, const double*,
+                                           const double*, const int*, const int*, const int*, int, void*,
+                                           void*, float*, float*, int32_t*, int, int, hipStream_t);
+template hipError_t launch_extract<float>(const Dims&, int, const float*, const float*, const float*,
+                                          const float*, const int*, const int*, const int*, int, void*,
+                                          void*, float*, float*, int32_t*, int, int, hipStream_t);
 
 // --------------------------------------------------------------------------
 // 5. projection C[j] = rnd(X[j] . B) for j in [s, L)
