@@ -93,7 +93,8 @@ typedef struct kvlr_config {
   int32_t pool_kernel;        /* kappa: odd max-pool width, 1 = no pooling     */
   int32_t local_window;       /* kvlr_local_window                             */
   int32_t eig_max_sweeps;     /* Jacobi sweeps enqueued by kvlr_build_bases;
-                                 0 = the default (24)                          */
+                                 0 = the default (16 for the fp32
+                                 eigensolve of bf16 storage, else 24)          */
   int32_t dtype;              /* kvlr_dtype of the storage tensors             */
 } kvlr_config;
 

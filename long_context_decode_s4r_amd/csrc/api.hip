@@ -42,7 +42,8 @@ size_t elem_bytes(const kvlr_config* c) { return c->dtype == KVLR_BF16 ? 2 : 4; 
 
 bool rank_supported_bf16(int r) { return r == 32 || r == 64 || r == 128 || r == 192 || r == 256; }
 
-constexpr int kDefaultEigSweeps = 24;
+constexpr int kDefaultEigSweeps = 24;     // fp64 eigensolve
+constexpr int kDefaultEigSweepsF32 = 16;  // fp32 eigensolve (converges in 9-10 on every workload here)
 // convergence of the fp32 eigensolve (bf16 storage): off(A)_F <= tol tr(A)
 #ifndef KVLR_EIG_TOL_F32
 #define KVLR_EIG_TOL_F32 1e-5
@@ -379,6 +380,7 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
   const double tol = 1e-13;
   int cur = 0;
   if (d.dtype != 0 && bjac_supported(n)) {
+    const int max_sweeps32 = cfg->eig_max_sweeps > 0 ? cfg->eig_max_sweeps : kDefaultEigSweepsF32;
     // bf16 bases: the block Jacobi runs in fp32, whose accuracy (eigenvectors
     // to ~1e-6) is far beyond the bf16 rounding of the stored basis (2^-9);
     // A32 and V32 take the V buffers, the Q blocks A[1]
@@ -387,14 +389,26 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
     float* Q32 = (float*)A[1];
     if ((he = launch_to_f32(n, nmat, A[0], A32, V32, st)) != hipSuccess) return hip_fail(he, "fp32 copy");
     const int nb = n / 32;
-    for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-      for (int rd = -1; rd < nb - 1; ++rd)
-        if ((he = launch_bjac_round<float>(n, nmat, A32, V32, Q32, frozen, rd, st)) != hipSuccess)
+    // the rounds' Q blocks alternate between two buffers; V's update of a
+    // round runs in the next round's launch (the last one in a launch of its own)
+    const size_t qsz = (size_t)nmat * (n / 64) * 64 * 64;
+    float* Qb[2] = {Q32, Q32 + qsz};
+    int r_all = 0, kv = 0, vs = -1;  // rounds launched; the pending V round (kv of sweep vs)
+    for (int sweep = 0; sweep < max_sweeps32; ++sweep) {
+      for (int rd = -1; rd < nb - 1; ++rd, ++r_all) {
+        if ((he = launch_bjac_round_f32(n, nmat, A32, V32, Qb[r_all & 1], Qb[(r_all + 1) & 1], frozen, done,
+                                        rd, 1, kv, vs, st)) != hipSuccess)
           return hip_fail(he, "block jacobi round");
+        kv = rd;
+        vs = sweep;
+      }
       if ((he = launch_jacobi_check<float>(n, nmat, A32, part, frozen, final_buf, done, 0, sweep,
                                            kEigTolF32, st)) != hipSuccess)
         return hip_fail(he, "jacobi check");
     }
+    if ((he = launch_bjac_round_f32(n, nmat, A32, V32, Qb[r_all & 1], Qb[(r_all + 1) & 1], frozen, done, 0, 0,
+                                    kv, vs, st)) != hipSuccess)
+      return hip_fail(he, "block jacobi V update");
     if ((he = launch_extract<float>(d, nmat, A32, A32, V32, V32, frozen, final_buf, done, 0, cache->basis_k,
                                     cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch, depth,
                                     st)) != hipSuccess)

@@ -202,6 +202,12 @@ size_t bjac_q_bytes(int n, int nmat);
 template <typename T>
 hipError_t launch_bjac_round(int n, int nmat, T* A, T* V, T* Qbuf, const int* frozen, int k,
                              hipStream_t st);
+// fp32 eigensolve: round k's subproblems (into Q; skipped when !do_eig) with V's
+// update of round kv of sweep vs (vs < 0: none) from Qv in one launch, then
+// A's update of round k; Q and Qv each hold bjac_q_bytes(n, nmat) / 2
+hipError_t launch_bjac_round_f32(int n, int nmat, float* A, float* V, float* Q, const float* Qv,
+                                 const int* frozen, const int* done_sweeps, int k, int do_eig, int kv,
+                                 int vs, hipStream_t st);
 // the Gram matrices rounded to fp32 and V32 = I (start of the fp32 eigensolve)
 hipError_t launch_to_f32(int n, int nmat, const double* A64, float* A32, float* V32, hipStream_t st);
 // convergence bookkeeping of the eigensolves, per matrix: frozen (converged,

@@ -425,17 +425,14 @@ __device__ __forceinline__ double bj_sqrt(double x) { return sqrt(x); }
 __device__ __forceinline__ float bj_sqrt(float x) { return sqrtf(x); }
 __device__ __forceinline__ double bj_rsqrt(double x) { return rsqrt(x); }
 __device__ __forceinline__ float bj_rsqrt(float x) { return rsqrtf(x); }
+// subproblem p of matrix m (called by all kBJEigThreads threads of a block)
 template <typename T>
-__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const T* __restrict__ Aall,
-                                                            T* __restrict__ Qall,
-                                                            const int* __restrict__ frozen, int n,
-                                                            int k) {
-  const int m = blockIdx.y;
-  if (frozen[m]) return;
+__device__ __forceinline__ void bjac_eig_block(const T* __restrict__ Aall, T* __restrict__ Qall, int n,
+                                               int k, int m, int p) {
   constexpr int NT = kBJEigThreads, NP = kBJ2 / 2;
   static_assert(NP * NP == NT && kBJ2 * NP == 2 * NT, "one 2x2 block and two Q pairs per thread");
   static_assert((kBJ & (kBJ - 1)) == 0, "cross-round pairs use a power-of-two block");
-  const int nb = n / kBJ, p = blockIdx.x, tid = threadIdx.x;
+  const int nb = n / kBJ, tid = threadIdx.x;
   int I, J;
   bj_pair(p, k, nb, &I, &J);
   const T* A = Aall + (int64_t)m * n * n;
@@ -561,6 +558,17 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const T* __restrict_
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eig(const T* __restrict__ Aall,
+                                                            T* __restrict__ Qall,
+                                                            const int* __restrict__ frozen, int n,
+                                                            int k) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  bjac_eig_block<T>(Aall, Qall, n, k, m, blockIdx.x);
+}
+
+
 // grid ((nb/2)^2 + (n/64)(nb/2), nmat), 256 threads: the in-place update of
 // A's tiles (P, P') and V's tiles (row tile R, pair P) of outer round k.
 // The 64 x 64 x 64 products run on fp64 MFMA 16x16x4 (lane l: A[l % 16][l / 16],
@@ -591,19 +599,17 @@ template <> struct BjMfma<float> {
   static __device__ __forceinline__ int row(int r4, int v) { return 4 * r4 + v; }
 };
 
+// tile `tile` of matrix m, by the 256 threads tid = 0..255 of a group that
+// owns the LDS tile X (the group's block barriers: A tiles 3, V tiles 1;
+// `active` false runs the barriers only)
 template <typename T>
-__global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
-                                                    T* __restrict__ Vall,
-                                                    const T* __restrict__ Qall,
-                                                    const int* __restrict__ frozen, int n, int k) {
+__device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restrict__ Vall,
+                                                const T* __restrict__ Qall, int n, int k, int m,
+                                                int tile, int tid, bool active, T (*X)[kBJLd]) {
   typedef BjMfma<T> Mf;
-  const int m = blockIdx.y;
-  if (frozen[m]) return;
-  const int nb = n / kBJ, np = nb / 2, tid = threadIdx.x;
+  const int nb = n / kBJ, np = nb / 2;
   const int l = tid & 63, w = tid >> 6, qi = w >> 1, qj = w & 1, c16 = l & 15, r4 = l >> 4;
-  const int tile = blockIdx.x;
   constexpr int NKS = kBJ2 / 4;  // MFMA k-steps
-  __shared__ __attribute__((aligned(16))) T X[kBJ2][kBJLd];  // the tile (V: transposed)
   const T* Qm = Qall + (int64_t)m * np * kBJ2 * kBJ2;
   typename Mf::acc acc[2][2];
   // the Q factors' MFMA operands come straight from memory (L2) into
@@ -611,8 +617,8 @@ __global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
   auto qfrag = [&](const T* Qp, int col, T (&f0)[NKS], T (&f1)[NKS]) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      f0[ks] = Qp[(4 * ks + r4) * kBJ2 + col + c16];
-      f1[ks] = Qp[(4 * ks + r4) * kBJ2 + col + 16 + c16];
+      f0[ks] = active ? Qp[(4 * ks + r4) * kBJ2 + col + c16] : T(0);
+      f1[ks] = active ? Qp[(4 * ks + r4) * kBJ2 + col + 16 + c16] : T(0);
     }
   };
   auto zero = [&]() {
@@ -658,7 +664,7 @@ __global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
     T* A = Aall + (int64_t)m * n * n;
     T qa0[NKS], qa1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qi, qa0, qa1);  // A' = Q_P (rows of Q_P^T)
-    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
+    for (int e = tid; active && e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
       const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
       X[i][j] = x.x;
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
       for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          A[(int64_t)bj_index(orow(ti, v), I, J) * n + bj_index(ocol(tj), I2, J2)] = acc[ti][tj][v];
+          if (active) A[(int64_t)bj_index(orow(ti, v), I, J) * n + bj_index(ocol(tj), I2, J2)] = acc[ti][tj][v];
   } else {
     const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
     int I, J;
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
     T* V = Vall + (int64_t)m * n * n;
     T qb0[NKS], qb1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P
-    for (int e = tid; e < kBJ2 * kBJ2 / 2; e += 256) {
+    for (int e = tid; active && e < kBJ2 * kBJ2 / 2; e += 256) {
       const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
       const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
       X[j][i] = x.x;
@@ -705,8 +711,47 @@ __global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
       for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          V[(int64_t)(kBJ2 * R + orow(ti, v)) * n + bj_index(ocol(tj), I, J)] = acc[ti][tj][v];
+          if (active) V[(int64_t)(kBJ2 * R + orow(ti, v)) * n + bj_index(ocol(tj), I, J)] = acc[ti][tj][v];
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_bjac_apply(T* __restrict__ Aall,
+                                                    T* __restrict__ Vall,
+                                                    const T* __restrict__ Qall,
+                                                    const int* __restrict__ frozen, int n, int k) {
+  const int m = blockIdx.y;
+  if (frozen[m]) return;
+  __shared__ __attribute__((aligned(16))) T X[kBJ2][kBJLd];  // the tile (V: transposed)
+  bjac_apply_tile<T>(Aall, Vall, Qall, n, k, m, blockIdx.x, threadIdx.x, true, X);
+}
+
+// fp32 eigensolve: round k's subproblems (blocks [0, nb/2), when do_eig) and,
+// in the same launch, V's update of the previous round kv with its Q blocks
+// Qv (blocks past nb/2, four V tiles each): the V update is not on the path
+// to the next round, so it runs on the CUs the subproblems leave idle.  The
+// V round belongs to sweep vs (-1: none) and runs for a matrix that was
+// still being solved in that sweep (not frozen, or frozen by that sweep's
+// check).
+template <typename T>
+__global__ __launch_bounds__(kBJEigThreads) void k_bjac_eigv(T* __restrict__ Aall, T* __restrict__ Qall,
+                                                             T* __restrict__ Vall, const T* __restrict__ Qv,
+                                                             const int* __restrict__ frozen,
+                                                             const int* __restrict__ done_sweeps, int n,
+                                                             int k, int do_eig, int kv, int vs) {
+  const int m = blockIdx.y, np = n / kBJ2;
+  if ((int)blockIdx.x < np) {
+    if (!do_eig || frozen[m]) return;
+    bjac_eig_block<T>(Aall, Qall, n, k, m, blockIdx.x);
+    return;
+  }
+  if (vs < 0 || (frozen[m] && done_sweeps[m] != vs + 1)) return;
+  constexpr int G = kBJEigThreads / 256;
+  __shared__ __attribute__((aligned(16))) T X[G][kBJ2][kBJLd];
+  const int grp = threadIdx.x >> 8;
+  const int tile = np * np + ((int)blockIdx.x - np) * G + grp;
+  const bool active = tile < np * np + (n / kBJ2) * np;
+  bjac_apply_tile<T>(Aall, Vall, Qv, n, kv, m, tile, threadIdx.x & 255, active, X[grp]);
 }
 
 bool bjac_supported(int n) { return n >= 2 * kBJ2 && n % kBJ2 == 0; }
@@ -724,6 +769,22 @@ hipError_t launch_bjac_round(int n, int nmat, T* A, T* V, T* Qbuf, const int* fr
                      frozen, n, k);
   return hipGetLastError();
 }
+// fp32 path: round k's subproblems with V's update of round kv (sweep vs,
+// Q blocks Qv) in one launch, then A's update of round k alone
+hipError_t launch_bjac_round_f32(int n, int nmat, float* A, float* V, float* Q, const float* Qv,
+                                 const int* frozen, const int* done_sweeps, int k, int do_eig, int kv,
+                                 int vs, hipStream_t st) {
+  const int np = n / kBJ2;
+  const int nvt = (n / kBJ2) * np;                       // V tiles
+  const int G = kBJEigThreads / 256;
+  hipLaunchKernelGGL(k_bjac_eigv<float>, dim3(np + (nvt + G - 1) / G, nmat), dim3(kBJEigThreads), 0, st,
+                     A, Q, V, Qv, frozen, done_sweeps, n, k, do_eig, kv, vs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !do_eig) return e;
+  hipLaunchKernelGGL(k_bjac_apply<float>, dim3(np * np, nmat), dim3(256), 0, st, A, V, Q, frozen, n, k);
+  return hipGetLastError();
+}
+
 template hipError_t launch_bjac_round<double>(int, int, double*, double*, double*, const int*, int,
                                               hipStream_t);
 template hipError_t launch_bjac_round<float>(int, int, float*, float*, float*, const int*, int,
