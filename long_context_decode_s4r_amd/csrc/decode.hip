@@ -1473,6 +1473,9 @@ static hipError_t launch_score_bf16(const Dims& d, int U, const CachePtrs& c, co
     hipLaunchKernelGGL((k_score_bf16<KS, 1, 1>), grid, dim3(512), 0, st, d, c, w);
   else if (nrb <= 2)
     hipLaunchKernelGGL((k_score_bf16<KS, 2, 1>), grid, dim3(512), 0, st, d, c, w);
+  else if (nrb <= 4 && KS == 16)  // r = 256: one row block and two column blocks per wave
+    // (measured faster than two row blocks per wave there; slower at r = 192)
+    hipLaunchKernelGGL((k_score_bf16<KS, 4, 1>), grid, dim3(512), 0, st, d, c, w);
   else if (nrb <= 4)
     hipLaunchKernelGGL((k_score_bf16<KS, 2, 2>), grid, dim3(512), 0, st, d, c, w);
   else if (nrb <= 8)
