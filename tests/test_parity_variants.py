@@ -81,6 +81,19 @@ def test_window_row_blocks_bf16(gpu_lib, shape):
     assert st.n_checked == 2 * (W + 2)
 
 
+@pytest.mark.parametrize("shape", [(32, 8, 12), (24, 8, 12), (16, 8, 8), (32, 8, 16)],
+                         ids=["G4W12", "G3W12", "G2W8", "G4W16"])
+def test_window_row_blocks_r256(gpu_lib, shape):
+    """r = 256 with 16..64 window rows (one, three or four 16-row blocks of
+    the latent scorer, one row block per wave; G = 3 leaves the last block
+    partly empty), over more steps than the window holds, with enough
+    candidates that every block streams several 64-position tiles."""
+    Hq, Hkv, W = shape
+    w = _LLAMA.with_(n_q_heads=Hq, n_kv_heads=Hkv, q_window=W)
+    st = _run(w, 12000, 2, W + 2)
+    assert st.n_checked == 2 * (W + 2)
+
+
 @pytest.mark.parametrize("w", [
     _F32.with_(local_window=1), _F32.with_(local_window=1, n_sink=0),
     _LLAMA.with_(local_window=1), _QWEN.with_(local_window=1, rank_v=192),
