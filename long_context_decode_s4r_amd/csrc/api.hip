@@ -137,7 +137,7 @@ int check_sample_fits(const kvlr_config* c, int64_t L) {
 
 // ---- workspace layouts ------------------------------------------------------
 struct BuildLayout {
-  size_t S, A0, A1, V0, V1, part, frozen, final_buf, done, total;
+  size_t S, gram, A0, A1, V0, V1, part, frozen, final_buf, done, total;
   int nchunk;
 };
 
@@ -149,6 +149,8 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
   size_t off = 0;
   b.S = off;
   off = align_up(off + (size_t)nmat * c->n_sample * D * elem_bytes(c));
+  b.gram = off;  // the Gram's channel-major sample and partial tiles (bf16)
+  off = align_up(off + gram_nt_ws_bytes(dims_of(c), (int)nmat));
   const size_t mat = (size_t)nmat * D * D * sizeof(double);
   b.A0 = off;
   off = align_up(off + mat);
@@ -366,7 +368,8 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
   hipError_t he;
   if ((he = launch_sample_normalize(d, (int)n_units, L, K, V, w + bl.S, st)) != hipSuccess)
     return hip_fail(he, "sample/normalise");
-  if ((he = launch_gram(d, nmat, w + bl.S, A[0], Vm[0], st)) != hipSuccess) return hip_fail(he, "gram");
+  if ((he = launch_gram(d, nmat, w + bl.S, A[0], Vm[0], w + bl.gram, st)) != hipSuccess)
+    return hip_fail(he, "gram");
   if ((he = launch_jacobi_init(nmat, frozen, final_buf, done, st)) != hipSuccess)
     return hip_fail(he, "jacobi init");
   if (depth > 1 &&

@@ -188,7 +188,10 @@ struct Dims {
 // prefill
 hipError_t launch_sample_normalize(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                    void* S, hipStream_t st);
-hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm,
+// gws: device workspace of gram_nt_ws_bytes(d, nmat) bytes for the bf16 GEMM
+// form (D' a multiple of 128); null (or 0 bytes needed) selects the direct kernel
+size_t gram_nt_ws_bytes(const Dims& d, int nmat);
+hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm, void* gws,
                        hipStream_t st);
 hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_dst,
                                const double* V_src, double* V_dst, const int* frozen,

@@ -135,6 +135,165 @@ __global__ __launch_bounds__(256) void k_gram_bf16(const uint16_t* __restrict__ 
   }
 }
 
+// bf16, D' a multiple of 128: the Gram as a GEMM whose operands are both
+// K-contiguous.  The sample is first copied channel-major (k_sample_t: S^T
+// [D'][Tp], Tp = T' rounded up to 64, zero-padded; 64 x 64 tiles through
+// LDS, coalesced reads and writes).  k_gram_nt: a block owns one 128 x 128
+// tile pair (ti <= tj) of one matrix and one of `nsp` equal stretches of the
+// tokens; 4 waves, wave w the 64 x 64 quadrant (w / 2, w % 2) as 2 x 2 MFMA
+// 32x32x16 tiles (fp32 accumulation).  Per 64-token chunk the block stages
+// the two 128-row operand slabs (16 KB each, rows padded to 144 bytes so the
+// operand reads of 8 consecutive rows hit distinct banks) through a 2-stage
+// LDS buffer, the next chunk's slabs loaded into registers during the
+// current one's products.  Each block stores its fp32 partial tile;
+// k_gram_reduce sums the stretches in fixed order in fp64 and writes A and
+// its mirror, so the result does not depend on scheduling.
+constexpr int kGT = 128;      // output tile edge
+constexpr int kGK = 64;       // tokens per chunk
+constexpr int kGLd = kGK + 8; // LDS row stride (bf16)
+
+__global__ __launch_bounds__(256) void k_sample_t(const uint16_t* __restrict__ S,
+                                                  uint16_t* __restrict__ ST, int nT, int Tp, int D) {
+  __shared__ uint16_t t[64][65];
+  const int m = blockIdx.z, t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const uint16_t* Sm = S + (int64_t)m * nT * D;
+  uint16_t* STm = ST + (int64_t)m * D * Tp;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;  // token t0 + r, channel c0 + c
+    t[r][c] = t0 + r < nT ? Sm[(int64_t)(t0 + r) * D + c0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int c = e >> 6, r = e & 63;  // channel c0 + c, token t0 + r
+    STm[(int64_t)(c0 + c) * Tp + t0 + r] = t[r][c];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gram_nt(const uint16_t* __restrict__ ST,
+                                                 float* __restrict__ part, int Tp, int D, int nt,
+                                                 int nsp) {
+  const int m = blockIdx.y;
+  const int npair = nt * (nt + 1) / 2;
+  const int pr = blockIdx.x / nsp, sp = blockIdx.x % nsp;
+  int idx = pr, ti = 0;
+  while (idx >= nt - ti) {
+    idx -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + idx;
+  // this block's tokens: whole chunks [c0, c1)
+  const int nch = Tp / kGK;
+  const int c0 = (int)((int64_t)nch * sp / nsp), c1 = (int)((int64_t)nch * (sp + 1) / nsp);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kGT * kGLd];  // [stage][A | B]
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
+  const uint16_t* STm = ST + (int64_t)m * D * Tp;
+  const uint16_t* rowA = STm + (int64_t)(ti * kGT) * Tp;
+  const uint16_t* rowB = STm + (int64_t)(tj * kGT) * Tp;
+  // loads of a chunk: 2 slabs x 128 rows x 8 pieces of 16 bytes; thread tid
+  // takes pieces tid + 256 q, q < 4, of each slab (row p / 8, piece p % 8)
+  u16x8 ra[4], rb[4];
+  auto load = [&](int ch) {
+    const int64_t tk = (int64_t)ch * kGK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q, r = p >> 3, pc = p & 7;
+      ra[q] = *reinterpret_cast<const u16x8*>(rowA + (int64_t)r * Tp + tk + 8 * pc);
+      rb[q] = *reinterpret_cast<const u16x8*>(rowB + (int64_t)r * Tp + tk + 8 * pc);
+    }
+  };
+  auto store = [&](int stg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p = tid + 256 * q, r = p >> 3, pc = p & 7;
+      *reinterpret_cast<u16x8*>(&lds[stg][0][r * kGLd + 8 * pc]) = ra[q];
+      *reinterpret_cast<u16x8*>(&lds[stg][1][r * kGLd + 8 * pc]) = rb[q];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  const int wr = 64 * (w >> 1), wc = 64 * (w & 1);
+  if (c0 < c1) {
+    load(c0);
+    store(0);
+    __syncthreads();
+    for (int ch = c0; ch < c1; ++ch) {
+      const int stg = (ch - c0) & 1;
+      if (ch + 1 < c1) load(ch + 1);
+#pragma unroll
+      for (int kk = 0; kk < kGK / 16; ++kk) {
+        bf16x8 a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(
+                                                &lds[stg][0][(wr + 32 * i + mm) * kGLd + 16 * kk + 8 * kg]));
+          b[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(
+                                                &lds[stg][1][(wc + 32 * i + mm) * kGLd + 16 * kk + 8 * kg]));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      }
+      if (ch + 1 < c1) store(stg ^ 1);
+      __syncthreads();
+    }
+  }
+  float* pt = part + (((int64_t)m * npair + pr) * nsp + sp) * kGT * kGT;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        pt[(wr + 32 * i + acc_row32(v, l)) * kGT + wc + 32 * j + mm] = acc[i][j][v];
+}
+
+// A[i][j] (and A[j][i]) = sum over the stretches of tile pair (ti <= tj), in order
+__global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ part,
+                                                     double* __restrict__ A, int D, int nt, int nsp) {
+  const int m = blockIdx.y;
+  const int npair = nt * (nt + 1) / 2;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)npair * kGT * kGT) return;
+  const int pr = (int)(e / (kGT * kGT)), x = (int)(e % (kGT * kGT));
+  int idx = pr, ti = 0;
+  while (idx >= nt - ti) {
+    idx -= nt - ti;
+    ++ti;
+  }
+  const int tj = ti + idx;
+  if (ti == tj && x / kGT > x % kGT) return;  // a diagonal tile: its upper triangle, mirrored
+  const float* pt = part + ((int64_t)m * npair + pr) * nsp * kGT * kGT + x;
+  double sum = 0.0;
+  for (int s2 = 0; s2 < nsp; ++s2) sum += (double)pt[(int64_t)s2 * kGT * kGT];
+  const int row = ti * kGT + x / kGT, col = tj * kGT + x % kGT;
+  double* Am = A + (int64_t)m * D * D;
+  Am[(int64_t)row * D + col] = sum;
+  Am[(int64_t)col * D + row] = sum;
+}
+
+bool gram_nt_supported(const Dims& d) { return d.dtype != 0 && d.D % kGT == 0; }
+
+// token stretches per tile pair: about 320 blocks in all, each with at least
+// 4 chunks of 64 tokens
+int gram_nt_splits(const Dims& d, int nmat) {
+  const int nt = d.D / kGT, npair = nt * (nt + 1) / 2;
+  const int nch = (d.T + kGK - 1) / kGK;
+  int nsp = (320 + npair * nmat - 1) / (npair * nmat);
+  nsp = nsp > nch / 4 ? nch / 4 : nsp;
+  return nsp < 1 ? 1 : (nsp > 64 ? 64 : nsp);
+}
+
+size_t gram_nt_ws_bytes(const Dims& d, int nmat) {
+  if (!gram_nt_supported(d)) return 0;
+  const int64_t Tp = (d.T + kGK - 1) / kGK * kGK;
+  const int nt = d.D / kGT, npair = nt * (nt + 1) / 2;
+  const size_t st = (size_t)nmat * d.D * Tp * 2;
+  const size_t pa = (size_t)nmat * npair * gram_nt_splits(d, nmat) * kGT * kGT * 4;
+  return (st + 255) / 256 * 256 + pa;
+}
+
 // fp32: plain fp64 accumulation, one output entry per thread
 __global__ __launch_bounds__(256) void k_gram_f32(const float* __restrict__ S,
                                                   double* __restrict__ A, int nT, int D) {
@@ -155,11 +314,24 @@ __global__ void k_eye(double* __restrict__ Vm, int D) {
   Vm[(int64_t)m * D * D + e] = (e / D == e % D) ? 1.0 : 0.0;
 }
 
-hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm,
+hipError_t launch_gram(const Dims& d, int nmat, const void* S, double* A, double* Vm, void* gws,
                        hipStream_t st) {
   const int D = d.D;
   const int64_t n2 = (int64_t)D * D;
-  if (d.dtype == 0) {
+  if (gram_nt_supported(d) && gws) {
+    const int Tp = (d.T + kGK - 1) / kGK * kGK;
+    const int nt = D / kGT, npair = nt * (nt + 1) / 2, nsp = gram_nt_splits(d, nmat);
+    uint16_t* ST = (uint16_t*)gws;
+    float* part = (float*)((char*)gws + ((size_t)nmat * D * Tp * 2 + 255) / 256 * 256);
+    hipLaunchKernelGGL(k_sample_t, dim3(Tp / 64, D / 64, nmat), dim3(256), 0, st, (const uint16_t*)S, ST,
+                       d.T, Tp, D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gram_nt, dim3(npair * nsp, nmat), dim3(256), 0, st, ST, part, Tp, D, nt, nsp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)((npair * kGT * kGT + 255) / 256), nmat), dim3(256), 0,
+                       st, part, A, D, nt, nsp);
+  } else if (d.dtype == 0) {
     hipLaunchKernelGGL(k_gram_f32, dim3((unsigned)((n2 + 255) / 256), nmat), dim3(256), 0, st,
                        (const float*)S, A, d.T, D);
   } else {
