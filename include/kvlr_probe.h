@@ -2,7 +2,7 @@
  * kvlr_probe.h -- measurement probes of the kvlr library (MI355X, gfx950).
  *
  * Not part of the method: plain kernels that measure what the hardware
- * delivers, so the path's kernels can be judged against measured ceilings
+ * delivers, so the path's kernels can be compared with measured ceilings
  * as well as against the vendor peaks (8 TB/s HBM3E, 2.5 PFLOP/s dense bf16
  * MFMA).  Every call enqueues one kernel on `stream` (a hipStream_t as void*)
  * and returns without waiting; the caller times it with events.  Pointers
