@@ -137,7 +137,7 @@ int check_sample_fits(const kvlr_config* c, int64_t L) {
 
 // ---- workspace layouts ------------------------------------------------------
 struct BuildLayout {
-  size_t S, gram, A0, A1, V0, V1, part, frozen, final_buf, done, total;
+  size_t S, gram, A0, A1, V0, V1, part, frozen, final_buf, done, eidx, total;
   int nchunk;
 };
 
@@ -168,6 +168,8 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
   off = align_up(off + (size_t)nmat * sizeof(int));
   b.done = off;
   off = align_up(off + (size_t)nmat * sizeof(int));
+  b.eidx = off;  // eigenvalue order, per output matrix
+  off = align_up(off + (size_t)nmat * D * sizeof(int));
   b.total = off;
   return b;
 }
@@ -414,7 +416,7 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
       return hip_fail(he, "block jacobi V update");
     if ((he = launch_extract<float>(d, nmat, A32, A32, V32, V32, frozen, final_buf, done, 0, cache->basis_k,
                                     cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch, depth,
-                                    st)) != hipSuccess)
+                                    (int*)(w + bl.eidx), st)) != hipSuccess)
       return hip_fail(he, "extract");
     return ok();
   }
@@ -452,7 +454,7 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
   }
   if ((he = launch_extract<double>(d, nmat, A[0], A[1], Vm[0], Vm[1], frozen, final_buf, done, cur,
                            cache->basis_k, cache->basis_v, eigvals_k, eigvals_v, sweeps, (int)batch,
-                           depth, st)) != hipSuccess)
+                           depth, (int*)(w + bl.eidx), st)) != hipSuccess)
     return hip_fail(he, "extract");
   return ok();
 }

@@ -225,7 +225,7 @@ template <typename S>
 hipError_t launch_extract(const Dims& d, int nmat, const S* A0, const S* A1, const S* V0, const S* V1,
                           const int* frozen, const int* final_buf, const int* done_sweeps, int cur,
                           void* basis_k, void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
-                          int batch, int depth, hipStream_t st);
+                          int batch, int depth, int* eidx, hipStream_t st);
 // bases shared over windows of `depth` layers: Grams summed into each
 // window's first layer, the other layers' matrices frozen
 hipError_t launch_gram_window_sum(int n, int n_layers, int batch, int depth, double* A, int* frozen,

@@ -980,9 +980,52 @@ hipError_t launch_to_f32(int n, int nmat, const double* A64, float* A32, float* 
 }
 
 // --------------------------------------------------------------------------
-// 4. eigenvalues descending (bitonic sort of (lambda, slot) in LDS), basis =
-//    the first r eigenvector columns, rounded to storage.
+// 4. eigenvalues descending (bitonic sort of (lambda, slot) in LDS, one block
+//    per output matrix; the sorted slots go to the workspace), basis = the
+//    first r eigenvector columns, rounded to storage (k_extract_gather, rows
+//    of V spread over many blocks).
 // --------------------------------------------------------------------------
+// the matrix whose eigensolve serves output m (= 2 unit + kind): its own, or,
+// with bases shared over a window of `depth` layers (units layer-major,
+// `batch` sequences per layer), the window's first layer's
+__device__ __forceinline__ int extract_source(int m, int batch, int depth) {
+  const int u = m >> 1, kind = m & 1;
+  const int layer = u / batch, seq = u % batch;
+  return 2 * ((layer - layer % depth) * batch + seq) + kind;
+}
+
+template <typename T, typename S>
+__global__ __launch_bounds__(256) void k_extract_gather(const S* __restrict__ V0,
+                                                        const S* __restrict__ V1,
+                                                        const int* __restrict__ frozen,
+                                                        const int* __restrict__ final_buf, int cur,
+                                                        const int* __restrict__ eidx, int n, int rk,
+                                                        int rv, T* __restrict__ BK, T* __restrict__ BV,
+                                                        int batch, int depth) {
+  const int m = blockIdx.y, u = m >> 1, kind = m & 1;
+  const int r = kind ? rv : rk;
+  const int ms = extract_source(m, batch, depth);
+  const int buf = frozen[ms] ? final_buf[ms] : cur;
+  const S* Vm = (buf ? V1 : V0) + (int64_t)ms * n * n;
+  const int* idx = eidx + (int64_t)m * n;
+  T* B = (kind ? BV : BK) + (int64_t)u * n * r;
+  // rows [4 bx, 4 bx + 4) of the basis; thread t: columns t, t + 256, ...
+  for (int c = threadIdx.x; c < r; c += 256) {
+    const int col = idx[c];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * blockIdx.x + q;
+      if (i < n) {
+        const double x = (double)Vm[(int64_t)i * n + col];
+        if constexpr (sizeof(T) == 2)
+          B[(int64_t)i * r + c] = d2bf(x);
+        else
+          B[(int64_t)i * r + c] = (float)x;
+      }
+    }
+  }
+}
+
 template <typename T, typename S>
 __global__ __launch_bounds__(1024) void k_extract(const S* __restrict__ A0,
                                                   const S* __restrict__ A1,
@@ -994,18 +1037,13 @@ __global__ __launch_bounds__(1024) void k_extract(const S* __restrict__ A0,
                                                   int n, int rk, int rv, T* __restrict__ BK,
                                                   T* __restrict__ BV, float* __restrict__ eigK,
                                                   float* __restrict__ eigV,
-                                                  int32_t* __restrict__ sweeps, int batch, int depth) {
+                                                  int32_t* __restrict__ sweeps, int batch, int depth,
+                                                  int* __restrict__ eidx) {
   extern __shared__ unsigned char smem_raw[];
   const int m = blockIdx.x, u = m >> 1, kind = m & 1;
-  const int r = kind ? rv : rk;
-  // the matrix whose eigensolve serves this unit: its own, or, with bases
-  // shared over a window of `depth` layers (units layer-major, `batch`
-  // sequences per layer), the window's first layer's
-  const int layer = u / batch, seq = u % batch;
-  const int ms = 2 * ((layer - layer % depth) * batch + seq) + kind;
+  const int ms = extract_source(m, batch, depth);
   const int buf = frozen[ms] ? final_buf[ms] : cur;
   const S* A = (buf ? A1 : A0) + (int64_t)ms * n * n;
-  const S* Vm = (buf ? V1 : V0) + (int64_t)ms * n * n;
   if (sweeps && threadIdx.x == 0) sweeps[m] = done_sweeps[ms] > 0 ? done_sweeps[ms] : -1;
   int np2 = 1;
   while (np2 < n) np2 <<= 1;
@@ -1041,42 +1079,39 @@ __global__ __launch_bounds__(1024) void k_extract(const S* __restrict__ A0,
   float* eig = kind ? eigV : eigK;
   if (eig)
     for (int i = threadIdx.x; i < n; i += blockDim.x) eig[(int64_t)u * n + i] = (float)key[i];
-  T* B = (kind ? BV : BK) + (int64_t)u * n * r;
-  // eigenvector entries rounded once to the storage type
-  for (int64_t e = threadIdx.x; e < (int64_t)n * r; e += blockDim.x) {
-    const int i = (int)(e / r), c = (int)(e % r);
-    const double x = (double)Vm[(int64_t)i * n + idx[c]];
-    if constexpr (sizeof(T) == 2)
-      B[e] = d2bf(x);
-    else
-      B[e] = (float)x;
-  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) eidx[(int64_t)m * n + i] = idx[i];
 }
 
 template <typename S>
 hipError_t launch_extract(const Dims& d, int nmat, const S* A0, const S* A1, const S* V0, const S* V1,
                           const int* frozen, const int* final_buf, const int* done_sweeps, int cur,
                           void* basis_k, void* basis_v, float* eig_k, float* eig_v, int32_t* sweeps,
-                          int batch, int depth, hipStream_t st) {
+                          int batch, int depth, int* eidx, hipStream_t st) {
   int np2 = 1;
   while (np2 < d.D) np2 <<= 1;
   const size_t lds = (size_t)np2 * (sizeof(double) + sizeof(int));
-  if (d.dtype == 0)
+  const dim3 gg((unsigned)((d.D + 3) / 4), nmat);
+  if (d.dtype == 0) {
     hipLaunchKernelGGL((k_extract<float, S>), dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1, frozen,
                        final_buf, done_sweeps, cur, d.D, d.r, d.rv, (float*)basis_k,
-                       (float*)basis_v, eig_k, eig_v, sweeps, batch, depth);
-  else
+                       (float*)basis_v, eig_k, eig_v, sweeps, batch, depth, eidx);
+    hipLaunchKernelGGL((k_extract_gather<float, S>), gg, dim3(256), 0, st, V0, V1, frozen, final_buf, cur, eidx,
+                       d.D, d.r, d.rv, (float*)basis_k, (float*)basis_v, batch, depth);
+  } else {
     hipLaunchKernelGGL((k_extract<uint16_t, S>), dim3(nmat), dim3(1024), lds, st, A0, A1, V0, V1,
                        frozen, final_buf, done_sweeps, cur, d.D, d.r, d.rv, (uint16_t*)basis_k,
-                       (uint16_t*)basis_v, eig_k, eig_v, sweeps, batch, depth);
+                       (uint16_t*)basis_v, eig_k, eig_v, sweeps, batch, depth, eidx);
+    hipLaunchKernelGGL((k_extract_gather<uint16_t, S>), gg, dim3(256), 0, st, V0, V1, frozen, final_buf, cur,
+                       eidx, d.D, d.r, d.rv, (uint16_t*)basis_k, (uint16_t*)basis_v, batch, depth);
+  }
   return hipGetLastError();
 }
 template hipError_t launch_extract<double>(const Dims&, int, const double*, const double*, const double*,
                                            const double*, const int*, const int*, const int*, int, void*,
-                                           void*, float*, float*, int32_t*, int, int, hipStream_t);
+                                           void*, float*, float*, int32_t*, int, int, int*, hipStream_t);
 template hipError_t launch_extract<float>(const Dims&, int, const float*, const float*, const float*,
                                           const float*, const int*, const int*, const int*, int, void*,
-                                          void*, float*, float*, int32_t*, int, int, hipStream_t);
+                                          void*, float*, float*, int32_t*, int, int, int*, hipStream_t);
 
 // --------------------------------------------------------------------------
 // 5. projection C[j] = rnd(X[j] . B) for j in [s, L)
