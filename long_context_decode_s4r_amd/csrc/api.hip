@@ -145,7 +145,7 @@ BuildLayout build_layout(const kvlr_config* c, int64_t U) {
   BuildLayout b;
   const int64_t D = (int64_t)c->n_kv_heads * c->head_dim;
   const int64_t nmat = 2 * U;
-  b.nchunk = (int)((D + 15) / 16);
+  b.nchunk = (int)((D + 3) / 4);  // row chunks of the off-diagonal norm (4 rows each)
   size_t off = 0;
   b.S = off;
   off = align_up(off + (size_t)nmat * c->n_sample * D * elem_bytes(c));

@@ -459,7 +459,7 @@ hipError_t launch_jacobi_round(int n, int nmat, const double* A_src, double* A_d
 
 // convergence test: off(A)_F <= tol * trace(A); partial sums per row chunk,
 // then one thread per matrix sums them in a fixed order
-constexpr int kJacRowsPerBlock = 16;
+constexpr int kJacRowsPerBlock = 4;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_offnorm(const T* __restrict__ A,
@@ -470,7 +470,13 @@ __global__ __launch_bounds__(256) void k_offnorm(const T* __restrict__ A,
   const T* Am = A + (int64_t)m * n * n;
   const int r0 = blockIdx.x * kJacRowsPerBlock;
   double off = 0.0, tr = 0.0;
-  for (int r = r0; r < min(r0 + kJacRowsPerBlock, n); ++r) {
+  // the block's rows and the thread's columns c = tid + 256 j: for D' <= 1024
+  // every load of the thread is issued before the first sum
+#pragma unroll
+  for (int dr = 0; dr < kJacRowsPerBlock; ++dr) {
+    const int r = r0 + dr;
+    if (r >= n) break;
+#pragma unroll 4
     for (int c = threadIdx.x; c < n; c += blockDim.x) {
       const double x = (double)Am[(int64_t)r * n + c];
       if (c == r)
@@ -499,14 +505,21 @@ __global__ __launch_bounds__(256) void k_offnorm(const T* __restrict__ A,
 __global__ void k_jacobi_check(const double* __restrict__ part, int* __restrict__ frozen,
                                int* __restrict__ final_buf, int* __restrict__ done_sweeps, int nmat,
                                int nchunk, int cur, int sweep, double tol) {
-  for (int m = threadIdx.x; m < nmat; m += blockDim.x) {
+  // a wave per matrix: lanes sum strided partials, then the wave's sum
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int m = threadIdx.x >> 6; m < nmat; m += nw) {
     if (frozen[m]) continue;
     double off = 0.0, tr = 0.0;
-    for (int c = 0; c < nchunk; ++c) {
+    for (int c = lane; c < nchunk; c += 64) {
       off += part[((int64_t)m * nchunk + c) * 2 + 0];
       tr += part[((int64_t)m * nchunk + c) * 2 + 1];
     }
-    if (sqrt(off) <= tol * fabs(tr) || off == 0.0) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      tr += __shfl_xor(tr, o);
+    }
+    if (lane == 0 && (sqrt(off) <= tol * fabs(tr) || off == 0.0)) {
       frozen[m] = 1;
       final_buf[m] = cur;
       done_sweeps[m] = sweep + 1;
