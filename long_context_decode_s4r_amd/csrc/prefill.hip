@@ -787,6 +787,11 @@ template <> struct BjMfma<float> {
 // tile `tile` of matrix m, by the 256 threads tid = 0..255 of a group that
 // owns the LDS tile X (the group's block barriers: A tiles 3, V tiles 1;
 // `active` false runs the barriers only)
+// A's update covers the upper triangle of subproblem pairs, P <= P2 (A is
+// symmetric: the tile of (P2, P) is the transpose of that of (P, P2) and is
+// written from it), so np (np + 1) / 2 A tiles; V's tiles follow them
+__host__ __device__ __forceinline__ int bj_natile(int np) { return np * (np + 1) / 2; }
+
 template <typename T>
 __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restrict__ Vall,
                                                 const T* __restrict__ Qall, int n, int k, int m,
@@ -841,8 +846,13 @@ __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restr
   // output element (ti, tj, v) of this lane: row orow(ti, v), column ocol(tj)
   auto orow = [&](int ti, int v) { return 32 * qi + 16 * ti + Mf::row(r4, v); };
   auto ocol = [&](int tj) { return 32 * qj + 16 * tj + c16; };
-  if (tile < np * np) {
-    const int P = tile / np, P2 = tile % np;
+  if (tile < bj_natile(np)) {
+    int P = 0, rem = tile;  // tile -> (P, P2), P <= P2
+    while (rem >= np - P) {
+      rem -= np - P;
+      ++P;
+    }
+    const int P2 = P + rem;
     int I, J, I2, J2;
     bj_pair(P, k, nb, &I, &J);
     bj_pair(P2, k, nb, &I2, &J2);
@@ -875,8 +885,25 @@ __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restr
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (active) A[(int64_t)bj_index(orow(ti, v), I, J) * n + bj_index(ocol(tj), I2, J2)] = acc[ti][tj][v];
+    if (P != P2) {  // the mirrored tile A[P2, P], through LDS for row-contiguous stores
+      __syncthreads();
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) X[ocol(tj)][orow(ti, v)] = acc[ti][tj][v];
+      __syncthreads();
+      for (int e = tid; active && e < kBJ2 * kBJ2 / 2; e += 256) {
+        const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));  // row i of P2, columns j, j + 1 of P
+        typename Mf::pair x;
+        x.x = X[i][j];
+        x.y = X[i][j + 1];
+        *reinterpret_cast<typename Mf::pair*>(A + (int64_t)bj_index(i, I2, J2) * n + bj_index(j, I, J)) = x;
+      }
+    }
   } else {
-    const int t2 = tile - np * np, R = t2 / np, P = t2 % np;
+    const int t2 = tile - bj_natile(np), R = t2 / np, P = t2 % np;
     int I, J;
     bj_pair(P, k, nb, &I, &J);
     T* V = Vall + (int64_t)m * n * n;
@@ -934,8 +961,8 @@ __global__ __launch_bounds__(kBJEigThreads) void k_bjac_eigv(T* __restrict__ Aal
   constexpr int G = kBJEigThreads / 256;
   __shared__ __attribute__((aligned(16))) T X[G][kBJ2][kBJLd];
   const int grp = threadIdx.x >> 8;
-  const int tile = np * np + ((int)blockIdx.x - np) * G + grp;
-  const bool active = tile < np * np + (n / kBJ2) * np;
+  const int tile = bj_natile(np) + ((int)blockIdx.x - np) * G + grp;
+  const bool active = tile < bj_natile(np) + (n / kBJ2) * np;
   bjac_apply_tile<T>(Aall, Vall, Qv, n, kv, m, tile, threadIdx.x & 255, active, X[grp]);
 }
 
@@ -950,7 +977,7 @@ hipError_t launch_bjac_round(int n, int nmat, T* A, T* V, T* Qbuf, const int* fr
   hipLaunchKernelGGL(k_bjac_eig<T>, dim3(np, nmat), dim3(kBJEigThreads), 0, st, A, Qbuf, frozen, n, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bjac_apply<T>, dim3(np * np + (n / kBJ2) * np, nmat), dim3(256), 0, st, A, V, Qbuf,
+  hipLaunchKernelGGL(k_bjac_apply<T>, dim3(bj_natile(np) + (n / kBJ2) * np, nmat), dim3(256), 0, st, A, V, Qbuf,
                      frozen, n, k);
   return hipGetLastError();
 }
@@ -966,7 +993,7 @@ hipError_t launch_bjac_round_f32(int n, int nmat, float* A, float* V, float* Q, 
                      A, Q, V, Qv, frozen, done_sweeps, n, k, do_eig, kv, vs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !do_eig) return e;
-  hipLaunchKernelGGL(k_bjac_apply<float>, dim3(np * np, nmat), dim3(256), 0, st, A, V, Q, frozen, n, k);
+  hipLaunchKernelGGL(k_bjac_apply<float>, dim3(bj_natile(np), nmat), dim3(256), 0, st, A, V, Q, frozen, n, k);
   return hipGetLastError();
 }
 
