@@ -164,6 +164,51 @@ def test_eigensolve_sweep_report(gpu_lib, storage, D):
 
 
 @pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_decode_graph_replay(gpu_lib, storage):
+    """Three kvlr_decode_step calls captured in one HIP graph and replayed four
+    times, with eager work and synchronisations between the replays: after
+    every replay the output, the top-k picks and every cache buffer equal, bit
+    for bit, those of the same three steps run eagerly on an identical cache
+    (the step records no memset node and keeps no host state across calls)."""
+    kvlr = _kvlr()
+    if storage == "f32":
+        w = configs.TINY_F32.with_(n_q_heads=4, n_kv_heads=2, head_dim=64, rank=32, q_window=4,
+                                   top_k=32, n_recent=8, n_sample=256)
+    else:
+        w = configs.LLAMA8B_32K.with_(batch=2, n_sample=512, top_k=128)
+    L, steps, reps = 4000, 3, 4
+    prompt = synth.make_prompt(w, L=L, batch=2)
+    dec = synth.make_decode_inputs(w, prompt, steps, batch=2)
+    q = [dec.q[t].cuda() for t in range(steps)]
+    kn = [dec.k[t].cuda() for t in range(steps)]
+    vn = [dec.v[t].cuda() for t in range(steps)]
+    ref, *_ = run_prefill(kvlr, w, prompt, L + steps * (reps + 1) + 8, eig=False)
+    kc, warm = ref.clone(), ref.clone()
+    shape = (2, w.n_q_heads, w.head_dim)
+    out_r, out_g, out_w = (torch.empty(shape, device="cuda") for _ in range(3))
+    tk_r, tk_g, tk_w = (torch.empty(2, w.top_k, dtype=torch.int32, device="cuda") for _ in range(3))
+    d_ref, d_g = kvlr.Decoder(ref, out_r, tk_r), kvlr.Decoder(kc, out_g, tk_g)
+    kvlr.Decoder(warm, out_w, tk_w).step(q[0], kn[0], vn[0])  # the library's one-time set-up, eagerly
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            d_g.step(q[t], kn[t], vn[t])
+    for rep in range(reps):
+        print(f"  replay {rep}", flush=True)
+        for t in range(steps):
+            d_ref.step(q[t], kn[t], vn[t])
+        out_w.fill_(float(rep))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_r), rep
+        assert torch.equal(tk_g, tk_r), rep
+        for name in kvlr.BUFFERS:
+            assert torch.equal(getattr(kc, name), getattr(ref, name)), (rep, name)
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
 def test_prefill_graph_replay(gpu_lib, storage):
     """kvlr_build_bases and kvlr_project captured in one HIP graph: every
     replay (with eager work and synchronisations between replays) gives
