@@ -257,11 +257,19 @@ def run_prefill_leg():
     t_p = _time_ms(lambda i: kvlr.project(kc, prompts[i % 2].K, prompts[i % 2].V, ws=pws), 20)
     n_proj = 2 * (w.L - w.n_sink)
     flops = 2.0 * n_proj * w.D * w.rank
+    # the projection's attainable ceiling: it reads the states and writes the
+    # coefficients (bf16), so below the ridge it is bound by HBM at its
+    # arithmetic intensity, min(MFMA peak, intensity x 8 TB/s)
+    proj_bytes = 2.0 * n_proj * (w.D + w.rank)
+    attainable = min(BF16_PEAK_TFLOPS, flops / proj_bytes * HBM_PEAK_GBPS / 1e3)
+    tflops = flops / (t_p / 1e3) / 1e12
     leg = {"workload": w.name, "tokens_per_s": round(w.L / ((t_b + t_p) / 1e3), 1),
            "build_bases_ms": round(t_b, 3), "project_ms": round(t_p, 4),
            "eig_sweeps_kv": sweeps,
-           "project_tflops": round(flops / (t_p / 1e3) / 1e12, 1),
-           "project_mfma_frac": round(flops / (t_p / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "project_tflops": round(tflops, 1),
+           "project_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+           "project_attainable_tflops": round(attainable, 1),
+           "project_frac_of_attainable": round(tflops / attainable, 4),
            "timing": "HIP events around 4 builds / 20 projections, two prompts alternating"}
     del ws
     torch.cuda.empty_cache()
