@@ -121,6 +121,7 @@ def run_probes(full: bool = True):
 
     if full:
         cfgs = [(0, b, dp) for b in (256, 512, 1024, 2048, 4096) for dp in (2, 4, 8, 16)] + [(1, 256, 0), (2, 256, 0)]
+        cfgs += [(m, 256, ch) for m in (3, 4) for ch in (64, 128, 256, 512, 2048)]
     else:
         cfgs = [(0, 256, 8), (0, 512, 4), (1, 256, 0), (2, 256, 0)]
     reads = []
@@ -130,9 +131,15 @@ def run_probes(full: bool = True):
                                      st.cuda_stream)
             assert rc == 0, rc
         ms = best_ms(launch)
-        reads.append({"method": ["register", "global_to_lds", "global_to_lds_nt"][method], "blocks": blocks,
+        reads.append({"method": ["register", "global_to_lds", "global_to_lds_nt", "lds_row_slabs",
+                                 "lds_row_slabs_nt"][method], "blocks": blocks,
                       "depth": depth, "gbps": round(nbytes / (ms / 1e3) / 1e9, 1)})
     del buf
+    # the ceiling is the best contiguous stream; the row-slab reads (the
+    # access pattern of the prefill projection: rows of 2048 B read in
+    # column slabs of `depth` bytes) are reported beside it
+    rows = [r for r in reads if r["method"].startswith("lds_row_slabs")]
+    reads = [r for r in reads if not r["method"].startswith("lds_row_slabs")]
     mfma = []
     for shape, fl in ((0, 16384), (1, 32768)):
         blocks, iters = 2048, 4000
@@ -145,7 +152,7 @@ def run_probes(full: bool = True):
                      "tflops": round(flops / (ms / 1e3) / 1e12, 1)})
     best_read = max(reads, key=lambda r: r["gbps"])
     torch.cuda.empty_cache()
-    return {"read": reads, "best_read_gbps": best_read["gbps"],
+    return {"read": reads, "row_slab_read": rows, "best_read_gbps": best_read["gbps"],
             "best_read_config": {k: best_read[k] for k in ("method", "blocks", "depth")},
             "mfma": mfma, "best_mfma_tflops": max(m["tflops"] for m in mfma)}
 
@@ -271,6 +278,21 @@ def run_prefill_leg():
            "project_attainable_tflops": round(attainable, 1),
            "project_frac_of_attainable": round(tflops / attainable, 4),
            "timing": "HIP events around 4 builds / 20 projections, two prompts alternating"}
+    # For reference only: the vendor library's GEMM (torch.matmul, hipBLASLt)
+    # on the same two products, x[s:] . B for K and V, bf16 out, same
+    # alternation.  Not part of the path.
+    outs = [torch.empty(w.L - w.n_sink, w.rank, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    bk, bv = kc.basis_k[0].contiguous(), kc.basis_v[0].contiguous()
+
+    def lib_gemm(i):
+        p = prompts[i % 2]
+        torch.matmul(p.K[0, w.n_sink:], bk, out=outs[0])
+        torch.matmul(p.V[0, w.n_sink:], bv, out=outs[1])
+    lib_gemm(0)
+    t_l = _time_ms(lib_gemm, 20)
+    leg["library_gemm_ms"] = round(t_l, 4)
+    leg["library_gemm_tflops"] = round(flops / (t_l / 1e3) / 1e12, 1)
+    del outs
     del ws
     torch.cuda.empty_cache()
     # the full-prompt baseline: every non-sink token in the Gram

@@ -28,7 +28,15 @@ extern "C" {
  *             block (the scheme of the latent scoring kernel, with no compute);
  *             `depth` is ignored;
  *   method 2: method 1 with non-temporal loads (the cache policy of the
- *             latent scan: streamed data is not kept in the caches).
+ *             latent scan: streamed data is not kept in the caches);
+ *   method 3: the ring of method 1 over rows of 2048 bytes (a token row of
+ *             D' = 1024 bf16 channels): a block owns tiles of 32768 / depth
+ *             rows and reads each tile in column slabs of `depth` bytes, one
+ *             slab per stage, as a product stepping over the channels reads
+ *             its token rows; depth in {64, 128, 256, 512, 2048} (2048 =
+ *             contiguous); `bytes` a multiple of one tile (32768 / depth
+ *             rows of 2048 bytes);
+ *   method 4: method 3 with non-temporal loads.
  *   sink      device, >= blocks uint32: written only if an impossible value
  *             turns up, so the loads cannot be optimised away. */
 int kvlr_probe_read(const void* src, size_t bytes, int method, int blocks, int depth,

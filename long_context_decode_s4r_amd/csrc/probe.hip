@@ -65,6 +65,45 @@ __global__ __launch_bounds__(512) void k_probe_read_lds(const uint8_t* __restric
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// LDS path over rows: the buffer is rows of 2048 bytes (a token row of
+// D' = 1024 bf16 channels); a block owns tiles of kPrStage / CH rows and
+// reads each tile in column slabs of CH bytes, one slab per stage, as a
+// K-stepped product reads its token rows.  Same ring as k_probe_read_lds.
+template <int CH, int AUX>
+__global__ __launch_bounds__(512) void k_probe_read_rows(const uint8_t* __restrict__ src, int64_t ntiles,
+                                                         uint32_t* __restrict__ sink) {
+  constexpr int ROWS = kPrStage / CH, NSTEP = 2048 / CH, LPR = CH / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4 * kPrStage];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t mine = ntiles > blockIdx.x ? (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+  const int64_t ns = mine * NSTEP;
+  auto issue = [&](int64_t t, uint8_t* stage) {
+    const int64_t tt = t < ns ? t : ns - 1;  // requests past the end re-read the last stage
+    const int64_t tile = blockIdx.x + (tt / NSTEP) * gridDim.x;
+    const uint8_t* base = src + tile * (int64_t)ROWS * 2048 + (tt % NSTEP) * CH;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int off = (wvu * 4 + q) * 1024, p = off / 16 + l;
+      __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)(p / LPR) * 2048 + 16 * (p % LPR)),
+                                       (__attribute__((address_space(3))) void*)(stage + off), 16, 0, AUX);
+    }
+  };
+  uint32_t acc = 0;
+  if (ns > 0) {
+    issue(0, ring);
+    issue(1, ring + kPrStage);
+    issue(2, ring + 2 * kPrStage);
+  }
+  for (int64_t t = 0; t < ns; ++t) {
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(t + 3, ring + ((t + 3) & 3) * kPrStage);
+    acc ^= *reinterpret_cast<const uint32_t*>(ring + (t & 3) * kPrStage + 4 * tid);
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
 template <int SHAPE>
 __global__ __launch_bounds__(256) void k_probe_mfma(int64_t iters, float* __restrict__ sink) {
   const int l = threadIdx.x & 63;
@@ -130,6 +169,21 @@ extern "C" int kvlr_probe_read(const void* src, size_t bytes, int method, int bl
     else
       hipLaunchKernelGGL(k_probe_read_lds<2>, dim3(blocks), dim3(512), 0, st, (const uint8_t*)src,
                          (int64_t)(bytes / kPrStage), sink);
+  } else if (method == 3 || method == 4) {
+    if (depth != 64 && depth != 128 && depth != 256 && depth != 512 && depth != 2048) return 1;
+    if (bytes % ((size_t)(kPrStage / depth) * 2048) != 0) return 1;
+    const int64_t ntiles = (int64_t)(bytes / ((size_t)(kPrStage / depth) * 2048));
+    switch (depth * 8 + method) {
+#define KVLR_PRR(CH, M, AUX)                                                                       \
+  case CH * 8 + M:                                                                                 \
+    hipLaunchKernelGGL((k_probe_read_rows<CH, AUX>), dim3(blocks), dim3(512), 0, st,               \
+                       (const uint8_t*)src, ntiles, sink);                                         \
+    break;
+      KVLR_PRR(64, 3, 0) KVLR_PRR(128, 3, 0) KVLR_PRR(256, 3, 0) KVLR_PRR(512, 3, 0) KVLR_PRR(2048, 3, 0)
+      KVLR_PRR(64, 4, 2) KVLR_PRR(128, 4, 2) KVLR_PRR(256, 4, 2) KVLR_PRR(512, 4, 2) KVLR_PRR(2048, 4, 2)
+#undef KVLR_PRR
+      default: return 1;
+    }
   } else {
     return 1;
   }
