@@ -559,11 +559,8 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(KVLR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   hipError_t he;
-  if ((he = launch_project(d, (int)n_units, L, cache->L_max, K, V, cache->basis_k, cache->basis_v,
-                           cache->coef_k, cache->coef_v, ws, st)) != hipSuccess)
+  if ((he = launch_project_call(d, (int)n_units, L, K, V, cache_ptrs(cache, d), ws, st)) != hipSuccess)
     return hip_fail(he, "project");
-  if ((he = launch_exact_and_reset(d, (int)n_units, L, K, V, cache_ptrs(cache, d), st)) != hipSuccess)
-    return hip_fail(he, "exact/reset");
   return ok();
 }
 

@@ -313,6 +313,10 @@ hipError_t launch_window_init(const Dims& d, int U, int64_t L, int n_tail, const
 
 // prefill: exact sinks and ring, window and decode state cleared, lens = {L, 0},
 // (bf16) B^K transposed into the unit state
+// the whole projection call: coefficients, exact rows, window reset and the
+// transposed B^K of the decode state
+hipError_t launch_project_call(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                               const CachePtrs& c, void* ws, hipStream_t st);
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                   const CachePtrs& c, hipStream_t st);
 

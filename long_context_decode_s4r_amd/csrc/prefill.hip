@@ -1243,27 +1243,20 @@ constexpr int kProjWaves = 8;    // waves per block
 constexpr int kProjK = 64;       // channels per K step
 constexpr int kProjRing = 4;     // X fragment ring depth (steps)
 
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ B, uint16_t* __restrict__ T,
+                                               int D, int r, int k0, int n0);
+
 __global__ __launch_bounds__(256) void k_basis_t(const uint16_t* __restrict__ BK,
                                                  const uint16_t* __restrict__ BV,
                                                  uint16_t* __restrict__ BT, int D, int rk, int rv) {
   // tile of 32 channels x 32 columns; per unit BT holds B^K^T [rk][D'] then
   // B^V^T [rv][D'], BT[n][k] = B[k][n]
-  __shared__ uint16_t t[32][33];
   const int um = blockIdx.z, u = um >> 1, kind = um & 1;
   const int r = kind ? rv : rk;
-  const uint16_t* B = (kind ? BV : BK) + (int64_t)u * D * r;
-  uint16_t* T = BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0);
-  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
-  if (n0 >= r) return;
-  for (int e = threadIdx.x; e < 1024; e += 256) {
-    const int kk = e >> 5, nn = e & 31;
-    if (k0 + kk < D && n0 + nn < r) t[kk][nn] = B[(int64_t)(k0 + kk) * r + n0 + nn];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 1024; e += 256) {
-    const int nn = e >> 5, kk = e & 31;
-    if (k0 + kk < D && n0 + nn < r) T[(int64_t)(n0 + nn) * D + k0 + kk] = t[kk][nn];
-  }
+  if ((int)blockIdx.y * 32 >= r) return;
+  transpose_tile((kind ? BV : BK) + (int64_t)u * D * r,
+                 BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0), D, r, blockIdx.x * 32,
+                 blockIdx.y * 32);
 }
 
 // NS = D' / 64 steps when known at compile time (the loop then unrolls), 0 =
@@ -1271,8 +1264,9 @@ __global__ __launch_bounds__(256) void k_basis_t(const uint16_t* __restrict__ BK
 template <int R, int NS>
 __global__ __launch_bounds__(kProjWaves * 64) void k_project_mfma(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ BT, uint16_t* __restrict__ CK, uint16_t* __restrict__ CV,
-    int64_t L, int64_t Lmax, int D, int s, int kind_only, int rk, int rv) {
+    const uint16_t* __restrict__ BTK, int64_t sk, const uint16_t* __restrict__ BTV, int64_t sv,
+    uint16_t* __restrict__ CK, uint16_t* __restrict__ CV,
+    int64_t L, int64_t Lmax, int D, int s, int kind_only) {
   constexpr int NT = kProjWaves * 64;
   constexpr int NCB = R / 32;
   constexpr int SB = R * kProjK * 2;         // stage bytes
@@ -1285,7 +1279,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void k_project_mfma(
   const int kind = kind_only < 0 ? blockIdx.y & 1 : kind_only;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, mm = l & 31, kg = l >> 5;
   const uint16_t* X = (kind ? V : K) + (int64_t)u * L * D;
-  const uint16_t* Bt = BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0);
+  const uint16_t* Bt = kind ? BTV + (int64_t)u * sv : BTK + (int64_t)u * sk;
   uint16_t* C = (kind ? CV : CK) + (int64_t)u * Lmax * R;
   const int64_t row0 = s + (int64_t)blockIdx.x * kProjRows;
   const int nsteps = NS > 0 ? NS : D / kProjK;
@@ -1383,17 +1377,22 @@ __global__ __launch_bounds__(256) void k_project_f32(const float* __restrict__ K
   (kind ? CV : CK)[((int64_t)u * Lmax + row) * r + c] = (float)acc;
 }
 
+// B^K and B^V transposed: BTK / BTV, unit strides sk / sv (elements)
+struct BasisT {
+  const uint16_t *k, *v;
+  int64_t sk, sv;
+};
+
 template <int R>
 static hipError_t launch_project_mfma(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
-                                      const void* V, void* CK, void* CV, const uint16_t* BT,
+                                      const void* V, void* CK, void* CV, const BasisT& bt,
                                       int kind_only, hipStream_t st) {
   const int64_t nrow = L - d.s;
   const dim3 grid((unsigned)((nrow + kProjRows - 1) / kProjRows), kind_only < 0 ? 2 * U : U);
 #define KVLR_PROJ_LAUNCH(NS)                                                                     \
   hipLaunchKernelGGL((k_project_mfma<R, NS>), grid, dim3(kProjWaves * 64), 0, st,               \
-                     (const uint16_t*)K,                                                        \
-                     (const uint16_t*)V, BT, (uint16_t*)CK, (uint16_t*)CV, L,                   \
-                     Lmax, d.D, d.s, kind_only, d.r, d.rv)
+                     (const uint16_t*)K, (const uint16_t*)V, bt.k, bt.sk, bt.v, bt.sv,         \
+                     (uint16_t*)CK, (uint16_t*)CV, L, Lmax, d.D, d.s, kind_only)
   switch (d.D / kProjK) {
     case 8: KVLR_PROJ_LAUNCH(8); break;
     case 16: KVLR_PROJ_LAUNCH(16); break;
@@ -1405,12 +1404,12 @@ static hipError_t launch_project_mfma(const Dims& d, int U, int64_t L, int64_t L
 
 static hipError_t launch_project_rank(int R, const Dims& d, int U, int64_t L, int64_t Lmax,
                                       const void* K, const void* V, void* CK, void* CV,
-                                      const uint16_t* BT, int kind_only, hipStream_t st) {
+                                      const BasisT& bt, int kind_only, hipStream_t st) {
   switch (R) {
-    case 64: return launch_project_mfma<64>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
-    case 128: return launch_project_mfma<128>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
-    case 192: return launch_project_mfma<192>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
-    case 256: return launch_project_mfma<256>(d, U, L, Lmax, K, V, CK, CV, BT, kind_only, st);
+    case 64: return launch_project_mfma<64>(d, U, L, Lmax, K, V, CK, CV, bt, kind_only, st);
+    case 128: return launch_project_mfma<128>(d, U, L, Lmax, K, V, CK, CV, bt, kind_only, st);
+    case 192: return launch_project_mfma<192>(d, U, L, Lmax, K, V, CK, CV, bt, kind_only, st);
+    case 256: return launch_project_mfma<256>(d, U, L, Lmax, K, V, CK, CV, bt, kind_only, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1437,10 +1436,12 @@ hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const v
                        (const uint16_t*)BK, (const uint16_t*)BV, BT, d.D, d.r, d.rv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, BT, -1, st);
-    e = launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, BT, 0, st);
+    const BasisT bt = {BT, BT + (int64_t)d.r * d.D, (int64_t)(d.r + d.rv) * d.D,
+                       (int64_t)(d.r + d.rv) * d.D};
+    if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, bt, -1, st);
+    e = launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, bt, 0, st);
     if (e != hipSuccess) return e;
-    return launch_project_rank(d.rv, d, U, L, Lmax, K, V, CK, CV, BT, 1, st);
+    return launch_project_rank(d.rv, d, U, L, Lmax, K, V, CK, CV, bt, 1, st);
   }
   if (d.dtype == 0) {
     const int64_t tot = nrow * (d.r > d.rv ? d.r : d.rv);
@@ -1459,13 +1460,11 @@ hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const v
 // --------------------------------------------------------------------------
 // 6. exact sinks + recent ring, window / statistics reset, lens = {L, 0}
 // --------------------------------------------------------------------------
+// block `row` of unit u: [0, s + nrec) exact rows, then one block for the reset
 template <typename T>
-__global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
-                                                     const T* __restrict__ V, CachePtrs c,
-                                                     int64_t L, int D, int s, int nrec,
-                                                     int qw_per_unit) {
-  const int u = blockIdx.y;
-  const int row = blockIdx.x;  // [0, s + nrec) exact rows, then one block for the reset
+__device__ __forceinline__ void exact_reset_block(const T* __restrict__ K, const T* __restrict__ V,
+                                                  const CachePtrs& c, int64_t L, int D, int s, int nrec,
+                                                  int qw_per_unit, int u, int row) {
   T* sk = (T*)c.sink_k;
   T* sv = (T*)c.sink_v;
   T* rk = (T*)c.ring_k;
@@ -1497,12 +1496,18 @@ __global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
   }
 }
 
-// B^K transposed into the unit state (bf16): tile of 32 channels x 32 columns
-__global__ __launch_bounds__(256) void k_basis_kt_state(CachePtrs c, int D, int r) {
+template <typename T>
+__global__ __launch_bounds__(256) void k_exact_reset(const T* __restrict__ K,
+                                                     const T* __restrict__ V, CachePtrs c,
+                                                     int64_t L, int D, int s, int nrec,
+                                                     int qw_per_unit) {
+  exact_reset_block<T>(K, V, c, L, D, s, nrec, qw_per_unit, blockIdx.y, blockIdx.x);
+}
+
+// One 32 x 32 tile of B [D][r] transposed into T [r][D] (T[n][k] = B[k][n]).
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ B, uint16_t* __restrict__ T,
+                                               int D, int r, int k0, int n0) {
   __shared__ uint16_t t[32][33];
-  const int u = blockIdx.z, k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
-  const uint16_t* B = (const uint16_t*)c.basis_k + (int64_t)u * D * r;
-  uint16_t* T = bkt_of(c, u);
   for (int e = threadIdx.x; e < 1024; e += 256) {
     const int kk = e >> 5, nn = e & 31;
     if (k0 + kk < D && n0 + nn < r) t[kk][nn] = B[(int64_t)(k0 + kk) * r + n0 + nn];
@@ -1512,6 +1517,39 @@ __global__ __launch_bounds__(256) void k_basis_kt_state(CachePtrs c, int D, int 
     const int nn = e >> 5, kk = e & 31;
     if (k0 + kk < D && n0 + nn < r) T[(int64_t)(n0 + nn) * D + k0 + kk] = t[kk][nn];
   }
+}
+
+// Everything the bf16 MFMA projection call does besides the products, in one
+// launch (grid.y = unit): blocks [0, s + nrec] the exact rows and the window
+// reset, then the tiles of B^K transposed into the unit state (the decode
+// prologue's operand, which the projection reads too), then the tiles of B^V
+// transposed into the call's workspace.
+__global__ __launch_bounds__(256) void k_project_prep(const uint16_t* __restrict__ K,
+                                                      const uint16_t* __restrict__ V, CachePtrs c,
+                                                      uint16_t* __restrict__ BTV, int64_t L, int D,
+                                                      int s, int nrec, int qw_per_unit, int rk, int rv) {
+  const int u = blockIdx.y, nE = s + nrec + 1, nkx = (D + 31) / 32;
+  const int x = blockIdx.x;
+  if (x < nE) {
+    exact_reset_block<uint16_t>(K, V, c, L, D, s, nrec, qw_per_unit, u, x);
+    return;
+  }
+  const int tk = x - nE, ntk = nkx * ((rk + 31) / 32);
+  if (tk < ntk) {
+    transpose_tile((const uint16_t*)c.basis_k + (int64_t)u * D * rk, bkt_of(c, u), D, rk, (tk % nkx) * 32,
+                   (tk / nkx) * 32);
+  } else {
+    const int tv = tk - ntk;
+    transpose_tile((const uint16_t*)c.basis_v + (int64_t)u * D * rv, BTV + (int64_t)u * rv * D, D, rv,
+                   (tv % nkx) * 32, (tv / nkx) * 32);
+  }
+}
+
+// B^K transposed into the unit state (bf16): tile of 32 channels x 32 columns
+__global__ __launch_bounds__(256) void k_basis_kt_state(CachePtrs c, int D, int r) {
+  const int u = blockIdx.z;
+  transpose_tile((const uint16_t*)c.basis_k + (int64_t)u * D * r, bkt_of(c, u), D, r, blockIdx.x * 32,
+                 blockIdx.y * 32);
 }
 
 hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K, const void* V,
@@ -1528,6 +1566,27 @@ hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K
                        st, c, d.D, d.r);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_project_call(const Dims& d, int U, int64_t L, const void* K, const void* V,
+                               const CachePtrs& c, void* ws, hipStream_t st) {
+  if (!(project_mfma_ok(d) && L > d.s && c.state_stride % 2 == 0)) {
+    hipError_t e = launch_project(d, U, L, c.Lmax, K, V, c.basis_k, c.basis_v, c.coef_k, c.coef_v, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_exact_and_reset(d, U, L, K, V, c, st);
+  }
+  uint16_t* BTV = (uint16_t*)ws;
+  const int nkx = (d.D + 31) / 32;
+  const int nb = d.s + d.nrec + 1 + nkx * ((d.r + 31) / 32) + nkx * ((d.rv + 31) / 32);
+  hipLaunchKernelGGL(k_project_prep, dim3(nb, U), dim3(256), 0, st, (const uint16_t*)K,
+                     (const uint16_t*)V, c, BTV, L, d.D, d.s, d.nrec, d.W * d.G * d.r, d.r, d.rv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const BasisT bt = {bkt_of(c, 0), BTV, c.state_stride / 2, (int64_t)d.rv * d.D};
+  if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, c.Lmax, K, V, c.coef_k, c.coef_v, bt, -1, st);
+  e = launch_project_rank(d.r, d, U, L, c.Lmax, K, V, c.coef_k, c.coef_v, bt, 0, st);
+  if (e != hipSuccess) return e;
+  return launch_project_rank(d.rv, d, U, L, c.Lmax, K, V, c.coef_k, c.coef_v, bt, 1, st);
 }
 
 // --------------------------------------------------------------------------
