@@ -182,7 +182,9 @@ def test_probe_argument_errors(lib):
     assert lib.kvlr_probe_read(None, 1 << 20, 0, 256, 4, 16, None) == 1
     assert lib.kvlr_probe_read(16, 1000, 0, 256, 4, 16, None) == 1       # not a multiple of 16 KiB
     assert lib.kvlr_probe_read(16, 1 << 20, 0, 256, 3, 16, None) == 1    # unsupported depth
-    assert lib.kvlr_probe_read(16, 1 << 20, 3, 256, 4, 16, None) == 1    # unknown method
+    assert lib.kvlr_probe_read(16, 1 << 20, 5, 256, 4, 16, None) == 1    # unknown method
+    assert lib.kvlr_probe_read(16, 1 << 20, 3, 256, 96, 16, None) == 1   # row slabs: unsupported width
+    assert lib.kvlr_probe_read(16, 1 << 19, 4, 256, 64, 16, None) == 1   # row slabs: not whole 1 MiB tiles
     assert lib.kvlr_probe_read(16, 1 << 14, 2, 256, 4, 16, None) == 1    # LDS paths: whole 32 KiB stages
     assert lib.kvlr_probe_mfma(2, 10, 256, 16, None) == 1
     assert lib.kvlr_probe_mfma(0, 0, 256, 16, None) == 1
