@@ -208,8 +208,10 @@ int kvlr_build_bases_shared(const kvlr_config* cfg, int64_t n_layers, int64_t ba
  *             (positions [L - n_recent, L)), zeroes qwin and state, sets
  *             lens = {L, 0}.  Requires L <= cache->L_max.
  *   ws        device workspace, ws_bytes >= kvlr_workspace_bytes(PROJECT): the
- *             bases transposed for the MFMA kernel; the size is 0 (ws may be
- *             NULL) for fp32 storage or ranks not a multiple of 64. */
+ *             value basis transposed for the MFMA kernel (the key basis
+ *             transposed is kept in the cache's state, where decoding reads
+ *             it too); the size is 0 (ws may be NULL) for fp32 storage or
+ *             ranks not a multiple of 64. */
 int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L,
                  const void* K, const void* V, kvlr_cache* cache,
                  void* ws, size_t ws_bytes, void* stream);

@@ -230,10 +230,7 @@ hipError_t launch_extract(const Dims& d, int nmat, const S* A0, const S* A1, con
 // window's first layer, the other layers' matrices frozen
 hipError_t launch_gram_window_sum(int n, int n_layers, int batch, int depth, double* A, int* frozen,
                                   hipStream_t st);
-hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
-                          const void* V, const void* BK, const void* BV, void* CK, void* CV,
-                          void* ws, hipStream_t st);
-// workspace bytes of launch_project (transposed bases; 0 when not used)
+// workspace bytes of launch_project_call (B^V transposed; 0 when not used)
 size_t project_ws_bytes(const Dims& d, int64_t U);
 
 // decode

@@ -1246,19 +1246,6 @@ constexpr int kProjRing = 4;     // X fragment ring depth (steps)
 __device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ B, uint16_t* __restrict__ T,
                                                int D, int r, int k0, int n0);
 
-__global__ __launch_bounds__(256) void k_basis_t(const uint16_t* __restrict__ BK,
-                                                 const uint16_t* __restrict__ BV,
-                                                 uint16_t* __restrict__ BT, int D, int rk, int rv) {
-  // tile of 32 channels x 32 columns; per unit BT holds B^K^T [rk][D'] then
-  // B^V^T [rv][D'], BT[n][k] = B[k][n]
-  const int um = blockIdx.z, u = um >> 1, kind = um & 1;
-  const int r = kind ? rv : rk;
-  if ((int)blockIdx.y * 32 >= r) return;
-  transpose_tile((kind ? BV : BK) + (int64_t)u * D * r,
-                 BT + (int64_t)u * (rk + rv) * D + (kind ? (int64_t)rk * D : 0), D, r, blockIdx.x * 32,
-                 blockIdx.y * 32);
-}
-
 // NS = D' / 64 steps when known at compile time (the loop then unrolls), 0 =
 // runtime
 template <int R, int NS>
@@ -1421,28 +1408,15 @@ static bool project_mfma_ok(const Dims& d) {
 
 size_t project_ws_bytes(const Dims& d, int64_t U) {
   if (!project_mfma_ok(d)) return 0;
-  return (size_t)U * (d.r + d.rv) * d.D * sizeof(uint16_t);
+  return (size_t)U * d.rv * d.D * sizeof(uint16_t);  // B^V transposed
 }
 
-hipError_t launch_project(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
-                          const void* V, const void* BK, const void* BV, void* CK, void* CV,
-                          void* ws, hipStream_t st) {
+// the projection kernels without MFMA (fp32 storage, other ranks)
+static hipError_t launch_project_plain(const Dims& d, int U, int64_t L, int64_t Lmax, const void* K,
+                                       const void* V, const void* BK, const void* BV, void* CK,
+                                       void* CV, hipStream_t st) {
   const int64_t nrow = L - d.s;
   if (nrow <= 0) return hipSuccess;
-  if (project_mfma_ok(d)) {
-    uint16_t* BT = (uint16_t*)ws;
-    const int rmax = d.r > d.rv ? d.r : d.rv;
-    hipLaunchKernelGGL(k_basis_t, dim3((d.D + 31) / 32, rmax / 32, 2 * U), dim3(256), 0, st,
-                       (const uint16_t*)BK, (const uint16_t*)BV, BT, d.D, d.r, d.rv);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const BasisT bt = {BT, BT + (int64_t)d.r * d.D, (int64_t)(d.r + d.rv) * d.D,
-                       (int64_t)(d.r + d.rv) * d.D};
-    if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, bt, -1, st);
-    e = launch_project_rank(d.r, d, U, L, Lmax, K, V, CK, CV, bt, 0, st);
-    if (e != hipSuccess) return e;
-    return launch_project_rank(d.rv, d, U, L, Lmax, K, V, CK, CV, bt, 1, st);
-  }
   if (d.dtype == 0) {
     const int64_t tot = nrow * (d.r > d.rv ? d.r : d.rv);
     hipLaunchKernelGGL(k_project_f32, dim3((unsigned)((tot + 255) / 256), 2 * U), dim3(256), 0, st,
@@ -1570,8 +1544,8 @@ hipError_t launch_exact_and_reset(const Dims& d, int U, int64_t L, const void* K
 
 hipError_t launch_project_call(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                const CachePtrs& c, void* ws, hipStream_t st) {
-  if (!(project_mfma_ok(d) && L > d.s && c.state_stride % 2 == 0)) {
-    hipError_t e = launch_project(d, U, L, c.Lmax, K, V, c.basis_k, c.basis_v, c.coef_k, c.coef_v, ws, st);
+  if (!project_mfma_ok(d)) {
+    hipError_t e = launch_project_plain(d, U, L, c.Lmax, K, V, c.basis_k, c.basis_v, c.coef_k, c.coef_v, st);
     if (e != hipSuccess) return e;
     return launch_exact_and_reset(d, U, L, K, V, c, st);
   }
@@ -1581,8 +1555,8 @@ hipError_t launch_project_call(const Dims& d, int U, int64_t L, const void* K, c
   hipLaunchKernelGGL(k_project_prep, dim3(nb, U), dim3(256), 0, st, (const uint16_t*)K,
                      (const uint16_t*)V, c, BTV, L, d.D, d.s, d.nrec, d.W * d.G * d.r, d.r, d.rv);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const BasisT bt = {bkt_of(c, 0), BTV, c.state_stride / 2, (int64_t)d.rv * d.D};
+  if (e != hipSuccess || L <= d.s) return e;
+  const BasisT bt = {bkt_of(c, 0), BTV, c.state_stride / (int64_t)sizeof(uint16_t), (int64_t)d.rv * d.D};
   if (d.r == d.rv) return launch_project_rank(d.r, d, U, L, c.Lmax, K, V, c.coef_k, c.coef_v, bt, -1, st);
   e = launch_project_rank(d.r, d, U, L, c.Lmax, K, V, c.coef_k, c.coef_v, bt, 0, st);
   if (e != hipSuccess) return e;
