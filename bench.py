@@ -293,6 +293,20 @@ def run_prefill_leg():
     leg["library_gemm_ms"] = round(t_l, 4)
     leg["library_gemm_tflops"] = round(flops / (t_l / 1e3) / 1e12, 1)
     del outs
+    # For reference only: the vendor eigensolver (torch.linalg.eigh, fp32,
+    # both D' x D' Grams in one batched call) on Grams of the same size and
+    # spectrum (the last T' rows, each divided by its norm).  Not part of the
+    # path; compare with build_bases_ms, which the eigensolve dominates.
+    grams = []
+    for X in (prompts[0].K[0], prompts[0].V[0]):
+        S = X[w.L - w.n_sample:].float()
+        S = S / S.norm(dim=1, keepdim=True)
+        grams.append(S.T @ S)
+    grams = torch.stack(grams)
+    torch.linalg.eigh(grams)
+    t_e = _time_ms(lambda i: torch.linalg.eigh(grams), 2)
+    leg["library_eigh_ms"] = round(t_e, 3)
+    del grams, S
     del ws
     torch.cuda.empty_cache()
     # the full-prompt baseline: every non-sink token in the Gram
