@@ -791,6 +791,7 @@ template <> struct BjMfma<float> {
 // symmetric: the tile of (P2, P) is the transpose of that of (P, P2) and is
 // written from it), so np (np + 1) / 2 A tiles; V's tiles follow them
 __host__ __device__ __forceinline__ int bj_natile(int np) { return np * (np + 1) / 2; }
+constexpr int kBJTileIt = kBJ2 * kBJ2 / 2 / 256;  // column pairs of a tile per thread of a group
 
 template <typename T>
 __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restrict__ Vall,
@@ -859,11 +860,19 @@ __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restr
     T* A = Aall + (int64_t)m * n * n;
     T qa0[NKS], qa1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qi, qa0, qa1);  // A' = Q_P (rows of Q_P^T)
-    for (int e = tid; active && e < kBJ2 * kBJ2 / 2; e += 256) {  // pairs of columns, 16-byte loads
-      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
-      const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
-      X[i][j] = x.x;
-      X[i][j + 1] = x.y;
+    if (active) {  // pairs of columns, 8- or 16-byte loads, all in flight before the first store
+      typename Mf::pair xs[kBJTileIt];
+#pragma unroll
+      for (int it = 0; it < kBJTileIt; ++it) {
+        const int e = tid + 256 * it, i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+        xs[it] = *reinterpret_cast<const typename Mf::pair*>(A + (int64_t)bj_index(i, I, J) * n + bj_index(j, I2, J2));
+      }
+#pragma unroll
+      for (int it = 0; it < kBJTileIt; ++it) {
+        const int e = tid + 256 * it, i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+        X[i][j] = xs[it].x;
+        X[i][j + 1] = xs[it].y;
+      }
     }
     __syncthreads();
     gemm_ra(qa0, qa1);  // T = Q_P^T X
@@ -909,11 +918,19 @@ __device__ __forceinline__ void bjac_apply_tile(T* __restrict__ Aall, T* __restr
     T* V = Vall + (int64_t)m * n * n;
     T qb0[NKS], qb1[NKS];
     qfrag(Qm + (int64_t)P * kBJ2 * kBJ2, 32 * qj, qb0, qb1);  // B' = Q_P
-    for (int e = tid; active && e < kBJ2 * kBJ2 / 2; e += 256) {
-      const int i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
-      const typename Mf::pair x = *reinterpret_cast<const typename Mf::pair*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
-      X[j][i] = x.x;
-      X[j + 1][i] = x.y;
+    if (active) {
+      typename Mf::pair xs[kBJTileIt];
+#pragma unroll
+      for (int it = 0; it < kBJTileIt; ++it) {
+        const int e = tid + 256 * it, i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+        xs[it] = *reinterpret_cast<const typename Mf::pair*>(V + (int64_t)(kBJ2 * R + i) * n + bj_index(j, I, J));
+      }
+#pragma unroll
+      for (int it = 0; it < kBJTileIt; ++it) {
+        const int e = tid + 256 * it, i = e / (kBJ2 / 2), j = 2 * (e % (kBJ2 / 2));
+        X[j][i] = xs[it].x;
+        X[j + 1][i] = xs[it].y;
+      }
     }
     __syncthreads();
     gemm_rb(qb0, qb1);  // V[R, P] Q_P
