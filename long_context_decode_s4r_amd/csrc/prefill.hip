@@ -39,27 +39,38 @@ __global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ 
     p = L - n_r + (i - n_u);
   }
   const T* row = X + ((int64_t)u * L + p) * D;
+  // the row in registers (D' <= 4096: at most 16 elements per thread), every
+  // element requested before the first is used; the norm's sum in fp64, over
+  // the lanes of a wave, then the four waves
+  constexpr int NPT = 4096 / 256;
+  float xv[NPT];
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int j = threadIdx.x + 256 * c;
+    const float v = Elem<T>::ld(row, min(j, D - 1));  // in bounds; elements past D' are zeroed
+    xv[c] = j < D ? v : 0.f;
+  }
   double ss = 0.0;
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    double x = (double)Elem<T>::ld(row, j);
-    ss += x * x;
-  }
-  __shared__ double red[256];
-  red[threadIdx.x] = ss;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) ss += (double)xv[c] * (double)xv[c];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  __shared__ double red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const double nrm = sqrt(red[0]);
+  const double nrm = sqrt((red[0] + red[1]) + (red[2] + red[3]));
   T* out = S + ((int64_t)m * nT + i) * D;
   // x / ||x|| in fp64, rounded once to the storage type (a zero row stays 0)
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    const double x = nrm > 0.0 ? (double)Elem<T>::ld(row, j) / nrm : 0.0;
-    if constexpr (sizeof(T) == 2)
-      out[j] = d2bf(x);
-    else
-      out[j] = (float)x;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int j = threadIdx.x + 256 * c;
+    if (j < D) {
+      const double x = nrm > 0.0 ? (double)xv[c] / nrm : 0.0;
+      if constexpr (sizeof(T) == 2)
+        out[j] = d2bf(x);
+      else
+        out[j] = (float)x;
+    }
   }
 }
 
@@ -625,10 +636,21 @@ __device__ __forceinline__ void bjac_eig_block(const T* __restrict__ Aall, T* __
   __shared__ T Q[kBJ2][kBJ2 + 1];
   __shared__ T rc[NP], rs[NP], rt[NP];
   __shared__ uint8_t pi[kBJ][NP], qi[kBJ][NP];
-  for (int e = tid; e < kBJ2 * kBJ2; e += NT) {
-    const int i = e / kBJ2, j = e % kBJ2;
-    S[i][j] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I, J)];
-    Q[i][j] = i == j ? T(1) : T(0);
+  {  // S = A[I u J, I u J]: every load of the thread in flight before the first store
+    constexpr int NIT = kBJ2 * kBJ2 / NT;
+    static_assert(NIT * NT == kBJ2 * kBJ2, "S splits evenly over the threads");
+    T sv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e = tid + NT * it, i = e / kBJ2, j = e % kBJ2;
+      sv[it] = A[(int64_t)bj_index(i, I, J) * n + bj_index(j, I, J)];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int e = tid + NT * it, i = e / kBJ2, j = e % kBJ2;
+      S[i][j] = sv[it];
+      Q[i][j] = i == j ? T(1) : T(0);
+    }
   }
   const int nround = k < 0 ? kBJ - 1 : kBJ;
   for (int e = tid; e < kBJ * NP; e += NT) {
