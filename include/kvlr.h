@@ -26,6 +26,9 @@
  *   - Every pointer argument named as device memory is a device pointer owned
  *     by the caller; the library never allocates, frees or keeps pointers
  *     after a call returns.  Host-memory arguments are named as such.
+ *   - Device buffers start on a 16-byte boundary (hipMalloc and torch
+ *     allocations start on 256): the kernels move rows in 16-byte pieces.  A
+ *     call given a device pointer that does not returns KVLR_EINVAL.
  *   - A "unit" is one (layer, sequence) pair; every per-unit buffer is
  *     unit-major ([n_units][...]).  Where layers matter (depth-shared bases)
  *     units are layer-major: unit = layer * batch + sequence.

@@ -208,15 +208,24 @@ DecodeLayout decode_layout(const kvlr_config* c, int64_t U, int64_t Lmax) {
   return L;
 }
 
+// device buffers are read and written in 16-byte pieces
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 int check_cache(const kvlr_cache* cache, bool need_state, int n_sink) {
   if (!cache) return fail(KVLR_EINVAL, "cache is NULL");
   if (!cache->basis_k || !cache->basis_v) return fail(KVLR_EINVAL, "cache bases are NULL");
+  if (!al16(cache->basis_k) || !al16(cache->basis_v))
+    return fail(KVLR_EINVAL, "cache bases must start on a 16-byte boundary");
   if (need_state) {
     if (n_sink > 0 && (!cache->sink_k || !cache->sink_v))
       return fail(KVLR_EINVAL, "sink buffers are NULL");
     if (!cache->ring_k || !cache->ring_v || !cache->coef_k || !cache->coef_v || !cache->qwin ||
         !cache->lens || !cache->state)
       return fail(KVLR_EINVAL, "a cache buffer is NULL");
+    if (!al16(cache->sink_k) || !al16(cache->sink_v) || !al16(cache->ring_k) || !al16(cache->ring_v) ||
+        !al16(cache->coef_k) || !al16(cache->coef_v) || !al16(cache->qwin) || !al16(cache->lens) ||
+        !al16(cache->state))
+      return fail(KVLR_EINVAL, "cache buffers must start on a 16-byte boundary");
     if (cache->L_max < 1) return fail(KVLR_EINVAL, "cache L_max must be >= 1");
   }
   return KVLR_OK;
@@ -258,6 +267,8 @@ int check_decode_args(const kvlr_config* cfg, int64_t n_units, const void* q, co
   if (e) return e;
   if (n_units < 1 || n_units > 65535) return fail(KVLR_EINVAL, "n_units must be in [1, 65535]");
   if (!q || !k_new || !v_new || !out) return fail(KVLR_EINVAL, "q, k_new, v_new or out is NULL");
+  if (!al16(q) || !al16(k_new) || !al16(v_new) || !al16(out))
+    return fail(KVLR_EINVAL, "q, k_new, v_new and out must start on a 16-byte boundary");
   if ((e = check_cache(cache, true, cfg->n_sink))) return e;
   if (cache->L_max > INT32_MAX - 1) return fail(KVLR_EINVAL, "L_max too large");
   *dl = decode_layout(cfg, n_units, cache->L_max);
@@ -353,6 +364,7 @@ int build_bases_impl(const kvlr_config* cfg, int64_t n_layers, int64_t batch, in
   if (n_units < 1 || n_units > (1 << 20)) return fail(KVLR_EINVAL, "n_units out of range");
   if ((e = check_sample_fits(cfg, L))) return e;
   if (!K || !V) return fail(KVLR_EINVAL, "K or V is NULL");
+  if (!al16(K) || !al16(V) || !al16(ws)) return fail(KVLR_EINVAL, "K, V and ws must start on a 16-byte boundary");
   if ((e = check_cache(cache, false, cfg->n_sink))) return e;
   const BuildLayout bl = build_layout(cfg, n_units);
   if (!ws || ws_bytes < bl.total)
@@ -530,6 +542,7 @@ int kvlr_init_window(const kvlr_config* cfg, int64_t n_units, int32_t n_tail, co
   if (n_tail < 1 || n_tail > cfg->q_window)
     return fail(KVLR_EINVAL, "n_tail %d must be in [1, q_window = %d]", n_tail, cfg->q_window);
   if (!q_tail) return fail(KVLR_EINVAL, "q_tail is NULL");
+  if (!al16(q_tail) || !al16(ws)) return fail(KVLR_EINVAL, "q_tail and ws must start on a 16-byte boundary");
   if ((e = check_cache(cache, true, cfg->n_sink))) return e;
   if (cache->L_max > INT32_MAX - 1) return fail(KVLR_EINVAL, "L_max too large");
   const Dims d = dims_of(cfg);
@@ -548,6 +561,7 @@ int kvlr_project(const kvlr_config* cfg, int64_t n_units, int64_t L, const void*
   if (e) return e;
   if (n_units < 1 || n_units > (1 << 20)) return fail(KVLR_EINVAL, "n_units out of range");
   if (!K || !V) return fail(KVLR_EINVAL, "K or V is NULL");
+  if (!al16(K) || !al16(V) || !al16(ws)) return fail(KVLR_EINVAL, "K, V and ws must start on a 16-byte boundary");
   if ((e = check_cache(cache, true, cfg->n_sink))) return e;
   if (L < (int64_t)cfg->n_sink + cfg->n_recent)
     return fail(KVLR_EINVAL, "prompt length %lld < n_sink + n_recent", (long long)L);
@@ -572,6 +586,7 @@ int kvlr_decode_step(const kvlr_config* cfg, int64_t n_units, const void* q, con
   if (e) return e;
   if (!ws || ws_bytes < dl.total)
     return fail(KVLR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", dl.total, ws_bytes);
+  if (!al16(ws)) return fail(KVLR_EINVAL, "ws must start on a 16-byte boundary");
   return decode_launch(cfg, n_units, q, k_new, v_new, cache, out, topk_idx, scores, dl, ws,
                        (hipStream_t)stream);
 }

@@ -152,6 +152,31 @@ def test_calls_reject_bad_arguments_without_device(lib):
     assert st == kvlr.EINVAL and b"L_max" in lib.kvlr_last_error()
 
 
+def test_calls_reject_device_pointers_off_16_byte_boundaries(lib):
+    # the kernels move rows in 16-byte pieces; every case is refused before any launch
+    cfg = _cfg()
+    cache = kvlr.CacheStruct()
+    for name in kvlr.BUFFERS:
+        setattr(cache, name, 4096)
+    cache.L_max = 40000
+    big = 1 << 40
+    v = ctypes.c_void_p
+
+    def decode(q=16, out=16, ws=16):
+        return lib.kvlr_decode_step(ctypes.byref(cfg), 1, v(q), v(16), v(16), ctypes.byref(cache), v(out),
+                                    None, None, v(ws), big, None)
+    for st in (decode(q=24), decode(out=8), decode(ws=20)):
+        assert st == kvlr.EINVAL and b"16-byte" in lib.kvlr_last_error()
+    cache.coef_k = 4104
+    assert decode() == kvlr.EINVAL and b"16-byte" in lib.kvlr_last_error()
+    cache.coef_k = 4096
+    st = lib.kvlr_project(ctypes.byref(cfg), 1, 30000, v(8), v(16), ctypes.byref(cache), None, 0, None)
+    assert st == kvlr.EINVAL and b"16-byte" in lib.kvlr_last_error()
+    st = lib.kvlr_build_bases(ctypes.byref(cfg), 1, 32768, v(16), v(18), ctypes.byref(cache),
+                              None, None, None, v(16), big, None)
+    assert st == kvlr.EINVAL and b"16-byte" in lib.kvlr_last_error()
+
+
 def test_profile_read_bad_args(lib):
     assert lib.kvlr_profile_read(None, 5, None) == kvlr.EINVAL
 
