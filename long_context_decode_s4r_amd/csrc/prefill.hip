@@ -20,6 +20,13 @@ namespace kvlr {
 //    sample position p(i): the first n_u entries are evenly spaced over
 //    [s, L - n_r), the last n_r are the most recent prompt positions.
 // --------------------------------------------------------------------------
+__device__ __forceinline__ int64_t sample_pos(int i, int nT, int64_t L, int s, int rnum, int rden) {
+  const int64_t n_r = ((int64_t)rnum * nT) / rden;
+  const int64_t n_u = nT - n_r;
+  if (i < n_u) return s + ((int64_t)i * (L - n_r - s)) / n_u;
+  return L - n_r + (i - n_u);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ K,
                                                           const T* __restrict__ V,
@@ -29,15 +36,7 @@ __global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ 
   const int m = blockIdx.y;
   const int u = m >> 1;
   const T* X = (m & 1) ? V : K;
-  const int64_t n_r = ((int64_t)rnum * nT) / rden;
-  const int64_t n_u = nT - n_r;
-  int64_t p;
-  if (i < n_u) {
-    const int64_t span = L - n_r - s;
-    p = s + ((int64_t)i * span) / n_u;
-  } else {
-    p = L - n_r + (i - n_u);
-  }
+  const int64_t p = sample_pos(i, nT, L, s, rnum, rden);
   const T* row = X + ((int64_t)u * L + p) * D;
   // the row in registers (D' <= 4096: at most 16 elements per thread), every
   // element requested before the first is used; the norm's sum in fp64, over
@@ -74,8 +73,55 @@ __global__ __launch_bounds__(256) void k_sample_normalize(const T* __restrict__ 
   }
 }
 
+// bf16 rows with D' a multiple of 8: a wave per sampled row, moved in
+// 16-byte pieces (the rows then start on 16-byte boundaries), the norm's sum
+// in fp64 over the wave's lanes; the same quotient and rounding as above
+__global__ __launch_bounds__(256) void k_sample_normalize_v8(const uint16_t* __restrict__ K,
+                                                             const uint16_t* __restrict__ V,
+                                                             uint16_t* __restrict__ S, int64_t L, int D,
+                                                             int nT, int s, int rnum, int rden) {
+  const int l = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = blockIdx.y, u = m >> 1;
+  if (i >= nT) return;  // whole waves; no block barrier below
+  const uint16_t* row = ((m & 1) ? V : K) + ((int64_t)u * L + sample_pos(i, nT, L, s, rnum, rden)) * D;
+  constexpr int NC = 4096 / 512;  // pieces of 8 per lane (D' <= 4096)
+  const int n8 = D / 8;
+  u16x8 xv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)  // every piece requested first (past the row: its last piece again)
+    xv[c] = *reinterpret_cast<const u16x8*>(row + 8 * min(l + 64 * c, n8 - 1));
+  double ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (l + 64 * c < n8)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double x = bf2f(xv[c][e]);
+        ss += x * x;
+      }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const double nrm = sqrt(ss);
+  uint16_t* out = S + ((int64_t)m * nT + i) * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (l + 64 * c < n8) {
+      u16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = d2bf(nrm > 0.0 ? (double)bf2f(xv[c][e]) / nrm : 0.0);
+      *reinterpret_cast<u16x8*>(out + 8 * (l + 64 * c)) = o;
+    }
+}
+
 hipError_t launch_sample_normalize(const Dims& d, int U, int64_t L, const void* K, const void* V,
                                    void* S, hipStream_t st) {
+  if (d.dtype != 0 && d.D % 8 == 0) {
+    hipLaunchKernelGGL(k_sample_normalize_v8, dim3((d.T + 3) / 4, 2 * U), dim3(256), 0, st,
+                       (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)S, L, d.D, d.T, d.s, d.rnum,
+                       d.rden);
+    return hipGetLastError();
+  }
   dim3 grid(d.T, 2 * U);
   if (d.dtype == 0)
     hipLaunchKernelGGL(k_sample_normalize<float>, grid, dim3(256), 0, st, (const float*)K,
