@@ -215,9 +215,17 @@ __global__ __launch_bounds__(256) void k_sample_t(const uint16_t* __restrict__ S
   const int m = blockIdx.z, t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const uint16_t* Sm = S + (int64_t)m * nT * D;
   uint16_t* STm = ST + (int64_t)m * D * Tp;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;  // token t0 + r, channel c0 + c
-    t[r][c] = t0 + r < nT ? Sm[(int64_t)(t0 + r) * D + c0 + c] : (uint16_t)0;
+  uint16_t v[64 * 64 / 256];  // every load of the thread in flight before the first store
+#pragma unroll
+  for (int k = 0; k < 64 * 64 / 256; ++k) {
+    const int e = threadIdx.x + 256 * k, r = e >> 6, c = e & 63;  // token t0 + r, channel c0 + c
+    const uint16_t x = Sm[(int64_t)min(t0 + r, nT - 1) * D + c0 + c];  // rows past nT: zero
+    v[k] = t0 + r < nT ? x : (uint16_t)0;
+  }
+#pragma unroll
+  for (int k = 0; k < 64 * 64 / 256; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    t[e >> 6][e & 63] = v[k];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
@@ -323,7 +331,14 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const float* __restrict__ p
   if (ti == tj && x / kGT > x % kGT) return;  // a diagonal tile: its upper triangle, mirrored
   const float* pt = part + ((int64_t)m * npair + pr) * nsp * kGT * kGT + x;
   double sum = 0.0;
-  for (int s2 = 0; s2 < nsp; ++s2) sum += (double)pt[(int64_t)s2 * kGT * kGT];
+  for (int s0 = 0; s0 < nsp; s0 += 8) {  // eight stretches requested together, summed in order
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = pt[(int64_t)min(s0 + q, nsp - 1) * kGT * kGT];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (s0 + q < nsp) sum += (double)v[q];
+  }
   const int row = ti * kGT + x / kGT, col = tj * kGT + x % kGT;
   double* Am = A + (int64_t)m * D * D;
   Am[(int64_t)row * D + col] = sum;
